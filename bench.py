@@ -1,0 +1,204 @@
+"""Benchmark: one decode step of query-aware sparse paged attention on one GPU.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is the whole hot path for one batch of decode queries: page scoring
+against key min/max metadata (with the GQA group-mean query), top-k page
+selection, and sparse attention over the selected pages (split-KV partials
+and their online-softmax combine).  Page metadata is built once beforehand,
+as it is during prefill.
+
+Default workload: Quest-style GQA decode, batch 1, 32 q / 8 KV heads,
+head_dim 128, 32768-token context in 16-token pages, 256-page budget, bf16
+KV.  Inputs are seeded synthetic data already resident in HBM.  Each timed
+step reads a different replica of the KV pool and metadata (R copies at
+distinct addresses, R * per-step bytes > 1 GiB), so the 256 MB Infinity
+Cache cannot serve repeated steps.
+
+Output: one JSON line with queries/s, the per-step algorithmic HBM bytes and
+rate, a roofline entry for the dominant kernel call (timed with HIP events
+on its stream) and the CPU oracle's rate on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "sparse decode attn+select: queries/sec and achieved HBM GB/s (% of peak)"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="quest_gqa_32k", choices=["quest_gqa_32k"])
+    ap.add_argument("--replicas", type=int, default=0, help="0 = enough for > 1 GiB per rotation")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle sample")
+    ap.add_argument("--no-cpu", action="store_true")
+    return ap.parse_args()
+
+
+def algorithmic_bytes(bt, k_pages):
+    """Bytes a step must move from HBM: every valid page's metadata for the
+    scoring, plus K and V of the selected pages."""
+    elem = 2 if bt.dtype == "bf16" else 4
+    g = bt.page_size // bt.logical_page
+    units = bt.batch * bt.n_kv_heads
+    n_pages = min(bt.max_pages, -(-int(bt.seq_lens[0]) // bt.page_size))
+    meta = units * n_pages * g * 2 * bt.head_dim * elem
+    kv = units * min(k_pages, n_pages) * bt.page_size * bt.head_dim * 2 * elem
+    return meta, kv
+
+
+def cpu_baseline(bt, k_pages, budget_s):
+    """The oracle as it stands, single-threaded, on a sample of (sequence,
+    KV head) units of the same workload; scaled to queries/s."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+    units_total = bt.batch * bt.n_kv_heads
+    meta, has = oracle.page_meta(bt)          # prefill-time work, not timed
+    done, t_used = 0, 0.0
+    with threadpool_limits(1):
+        while t_used < budget_s and done < units_total:
+            b, h = divmod(done, bt.n_kv_heads)
+            t0 = time.perf_counter()
+            qbar = oracle.group_query(bt)[b, h]
+            n = oracle.n_pages(bt.seq_lens[b], bt.page_size)
+            row = np.full(bt.max_pages, -math.inf)
+            for j in range(n):
+                slot = bt.page_table[b][j]
+                row[j] = oracle.criticality(qbar, meta[slot, h, 0, 0], meta[slot, h, 0, 1])
+            ids = oracle.topk_pages(row, n, k_pages)
+            oracle.attend_pages(bt, b, h, ids)
+            t_used += time.perf_counter() - t0
+            done += 1
+    per_query = t_used / done * units_total   # all KV heads of one sequence = one query
+    return {"value": 1.0 / per_query, "unit": "queries/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} of {units_total} (sequence, KV head) units of one decode step, "
+                      f"{t_used:.1f} s single-threaded fp64 numpy; scaled to all units"}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(json.dumps({"error": "this build runs on exactly one GPU; multi-GPU sharding is described "
+                                   "in the design notes but not built", "n_gpus": a.gpus}))
+        sys.exit(2)
+    import torch
+    import workloads as wl
+    import dynamic_sparse_attention_page_amd as dsa
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    bt = wl.make(a.workload)
+    k_pages = bt.topk
+    meta_b, kv_b = algorithmic_bytes(bt, k_pages)
+    step_bytes = meta_b + kv_b
+    R = a.replicas or max(1, math.ceil((1 << 30) / step_bytes))
+
+    # --- resident inputs: R replicas of pool, tables and metadata ---------
+    q = dsa.upload_q(bt.q, bt.dtype)
+    base = dsa.PagedKV.from_numpy(bt.k, bt.v, bt.page_table, bt.seq_lens, bt.dtype)
+    S = base.num_slots
+    kbig = base.k.repeat(R, 1, 1, 1)
+    vbig = base.v.repeat(R, 1, 1, 1)
+    pts = torch.cat([base.page_table + r * S for r in range(R)], 0).contiguous()
+    pts = torch.where(base.page_table.repeat(R, 1) < 0, torch.full_like(pts, -1), pts).contiguous()
+    sls = base.seq_lens.repeat(R).contiguous()
+    allkv = dsa.PagedKV(kbig, vbig, pts, sls)
+    meta = dsa.page_meta_build(allkv, bt.logical_page)
+    del base
+    B = bt.batch
+    kvs = [dsa.PagedKV(kbig, vbig, pts[r * B:(r + 1) * B].contiguous(), sls[r * B:(r + 1) * B].contiguous())
+           for r in range(R)]
+    Hq, Hkv, D, N = bt.n_q_heads, bt.n_kv_heads, bt.head_dim, bt.max_pages
+    scores = torch.empty((B, Hkv, N), dtype=torch.float32, device=dev)
+    ids = torch.empty((B, Hkv, k_pages), dtype=torch.int32, device=dev)
+    counts = torch.empty((B, Hkv), dtype=torch.int32, device=dev)
+    O = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    l = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    m = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    ws = torch.empty(dsa.workspace_bytes(dsa.OP_SPARSE_DECODE_ATTN, kvs[0], Hq, k_pages), dtype=torch.uint8,
+                     device=dev)
+    scale = float(bt.scale)
+
+    def step(r, ev=None):
+        kv = kvs[r % R]
+        if ev is not None: ev[0].record()
+        dsa.page_score(q, kv, meta, bt.logical_page, scores=scores)
+        if ev is not None: ev[1].record()
+        dsa.page_select_topk(scores, kv.seq_lens, bt.page_size, k_pages, ids=ids, counts=counts)
+        if ev is not None: ev[2].record()
+        dsa.sparse_decode_attn(q, kv, ids, counts, scale=scale, out=(O, l, m), ws=ws)
+        if ev is not None: ev[3].record()
+
+    for i in range(a.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(a.steps):
+        step(i)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1)
+    ms_step = ms / a.steps
+
+    # --- per-call durations (events on the launch stream) -----------------
+    n_prof = max(20, min(a.steps, 200))
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_prof)]
+    for i in range(n_prof):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    per = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(3)] for e in evs]).mean(axis=0) * 1e3  # us
+    ops = {"page_score": (per[0], meta_b), "page_select_topk": (per[1], None),
+           "sparse_decode_attn": (per[2], kv_b)}
+    dom = max(ops, key=lambda k: ops[k][0])
+    if ops[dom][1] is None:       # top-k moves ~no bytes: report the larger HBM-bound call
+        dom = max(("page_score", "sparse_decode_attn"), key=lambda k: ops[k][0])
+    dur_us, dom_bytes = ops[dom]
+    achieved = dom_bytes / (dur_us * 1e-6) / 1e9
+
+    res = {
+        "metric": METRIC,
+        "value": B * a.steps / (ms * 1e-3),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": a.workload, "batch": B, "n_q_heads": Hq, "n_kv_heads": Hkv, "head_dim": D,
+                   "seq_len": int(bt.seq_lens[0]), "page_size": bt.page_size, "topk_pages": k_pages,
+                   "replicas": R, "parallelism": "single GPU"},
+        "step_bytes": step_bytes,
+        "step_GBps": step_bytes / (ms_step * 1e-3) / 1e9,
+        "step_hbm_frac": step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "op_us": {k: round(v[0], 3) for k, v in ops.items()},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "bytes_per_launch": dom_bytes, "avg_launch_us": dur_us},
+    }
+    if not a.no_cpu:
+        res["cpu_baseline"] = cpu_baseline(bt, k_pages, a.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

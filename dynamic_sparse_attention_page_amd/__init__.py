@@ -1,0 +1,308 @@
+"""Query-aware block-sparse paged decode attention for MI355X (gfx950).
+
+Thin ctypes binding of ``libdsa.so`` (declared in ``include/dsa.h``): each
+function below marshals torch tensors into the C ABI call of the same name
+and launches on the current HIP stream.  Every step of the computation runs
+in the library's HIP kernels; torch only provides device memory and streams.
+Importing this module fails loudly if the library has not been built
+(``python -m dynamic_sparse_attention_page_amd.build``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+__all__ = [
+    "DsaError", "PagedKV", "Streaming", "lib", "LIB_PATH",
+    "page_meta_build", "page_score", "page_select_topk", "page_select_progressive",
+    "sparse_decode_attn", "attn_repair", "ema_predict_update", "workspace_bytes",
+    "OP_SPARSE_DECODE_ATTN", "OP_ATTN_REPAIR", "EXPORTED",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsa.so")
+
+DSA_F32, DSA_BF16 = 0, 1
+OP_SPARSE_DECODE_ATTN, OP_ATTN_REPAIR = 1, 2
+EXPORTED = (
+    "dsa_status_str", "dsa_version", "dsa_page_meta_build", "dsa_page_score", "dsa_page_select_topk",
+    "dsa_page_select_progressive", "dsa_sparse_decode_attn", "dsa_attn_repair", "dsa_ema_predict_update",
+    "dsa_workspace_bytes",
+)
+
+
+class DsaError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn}: {lib.dsa_status_str(status).decode()} (status {status})")
+
+
+class _KV(ctypes.Structure):
+    _fields_ = [
+        ("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("dtype", ctypes.c_int32),
+        ("num_slots", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32), ("page_size", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("batch", ctypes.c_int32), ("max_pages", ctypes.c_int32),
+        ("page_table", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p),
+    ]
+
+
+class _Stream(ctypes.Structure):
+    _fields_ = [("kv_head_streaming", ctypes.c_void_p), ("sink", ctypes.c_int32), ("local", ctypes.c_int32)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m dynamic_sparse_attention_page_amd.build` (hipcc, gfx950)")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, F32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    KV, ST = ctypes.POINTER(_KV), ctypes.POINTER(_Stream)
+    sig = {
+        "dsa_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+        "dsa_version": (ctypes.c_int, []),
+        "dsa_page_meta_build": (ctypes.c_int, [KV, I32, P, I32, I32, P]),
+        "dsa_page_score": (ctypes.c_int, [P, I32, KV, P, I32, ST, P, P]),
+        "dsa_page_select_topk": (ctypes.c_int, [P, I32, I32, I32, P, I32, I32, ST, P, P, P]),
+        "dsa_page_select_progressive": (ctypes.c_int, [P, I32, KV, P, F32, I32, F32, P, P, P, P, P, P]),
+        "dsa_sparse_decode_attn": (ctypes.c_int, [P, I32, KV, P, P, I32, ST, F32, P, P, P, P, SZ, P]),
+        "dsa_attn_repair": (ctypes.c_int, [P, I32, KV, P, P, P, P, I32, F32, P, P, P, P, SZ, P]),
+        "dsa_ema_predict_update": (ctypes.c_int, [P, P, P, P, I64, F32, F32, F32, I32, P]),
+        "dsa_workspace_bytes": (SZ, [I32, KV, I32, I32]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype, fn.argtypes = res, args
+    return L
+
+
+lib = _load()
+
+
+# --------------------------------------------------------------------------
+# marshalling helpers
+# --------------------------------------------------------------------------
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise DsaError(fn, status)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return DSA_BF16
+    if t.dtype == torch.float32:
+        return DSA_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bf16 or fp32)")
+
+
+@dataclass
+class PagedKV:
+    """Device-resident paged KV pool: k/v [num_slots][n_kv_heads][page_size][head_dim]
+    (bf16 or fp32), page_table int32 [batch][max_pages], seq_lens int32 [batch]."""
+    k: torch.Tensor
+    v: torch.Tensor
+    page_table: torch.Tensor
+    seq_lens: torch.Tensor
+
+    def __post_init__(self):
+        for name in ("k", "v", "page_table", "seq_lens"):
+            if not getattr(self, name).is_contiguous():
+                raise ValueError(f"{name} must be contiguous")
+        if self.k.shape != self.v.shape or self.k.dtype != self.v.dtype or self.k.dim() != 4:
+            raise ValueError("k and v must be equal-shaped [slots][heads][page][dim] tensors")
+        if self.page_table.dtype != torch.int32 or self.seq_lens.dtype != torch.int32:
+            raise TypeError("page_table and seq_lens must be int32")
+
+    @property
+    def num_slots(self): return self.k.shape[0]
+
+    @property
+    def n_kv_heads(self): return self.k.shape[1]
+
+    @property
+    def page_size(self): return self.k.shape[2]
+
+    @property
+    def head_dim(self): return self.k.shape[3]
+
+    @property
+    def batch(self): return self.page_table.shape[0]
+
+    @property
+    def max_pages(self): return self.page_table.shape[1]
+
+    def c(self) -> _KV:
+        return _KV(self.k.data_ptr(), self.v.data_ptr(), _dtype_code(self.k), self.num_slots, self.n_kv_heads,
+                   self.page_size, self.head_dim, self.batch, self.max_pages, self.page_table.data_ptr(),
+                   self.seq_lens.data_ptr())
+
+    @staticmethod
+    def from_numpy(k, v, page_table, seq_lens, dtype: str, device="cuda") -> "PagedKV":
+        """Upload host arrays (bf16 as uint16 bit patterns, or float32)."""
+        def up(x):
+            if dtype == "bf16":
+                return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(device).view(torch.bfloat16)
+            return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(device)
+        return PagedKV(up(k), up(v), torch.from_numpy(np.ascontiguousarray(page_table, np.int32)).to(device),
+                       torch.from_numpy(np.ascontiguousarray(seq_lens, np.int32)).to(device))
+
+
+@dataclass
+class Streaming:
+    """Streaming (Lambda-mask) KV heads: flags[n_kv_heads], sink and local token counts."""
+    flags: np.ndarray
+    sink: int
+    local: int
+
+    def c(self):
+        self._buf = np.ascontiguousarray(self.flags, dtype=np.uint8)
+        return _Stream(self._buf.ctypes.data, int(self.sink), int(self.local))
+
+
+def _stream_arg(streaming: Streaming | None):
+    return None if streaming is None else ctypes.byref(streaming.c())
+
+
+def upload_q(q: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(q).view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(q, np.float32)).to(device)
+
+
+_ws_cache: dict = {}
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    key = (str(device),)
+    t = _ws_cache.get(key)
+    if t is None or t.numel() < nbytes:
+        t = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _ws_cache[key] = t
+    return t
+
+
+def _default_scale(head_dim: int) -> float:
+    return float(np.float32(1.0 / np.sqrt(head_dim)))
+
+
+# --------------------------------------------------------------------------
+# the C ABI, one function each
+# --------------------------------------------------------------------------
+def workspace_bytes(op: int, kv: PagedKV, n_q_heads: int, ids_stride: int) -> int:
+    return int(lib.dsa_workspace_bytes(op, ctypes.byref(kv.c()), n_q_heads, ids_stride))
+
+
+def page_meta_build(kv: PagedKV, logical_page: int | None = None, meta: torch.Tensor | None = None,
+                    first_page: int = 0, n_pages: int = -1) -> torch.Tensor:
+    """kmin/kmax per logical page: meta [num_slots][n_kv_heads][g][2][head_dim]."""
+    lp = logical_page or kv.page_size
+    g = kv.page_size // lp
+    if meta is None:
+        meta = torch.zeros((kv.num_slots, kv.n_kv_heads, g, 2, kv.head_dim), dtype=kv.k.dtype, device=kv.k.device)
+    _check("dsa_page_meta_build", lib.dsa_page_meta_build(ctypes.byref(kv.c()), lp, _ptr(meta), first_page,
+                                                          n_pages, _stream()))
+    return meta
+
+
+def page_score(q: torch.Tensor, kv: PagedKV, meta: torch.Tensor, logical_page: int | None = None,
+               streaming: Streaming | None = None, scores: torch.Tensor | None = None) -> torch.Tensor:
+    """Page criticality scores [batch][n_kv_heads][max_pages] (float32)."""
+    lp = logical_page or kv.page_size
+    if scores is None:
+        scores = torch.empty((kv.batch, kv.n_kv_heads, kv.max_pages), dtype=torch.float32, device=kv.k.device)
+    _check("dsa_page_score", lib.dsa_page_score(_ptr(q), q.shape[1], ctypes.byref(kv.c()), _ptr(meta), lp,
+                                                _stream_arg(streaming), _ptr(scores), _stream()))
+    return scores
+
+
+def page_select_topk(scores: torch.Tensor, seq_lens: torch.Tensor, page_size: int, k: int,
+                     streaming: Streaming | None = None, ids: torch.Tensor | None = None,
+                     counts: torch.Tensor | None = None):
+    """Top-k page ids [batch][n_kv_heads][k] (ascending, -1 padded) and counts."""
+    B, H, N = scores.shape
+    if ids is None:
+        ids = torch.empty((B, H, k), dtype=torch.int32, device=scores.device)
+    if counts is None:
+        counts = torch.empty((B, H), dtype=torch.int32, device=scores.device)
+    _check("dsa_page_select_topk", lib.dsa_page_select_topk(_ptr(scores), B, H, N, _ptr(seq_lens), page_size, k,
+                                                            _stream_arg(streaming), _ptr(ids), _ptr(counts),
+                                                            _stream()))
+    return ids, counts
+
+
+def page_select_progressive(q: torch.Tensor, kv: PagedKV, scores: torch.Tensor, threshold: float,
+                            stop_mode: int = 0, scale: float | None = None, out=None):
+    """PSA progressive selection + attention: (ids, counts, O, l, m)."""
+    B, Hq = q.shape[0], q.shape[1]
+    dev = kv.k.device
+    if out is None:
+        out = (torch.empty((kv.batch, kv.n_kv_heads, kv.max_pages), dtype=torch.int32, device=dev),
+               torch.empty((kv.batch, kv.n_kv_heads), dtype=torch.int32, device=dev),
+               torch.empty((B, Hq, kv.head_dim), dtype=torch.float32, device=dev),
+               torch.empty((B, Hq), dtype=torch.float32, device=dev),
+               torch.empty((B, Hq), dtype=torch.float32, device=dev))
+    ids, counts, O, l, m = out
+    sc = _default_scale(kv.head_dim) if scale is None else scale
+    _check("dsa_page_select_progressive", lib.dsa_page_select_progressive(
+        _ptr(q), Hq, ctypes.byref(kv.c()), _ptr(scores), float(threshold), stop_mode, sc, _ptr(ids), _ptr(counts),
+        _ptr(O), _ptr(l), _ptr(m), _stream()))
+    return ids, counts, O, l, m
+
+
+def sparse_decode_attn(q: torch.Tensor, kv: PagedKV, ids: torch.Tensor, counts: torch.Tensor,
+                       streaming: Streaming | None = None, scale: float | None = None, out=None,
+                       ws: torch.Tensor | None = None):
+    """Attention over the selected pages: (O [B][Hq][D], l [B][Hq], m [B][Hq])."""
+    B, Hq = q.shape[0], q.shape[1]
+    stride = ids.shape[-1]
+    dev = kv.k.device
+    if out is None:
+        out = (torch.empty((B, Hq, kv.head_dim), dtype=torch.float32, device=dev),
+               torch.empty((B, Hq), dtype=torch.float32, device=dev),
+               torch.empty((B, Hq), dtype=torch.float32, device=dev))
+    O, l, m = out
+    need = workspace_bytes(OP_SPARSE_DECODE_ATTN, kv, Hq, stride)
+    if ws is None:
+        ws = _workspace(need, dev)
+    sc = _default_scale(kv.head_dim) if scale is None else scale
+    _check("dsa_sparse_decode_attn", lib.dsa_sparse_decode_attn(
+        _ptr(q), Hq, ctypes.byref(kv.c()), _ptr(ids), _ptr(counts), stride, _stream_arg(streaming), sc,
+        _ptr(O), _ptr(l), _ptr(m), _ptr(ws), ws.numel() * ws.element_size(), _stream()))
+    return O, l, m
+
+
+def attn_repair(q: torch.Tensor, kv: PagedKV, a_ids, a_counts, p_ids, p_counts, O, l, m,
+                scale: float | None = None, ws: torch.Tensor | None = None):
+    """Fold attention over A \\ P into the speculative (O, l, m) in place."""
+    Hq = q.shape[1]
+    stride = a_ids.shape[-1]
+    if p_ids.shape[-1] != stride:
+        raise ValueError("a_ids and p_ids must share the same stride")
+    need = workspace_bytes(OP_ATTN_REPAIR, kv, Hq, stride)
+    if ws is None:
+        ws = _workspace(need, kv.k.device)
+    sc = _default_scale(kv.head_dim) if scale is None else scale
+    _check("dsa_attn_repair", lib.dsa_attn_repair(
+        _ptr(q), Hq, ctypes.byref(kv.c()), _ptr(a_ids), _ptr(a_counts), _ptr(p_ids), _ptr(p_counts), stride, sc,
+        _ptr(O), _ptr(l), _ptr(m), _ptr(ws), ws.numel() * ws.element_size(), _stream()))
+    return O, l, m
+
+
+def ema_predict_update(is_true, level: torch.Tensor, trend: torch.Tensor, pred: torch.Tensor,
+                       alpha: float, beta: float, gamma: float, init: bool = False):
+    """EMA predictor step over flat float32 arrays (is_true None = predict only)."""
+    n = level.numel()
+    _check("dsa_ema_predict_update", lib.dsa_ema_predict_update(
+        _ptr(is_true), _ptr(level), _ptr(trend), _ptr(pred), n, float(alpha), float(beta), float(gamma),
+        int(bool(init)), _stream()))
+    return pred

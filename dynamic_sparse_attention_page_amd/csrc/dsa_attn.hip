@@ -1,0 +1,614 @@
+// Sparse decode attention over selected pages, its split-KV combine, PRR's
+// repair and PSA's progressive selection.
+//
+// sparse_decode_attn (LServe, section 3.3: the decode kernel iterates only
+//   over the needed pages, loop step -> page index -> cache slot; PRR,
+//   section 3.3: the speculative kernel also emits l and m per head).
+//   Split-KV: a workgroup of 4 waves takes one (sequence, KV head, range of
+//   16-token tiles of the selected pages), computes all G q heads of the
+//   group from one read of each K/V tile, merges its waves through LDS and
+//   writes one unnormalised partial (o, l, m); the combine kernel folds the
+//   partials of a head with the online-softmax merge.
+// attn_repair (PRR, sections 3.3-3.4): an LDS bitmap of P filters A into the
+//   missing set M = A \ P, the split-KV path attends over M only, and the
+//   combine folds the caller's speculative (O, l, m) in as one more partial.
+// page_select_progressive (PSA, section 3.2, with the GPU-side weight check
+//   of section 3.3): one workgroup per (sequence, KV head) sorts the pages by
+//   score, computes the (o, l, m) of 16 pages at a time in parallel, then one
+//   thread walks them in rank order applying the stop test; no host sync.
+#include "dsa_attn_core.hpp"
+#include "dsa_host.hpp"
+
+namespace dsa {
+
+constexpr int kWgWaves = 4;
+
+// ============================================================ split-KV partial
+template <typename T, int D, int G>
+__global__ __launch_bounds__(256) void attn_partial_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const int32_t* __restrict__ page_table, const int32_t* __restrict__ seq_lens,
+    const int32_t* __restrict__ ids, const int32_t* __restrict__ counts, int ids_stride, int n_kv_heads, int P,
+    int max_pages, int num_slots, unsigned long long streaming, int sink, int local, float scale, float c,
+    int tiles_per_split, int n_splits, float* __restrict__ part_o, float* __restrict__ part_ml) {
+  using A = AttnWave<T, D, G>;
+  constexpr int CPL = A::CPL, DW = A::DW;
+  __shared__ __align__(16) float lds_rows[kWgWaves][A::LDS_FLOATS];
+  __shared__ __align__(16) float lds_o[kWgWaves][G][D];
+  __shared__ float lds_ml[kWgWaves][G][2];
+
+  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int unit = b * n_kv_heads + h;
+  const int TPP = P / 16;
+  int cnt = counts[unit];
+  cnt = cnt < 0 ? 0 : (cnt > ids_stride ? ids_stride : cnt);
+  const int n_tiles = cnt * TPP;
+  const int t_begin = split * tiles_per_split;
+  if (t_begin >= n_tiles) return;  // whole workgroup: the combine reads only active splits
+  const int t_end = min(n_tiles, t_begin + tiles_per_split);
+  const int L = clamp_len(seq_lens[b], max_pages, P);
+  const int np = (L + P - 1) / P;
+  const bool smask = (streaming >> h) & 1ull;
+
+  A st;
+  st.init(q + ((size_t)b * n_kv_heads * G + (size_t)h * G) * D, lds_rows[wave]);
+
+  // Two-level index (list entry -> page -> slot) for the pages of this split:
+  // lane x resolves entry first_entry + x once.
+  const int first_entry = t_begin / TPP;
+  const int n_entries = (t_end - 1) / TPP - first_entry + 1;
+  int my_page = -1, my_slot = -1;
+  if (lane < n_entries) {
+    const int pg = ids[(size_t)unit * ids_stride + first_entry + lane];
+    if (pg >= 0 && pg < np) {
+      const int sl = page_table[(size_t)b * max_pages + pg];
+      if (sl >= 0 && sl < num_slots) { my_page = pg; my_slot = sl; }
+    }
+  }
+  const size_t slot_stride = (size_t)n_kv_heads * P * D;
+  const size_t head_off = (size_t)h * P * D;
+
+  // Software pipeline: tile t+4 (this wave's next) is loaded while t is computed.
+  uint32_t ka[4][DW], va[4][DW], kb[4][DW], vb[4][DW];
+  int nva = 0, tka = 0, nvb = 0, tkb = 0;
+  auto fetch = [&](int t, uint32_t (&kd)[4][DW], uint32_t (&vd)[4][DW], int& nvalid, int& tok0) {
+    nvalid = 0;
+    tok0 = 0;
+    if (t >= t_end) return;
+    const int e = t / TPP - first_entry, tin = t % TPP;
+    const int page = __shfl(my_page, e, 64);
+    const int slot = __shfl(my_slot, e, 64);
+    if (slot < 0) return;
+    tok0 = page * P + tin * 16;
+    nvalid = min(16, L - tok0);
+    const size_t off = (size_t)slot * slot_stride + head_off + (size_t)tin * 16 * D;
+    A::load_tile(k + off, lane, kd);
+    A::load_tile(v + off, lane, vd);
+  };
+  int t = t_begin + wave;
+  fetch(t, ka, va, nva, tka);
+  while (t < t_end) {
+    fetch(t + kWgWaves, kb, vb, nvb, tkb);
+    if (nva > 0) st.tile(ka, va, nva, smask, tka, L, sink, local, c);
+    t += kWgWaves;
+    if (t >= t_end) break;
+    fetch(t + kWgWaves, ka, va, nva, tka);
+    if (nvb > 0) st.tile(kb, vb, nvb, smask, tkb, L, sink, local, c);
+    t += kWgWaves;
+  }
+
+  float m[G], l[G];
+  st.finish(m, l, c);
+  if (lane < 16) {
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+      for (int cc = 0; cc < CPL; ++cc) lds_o[wave][hh][lane * CPL + cc] = st.o[hh][cc];
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) { lds_ml[wave][hh][0] = m[hh]; lds_ml[wave][hh][1] = l[hh]; }
+  }
+  __syncthreads();
+  const size_t pbase = ((size_t)unit * n_splits + split) * G;
+  for (int idx = threadIdx.x; idx < G * D; idx += 256) {
+    const int hh = idx / D, cc = idx % D;
+    float mm = kNegInf;
+#pragma unroll
+    for (int w = 0; w < kWgWaves; ++w) mm = fmaxf(mm, lds_ml[w][hh][0]);
+    float acc = 0.0f, ls = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWgWaves; ++w) {
+      const float wt = exp2_diff(lds_ml[w][hh][0], mm, c);
+      acc = fmaf(lds_o[w][hh][cc], wt, acc);
+      ls = fmaf(lds_ml[w][hh][1], wt, ls);
+    }
+    part_o[(pbase + hh) * D + cc] = acc;
+    if (cc == 0) {
+      part_ml[(pbase + hh) * 2 + 0] = (mm == kNegInf) ? kNegInf : mm * scale;  // natural-log units
+      part_ml[(pbase + hh) * 2 + 1] = ls;
+    }
+  }
+}
+
+// ============================================================ combine
+// One wave per (sequence, q head): folds the active splits (and, for repair,
+// the caller's (O, l, m)) with the online-softmax merge; writes normalised O.
+template <int D>
+__global__ __launch_bounds__(64) void attn_combine_kernel(
+    const float* __restrict__ part_o, const float* __restrict__ part_ml, const int32_t* __restrict__ counts,
+    int ids_stride, int n_kv_heads, int G, int TPP, int tiles_per_split, int n_splits, int fold,
+    float* __restrict__ O, float* __restrict__ l, float* __restrict__ m) {
+  constexpr int CPT = D / 64;
+  const int hq = blockIdx.x, b = blockIdx.y;
+  const int Hq = n_kv_heads * G;
+  const int h = hq / G, g = hq % G;
+  const int unit = b * n_kv_heads + h;
+  const int lane = threadIdx.x;
+  int cnt = counts[unit];
+  cnt = cnt < 0 ? 0 : (cnt > ids_stride ? ids_stride : cnt);
+  const int active = min(n_splits, (cnt * TPP + tiles_per_split - 1) / tiles_per_split);
+  const size_t row = (size_t)b * Hq + hq;
+
+  float mm = kNegInf;
+  for (int s = 0; s < active; ++s) mm = fmaxf(mm, part_ml[(((size_t)unit * n_splits + s) * G + g) * 2]);
+  float m_in = kNegInf, l_in = 0.0f;
+  if (fold) {
+    m_in = m[row];
+    l_in = l[row];
+    if (!(l_in > 0.0f)) m_in = kNegInf;
+    mm = fmaxf(mm, m_in);
+  }
+  float acc[CPT], ls = 0.0f;
+#pragma unroll
+  for (int x = 0; x < CPT; ++x) acc[x] = 0.0f;
+  for (int s = 0; s < active; ++s) {
+    const size_t pi = ((size_t)unit * n_splits + s) * G + g;
+    const float ms = part_ml[pi * 2], lsp = part_ml[pi * 2 + 1];
+    const float wt = (mm == kNegInf || ms == kNegInf) ? 0.0f : expf(ms - mm);
+    ls = fmaf(lsp, wt, ls);
+#pragma unroll
+    for (int x = 0; x < CPT; ++x) acc[x] = fmaf(part_o[pi * D + lane + 64 * x], wt, acc[x]);
+  }
+  if (fold && m_in != kNegInf) {
+    const float wt = expf(m_in - mm) * l_in;
+    ls += wt;
+#pragma unroll
+    for (int x = 0; x < CPT; ++x) acc[x] = fmaf(O[row * D + lane + 64 * x], wt, acc[x]);
+  }
+  const float inv = ls > 0.0f ? 1.0f / ls : 0.0f;
+#pragma unroll
+  for (int x = 0; x < CPT; ++x) O[row * D + lane + 64 * x] = acc[x] * inv;
+  if (lane == 0) {
+    l[row] = ls;
+    m[row] = ls > 0.0f ? mm : kNegInf;
+  }
+}
+
+// ============================================================ repair filter
+// M = entries of A not in P, in A's order (one workgroup per unit).
+__global__ __launch_bounds__(256) void missing_set_kernel(const int32_t* __restrict__ a_ids,
+                                                          const int32_t* __restrict__ a_counts,
+                                                          const int32_t* __restrict__ p_ids,
+                                                          const int32_t* __restrict__ p_counts, int ids_stride,
+                                                          int max_pages, int32_t* __restrict__ m_ids,
+                                                          int32_t* __restrict__ m_counts) {
+  extern __shared__ uint32_t bits[];  // ceil(max_pages / 32) words
+  __shared__ int wave_tot[4];
+  const int unit = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nwords = (max_pages + 31) / 32;
+  for (int x = tid; x < nwords; x += 256) bits[x] = 0u;
+  __syncthreads();
+  int pc = p_counts[unit];
+  pc = pc < 0 ? 0 : (pc > ids_stride ? ids_stride : pc);
+  for (int x = tid; x < pc; x += 256) {
+    const int pg = p_ids[(size_t)unit * ids_stride + x];
+    if (pg >= 0 && pg < max_pages) atomicOr(&bits[pg >> 5], 1u << (pg & 31));
+  }
+  __syncthreads();
+  int ac = a_counts[unit];
+  ac = ac < 0 ? 0 : (ac > ids_stride ? ids_stride : ac);
+  int base = 0;
+  for (int x0 = 0; x0 < ac; x0 += 256) {
+    const int x = x0 + tid;
+    int pg = -1;
+    bool keep = false;
+    if (x < ac) {
+      pg = a_ids[(size_t)unit * ids_stride + x];
+      keep = pg >= 0 && pg < max_pages && !((bits[pg >> 5] >> (pg & 31)) & 1u);
+    }
+    const unsigned long long mask = __ballot(keep);
+    const int before = __popcll(mask & ((1ull << lane) - 1ull));
+    if (lane == 0) wave_tot[wave] = __popcll(mask);
+    __syncthreads();
+    int off = base;
+    for (int w = 0; w < wave; ++w) off += wave_tot[w];
+    if (keep) m_ids[(size_t)unit * ids_stride + off + before] = pg;
+    base += wave_tot[0] + wave_tot[1] + wave_tot[2] + wave_tot[3];
+    __syncthreads();
+  }
+  if (tid == 0) m_counts[unit] = base;
+}
+
+// ============================================================ PSA progressive
+constexpr int kPsaWaves = 16;
+
+__device__ __forceinline__ float log_add(float a, float b) {
+  const float mx = fmaxf(a, b), mn = fminf(a, b);
+  if (mn == kNegInf) return mx;
+  return mx + log1pf(expf(mn - mx));
+}
+
+template <typename T, int D, int G>
+__global__ __launch_bounds__(1024) void psa_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const int32_t* __restrict__ page_table, const int32_t* __restrict__ seq_lens, const float* __restrict__ scores,
+    int n_kv_heads, int P, int max_pages, int num_slots, int np2, int stop_mode, int never_stop, int always_stop,
+    float ln_odds, float scale, float c, int32_t* __restrict__ ids, int32_t* __restrict__ counts,
+    float* __restrict__ O, float* __restrict__ l, float* __restrict__ m) {
+  using A = AttnWave<T, D, G>;
+  constexpr int CPL = A::CPL, DW = A::DW;
+  extern __shared__ unsigned long long keys[];  // np2 composite keys
+  __shared__ __align__(16) float lds_rows[kPsaWaves][A::LDS_FLOATS];
+  __shared__ __align__(16) float ch_o[kPsaWaves][G][D];
+  __shared__ float ch_ml[kPsaWaves][G][2];
+  __shared__ int s_take, s_stop;
+  __shared__ float s_lnacc, s_lnmin;
+  __shared__ int s_left;
+
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int unit = b * n_kv_heads + h;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int L = clamp_len(seq_lens[b], max_pages, P);
+  const int np = (L + P - 1) / P;
+  const float* srow = scores + (size_t)unit * max_pages;
+
+  // 1. rank: composite key (score order key << 32 | ~index), sorted descending
+  for (int x = tid; x < np2; x += 1024) {
+    unsigned long long key = 0ull;
+    if (x < np) {
+      uint32_t u = __float_as_uint(srow[x]);
+      if (u == 0x80000000u) u = 0u;
+      u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+      key = ((unsigned long long)u << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)x);
+    }
+    keys[x] = key;
+  }
+  __syncthreads();
+  for (int size = 2; size <= np2; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = tid; i < np2 / 2; i += 1024) {
+        const int lo = 2 * stride * (i / stride) + (i % stride), hi = lo + stride;
+        const unsigned long long a = keys[lo], bq = keys[hi];
+        const bool desc = (lo & size) == 0;
+        if (desc ? (a < bq) : (a > bq)) { keys[lo] = bq; keys[hi] = a; }
+      }
+      __syncthreads();
+    }
+  }
+
+  // 2. progressive walk, 16 pages per chunk
+  A st;
+  st.init(q + ((size_t)b * n_kv_heads * G + (size_t)h * G) * D, lds_rows[wave]);
+  const size_t slot_stride = (size_t)n_kv_heads * P * D;
+  const size_t head_off = (size_t)h * P * D;
+  const int TPP = P / 16;
+  float acc_o = 0.0f, acc_l = 0.0f, acc_m = kNegInf;  // thread tid < G*D owns element tid
+  const int my_h = tid / D, my_c = tid % D;
+  if (tid == 0) { s_lnacc = kNegInf; s_lnmin = __builtin_huge_valf(); s_left = np; }
+  int visited = 0;
+  for (int cs = 0; cs < np; cs += kPsaWaves) {
+    const int pos = cs + wave;
+    st.reset();
+    float pm[G], pl[G];
+    if (pos < np) {
+      const int page = (int)(0xFFFFFFFFu - (uint32_t)(keys[pos] & 0xFFFFFFFFull));
+      const int slot = page_table[(size_t)b * max_pages + page];
+      if (slot >= 0 && slot < num_slots) {
+        for (int tin = 0; tin < TPP; ++tin) {
+          const int tok0 = page * P + tin * 16;
+          const int nvalid = min(16, L - tok0);
+          if (nvalid <= 0) break;
+          uint32_t kd[4][DW], vd[4][DW];
+          const size_t off = (size_t)slot * slot_stride + head_off + (size_t)tin * 16 * D;
+          A::load_tile(k + off, lane, kd);
+          A::load_tile(v + off, lane, vd);
+          st.tile(kd, vd, nvalid, false, tok0, L, 0, 0, c);
+        }
+      }
+    }
+    st.finish(pm, pl, c);
+    if (lane < 16) {
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+        for (int cc = 0; cc < CPL; ++cc) ch_o[wave][hh][lane * CPL + cc] = st.o[hh][cc];
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        ch_ml[wave][hh][0] = (pm[hh] == kNegInf) ? kNegInf : pm[hh] * scale;
+        ch_ml[wave][hh][1] = pl[hh];
+      }
+    }
+    __syncthreads();
+    // on-device stop test, in rank order
+    if (tid == 0) {
+      const int n_here = min(kPsaWaves, np - cs);
+      int take = n_here, stop = 0;
+      float lnacc = s_lnacc, lnmin = s_lnmin;
+      int left = s_left;
+      for (int w = 0; w < n_here; ++w) {
+        float ln_as = kNegInf;  // block mass summed over the group's heads, log domain
+        for (int hh = 0; hh < G; ++hh)
+          if (ch_ml[w][hh][1] > 0.0f) ln_as = log_add(ln_as, ch_ml[w][hh][0] + logf(ch_ml[w][hh][1]));
+        lnacc = log_add(lnacc, ln_as);
+        lnmin = fminf(lnmin, ln_as);
+        --left;
+        bool pass;
+        if (never_stop) pass = false;
+        else if (always_stop) pass = true;
+        else if (stop_mode == 0) pass = lnacc - lnmin >= ln_odds;
+        else pass = (left == 0) || (lnacc - (lnmin + logf((float)left)) >= ln_odds);
+        if (pass) { take = w + 1; stop = 1; break; }
+      }
+      s_take = take;
+      s_stop = stop;
+      s_lnacc = lnacc;
+      s_lnmin = lnmin;
+      s_left = left;
+    }
+    __syncthreads();
+    const int take = s_take;
+    if (tid < G * D) {
+      for (int w = 0; w < take; ++w) {
+        const float mw = ch_ml[w][my_h][0];
+        const float mn = fmaxf(acc_m, mw);
+        if (mn == kNegInf) continue;
+        const float a = (acc_m == kNegInf) ? 0.0f : expf(acc_m - mn);
+        const float bw = (mw == kNegInf) ? 0.0f : expf(mw - mn);
+        acc_o = acc_o * a + ch_o[w][my_h][my_c] * bw;
+        acc_l = acc_l * a + ch_ml[w][my_h][1] * bw;
+        acc_m = mn;
+      }
+    }
+    visited = cs + take;
+    const int stop = s_stop;
+    __syncthreads();
+    if (stop) break;
+  }
+
+  // 3. outputs
+  int32_t* irow = ids + (size_t)unit * max_pages;
+  for (int x = tid; x < max_pages; x += 1024)
+    irow[x] = (x < visited) ? (int)(0xFFFFFFFFu - (uint32_t)(keys[x] & 0xFFFFFFFFull)) : -1;
+  if (tid == 0) counts[unit] = visited;
+  if (tid < G * D) {
+    const size_t row = (size_t)b * n_kv_heads * G + (size_t)h * G + my_h;
+    O[row * D + my_c] = acc_l > 0.0f ? acc_o / acc_l : 0.0f;
+    if (my_c == 0) {
+      l[row] = acc_l;
+      m[row] = acc_l > 0.0f ? acc_m : kNegInf;
+    }
+  }
+}
+
+// ============================================================ host planning
+struct SplitPlan {
+  int tiles_per_split, n_splits, TPP;
+};
+
+// Tiles per workgroup so that ~1024 workgroups cover the largest possible
+// selection (counts live on the device, so the grid is sized for ids_stride).
+inline SplitPlan plan_splits(const dsa_kv* kv, int ids_stride) {
+  SplitPlan p;
+  p.TPP = kv->page_size / 16;
+  const long long tiles_max = (long long)ids_stride * p.TPP;
+  const long long total = tiles_max * kv->batch * kv->n_kv_heads;
+  long long tps = kWgWaves;
+  while (tps < 64 && total / tps > 1024) tps <<= 1;
+  p.tiles_per_split = (int)tps;
+  p.n_splits = (int)((tiles_max + tps - 1) / tps);
+  if (p.n_splits < 1) p.n_splits = 1;
+  return p;
+}
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+inline size_t partial_bytes(const dsa_kv* kv, int G, const SplitPlan& p) {
+  const size_t units = (size_t)kv->batch * kv->n_kv_heads;
+  return align256(units * p.n_splits * G * kv->head_dim * sizeof(float)) +
+         align256(units * p.n_splits * G * 2 * sizeof(float));
+}
+
+template <typename T, int D, int G>
+static int launch_attn_g(const void* q, const dsa_kv* kv, const int32_t* ids, const int32_t* counts,
+                         int ids_stride, uint64_t smask, int sink, int local, float scale, float* O, float* l,
+                         float* m, void* ws, int fold, hipStream_t st) {
+  const SplitPlan p = plan_splits(kv, ids_stride);
+  const size_t units = (size_t)kv->batch * kv->n_kv_heads;
+  float* part_o = (float*)ws;
+  float* part_ml = (float*)((char*)ws + align256(units * p.n_splits * G * D * sizeof(float)));
+  const float c = scale * kLog2e;
+  dim3 grid(p.n_splits, kv->n_kv_heads, kv->batch);
+  hipLaunchKernelGGL((attn_partial_kernel<T, D, G>), grid, dim3(256), 0, st, (const T*)q, (const T*)kv->k,
+                     (const T*)kv->v, kv->page_table, kv->seq_lens, ids, counts, ids_stride, kv->n_kv_heads,
+                     kv->page_size, kv->max_pages, kv->num_slots, (unsigned long long)smask, sink, local, scale, c,
+                     p.tiles_per_split, p.n_splits, part_o, part_ml);
+  int rc = launch_status();
+  if (rc) return rc;
+  hipLaunchKernelGGL((attn_combine_kernel<D>), dim3(kv->n_kv_heads * G, kv->batch), dim3(64), 0, st, part_o,
+                     part_ml, counts, ids_stride, kv->n_kv_heads, G, p.TPP, p.tiles_per_split, p.n_splits, fold, O,
+                     l, m);
+  return launch_status();
+}
+
+template <typename T, int D>
+static int launch_attn_d(const void* q, int G, const dsa_kv* kv, const int32_t* ids, const int32_t* counts,
+                         int ids_stride, uint64_t smask, int sink, int local, float scale, float* O, float* l,
+                         float* m, void* ws, int fold, hipStream_t st) {
+  switch (G) {
+    case 1: return launch_attn_g<T, D, 1>(q, kv, ids, counts, ids_stride, smask, sink, local, scale, O, l, m, ws, fold, st);
+    case 2: return launch_attn_g<T, D, 2>(q, kv, ids, counts, ids_stride, smask, sink, local, scale, O, l, m, ws, fold, st);
+    case 4: return launch_attn_g<T, D, 4>(q, kv, ids, counts, ids_stride, smask, sink, local, scale, O, l, m, ws, fold, st);
+    case 8: return launch_attn_g<T, D, 8>(q, kv, ids, counts, ids_stride, smask, sink, local, scale, O, l, m, ws, fold, st);
+    case 16: return launch_attn_g<T, D, 16>(q, kv, ids, counts, ids_stride, smask, sink, local, scale, O, l, m, ws, fold, st);
+  }
+  return DSA_ERR_UNSUPPORTED;
+}
+
+static int launch_attn(const void* q, int G, const dsa_kv* kv, const int32_t* ids, const int32_t* counts,
+                       int ids_stride, uint64_t smask, int sink, int local, float scale, float* O, float* l,
+                       float* m, void* ws, int fold, hipStream_t st) {
+  const bool bf = kv->dtype == DSA_BF16;
+  if (kv->head_dim == 128)
+    return bf ? launch_attn_d<uint16_t, 128>(q, G, kv, ids, counts, ids_stride, smask, sink, local, scale, O, l, m, ws, fold, st)
+              : launch_attn_d<float, 128>(q, G, kv, ids, counts, ids_stride, smask, sink, local, scale, O, l, m, ws, fold, st);
+  return bf ? launch_attn_d<uint16_t, 64>(q, G, kv, ids, counts, ids_stride, smask, sink, local, scale, O, l, m, ws, fold, st)
+            : launch_attn_d<float, 64>(q, G, kv, ids, counts, ids_stride, smask, sink, local, scale, O, l, m, ws, fold, st);
+}
+
+static int check_attn_common(const void* q, int n_q_heads, const dsa_kv* kv, float scale, int* G) {
+  int rc = check_kv(kv, true);
+  if (rc) return rc;
+  if (n_q_heads < 1 || n_q_heads % kv->n_kv_heads) return DSA_ERR_SHAPE;
+  *G = n_q_heads / kv->n_kv_heads;
+  if (!pow2_group(*G)) return DSA_ERR_UNSUPPORTED;
+  if (!(scale > 0.0f) || !(scale < __builtin_huge_valf())) return DSA_ERR_SHAPE;
+  if (kv->batch > 0) {
+    if (!q) return DSA_ERR_NULL;
+    if (!aligned16(q)) return DSA_ERR_ALIGN;
+  }
+  return DSA_OK;
+}
+
+static size_t repair_ids_bytes(const dsa_kv* kv, int ids_stride) {
+  const size_t units = (size_t)kv->batch * kv->n_kv_heads;
+  return align256(units * ids_stride * sizeof(int32_t)) + align256(units * sizeof(int32_t));
+}
+
+static int max_lds_per_block() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 65536;
+  if (!cached[dev]) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess || v <= 0) v = 65536;
+    cached[dev] = v;
+  }
+  return cached[dev];
+}
+
+template <typename T, int D, int G>
+static int launch_psa_g(const void* q, const dsa_kv* kv, const float* scores, float thr, int stop_mode, float scale,
+                        int32_t* ids, int32_t* counts, float* O, float* l, float* m, hipStream_t st) {
+  using A = AttnWave<T, D, G>;
+  int np2 = 2;
+  while (np2 < kv->max_pages) np2 <<= 1;
+  const size_t dyn = (size_t)np2 * sizeof(unsigned long long);
+  const size_t stat = sizeof(float) * (kPsaWaves * A::LDS_FLOATS + kPsaWaves * G * D + kPsaWaves * G * 2) + 64;
+  if ((int)(dyn + stat) > max_lds_per_block()) return DSA_ERR_UNSUPPORTED;
+  const int never_stop = thr >= 1.0f;
+  const int always_stop = thr <= 0.0f;
+  const float ln_odds = (never_stop || always_stop) ? 0.0f : (float)log((double)thr / (1.0 - (double)thr));
+  const float c = scale * kLog2e;
+  hipLaunchKernelGGL((psa_kernel<T, D, G>), dim3(kv->n_kv_heads, kv->batch), dim3(1024), dyn, st, (const T*)q,
+                     (const T*)kv->k, (const T*)kv->v, kv->page_table, kv->seq_lens, scores, kv->n_kv_heads,
+                     kv->page_size, kv->max_pages, kv->num_slots, np2, stop_mode, never_stop, always_stop, ln_odds,
+                     scale, c, ids, counts, O, l, m);
+  return launch_status();
+}
+
+template <typename T, int D>
+static int launch_psa_d(const void* q, int G, const dsa_kv* kv, const float* scores, float thr, int stop_mode,
+                        float scale, int32_t* ids, int32_t* counts, float* O, float* l, float* m, hipStream_t st) {
+  switch (G) {
+    case 1: return launch_psa_g<T, D, 1>(q, kv, scores, thr, stop_mode, scale, ids, counts, O, l, m, st);
+    case 2: return launch_psa_g<T, D, 2>(q, kv, scores, thr, stop_mode, scale, ids, counts, O, l, m, st);
+    case 4: return launch_psa_g<T, D, 4>(q, kv, scores, thr, stop_mode, scale, ids, counts, O, l, m, st);
+  }
+  return DSA_ERR_UNSUPPORTED;
+}
+
+}  // namespace dsa
+
+using namespace dsa;
+
+// ============================================================ C ABI
+extern "C" size_t dsa_workspace_bytes(int32_t op, const dsa_kv* kv, int32_t n_q_heads, int32_t ids_stride) {
+  if (check_kv(kv, false) != DSA_OK || n_q_heads < 1 || n_q_heads % kv->n_kv_heads || ids_stride < 1) return 0;
+  const int G = n_q_heads / kv->n_kv_heads;
+  if (!pow2_group(G)) return 0;
+  const SplitPlan p = plan_splits(kv, ids_stride);
+  const size_t part = partial_bytes(kv, G, p);
+  if (op == DSA_OP_SPARSE_DECODE_ATTN) return part;
+  if (op == DSA_OP_ATTN_REPAIR) return repair_ids_bytes(kv, ids_stride) + part;
+  return 0;
+}
+
+extern "C" int dsa_sparse_decode_attn(const void* q, int32_t n_q_heads, const dsa_kv* kv, const int32_t* ids,
+                                      const int32_t* counts, int32_t ids_stride, const dsa_stream_cfg* stream_cfg,
+                                      float scale, float* O, float* l, float* m, void* ws, size_t ws_bytes,
+                                      void* stream) {
+  int G = 0;
+  int rc = check_attn_common(q, n_q_heads, kv, scale, &G);
+  if (rc) return rc;
+  if (ids_stride < 1) return DSA_ERR_SHAPE;
+  uint64_t smask;
+  if ((rc = streaming_mask(stream_cfg, kv->n_kv_heads, &smask))) return rc;
+  if (kv->batch == 0) return DSA_OK;
+  if (!ids || !counts || !O || !l || !m) return DSA_ERR_NULL;
+  const size_t need = dsa_workspace_bytes(DSA_OP_SPARSE_DECODE_ATTN, kv, n_q_heads, ids_stride);
+  if (!ws || ws_bytes < need) return DSA_ERR_WORKSPACE;
+  if (!aligned16(ws)) return DSA_ERR_ALIGN;
+  const int sink = stream_cfg ? stream_cfg->sink : 0, local = stream_cfg ? stream_cfg->local : 0;
+  return launch_attn(q, G, kv, ids, counts, ids_stride, smask, sink, local, scale, O, l, m, ws, 0,
+                     (hipStream_t)stream);
+}
+
+extern "C" int dsa_attn_repair(const void* q, int32_t n_q_heads, const dsa_kv* kv, const int32_t* a_ids,
+                               const int32_t* a_counts, const int32_t* p_ids, const int32_t* p_counts,
+                               int32_t ids_stride, float scale, float* O, float* l, float* m, void* ws,
+                               size_t ws_bytes, void* stream) {
+  int G = 0;
+  int rc = check_attn_common(q, n_q_heads, kv, scale, &G);
+  if (rc) return rc;
+  if (ids_stride < 1) return DSA_ERR_SHAPE;
+  if (kv->batch == 0) return DSA_OK;
+  if (!a_ids || !a_counts || !p_ids || !p_counts || !O || !l || !m) return DSA_ERR_NULL;
+  const size_t need = dsa_workspace_bytes(DSA_OP_ATTN_REPAIR, kv, n_q_heads, ids_stride);
+  if (!ws || ws_bytes < need) return DSA_ERR_WORKSPACE;
+  if (!aligned16(ws)) return DSA_ERR_ALIGN;
+  const size_t lds = (size_t)((kv->max_pages + 31) / 32) * sizeof(uint32_t);
+  if ((int)lds + 64 > max_lds_per_block()) return DSA_ERR_UNSUPPORTED;
+  hipStream_t st = (hipStream_t)stream;
+  const size_t units = (size_t)kv->batch * kv->n_kv_heads;
+  int32_t* m_ids = (int32_t*)ws;
+  int32_t* m_counts = (int32_t*)((char*)ws + align256(units * ids_stride * sizeof(int32_t)));
+  void* part = (char*)ws + repair_ids_bytes(kv, ids_stride);
+  hipLaunchKernelGGL(missing_set_kernel, dim3((unsigned)units), dim3(256), lds, st, a_ids, a_counts, p_ids, p_counts,
+                     ids_stride, kv->max_pages, m_ids, m_counts);
+  if ((rc = launch_status())) return rc;
+  return launch_attn(q, G, kv, m_ids, m_counts, ids_stride, 0, 0, 0, scale, O, l, m, part, 1, st);
+}
+
+extern "C" int dsa_page_select_progressive(const void* q, int32_t n_q_heads, const dsa_kv* kv, const float* scores,
+                                           float threshold, int32_t stop_mode, float scale, int32_t* ids,
+                                           int32_t* counts, float* O, float* l, float* m, void* stream) {
+  int G = 0;
+  int rc = check_attn_common(q, n_q_heads, kv, scale, &G);
+  if (rc) return rc;
+  if (stop_mode != 0 && stop_mode != 1) return DSA_ERR_SHAPE;
+  if (threshold != threshold) return DSA_ERR_SHAPE;
+  if (kv->max_pages > 8192) return DSA_ERR_UNSUPPORTED;
+  if (kv->batch == 0) return DSA_OK;
+  if (!scores || !ids || !counts || !O || !l || !m) return DSA_ERR_NULL;
+  hipStream_t st = (hipStream_t)stream;
+  const bool bf = kv->dtype == DSA_BF16;
+  if (kv->head_dim == 128)
+    return bf ? launch_psa_d<uint16_t, 128>(q, G, kv, scores, threshold, stop_mode, scale, ids, counts, O, l, m, st)
+              : launch_psa_d<float, 128>(q, G, kv, scores, threshold, stop_mode, scale, ids, counts, O, l, m, st);
+  return bf ? launch_psa_d<uint16_t, 64>(q, G, kv, scores, threshold, stop_mode, scale, ids, counts, O, l, m, st)
+            : launch_psa_d<float, 64>(q, G, kv, scores, threshold, stop_mode, scale, ids, counts, O, l, m, st);
+}

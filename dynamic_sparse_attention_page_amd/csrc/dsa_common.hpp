@@ -1,0 +1,162 @@
+// Shared device helpers of libdsa (gfx950, wave64).
+//
+// Lane layout used by every kernel that streams keys, values or metadata:
+// a head_dim-long vector is covered by the 16 lanes of one DPP row, each
+// lane holding CPL = head_dim/16 consecutive channels (8 B or 16 B of bf16,
+// 16 B or 32 B of fp32).  A wave therefore holds 4 vectors per load, one per
+// row, and consecutive lanes read consecutive bytes, so every wave-wide load
+// is fully coalesced.  Reductions over a vector use DPP row operations; the
+// 4 rows are combined with cross-row shuffles only when needed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dsa.h"
+
+namespace dsa {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+// ---------------------------------------------------------------- bf16
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// a.lo*b.lo + a.hi*b.hi + c with bf16 pairs packed in dwords (v_dot2_f32_bf16):
+// the bf16 products are exact in fp32.
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c,
+                                         false);
+}
+
+// ---------------------------------------------------------------- DPP
+// Row = 16 consecutive lanes.  Partner patterns inside a row:
+constexpr int DPP_ROW_MIRROR = 0x140;       // j <- j ^ 15
+constexpr int DPP_ROW_HALF_MIRROR = 0x141;  // j <- j ^ 7
+constexpr int DPP_QUAD_XOR3 = 0x1B;         // j <- j ^ 3   (quad_perm 3,2,1,0)
+constexpr int DPP_QUAD_XOR1 = 0xB1;         // j <- j ^ 1   (quad_perm 1,0,3,2)
+constexpr int DPP_ROW_ROR4 = 0x124;         // j <- (j + 4) & 15
+constexpr int DPP_ROW_ROR8 = 0x128;         // j <- (j + 8) & 15
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+
+template <int N, int BIT, int CTRL>
+__device__ __forceinline__ void rs_step(float* v, int j) {
+  const bool up = (j >> BIT) & 1;
+#pragma unroll
+  for (int k = 0; k < N / 2; ++k) {
+    const float send = up ? v[k] : v[k + N / 2];
+    const float keep = up ? v[k + N / 2] : v[k];
+    v[k] = keep + dpp<CTRL>(send);
+  }
+}
+
+// Sum NV values over the 16 lanes of each row (reduce-scatter).  Afterwards
+// lane j of the row holds in v[0 .. max(1, NV/16)) the row totals of values
+//   NV >= 16: [j*NV/16, (j+1)*NV/16)      NV == 8: j>>1      NV == 4: j>>2
+// Each step pairs lanes that differ in one more bit (15, 7, 3, 1), keeping
+// the half of the values selected by that bit of j.
+template <int NV>
+__device__ __forceinline__ void row_sum_scatter(float (&v)[NV], int j) {
+  static_assert(NV == 4 || NV == 8 || NV == 16 || NV == 32 || NV == 64, "unsupported value count");
+  rs_step<NV, 3, DPP_ROW_MIRROR>(v, j);
+  if constexpr (NV / 2 >= 2) rs_step<NV / 2, 2, DPP_ROW_HALF_MIRROR>(v, j);
+  else v[0] += dpp<DPP_ROW_HALF_MIRROR>(v[0]);
+  if constexpr (NV / 4 >= 2) rs_step<NV / 4, 1, DPP_QUAD_XOR3>(v, j);
+  else v[0] += dpp<DPP_QUAD_XOR3>(v[0]);
+  if constexpr (NV / 8 >= 2) rs_step<NV / 8, 0, DPP_QUAD_XOR1>(v, j);
+  else v[0] += dpp<DPP_QUAD_XOR1>(v[0]);
+}
+
+// All-reduce over the 16 lanes of a row.
+__device__ __forceinline__ float row_sum(float x) {
+  x += dpp<DPP_ROW_MIRROR>(x);
+  x += dpp<DPP_ROW_HALF_MIRROR>(x);
+  x += dpp<DPP_QUAD_XOR3>(x);
+  x += dpp<DPP_QUAD_XOR1>(x);
+  return x;
+}
+
+// Max / sum over the 4 lanes j, j+4, j+8, j+12 of a row.
+__device__ __forceinline__ float ror_max4(float x) {
+  x = fmaxf(x, dpp<DPP_ROW_ROR4>(x));
+  return fmaxf(x, dpp<DPP_ROW_ROR8>(x));
+}
+__device__ __forceinline__ float ror_sum4(float x) {
+  x += dpp<DPP_ROW_ROR4>(x);
+  return x + dpp<DPP_ROW_ROR8>(x);
+}
+
+// Orders this wave's LDS writes before its later LDS reads (a wave's LDS
+// operations complete in issue order; this keeps the compiler from moving
+// them across the point).
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ float shfl_xor_f(float x, int mask) { return __shfl_xor(x, mask, 64); }
+
+// exp2 that maps the empty-set case (both operands -inf) to 0.
+__device__ __forceinline__ float exp2_diff(float a, float m, float c) {
+  return (m == kNegInf) ? 0.0f : exp2f((a - m) * c);
+}
+
+// ---------------------------------------------------------------- layout
+template <typename T, int D>
+struct Lay {
+  static constexpr int CPL = D / 16;                        // channels per lane
+  static constexpr int DW = CPL * (int)sizeof(T) / 4;       // dwords per lane per vector
+  static_assert(DW == 2 || DW == 4 || DW == 8, "unsupported layout");
+};
+
+// Load DW dwords at p (16-byte aligned when DW >= 4, 8-byte when DW == 2).
+template <int DW>
+__device__ __forceinline__ void load_dw(const void* p, uint32_t* out) {
+  if constexpr (DW == 2) {
+    const uint2 x = *reinterpret_cast<const uint2*>(p);
+    out[0] = x.x; out[1] = x.y;
+  } else {
+#pragma unroll
+    for (int u = 0; u < DW / 4; ++u) {
+      const uint4 x = reinterpret_cast<const uint4*>(p)[u];
+      out[4 * u + 0] = x.x; out[4 * u + 1] = x.y; out[4 * u + 2] = x.z; out[4 * u + 3] = x.w;
+    }
+  }
+}
+
+// Channel c (0 <= c < CPL) of a lane's raw dwords as float.
+template <typename T>
+__device__ __forceinline__ float chan(const uint32_t* w, int c) {
+  if constexpr (sizeof(T) == 2) return (c & 1) ? bf_hi(w[c >> 1]) : bf_lo(w[c >> 1]);
+  else return __uint_as_float(w[c]);
+}
+
+// Dot product of a lane's CPL channels of a key with the same channels of q
+// (stored the same way as the key).
+template <typename T, int DW>
+__device__ __forceinline__ float lane_dot(const uint32_t* k, const uint32_t* q) {
+  float acc = 0.0f;
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int x = 0; x < DW; ++x) acc = dot2_bf16(k[x], q[x], acc);
+  } else {
+#pragma unroll
+    for (int x = 0; x < DW; ++x) acc = fmaf(__uint_as_float(k[x]), __uint_as_float(q[x]), acc);
+  }
+  return acc;
+}
+
+__device__ __forceinline__ int clamp_len(int L, int max_pages, int P) {
+  const long long cap = (long long)max_pages * P;
+  return L < 0 ? 0 : (L > cap ? (int)cap : L);
+}
+
+}  // namespace dsa

@@ -1,0 +1,267 @@
+/*
+ * dsa.h -- C ABI of the MI355X (gfx950) query-aware block-sparse paged
+ * decode attention library, libdsa.so.
+ *
+ * One decode step of dynamic sparse attention over a paged KV cache:
+ *   page_meta_build        per-page key min/max metadata
+ *   page_score             page criticality against that metadata, with a
+ *                          group-mean query and a logical->physical max
+ *   page_select_topk       fixed top-k pages (ties to the lower index)
+ *   page_select_progressive  PSA's threshold-driven progressive selection,
+ *                          fused with the attention it drives
+ *   sparse_decode_attn     softmax attention over the selected pages only,
+ *                          emitting (O, l, m)
+ *   attn_repair            folds the pages of A that the speculative set P
+ *                          missed into a speculative (O, l, m)
+ *   ema_predict_update     PRR's EMA page-score predictor
+ *
+ * Sources, cited by page title and section:
+ *   [PSA]    "PSA: Progressive Sparse Attention -- Algorithm and System
+ *            Co-design for Efficient Attention in LLM Serving"
+ *   [LServe] "LServe: Efficient Long-sequence LLM Serving with Unified
+ *            Sparse Attention"
+ *   [PRR]    "Predict, Reuse, and Repair: Accelerating Dynamic Sparse
+ *            Attention for Long-Context LLM Decoding"
+ *
+ * Common conventions
+ * ------------------
+ * - Every data pointer is DEVICE memory owned by the caller unless marked
+ *   HOST.  The library never allocates, frees, copies to the host or
+ *   synchronises; each call only enqueues kernels on `stream` (a
+ *   hipStream_t; NULL = the default stream) and returns.  Buffers must stay
+ *   alive until that stream work completes.  Scratch memory comes from the
+ *   caller's workspace `ws` of `ws_bytes` bytes, sized by
+ *   dsa_workspace_bytes().
+ * - Return value: DSA_OK (0) or a negative DSA_ERR_* code.  All arguments
+ *   are validated on the host before anything is enqueued, so an error means
+ *   no work was queued.  Errors inside a kernel surface at the caller's next
+ *   synchronisation.  Calls on distinct streams with distinct outputs may
+ *   run concurrently; the library keeps no state between calls.
+ * - KV pool (struct dsa_kv): one block pool cut into equal slots shared by
+ *   all sequences ([PSA] section 3.4; [LServe] section 3.2.1):
+ *     k, v        [num_slots][n_kv_heads][page_size][head_dim], dtype
+ *     page_table  int32 [batch][max_pages]: slot of page j of a sequence,
+ *                 i.e. of its tokens [j*page_size, (j+1)*page_size)
+ *     seq_lens    int32 [batch]: tokens of each sequence
+ *   Page j of sequence b is valid when j*page_size < seq_lens[b] and
+ *   j < max_pages (longer sequences are clamped to max_pages pages).  Rows of
+ *   a valid page past seq_lens[b] are never read.  A page-table entry outside
+ *   [0, num_slots) makes that page hold no tokens; entries of invalid pages
+ *   are never read.
+ * - Supported shapes: dtype DSA_BF16 or DSA_F32; head_dim 64 or 128;
+ *   page_size 16, 32 or 64; logical_page a multiple of 16 that divides
+ *   page_size; n_q_heads = G * n_kv_heads with G in {1, 2, 4, 8, 16};
+ *   q head h belongs to KV head h / G.  k, v, q and meta 16-byte aligned.
+ * - Selected page ids are page indices j of the sequence (page-table
+ *   columns), never slots.
+ * - Logits are scale * q.k with the caller's scale (> 0; normally
+ *   1/sqrt(head_dim) rounded to float).  Attention outputs, per q head:
+ *   m = max logit, l = sum exp(logit - m), O = sum exp(logit - m) v / l; an
+ *   empty page set gives O = 0, l = 0, m = -inf.  Accumulation is fp32.
+ */
+#ifndef DSA_H
+#define DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  DSA_OK = 0,
+  DSA_ERR_NULL = -1,        /* a required pointer is NULL                    */
+  DSA_ERR_SHAPE = -2,       /* a size or count is out of range / inconsistent */
+  DSA_ERR_DTYPE = -3,       /* unknown dtype                                  */
+  DSA_ERR_UNSUPPORTED = -4, /* valid but not built (head_dim, group, ...)     */
+  DSA_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than required        */
+  DSA_ERR_ALIGN = -6,       /* pointer not 16-byte aligned                    */
+  DSA_ERR_LAUNCH = -7       /* the HIP runtime rejected a launch              */
+};
+
+enum { DSA_F32 = 0, DSA_BF16 = 1 };
+
+typedef struct dsa_kv {
+  const void *k;               /* device [num_slots][n_kv_heads][page_size][head_dim] */
+  const void *v;               /* device, same layout as k                     */
+  int32_t dtype;               /* DSA_F32 | DSA_BF16 (also the dtype of q and meta) */
+  int32_t num_slots;
+  int32_t n_kv_heads;
+  int32_t page_size;
+  int32_t head_dim;
+  int32_t batch;
+  int32_t max_pages;
+  const int32_t *page_table;   /* device int32 [batch][max_pages]              */
+  const int32_t *seq_lens;     /* device int32 [batch]                         */
+} dsa_kv;
+
+/* Streaming heads ([LServe] section 4.1): a KV head flagged here attends
+ * only to its sink tokens [0, sink) and local tokens [L - local, L). */
+typedef struct dsa_stream_cfg {
+  const uint8_t *kv_head_streaming; /* HOST [n_kv_heads], nonzero = streaming; at most 64 heads */
+  int32_t sink;
+  int32_t local;
+} dsa_stream_cfg;
+
+/* Operation ids for dsa_workspace_bytes(). */
+enum { DSA_OP_SPARSE_DECODE_ATTN = 1, DSA_OP_ATTN_REPAIR = 2 };
+
+/* Human-readable name of a status code (static storage). */
+const char *dsa_status_str(int status);
+
+/* Library version, as major*10000 + minor*100 + patch. */
+int dsa_version(void);
+
+/*
+ * dsa_page_meta_build -- per-page key metadata ([LServe] section 4.2 and
+ * Figure 7: kmin/kmax vectors attached to each physical page, built during
+ * prefill and earlier decode steps; [PSA] section 3.1: block metadata kept
+ * in GPU memory).
+ *
+ * For pages j in [first_page, first_page + n_pages) of every sequence
+ * (n_pages < 0: all valid pages), for every KV head and every logical
+ * sub-page s (g = page_size / logical_page of them), writes the per-channel
+ * minimum and maximum of the keys of the sub-page's valid tokens:
+ *   meta[slot][h][s][0][c] = min_t k[t][c],  meta[slot][h][s][1][c] = max_t k[t][c]
+ * meta: device [num_slots][n_kv_heads][g][2][head_dim] in kv->dtype (exact:
+ * the min/max of stored values).  A sub-page with no valid token is written
+ * as zeros (page_score never reads it).  Slots of pages outside the range
+ * are left untouched.
+ */
+int dsa_page_meta_build(const dsa_kv *kv, int32_t logical_page, void *meta,
+                        int32_t first_page, int32_t n_pages, void *stream);
+
+/*
+ * dsa_page_score -- page criticality ([LServe] section 4.2, importance of a
+ * logical page and max-reduction to the physical page; [PSA] section 3.2,
+ * the CS step; [PRR] section 5, the Quest GQA extension's representative
+ * query).
+ *
+ * Per (sequence b, KV head h): qbar = mean of the G q heads of h (fp32);
+ * for each valid logical sub-page s of page j:
+ *   S_s = sum_c max(qbar[c] * kmax_s[c], qbar[c] * kmin_s[c])
+ * and scores[b][h][j] = max over the page's valid sub-pages of S_s.
+ * Invalid pages and every page of a streaming head score -inf.
+ * q: device [batch][n_q_heads][head_dim] in kv->dtype.  meta as written by
+ * dsa_page_meta_build with the same logical_page.  stream_cfg may be NULL.
+ * scores: device float [batch][n_kv_heads][max_pages].
+ */
+int dsa_page_score(const void *q, int32_t n_q_heads, const dsa_kv *kv, const void *meta,
+                   int32_t logical_page, const dsa_stream_cfg *stream_cfg, float *scores,
+                   void *stream);
+
+/*
+ * dsa_page_select_topk -- fixed top-k page selection ([PSA] section 2.2;
+ * [PRR] section 2, the selection stage of a DSA step).
+ *
+ * Per (b, h) row of scores[batch][n_kv_heads][max_pages] (float, device),
+ * considers the valid pages j < ceil(seq_lens[b] / page_size) (clamped to
+ * max_pages) and keeps the min(k, valid) highest scores; equal scores are
+ * kept in favour of the lower page index; -0.0 equals +0.0.  Writes the kept
+ * ids in ascending order to ids[b][h][0..count) and -1 to the rest of
+ * ids[b][h][0..k); counts[b][h] = count.  For a streaming head (stream_cfg
+ * non-NULL and flagged) the ids are instead the pages holding a sink token
+ * or a local token, ascending; the call fails with DSA_ERR_SHAPE if that
+ * list could exceed k.  NaN scores are not supported.
+ * ids: device int32 [batch][n_kv_heads][k]; counts: device int32 [batch][n_kv_heads].
+ * Requires 1 <= k and max_pages <= 65536.
+ */
+int dsa_page_select_topk(const float *scores, int32_t batch, int32_t n_kv_heads,
+                         int32_t max_pages, const int32_t *seq_lens, int32_t page_size,
+                         int32_t k, const dsa_stream_cfg *stream_cfg, int32_t *ids,
+                         int32_t *counts, void *stream);
+
+/*
+ * dsa_page_select_progressive -- PSA progressive sparse attention ([PSA]
+ * section 3.2, the PSAttention algorithm; section 3.3, the on-GPU check of
+ * the accumulated weight; section 5, on-chip aggregation of block weights).
+ *
+ * Per (b, KV head h): ranks the valid pages by descending score (ties: lower
+ * index), then visits them in rank order, computing each page's attention
+ * for the G q heads and its block weight AS = sum over the page's tokens and
+ * the G heads of exp(logit).  After each page: AS_acc += AS,
+ * AS_min = min(AS_min, AS), and the walk stops when
+ *   stop_mode 0:  AS_acc / (AS_acc + AS_min) >= threshold            (printed rule)
+ *   stop_mode 1:  AS_acc / (AS_acc + N_left * AS_min) >= threshold   (N_left = pages not visited)
+ * threshold >= 1 never stops early; if the test never passes, every valid
+ * page is visited.  The test is evaluated on the device in the log domain
+ * (no host round trip).  Outputs: ids[b][h][0..n) the visited pages in rank
+ * order, -1 after; counts[b][h] = n; O/l/m for the G q heads = attention
+ * over the visited pages.
+ * scores as from dsa_page_score; ids: device int32 [batch][n_kv_heads][max_pages];
+ * O: device float [batch][n_q_heads][head_dim]; l, m: device float [batch][n_q_heads].
+ * Requires max_pages <= 8192.  Streaming heads are not supported here.
+ */
+int dsa_page_select_progressive(const void *q, int32_t n_q_heads, const dsa_kv *kv,
+                                const float *scores, float threshold, int32_t stop_mode,
+                                float scale, int32_t *ids, int32_t *counts, float *O, float *l,
+                                float *m, void *stream);
+
+/*
+ * dsa_sparse_decode_attn -- attention over the selected pages only ([LServe]
+ * section 3.3: the decode kernel loops only over the needed pages through a
+ * two-level index, step -> page -> cache slot; [PRR] section 3.3: the
+ * speculative kernel also writes the softmax denominator l and the running
+ * max m per head).
+ *
+ * Per (b, KV head h): the pages ids[b][h][0..counts[b][h]) (each a valid
+ * page index; duplicates are attended twice), through page_table to slots.
+ * For a streaming head only sink and local tokens of those pages count.
+ * Writes O[b][hq][:], l[b][hq], m[b][hq] for the G q heads hq of h.
+ * ids: device int32 [batch][n_kv_heads][ids_stride], counts <= ids_stride.
+ * ws: device scratch of dsa_workspace_bytes(DSA_OP_SPARSE_DECODE_ATTN, ...).
+ */
+int dsa_sparse_decode_attn(const void *q, int32_t n_q_heads, const dsa_kv *kv,
+                           const int32_t *ids, const int32_t *counts, int32_t ids_stride,
+                           const dsa_stream_cfg *stream_cfg, float scale, float *O, float *l,
+                           float *m, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * dsa_attn_repair -- PRR incremental repair ([PRR] section 3.3, the repair
+ * kernel's online-softmax recurrence; section 3.4, the missing set M = A\P).
+ *
+ * On entry O, l, m hold a speculative result over page set P (e.g. from
+ * dsa_sparse_decode_attn over p_ids).  Per (b, KV head h) the call forms
+ * M = the entries of a_ids[b][h][0..a_counts) not among
+ * p_ids[b][h][0..p_counts), in a_ids order, attends over M only, and folds
+ * that into (O, l, m) in place:
+ *   m' = max(m, m~), l' = e^(m-m') l + e^(m~-m') l~,
+ *   O' = (e^(m-m') l O + e^(m~-m') l~ O~) / l'
+ * so the result is attention over P u A.  Work and traffic scale with |M|.
+ * a_ids, p_ids: device int32 [batch][n_kv_heads][ids_stride] with page ids
+ * < max_pages.  Streaming heads are not supported here.
+ * ws: device scratch of dsa_workspace_bytes(DSA_OP_ATTN_REPAIR, ...).
+ */
+int dsa_attn_repair(const void *q, int32_t n_q_heads, const dsa_kv *kv, const int32_t *a_ids,
+                    const int32_t *a_counts, const int32_t *p_ids, const int32_t *p_counts,
+                    int32_t ids_stride, float scale, float *O, float *l, float *m, void *ws,
+                    size_t ws_bytes, void *stream);
+
+/*
+ * dsa_ema_predict_update -- PRR EMA predictor ([PRR] section 3.1).
+ *
+ * Elementwise over n blocks (float, device):
+ *   is_true == NULL:  pred = level + gamma * trend                (predict only)
+ *   init != 0:        level = IS, trend = 0, pred = IS            (first observation)
+ *   otherwise:        trend' = beta*(IS - level) + (1-beta)*trend,
+ *                     level' = alpha*IS + (1-alpha)*level   (both read the old level),
+ *                     pred = level' + gamma * trend'        (the next step's prediction)
+ * level and trend are updated in place; pred may not alias them.
+ */
+int dsa_ema_predict_update(const float *is_true, float *level, float *trend, float *pred,
+                           int64_t n, float alpha, float beta, float gamma, int32_t init,
+                           void *stream);
+
+/*
+ * dsa_workspace_bytes -- scratch needed by dsa_sparse_decode_attn (op
+ * DSA_OP_SPARSE_DECODE_ATTN) or dsa_attn_repair (DSA_OP_ATTN_REPAIR) for
+ * this pool, n_q_heads and ids_stride.  Returns 0 for invalid arguments.
+ */
+size_t dsa_workspace_bytes(int32_t op, const dsa_kv *kv, int32_t n_q_heads, int32_t ids_stride);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_H */

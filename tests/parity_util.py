@@ -1,0 +1,73 @@
+"""Helpers shared by the GPU parity tests: upload a generated batch, run the
+HIP path through the C ABI, and the parity rules that compare it with the
+oracle."""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+
+# Output tolerances (max-abs on O; m absolute; l relative).
+TOL = {
+    "bf16": dict(O=2e-3, m=1e-4, l=1e-4),
+    "f32": dict(O=1e-5, m=1e-6, l=1e-5),
+}
+SCORE_REL = 1e-5   # selection boundary exemption, relative to the k-th score
+
+
+def to_device(dsa, batch):
+    q = dsa.upload_q(batch.q, batch.dtype)
+    kv = dsa.PagedKV.from_numpy(batch.k, batch.v, batch.page_table, batch.seq_lens, batch.dtype)
+    st = None
+    if batch.streaming is not None:
+        st = dsa.Streaming(batch.streaming, batch.sink, batch.local)
+    return q, kv, st
+
+
+def np_(t):
+    return t.detach().cpu().numpy()
+
+
+def check_selection(gpu_ids: np.ndarray, gpu_count: int, oracle_row: np.ndarray, n_valid: int, k: int, what=""):
+    """Rule (i): the selected sets match exactly, except pairs in the
+    symmetric difference whose oracle scores both lie within SCORE_REL of the
+    oracle's k-th score (never pairs of exactly equal oracle scores)."""
+    ref = oracle.topk_pages(oracle_row, n_valid, k)
+    got = gpu_ids[:gpu_count]
+    assert gpu_count == len(ref), f"{what}: count {gpu_count} != {len(ref)}"
+    assert np.all(np.diff(got) > 0), f"{what}: ids not strictly ascending"
+    assert np.all(gpu_ids[gpu_count:] == -1), f"{what}: padding not -1"
+    diff = set(got.tolist()) ^ set(ref.tolist())
+    if not diff:
+        return 0
+    ranked = oracle.rank_pages(oracle_row, n_valid)
+    tau = oracle_row[ranked[len(ref) - 1]]
+    band = SCORE_REL * abs(tau)
+    for x in diff:
+        assert abs(oracle_row[x] - tau) <= band, \
+            f"{what}: page {x} (score {oracle_row[x]!r}) differs from oracle, k-th score {tau!r}"
+    vals = [oracle_row[x] for x in diff]
+    assert len(set(vals)) == len(vals), f"{what}: exact ties resolved differently"
+    return len(diff) // 2
+
+
+def check_attention(dtype: str, O, l, m, ref_O, ref_l, ref_m, what=""):
+    t = TOL[dtype]
+    ref_m = np.asarray(ref_m, float)
+    empty = np.isneginf(ref_m)
+    assert np.array_equal(np.isneginf(m), empty), f"{what}: empty-set pattern differs"
+    assert np.all(l[empty] == 0) and np.all(O[empty] == 0), f"{what}: empty set must give O=0, l=0"
+    ok = ~empty
+    if ok.any():
+        dO = np.abs(O[ok] - ref_O[ok]).max()
+        dm = np.abs(m[ok] - ref_m[ok]).max()
+        dl = (np.abs(l[ok] - ref_l[ok]) / ref_l[ok]).max()
+        assert dO <= t["O"], f"{what}: max|dO| = {dO:.3g} > {t['O']}"
+        assert dm <= t["m"] * max(1.0, np.abs(ref_m[ok]).max()), f"{what}: max|dm| = {dm:.3g}"
+        assert dl <= t["l"], f"{what}: max rel dl = {dl:.3g}"
+
+
+def ids_lists(ids: np.ndarray, counts: np.ndarray):
+    """[B][H][stride] + counts -> nested python lists of id arrays."""
+    B, H = counts.shape
+    return [[ids[b, h, :counts[b, h]].astype(np.int64) for h in range(H)] for b in range(B)]
