@@ -41,10 +41,19 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int unit = b * n_kv_heads + h;
   const int TPP = P / 16;
+  const int t_begin = split * tiles_per_split;
+  const int first_entry = t_begin / TPP;
+  // The id and its slot are fetched together with the count (the count only
+  // decides later which of them are used): entry -> page -> slot is one
+  // dependent hop instead of two.
+  int pg_raw = -1, sl_raw = -1;
+  if (lane < tiles_per_split / TPP && first_entry + lane < ids_stride) {
+    pg_raw = ids[(size_t)unit * ids_stride + first_entry + lane];
+    if (pg_raw >= 0 && pg_raw < max_pages) sl_raw = page_table[(size_t)b * max_pages + pg_raw];
+  }
   int cnt = counts[unit];
   cnt = cnt < 0 ? 0 : (cnt > ids_stride ? ids_stride : cnt);
   const int n_tiles = cnt * TPP;
-  const int t_begin = split * tiles_per_split;
   if (t_begin >= n_tiles) return;  // whole workgroup: the combine reads only active splits
   const int t_end = min(n_tiles, t_begin + tiles_per_split);
   const int L = clamp_len(seq_lens[b], max_pages, P);
@@ -54,17 +63,11 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
   A st;
   st.init(q + ((size_t)b * n_kv_heads * G + (size_t)h * G) * D, lds_rows[wave]);
 
-  // Two-level index (list entry -> page -> slot) for the pages of this split:
-  // lane x resolves entry first_entry + x once.
-  const int first_entry = t_begin / TPP;
   const int n_entries = (t_end - 1) / TPP - first_entry + 1;
   int my_page = -1, my_slot = -1;
-  if (lane < n_entries) {
-    const int pg = ids[(size_t)unit * ids_stride + first_entry + lane];
-    if (pg >= 0 && pg < np) {
-      const int sl = page_table[(size_t)b * max_pages + pg];
-      if (sl >= 0 && sl < num_slots) { my_page = pg; my_slot = sl; }
-    }
+  if (lane < n_entries && pg_raw >= 0 && pg_raw < np && sl_raw >= 0 && sl_raw < num_slots) {
+    my_page = pg_raw;
+    my_slot = sl_raw;
   }
   const size_t slot_stride = (size_t)n_kv_heads * P * D;
   const size_t head_off = (size_t)h * P * D;
@@ -133,56 +136,78 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
 }
 
 // ============================================================ combine
-// One wave per (sequence, q head): folds the active splits (and, for repair,
-// the caller's (O, l, m)) with the online-softmax merge; writes normalised O.
+// One workgroup (4 waves) per (sequence, q head).  The active splits' maxima
+// are reduced first; then wave w sums splits w, w+4, ... with weights
+// exp(m_s - M) (lanes over channels, loads independent across splits), and
+// the 4 wave sums meet in LDS.  For repair the caller's (O, l, m) is one more
+// term.  Writes normalised O.
 template <int D>
-__global__ __launch_bounds__(64) void attn_combine_kernel(
+__global__ __launch_bounds__(256) void attn_combine_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_ml, const int32_t* __restrict__ counts,
     int ids_stride, int n_kv_heads, int G, int TPP, int tiles_per_split, int n_splits, int fold,
     float* __restrict__ O, float* __restrict__ l, float* __restrict__ m) {
   constexpr int CPT = D / 64;
+  __shared__ float s_red[4];
+  __shared__ float s_acc[4][D];
+  __shared__ float s_l[4];
   const int hq = blockIdx.x, b = blockIdx.y;
   const int Hq = n_kv_heads * G;
   const int h = hq / G, g = hq % G;
   const int unit = b * n_kv_heads + h;
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int cnt = counts[unit];
   cnt = cnt < 0 ? 0 : (cnt > ids_stride ? ids_stride : cnt);
   const int active = min(n_splits, (cnt * TPP + tiles_per_split - 1) / tiles_per_split);
   const size_t row = (size_t)b * Hq + hq;
+  const float* ml = part_ml + ((size_t)unit * n_splits * G + g) * 2;   // split s at ml[s * 2G]
 
-  float mm = kNegInf;
-  for (int s = 0; s < active; ++s) mm = fmaxf(mm, part_ml[(((size_t)unit * n_splits + s) * G + g) * 2]);
+  float mx = kNegInf;
+  for (int s = tid; s < active; s += 256) mx = fmaxf(mx, ml[(size_t)s * 2 * G]);
+  for (int d = 32; d >= 1; d >>= 1) mx = fmaxf(mx, __shfl_xor(mx, d, 64));
+  if (lane == 0) s_red[wave] = mx;
   float m_in = kNegInf, l_in = 0.0f;
   if (fold) {
     m_in = m[row];
     l_in = l[row];
     if (!(l_in > 0.0f)) m_in = kNegInf;
-    mm = fmaxf(mm, m_in);
   }
+  __syncthreads();
+  const float M = fmaxf(fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3])), m_in);
+
   float acc[CPT], ls = 0.0f;
 #pragma unroll
   for (int x = 0; x < CPT; ++x) acc[x] = 0.0f;
-  for (int s = 0; s < active; ++s) {
+#pragma unroll 4
+  for (int s = wave; s < active; s += 4) {
     const size_t pi = ((size_t)unit * n_splits + s) * G + g;
     const float ms = part_ml[pi * 2], lsp = part_ml[pi * 2 + 1];
-    const float wt = (mm == kNegInf || ms == kNegInf) ? 0.0f : expf(ms - mm);
+    const float wt = (ms == kNegInf) ? 0.0f : expf(ms - M);
     ls = fmaf(lsp, wt, ls);
 #pragma unroll
     for (int x = 0; x < CPT; ++x) acc[x] = fmaf(part_o[pi * D + lane + 64 * x], wt, acc[x]);
   }
-  if (fold && m_in != kNegInf) {
-    const float wt = expf(m_in - mm) * l_in;
+  if (wave == 0 && fold && m_in != kNegInf) {
+    const float wt = expf(m_in - M) * l_in;
     ls += wt;
 #pragma unroll
     for (int x = 0; x < CPT; ++x) acc[x] = fmaf(O[row * D + lane + 64 * x], wt, acc[x]);
   }
-  const float inv = ls > 0.0f ? 1.0f / ls : 0.0f;
 #pragma unroll
-  for (int x = 0; x < CPT; ++x) O[row * D + lane + 64 * x] = acc[x] * inv;
-  if (lane == 0) {
-    l[row] = ls;
-    m[row] = ls > 0.0f ? mm : kNegInf;
+  for (int x = 0; x < CPT; ++x) s_acc[wave][lane + 64 * x] = acc[x];
+  if (lane == 0) s_l[wave] = ls;
+  __syncthreads();
+  if (wave == 0) {
+    const float L = s_l[0] + s_l[1] + s_l[2] + s_l[3];
+    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+#pragma unroll
+    for (int x = 0; x < CPT; ++x) {
+      const int c = lane + 64 * x;
+      O[row * D + c] = (s_acc[0][c] + s_acc[1][c] + s_acc[2][c] + s_acc[3][c]) * inv;
+    }
+    if (lane == 0) {
+      l[row] = L;
+      m[row] = L > 0.0f ? M : kNegInf;
+    }
   }
 }
 
@@ -401,13 +426,16 @@ struct SplitPlan {
 
 // Tiles per workgroup so that ~1024 workgroups cover the largest possible
 // selection (counts live on the device, so the grid is sized for ids_stride).
-inline SplitPlan plan_splits(const dsa_kv* kv, int ids_stride) {
+inline SplitPlan plan_splits(const dsa_kv* kv, int ids_stride, int n_streaming_heads) {
   SplitPlan p;
   p.TPP = kv->page_size / 16;
   const long long tiles_max = (long long)ids_stride * p.TPP;
-  const long long total = tiles_max * kv->batch * kv->n_kv_heads;
-  long long tps = kWgWaves;
-  while (tps < 64 && total / tps > 1024) tps <<= 1;
+  const int dense_heads = kv->n_kv_heads - n_streaming_heads;
+  const long long total = tiles_max * kv->batch * (dense_heads > 0 ? dense_heads : 1);
+  // a split's pages must fit the 64 lanes that resolve them
+  const long long cap = 64LL * p.TPP < 128 ? 64LL * p.TPP : 128;
+  long long tps = 2 * kWgWaves;
+  while (tps < cap && total / tps > 384) tps <<= 1;
   p.tiles_per_split = (int)tps;
   p.n_splits = (int)((tiles_max + tps - 1) / tps);
   if (p.n_splits < 1) p.n_splits = 1;
@@ -416,17 +444,21 @@ inline SplitPlan plan_splits(const dsa_kv* kv, int ids_stride) {
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-inline size_t partial_bytes(const dsa_kv* kv, int G, const SplitPlan& p) {
+// Workspace for any plan of this shape: the smallest split size gives the
+// most splits.
+inline size_t partial_bytes(const dsa_kv* kv, int G, int ids_stride) {
   const size_t units = (size_t)kv->batch * kv->n_kv_heads;
-  return align256(units * p.n_splits * G * kv->head_dim * sizeof(float)) +
-         align256(units * p.n_splits * G * 2 * sizeof(float));
+  const size_t tiles_max = (size_t)ids_stride * (kv->page_size / 16);
+  const size_t max_splits = (tiles_max + 2 * kWgWaves - 1) / (2 * kWgWaves);
+  return align256(units * max_splits * G * kv->head_dim * sizeof(float)) +
+         align256(units * max_splits * G * 2 * sizeof(float));
 }
 
 template <typename T, int D, int G>
 static int launch_attn_g(const void* q, const dsa_kv* kv, const int32_t* ids, const int32_t* counts,
                          int ids_stride, uint64_t smask, int sink, int local, float scale, float* O, float* l,
                          float* m, void* ws, int fold, hipStream_t st) {
-  const SplitPlan p = plan_splits(kv, ids_stride);
+  const SplitPlan p = plan_splits(kv, ids_stride, __builtin_popcountll(smask));
   const size_t units = (size_t)kv->batch * kv->n_kv_heads;
   float* part_o = (float*)ws;
   float* part_ml = (float*)((char*)ws + align256(units * p.n_splits * G * D * sizeof(float)));
@@ -438,7 +470,7 @@ static int launch_attn_g(const void* q, const dsa_kv* kv, const int32_t* ids, co
                      p.tiles_per_split, p.n_splits, part_o, part_ml);
   int rc = launch_status();
   if (rc) return rc;
-  hipLaunchKernelGGL((attn_combine_kernel<D>), dim3(kv->n_kv_heads * G, kv->batch), dim3(64), 0, st, part_o,
+  hipLaunchKernelGGL((attn_combine_kernel<D>), dim3(kv->n_kv_heads * G, kv->batch), dim3(256), 0, st, part_o,
                      part_ml, counts, ids_stride, kv->n_kv_heads, G, p.TPP, p.tiles_per_split, p.n_splits, fold, O,
                      l, m);
   return launch_status();
@@ -540,8 +572,7 @@ extern "C" size_t dsa_workspace_bytes(int32_t op, const dsa_kv* kv, int32_t n_q_
   if (check_kv(kv, false) != DSA_OK || n_q_heads < 1 || n_q_heads % kv->n_kv_heads || ids_stride < 1) return 0;
   const int G = n_q_heads / kv->n_kv_heads;
   if (!pow2_group(G)) return 0;
-  const SplitPlan p = plan_splits(kv, ids_stride);
-  const size_t part = partial_bytes(kv, G, p);
+  const size_t part = partial_bytes(kv, G, ids_stride);
   if (op == DSA_OP_SPARSE_DECODE_ATTN) return part;
   if (op == DSA_OP_ATTN_REPAIR) return repair_ids_bytes(kv, ids_stride) + part;
   return 0;

@@ -2,27 +2,24 @@
 // selection stage of a dynamic sparse attention step) and the fixed
 // sink/local page lists of streaming heads (LServe, section 4.1).
 //
-// One workgroup per (sequence, KV head).  Thread t owns the E consecutive
-// page indices [t*E, (t+1)*E) of the score row, held in registers as
-// order-preserving 32-bit keys.  The k-th largest key is found MSB-first,
-// 4 bits per pass (8 passes): per-thread digit counters packed into 8-bit
-// fields, a DPP row reduce-scatter plus two cross-row shuffles turn them
-// into per-wave histograms, 16 LDS atomics per wave make the block
-// histogram.  Keys above the threshold are all kept; keys equal to it are
-// kept in index order until k is reached, which implements the lower-index
-// tie rule exactly.  Two block scans then compact the kept indices in
-// ascending order.
+// One workgroup per (sequence, KV head); thread t owns the E consecutive
+// page indices [t*E, (t+1)*E) of the score row in registers, as 32-bit keys
+// with the order of the float scores (-0 and +0 equal).  Adaptive radix
+// select: the keys still in play span [klo, khi]; bucket (key - klo) >> s,
+// with s chosen so the span fills at most 2048 buckets, is monotone in the
+// score and equal scores share a bucket.  An LDS histogram and a block
+// suffix scan find the bucket holding the k-th largest score; pages in
+// higher buckets are kept, lower ones dropped, and the pass repeats on that
+// bucket (each pass removes 11 bits of span, so at most 3) until it holds
+// exactly the pages still needed or only equal keys.  Those are taken in
+// index order -- the lower-index tie rule.  A block scan then writes the
+// kept indices in ascending order.
 #include "dsa_common.hpp"
 #include "dsa_host.hpp"
 
 namespace dsa {
 
-// float -> uint32 with the same order; -0.0 maps like +0.0.
-__device__ __forceinline__ uint32_t order_key(float f) {
-  uint32_t u = __float_as_uint(f);
-  if (u == 0x80000000u) u = 0u;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
+constexpr int kBuckets = 2048;
 
 // Exclusive prefix sum over the block (threads in index order) and the total.
 template <int NW>
@@ -48,6 +45,30 @@ __device__ __forceinline__ int block_excl_scan(int x, int* smem /* NW ints */, i
   return before + incl - x;
 }
 
+template <int NW>
+__device__ __forceinline__ void block_minmax_u32(uint32_t& lo, uint32_t& hi, uint32_t* smem /* 2*NW */) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) {
+    lo = min(lo, (uint32_t)__shfl_xor((int)lo, d, 64));
+    hi = max(hi, (uint32_t)__shfl_xor((int)hi, d, 64));
+  }
+  if (lane == 0) { smem[2 * wave] = lo; smem[2 * wave + 1] = hi; }
+  __syncthreads();
+  lo = smem[0];
+  hi = smem[1];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) { lo = min(lo, smem[2 * w]); hi = max(hi, smem[2 * w + 1]); }
+  __syncthreads();
+}
+
+// float -> uint32 with the same order; -0.0 maps like +0.0.
+__device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
 template <int E, int NW>
 __global__ __launch_bounds__(NW * 64) void topk_kernel(const float* __restrict__ scores,
                                                          const int32_t* __restrict__ seq_lens, int n_kv_heads,
@@ -55,11 +76,14 @@ __global__ __launch_bounds__(NW * 64) void topk_kernel(const float* __restrict__
                                                          int sink, int local, int32_t* __restrict__ ids,
                                                          int32_t* __restrict__ counts) {
   constexpr int NT = NW * 64;
-  __shared__ unsigned hist[8][16];
+  constexpr int BPT = kBuckets / NT;  // buckets per thread in the suffix scan
+  __shared__ unsigned hist[kBuckets];
   __shared__ int scan_smem[NW];
+  __shared__ uint32_t mm_smem[2 * NW];
+  __shared__ int s_bstar, s_above;
   const int h = blockIdx.x, b = blockIdx.y;
   const int unit = b * n_kv_heads + h;
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int tid = threadIdx.x;
   const int L = clamp_len(seq_lens[b], max_pages, P);
   const int np = (L + P - 1) / P;
   int32_t* out = ids + (size_t)unit * k;
@@ -80,81 +104,84 @@ __global__ __launch_bounds__(NW * 64) void topk_kernel(const float* __restrict__
     return;
   }
 
-  for (int x = tid; x < 8 * 16; x += NT) (&hist[0][0])[x] = 0u;
   const int keff = min(k, np);
   uint32_t key[E];
-  bool valid[E];
+  unsigned long long actm = 0ull, selm = 0ull;  // bit e: page tid*E+e still in play / kept
   const float* srow = scores + (size_t)unit * max_pages;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int idx = tid * E + e;
-    valid[e] = idx < np;
-    key[e] = valid[e] ? order_key(srow[idx]) : 0u;
+    key[e] = idx < np ? order_key(srow[idx]) : 0u;
+    if (idx < np) actm |= 1ull << e;
   }
-  __syncthreads();
-
-  uint32_t prefix = 0u, pmask = 0u;
-  int krem = keff;
-  if (keff > 0) {
-    const int j = lane & 15;
-#pragma unroll 1
-    for (int pass = 0; pass < 8; ++pass) {
-      const int shift = 28 - 4 * pass;
-      unsigned long long c_lo = 0ull, c_hi = 0ull;  // 8-bit counters for digits 0-7 / 8-15
+  int need = keff, n_act = np;
+  if (need > 0) {
+    for (int iter = 0; iter < 4; ++iter) {
+      uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        if ((actm >> e) & 1ull) { lo = min(lo, key[e]); hi = max(hi, key[e]); }
+      block_minmax_u32<NW>(lo, hi, mm_smem);
+      if (n_act == need || lo == hi) break;
+      const uint32_t span = hi - lo;
+      const int shift = span < (uint32_t)kBuckets ? 0 : (32 - __clz((int)span) - 11);
+      for (int x = tid; x < kBuckets; x += NT) hist[x] = 0u;
+      __syncthreads();
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        if ((actm >> e) & 1ull) atomicAdd(&hist[(key[e] - lo) >> shift], 1u);
+      __syncthreads();
+      // suffix scan: thread t owns buckets [(NT-1-t)*BPT, +BPT), so lower t = higher buckets
+      const int b0 = (NT - 1 - tid) * BPT;
+      int mine = 0;
+#pragma unroll
+      for (int x = 0; x < BPT; ++x) mine += (int)hist[b0 + x];
+      int tot;
+      int acc = block_excl_scan<NW>(mine, scan_smem, tot);
+      if (acc < need && need <= acc + mine) {
+        for (int x = BPT - 1; x >= 0; --x) {
+          const int hb = (int)hist[b0 + x];
+          if (acc + hb >= need) { s_bstar = b0 + x; s_above = acc; break; }
+          acc += hb;
+        }
+      }
+      __syncthreads();
+      const uint32_t bstar = (uint32_t)s_bstar;
+      const int above = s_above;
 #pragma unroll
       for (int e = 0; e < E; ++e) {
-        const bool act = valid[e] && ((key[e] & pmask) == prefix);
-        const uint32_t d = (key[e] >> shift) & 15u;
-        const unsigned long long inc = act ? (1ull << (8 * (d & 7u))) : 0ull;
-        if (d < 8) c_lo += inc; else c_hi += inc;
+        const unsigned long long bit = 1ull << e;
+        if (actm & bit) {
+          const uint32_t bk = (key[e] - lo) >> shift;
+          if (bk > bstar) { selm |= bit; actm &= ~bit; }
+          else if (bk < bstar) actm &= ~bit;
+        }
       }
-      float v[16];
-#pragma unroll
-      for (int d = 0; d < 8; ++d) {
-        v[d] = (float)((c_lo >> (8 * d)) & 0xffull);
-        v[d + 8] = (float)((c_hi >> (8 * d)) & 0xffull);
-      }
-      row_sum_scatter<16>(v, j);  // lane j of each row: that row's count of digit j
-      float t = v[0];
-      t += shfl_xor_f(t, 16);
-      t += shfl_xor_f(t, 32);
-      if (lane < 16 && t > 0.0f) atomicAdd(&hist[pass][lane], (unsigned)t);
-      __syncthreads();
-      unsigned above = 0u;
-      int dsel = 0;
-      for (int d = 15; d >= 0; --d) {
-        const unsigned hd = hist[pass][d];
-        if (above + hd >= (unsigned)krem) { dsel = d; break; }
-        above += hd;
-      }
-      krem -= (int)above;
-      prefix |= (uint32_t)dsel << shift;
-      pmask |= 15u << shift;
+      need -= above;
+      n_act = (int)hist[bstar];
+      __syncthreads();  // hist is rewritten by the next pass
     }
+  } else {
+    actm = 0ull;
   }
-  // prefix is now the k-th largest key; krem keys equal to it are kept.
-  int eq_local = 0;
+  // the keys still in play are equal (or exactly `need` of them are left):
+  // take them in index order
+  {
+    int a_tot;
+    int before = block_excl_scan<NW>(__popcll(actm), scan_smem, a_tot);
 #pragma unroll
-  for (int e = 0; e < E; ++e) eq_local += (keff > 0 && valid[e] && key[e] == prefix) ? 1 : 0;
-  int eq_total;
-  const int eq_before = block_excl_scan<NW>(eq_local, scan_smem, eq_total);
-  bool take[E];
-  int sel_local = 0, eq_seen = 0;
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    bool tk = false;
-    if (keff > 0 && valid[e]) {
-      if (key[e] > prefix) tk = true;
-      else if (key[e] == prefix) { tk = (eq_before + eq_seen) < krem; ++eq_seen; }
+    for (int e = 0; e < E; ++e) {
+      if ((actm >> e) & 1ull) {
+        if (before < need) selm |= 1ull << e;
+        ++before;
+      }
     }
-    take[e] = tk;
-    sel_local += tk ? 1 : 0;
   }
   int sel_total;
-  int pos = block_excl_scan<NW>(sel_local, scan_smem, sel_total);
+  int pos = block_excl_scan<NW>(__popcll(selm), scan_smem, sel_total);
 #pragma unroll
   for (int e = 0; e < E; ++e)
-    if (take[e] && pos < keff) out[pos++] = tid * E + e;
+    if (((selm >> e) & 1ull) && pos < keff) out[pos++] = tid * E + e;
   for (int x = keff + tid; x < k; x += NT) out[x] = -1;
   if (tid == 0) counts[unit] = keff;
 }

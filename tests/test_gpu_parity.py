@@ -324,3 +324,43 @@ def test_ema(gpu_lib, n):
     pr2 = torch.empty(n, device="cuda")
     dsa.ema_predict_update(None, lv, tr, pr2, a, b_, g)
     assert np.allclose(np_(pr2), oracle.ema_predict(np_(lv), np_(tr), g), rtol=1e-6, atol=1e-5)
+
+
+# ---------------------------------------------------------------- HIP graph replay
+def test_graph_replay_matches_eager(gpu_lib):
+    """The decode step captured in a HIP graph gives the eager result on every
+    replay, with eager work and synchronisations between replays."""
+    dsa = gpu_lib
+    bt = wl.quest_gqa(seed=3, seq_len=16 * 300 + 5, n_q_heads=8, n_kv_heads=2)
+    q, kv, _ = to_device(dsa, bt)
+    meta = dsa.page_meta_build(kv)
+    B, Hkv, N = kv.batch, kv.n_kv_heads, kv.max_pages
+    sc = torch.empty((B, Hkv, N), device="cuda")
+    ids = torch.empty((B, Hkv, 40), dtype=torch.int32, device="cuda")
+    cnt = torch.empty((B, Hkv), dtype=torch.int32, device="cuda")
+    O = torch.empty((B, 8, 128), device="cuda")
+    l = torch.empty((B, 8), device="cuda")
+    m = torch.empty((B, 8), device="cuda")
+    ws = torch.empty(dsa.workspace_bytes(dsa.OP_SPARSE_DECODE_ATTN, kv, 8, 40), dtype=torch.uint8, device="cuda")
+
+    def step():
+        dsa.page_score(q, kv, meta, scores=sc)
+        dsa.page_select_topk(sc, kv.seq_lens, 16, 40, ids=ids, counts=cnt)
+        dsa.sparse_decode_attn(q, kv, ids, cnt, out=(O, l, m), ws=ws)
+
+    step()
+    torch.cuda.synchronize()
+    ref = [np_(x).copy() for x in (sc, ids, cnt, O, l, m)]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        for x in (sc, O, l, m):
+            x.fill_(float("nan"))
+        ids.fill_(-7)
+        g.replay()
+        torch.cuda.synchronize()
+        got = [np_(x) for x in (sc, ids, cnt, O, l, m)]
+        for a_, b_ in zip(got, ref):
+            assert np.array_equal(a_, b_), f"replay {rep} differs"
+        _ = (torch.randn(1000, device="cuda") * 2).sum().item()   # eager work between replays
