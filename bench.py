@@ -44,9 +44,24 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="quest_gqa_32k", choices=["quest_gqa_32k"])
     ap.add_argument("--replicas", type=int, default=0, help="0 = enough for > 1 GiB per rotation")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU oracle sample")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run 10 plain device copies of BYTES (HBM counter calibration) and exit")
     return ap.parse_args()
+
+
+def copy_calibration(nbytes: int):
+    """A plain device-to-device copy of known size: its FETCH_SIZE/WRITE_SIZE
+    readings per dispatch calibrate the HBM traffic counters."""
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(10):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "dispatches": 10}))
 
 
 def algorithmic_bytes(bt, k_pages):
@@ -62,35 +77,53 @@ def algorithmic_bytes(bt, k_pages):
 
 
 def cpu_baseline(bt, k_pages, budget_s):
-    """The oracle as it stands, single-threaded, on a sample of (sequence,
-    KV head) units of the same workload; scaled to queries/s."""
+    """The oracle as it stands, single-threaded: whole decode steps of the
+    same workload (score every page of every (sequence, KV head), top-k,
+    attention of the group's q heads) repeated for about `budget_s` seconds;
+    queries/s = sequences * steps / time."""
     import oracle
     from threadpoolctl import threadpool_limits
-    units_total = bt.batch * bt.n_kv_heads
     meta, has = oracle.page_meta(bt)          # prefill-time work, not timed
-    done, t_used = 0, 0.0
+    steps, t_used = 0, 0.0
     with threadpool_limits(1):
-        while t_used < budget_s and done < units_total:
-            b, h = divmod(done, bt.n_kv_heads)
+        while t_used < budget_s:
             t0 = time.perf_counter()
-            qbar = oracle.group_query(bt)[b, h]
-            n = oracle.n_pages(bt.seq_lens[b], bt.page_size)
-            row = np.full(bt.max_pages, -math.inf)
-            for j in range(n):
-                slot = bt.page_table[b][j]
-                row[j] = oracle.criticality(qbar, meta[slot, h, 0, 0], meta[slot, h, 0, 1])
-            ids = oracle.topk_pages(row, n, k_pages)
-            oracle.attend_pages(bt, b, h, ids)
+            scores = oracle.page_scores(bt, meta=meta, has=has)
+            ids = oracle.select_topk(bt, scores, k_pages)
+            oracle.sparse_decode(bt, ids)
             t_used += time.perf_counter() - t0
-            done += 1
-    per_query = t_used / done * units_total   # all KV heads of one sequence = one query
-    return {"value": 1.0 / per_query, "unit": "queries/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} of {units_total} (sequence, KV head) units of one decode step, "
-                      f"{t_used:.1f} s single-threaded fp64 numpy; scaled to all units"}
+            steps += 1
+    return {"value": bt.batch * steps / t_used, "unit": "queries/s", "cores": 1, "kind": "oracle",
+            "sample": f"{steps} whole decode steps of the workload ({bt.batch * bt.n_kv_heads} (sequence, KV head) "
+                      f"units each), {t_used:.1f} s single-threaded fp64 numpy"}
+
+
+def profiled_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary, if the kernel sources still hash to what was profiled."""
+    import glob
+    import hashlib
+    import re
+    for path in glob.glob(os.path.join(ROOT, "profiles", "*.md")):
+        m = re.search(r"```json\n(\{.*?\})\n```", open(path).read(), re.S)
+        if not m:
+            continue
+        rec = json.loads(m.group(1))
+        if rec.get("kernel") != kernel or rec.get("workload") != workload:
+            continue
+        h = hashlib.sha256()
+        for f in rec["source_files"]:
+            h.update(open(os.path.join(ROOT, f), "rb").read())
+        if h.hexdigest()[:16] == rec["source_sha256"]:
+            return rec["traffic_bytes_per_launch"]
+    return None
 
 
 def main():
     a = parse()
+    if a.copy_calibration:
+        copy_calibration(a.copy_calibration)
+        return
     if a.gpus != 1:
         print(json.dumps({"error": "this build runs on exactly one GPU; multi-GPU sharding is described "
                                    "in the design notes but not built", "n_gpus": a.gpus}))
@@ -129,7 +162,7 @@ def main():
     O = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
     l = torch.empty((B, Hq), dtype=torch.float32, device=dev)
     m = torch.empty((B, Hq), dtype=torch.float32, device=dev)
-    ws = torch.empty(dsa.workspace_bytes(dsa.OP_SPARSE_DECODE_ATTN, kvs[0], Hq, k_pages), dtype=torch.uint8,
+    ws = torch.zeros(dsa.workspace_bytes(dsa.OP_SPARSE_DECODE_ATTN, kvs[0], Hq, k_pages), dtype=torch.uint8,
                      device=dev)
     scale = float(bt.scale)
 
@@ -222,7 +255,7 @@ def main():
         "eager_ms_per_step": eager_ms_step,
         "timing": "HIP graph of one step per replica, replayed; events on the replay stream",
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": profiled_traffic(dom, a.workload),
                      "bytes_per_launch": dom_bytes, "avg_launch_us": dur_us},
     }
     if not a.no_cpu:

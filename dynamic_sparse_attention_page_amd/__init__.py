@@ -53,11 +53,11 @@ class _Stream(ctypes.Structure):
     _fields_ = [("kv_head_streaming", ctypes.c_void_p), ("sink", ctypes.c_int32), ("local", ctypes.c_int32)]
 
 
-def _load():
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with "
+def _load(path: str = LIB_PATH):
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with "
                           "`python -m dynamic_sparse_attention_page_amd.build` (hipcc, gfx950)")
-    L = ctypes.CDLL(LIB_PATH)
+    L = ctypes.CDLL(path)
     P, I32, I64, F32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
     KV, ST = ctypes.POINTER(_KV), ctypes.POINTER(_Stream)
     sig = {
@@ -186,7 +186,7 @@ def _workspace(nbytes: int, device) -> torch.Tensor:
     key = (str(device),)
     t = _ws_cache.get(key)
     if t is None or t.numel() < nbytes:
-        t = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        t = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)   # tickets start at zero
         _ws_cache[key] = t
     return t
 

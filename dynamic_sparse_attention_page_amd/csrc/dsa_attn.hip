@@ -19,6 +19,10 @@
 #include "dsa_attn_core.hpp"
 #include "dsa_host.hpp"
 
+#ifndef DSA_SPLIT_TARGET
+#define DSA_SPLIT_TARGET 384  // target workgroups of the split-KV grid
+#endif
+
 namespace dsa {
 
 constexpr int kWgWaves = 4;
@@ -34,8 +38,13 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
   using A = AttnWave<T, D, G>;
   constexpr int CPL = A::CPL, DW = A::DW;
   __shared__ __align__(16) float lds_rows[kWgWaves][A::LDS_FLOATS];
-  __shared__ __align__(16) float lds_o[kWgWaves][G][D];
-  __shared__ float lds_ml[kWgWaves][G][2];
+  // row-state merge buffers: 16 row states for G <= 4, 4 wave states above
+  constexpr int NSTATE = G <= 4 ? 16 : 1;
+  constexpr int NWS = G <= 4 ? 1 : kWgWaves;
+  __shared__ __align__(16) float rs_o[NSTATE][G][D];
+  __shared__ float rs_ml[NSTATE][G][2];
+  __shared__ __align__(16) float lds_o[NWS][G][D];
+  __shared__ float lds_ml[NWS][G][2];
 
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -80,8 +89,8 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
     tok0 = 0;
     if (t >= t_end) return;
     const int e = t / TPP - first_entry, tin = t % TPP;
-    const int page = __shfl(my_page, e, 64);
-    const int slot = __shfl(my_slot, e, 64);
+    const int page = __builtin_amdgcn_readlane(my_page, e);   // e is wave-uniform
+    const int slot = __builtin_amdgcn_readlane(my_slot, e);
     if (slot < 0) return;
     tok0 = page * P + tin * 16;
     nvalid = min(16, L - tok0);
@@ -101,36 +110,70 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
     t += kWgWaves;
   }
 
-  float m[G], l[G];
-  st.finish(m, l, c);
-  if (lane < 16) {
+  const size_t pbase = ((size_t)unit * n_splits + split) * G;
+  if constexpr (G <= 4) {
+    // 16 row states (4 waves x 4 rows) meet in LDS; one pass merges them
+    float m[G], l[G];
+    st.row_totals(m, l);
+    const int row = wave * 4 + (lane >> 4);
 #pragma unroll
     for (int hh = 0; hh < G; ++hh)
 #pragma unroll
-      for (int cc = 0; cc < CPL; ++cc) lds_o[wave][hh][lane * CPL + cc] = st.o[hh][cc];
-  }
-  if (lane == 0) {
+      for (int cc = 0; cc < CPL; ++cc) rs_o[row][hh][(lane & 15) * CPL + cc] = st.o[hh][cc];
+    if ((lane & 15) == 0) {
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh) { lds_ml[wave][hh][0] = m[hh]; lds_ml[wave][hh][1] = l[hh]; }
-  }
-  __syncthreads();
-  const size_t pbase = ((size_t)unit * n_splits + split) * G;
-  for (int idx = threadIdx.x; idx < G * D; idx += 256) {
-    const int hh = idx / D, cc = idx % D;
-    float mm = kNegInf;
-#pragma unroll
-    for (int w = 0; w < kWgWaves; ++w) mm = fmaxf(mm, lds_ml[w][hh][0]);
-    float acc = 0.0f, ls = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kWgWaves; ++w) {
-      const float wt = exp2_diff(lds_ml[w][hh][0], mm, c);
-      acc = fmaf(lds_o[w][hh][cc], wt, acc);
-      ls = fmaf(lds_ml[w][hh][1], wt, ls);
+      for (int hh = 0; hh < G; ++hh) { rs_ml[row][hh][0] = m[hh]; rs_ml[row][hh][1] = l[hh]; }
     }
-    part_o[(pbase + hh) * D + cc] = acc;
-    if (cc == 0) {
-      part_ml[(pbase + hh) * 2 + 0] = (mm == kNegInf) ? kNegInf : mm * scale;  // natural-log units
-      part_ml[(pbase + hh) * 2 + 1] = ls;
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < G * D; idx += 256) {
+      const int hh = idx / D, cc = idx % D;
+      float mm = kNegInf;
+#pragma unroll
+      for (int w = 0; w < 16; ++w) mm = fmaxf(mm, rs_ml[w][hh][0]);
+      float acc = 0.0f, ls = 0.0f;
+#pragma unroll
+      for (int w = 0; w < 16; ++w) {
+        const float wt = exp2_diff(rs_ml[w][hh][0], mm, c);
+        acc = fmaf(rs_o[w][hh][cc], wt, acc);
+        ls = fmaf(rs_ml[w][hh][1], wt, ls);
+      }
+      part_o[(pbase + hh) * D + cc] = acc;
+      if (cc == 0) {
+        part_ml[(pbase + hh) * 2 + 0] = (mm == kNegInf) ? kNegInf : mm * scale;  // natural-log units
+        part_ml[(pbase + hh) * 2 + 1] = ls;
+      }
+    }
+  } else {
+    float m[G], l[G];
+    st.finish(m, l, c);
+    if (lane < 16) {
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+        for (int cc = 0; cc < CPL; ++cc) lds_o[wave][hh][lane * CPL + cc] = st.o[hh][cc];
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) { lds_ml[wave][hh][0] = m[hh]; lds_ml[wave][hh][1] = l[hh]; }
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < G * D; idx += 256) {
+      const int hh = idx / D, cc = idx % D;
+      float mm = kNegInf;
+#pragma unroll
+      for (int w = 0; w < kWgWaves; ++w) mm = fmaxf(mm, lds_ml[w][hh][0]);
+      float acc = 0.0f, ls = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kWgWaves; ++w) {
+        const float wt = exp2_diff(lds_ml[w][hh][0], mm, c);
+        acc = fmaf(lds_o[w][hh][cc], wt, acc);
+        ls = fmaf(lds_ml[w][hh][1], wt, ls);
+      }
+      part_o[(pbase + hh) * D + cc] = acc;
+      if (cc == 0) {
+        part_ml[(pbase + hh) * 2 + 0] = (mm == kNegInf) ? kNegInf : mm * scale;  // natural-log units
+        part_ml[(pbase + hh) * 2 + 1] = ls;
+      }
     }
   }
 }
@@ -435,7 +478,7 @@ inline SplitPlan plan_splits(const dsa_kv* kv, int ids_stride, int n_streaming_h
   // a split's pages must fit the 64 lanes that resolve them
   const long long cap = 64LL * p.TPP < 128 ? 64LL * p.TPP : 128;
   long long tps = 2 * kWgWaves;
-  while (tps < cap && total / tps > 384) tps <<= 1;
+  while (tps < cap && total / tps > DSA_SPLIT_TARGET) tps <<= 1;
   p.tiles_per_split = (int)tps;
   p.n_splits = (int)((tiles_max + tps - 1) / tps);
   if (p.n_splits < 1) p.n_splits = 1;
@@ -446,12 +489,15 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Workspace for any plan of this shape: the smallest split size gives the
 // most splits.
+inline size_t max_splits_of(const dsa_kv* kv, int ids_stride) {
+  const size_t tiles_max = (size_t)ids_stride * (kv->page_size / 16);
+  return (tiles_max + 2 * kWgWaves - 1) / (2 * kWgWaves);
+}
+
 inline size_t partial_bytes(const dsa_kv* kv, int G, int ids_stride) {
   const size_t units = (size_t)kv->batch * kv->n_kv_heads;
-  const size_t tiles_max = (size_t)ids_stride * (kv->page_size / 16);
-  const size_t max_splits = (tiles_max + 2 * kWgWaves - 1) / (2 * kWgWaves);
-  return align256(units * max_splits * G * kv->head_dim * sizeof(float)) +
-         align256(units * max_splits * G * 2 * sizeof(float));
+  const size_t ms = max_splits_of(kv, ids_stride);
+  return align256(units * ms * G * kv->head_dim * sizeof(float)) + align256(units * ms * G * 2 * sizeof(float));
 }
 
 template <typename T, int D, int G>
@@ -461,7 +507,7 @@ static int launch_attn_g(const void* q, const dsa_kv* kv, const int32_t* ids, co
   const SplitPlan p = plan_splits(kv, ids_stride, __builtin_popcountll(smask));
   const size_t units = (size_t)kv->batch * kv->n_kv_heads;
   float* part_o = (float*)ws;
-  float* part_ml = (float*)((char*)ws + align256(units * p.n_splits * G * D * sizeof(float)));
+  float* part_ml = (float*)((char*)ws + align256(units * max_splits_of(kv, ids_stride) * G * D * sizeof(float)));
   const float c = scale * kLog2e;
   dim3 grid(p.n_splits, kv->n_kv_heads, kv->batch);
   hipLaunchKernelGGL((attn_partial_kernel<T, D, G>), grid, dim3(256), 0, st, (const T*)q, (const T*)kv->k,

@@ -95,7 +95,7 @@ struct AttnWave {
     for (int u = 0; u < NOWN; ++u) {
       const float su = ok ? s[u] : kNegInf;
       const float mn = fmaxf(m_own[u], ror_max4(su));
-      const float alpha = (mn == kNegInf) ? 1.0f : exp2f((m_own[u] - mn) * c);
+      const float alpha = (mn == kNegInf) ? 1.0f : fast_exp2((m_own[u] - mn) * c);
       const float p = exp2_diff(su, mn, c);
       lp[u] = fmaf(lp[u], alpha, p);
       m_own[u] = mn;
@@ -119,10 +119,15 @@ struct AttnWave {
 #pragma unroll
           for (int x = 0; x < DW; ++x) vd[i][x] = 0u;
     }
+    bool moved = false;
 #pragma unroll
-    for (int h = 0; h < G; ++h)
+    for (int h = 0; h < G; ++h) moved |= al[h] != 1.0f;
+    if (__builtin_amdgcn_read_exec() & __ballot(moved)) {  // skip the rescale once the maxima settle
 #pragma unroll
-      for (int cc = 0; cc < CPL; ++cc) o[h][cc] *= al[h];
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int cc = 0; cc < CPL; ++cc) o[h][cc] *= al[h];
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -132,6 +137,24 @@ struct AttnWave {
         for (int h = 0; h < G; ++h) o[h][cc] = fmaf(pr[i * G + h], v, o[h][cc]);
       }
     }
+  }
+
+  // Row totals without the cross-row merge: every lane gets m[h] (raw max)
+  // and l[h] of its own row; o stays per row.
+  __device__ __forceinline__ void row_totals(float (&m)[G], float (&l)[G]) {
+    float* pb = lds + r * LDS_ROW;
+#pragma unroll
+    for (int u = 0; u < NOWN; ++u) {
+      const float ls = ror_sum4(lp[u]);
+      if (i_own == 0) {
+        pb[4 * G + hbase + u] = ls;
+        pb[5 * G + hbase + u] = m_own[u];
+      }
+    }
+    wave_sync();
+#pragma unroll
+    for (int h = 0; h < G; ++h) { l[h] = pb[4 * G + h]; m[h] = pb[5 * G + h]; }
+    wave_sync();
   }
 
   // Collapse the 4 row states into one wave state.  Afterwards every lane

@@ -93,6 +93,45 @@ __device__ __forceinline__ float ror_sum4(float x) {
   return x + dpp<DPP_ROW_ROR8>(x);
 }
 
+// ---------------------------------------------------------------- wave scans
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ int dpp_i(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, ROW_MASK, 0xF, true);
+}
+
+// Inclusive prefix sum over the 64 lanes: shifts inside each row, then the
+// last lane of row 0 (row 2) is added to row 1 (row 3) and the last lane of
+// row 1 to rows 2 and 3.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += dpp_i<0x111>(x);        // row_shr:1
+  x += dpp_i<0x112>(x);        // row_shr:2
+  x += dpp_i<0x114>(x);        // row_shr:4
+  x += dpp_i<0x118>(x);        // row_shr:8
+  x += dpp_i<0x142, 0xA>(x);   // row_bcast:15 into rows 1, 3
+  x += dpp_i<0x143, 0xC>(x);   // row_bcast:31 into rows 2, 3
+  return x;
+}
+
+// Min / max of a uint32 over the wave, returned to every lane.
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
+  x = min(x, (uint32_t)dpp_i<DPP_ROW_MIRROR>((int)x));
+  x = min(x, (uint32_t)dpp_i<DPP_ROW_HALF_MIRROR>((int)x));
+  x = min(x, (uint32_t)dpp_i<DPP_QUAD_XOR3>((int)x));
+  x = min(x, (uint32_t)dpp_i<DPP_QUAD_XOR1>((int)x));
+  const uint32_t a = __builtin_amdgcn_readlane(x, 0), b = __builtin_amdgcn_readlane(x, 16);
+  const uint32_t c = __builtin_amdgcn_readlane(x, 32), d = __builtin_amdgcn_readlane(x, 48);
+  return min(min(a, b), min(c, d));
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  x = max(x, (uint32_t)dpp_i<DPP_ROW_MIRROR>((int)x));
+  x = max(x, (uint32_t)dpp_i<DPP_ROW_HALF_MIRROR>((int)x));
+  x = max(x, (uint32_t)dpp_i<DPP_QUAD_XOR3>((int)x));
+  x = max(x, (uint32_t)dpp_i<DPP_QUAD_XOR1>((int)x));
+  const uint32_t a = __builtin_amdgcn_readlane(x, 0), b = __builtin_amdgcn_readlane(x, 16);
+  const uint32_t c = __builtin_amdgcn_readlane(x, 32), d = __builtin_amdgcn_readlane(x, 48);
+  return max(max(a, b), max(c, d));
+}
+
 // Orders this wave's LDS writes before its later LDS reads (a wave's LDS
 // operations complete in issue order; this keeps the compiler from moving
 // them across the point).
@@ -104,9 +143,13 @@ __device__ __forceinline__ void wave_sync() {
 
 __device__ __forceinline__ float shfl_xor_f(float x, int mask) { return __shfl_xor(x, mask, 64); }
 
+// 2^x on the transcendental unit (v_exp_f32; results below 2^-126 may
+// flush to zero, which is below any tolerance here).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // exp2 that maps the empty-set case (both operands -inf) to 0.
 __device__ __forceinline__ float exp2_diff(float a, float m, float c) {
-  return (m == kNegInf) ? 0.0f : exp2f((a - m) * c);
+  return (m == kNegInf) ? 0.0f : fast_exp2((a - m) * c);
 }
 
 // ---------------------------------------------------------------- layout

@@ -13,6 +13,13 @@
 #include "dsa_common.hpp"
 #include "dsa_host.hpp"
 
+#ifndef DSA_SCORE_LOADS
+#define DSA_SCORE_LOADS 8  // metadata loads in flight per lane
+#endif
+#ifndef DSA_SCORE_WAVES
+#define DSA_SCORE_WAVES 8192  // target waves of the score grid
+#endif
+
 namespace dsa {
 
 // ============================================================ metadata build
@@ -106,7 +113,7 @@ __global__ __launch_bounds__(256) void score_kernel(
   using L_ = Lay<T, D>;
   constexpr int CPL = L_::CPL, DW = L_::DW;
   constexpr int LOADS_PER_64 = 64 * GL / 2;  // wave loads per 64 physical pages
-  constexpr int U = 4;                       // loads in flight per lane
+  constexpr int U = DSA_SCORE_LOADS;         // loads in flight per lane
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int b = blockIdx.z, h = blockIdx.y;
   const int j0 = (blockIdx.x * 4 + wave) * pages_per_wave;
@@ -236,10 +243,10 @@ static int launch_score_g(const void* q, const dsa_kv* kv, const void* meta, int
                           float* scores, hipStream_t st) {
   // Aim for ~8 waves per CU over 256 CUs; each wave walks a page range.
   const long long units = (long long)kv->batch * kv->n_kv_heads;
-  const long long target_waves = 2048;
+  const long long target_waves = DSA_SCORE_WAVES;
   long long ppw = (units * kv->max_pages + target_waves - 1) / target_waves;
-  ppw = ppw < 16 ? 16 : (ppw > 2048 ? 2048 : ppw);
-  ppw = (ppw + 15) / 16 * 16;
+  ppw = ppw < 8 ? 8 : (ppw > 2048 ? 2048 : ppw);
+  ppw = (ppw + 7) / 8 * 8;
   const int waves = ceil_div(kv->max_pages, ppw);
   dim3 grid(ceil_div(waves, 4), kv->n_kv_heads, kv->batch);
   hipLaunchKernelGGL((score_kernel<T, D, G, GL>), grid, dim3(256), 0, st, (const T*)q, (const T*)meta,

@@ -24,42 +24,48 @@ constexpr int kBuckets = 2048;
 // Exclusive prefix sum over the block (threads in index order) and the total.
 template <int NW>
 __device__ __forceinline__ int block_excl_scan(int x, int* smem /* NW ints */, int& total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int incl = x;
+  const int incl = wave_incl_scan(x);
+  if constexpr (NW == 1) {
+    total = __builtin_amdgcn_readlane(incl, 63);
+    return incl - x;
+  } else {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 63) smem[wave] = incl;
+    __syncthreads();
+    int before = 0;
+    total = 0;
 #pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int y = __shfl_up(incl, d, 64);
-    if (lane >= d) incl += y;
+    for (int w = 0; w < NW; ++w) {
+      const int s = smem[w];
+      if (w < wave) before += s;
+      total += s;
+    }
+    __syncthreads();
+    return before + incl - x;
   }
-  if (lane == 63) smem[wave] = incl;
-  __syncthreads();
-  int before = 0;
-  total = 0;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    const int s = smem[w];
-    if (w < wave) before += s;
-    total += s;
-  }
-  __syncthreads();
-  return before + incl - x;
 }
 
 template <int NW>
 __device__ __forceinline__ void block_minmax_u32(uint32_t& lo, uint32_t& hi, uint32_t* smem /* 2*NW */) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  lo = wave_min_u32(lo);
+  hi = wave_max_u32(hi);
+  if constexpr (NW > 1) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) { smem[2 * wave] = lo; smem[2 * wave + 1] = hi; }
+    __syncthreads();
+    lo = smem[0];
+    hi = smem[1];
 #pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) {
-    lo = min(lo, (uint32_t)__shfl_xor((int)lo, d, 64));
-    hi = max(hi, (uint32_t)__shfl_xor((int)hi, d, 64));
+    for (int w = 1; w < NW; ++w) { lo = min(lo, smem[2 * w]); hi = max(hi, smem[2 * w + 1]); }
+    __syncthreads();
   }
-  if (lane == 0) { smem[2 * wave] = lo; smem[2 * wave + 1] = hi; }
-  __syncthreads();
-  lo = smem[0];
-  hi = smem[1];
-#pragma unroll
-  for (int w = 1; w < NW; ++w) { lo = min(lo, smem[2 * w]); hi = max(hi, smem[2 * w + 1]); }
-  __syncthreads();
+}
+
+// Workgroup-wide LDS ordering point: a barrier, or for one wave a fence.
+template <int NW>
+__device__ __forceinline__ void group_sync() {
+  if constexpr (NW == 1) wave_sync();
+  else __syncthreads();
 }
 
 // float -> uint32 with the same order; -0.0 maps like +0.0.
@@ -89,18 +95,13 @@ __global__ __launch_bounds__(NW * 64) void topk_kernel(const float* __restrict__
   int32_t* out = ids + (size_t)unit * k;
 
   if ((streaming >> h) & 1ull) {
-    // pages holding a sink token or a local token, ascending
-    if (tid == 0) {
-      const int s_end = min(sink, L);
-      const int sink_pages = (s_end + P - 1) / P;
-      const int l_begin = max(0, L - local);
-      const int loc_first = (local > 0 && L > 0) ? l_begin / P : np;
-      int n = 0;
-      for (int pg = 0; pg < np && n < k; ++pg)
-        if (pg < sink_pages || pg >= loc_first) out[n++] = pg;
-      counts[unit] = n;
-      for (int x = n; x < k; ++x) out[x] = -1;
-    }
+    // pages holding a sink token or a local token, ascending: the list is
+    // [0, n_sink) followed by [l_first, np), so entry x is computed directly
+    const int n_sink = min(np, (min(sink, L) + P - 1) / P);
+    const int l_first = max(n_sink, (local > 0 && L > 0) ? max(0, L - local) / P : np);
+    const int n = min(k, n_sink + (np - l_first));
+    for (int x = tid; x < k; x += NT) out[x] = x < n ? (x < n_sink ? x : l_first + (x - n_sink)) : -1;
+    if (tid == 0) counts[unit] = n;
     return;
   }
 
@@ -126,11 +127,11 @@ __global__ __launch_bounds__(NW * 64) void topk_kernel(const float* __restrict__
       const uint32_t span = hi - lo;
       const int shift = span < (uint32_t)kBuckets ? 0 : (32 - __clz((int)span) - 11);
       for (int x = tid; x < kBuckets; x += NT) hist[x] = 0u;
-      __syncthreads();
+      group_sync<NW>();
 #pragma unroll
       for (int e = 0; e < E; ++e)
         if ((actm >> e) & 1ull) atomicAdd(&hist[(key[e] - lo) >> shift], 1u);
-      __syncthreads();
+      group_sync<NW>();
       // suffix scan: thread t owns buckets [(NT-1-t)*BPT, +BPT), so lower t = higher buckets
       const int b0 = (NT - 1 - tid) * BPT;
       int mine = 0;
@@ -145,7 +146,7 @@ __global__ __launch_bounds__(NW * 64) void topk_kernel(const float* __restrict__
           acc += hb;
         }
       }
-      __syncthreads();
+      group_sync<NW>();
       const uint32_t bstar = (uint32_t)s_bstar;
       const int above = s_above;
 #pragma unroll
@@ -159,7 +160,7 @@ __global__ __launch_bounds__(NW * 64) void topk_kernel(const float* __restrict__
       }
       need -= above;
       n_act = (int)hist[bstar];
-      __syncthreads();  // hist is rewritten by the next pass
+      group_sync<NW>();  // hist is rewritten by the next pass
     }
   } else {
     actm = 0ull;
@@ -217,14 +218,18 @@ extern "C" int dsa_page_select_topk(const float* scores, int32_t batch, int32_t 
   if (!scores || !seq_lens || !ids || !counts) return DSA_ERR_NULL;
   const int sink = stream_cfg ? stream_cfg->sink : 0, local = stream_cfg ? stream_cfg->local : 0;
   hipStream_t st = (hipStream_t)stream;
-  // ~8 keys per thread; 64..1024 threads
-  if (max_pages <= 128) return launch_topk_e<2, 1>(scores, batch, n_kv_heads, max_pages, seq_lens, page_size, k, smask, sink, local, ids, counts, st);
-  if (max_pages <= 512) return launch_topk_e<8, 1>(scores, batch, n_kv_heads, max_pages, seq_lens, page_size, k, smask, sink, local, ids, counts, st);
-  if (max_pages <= 1024) return launch_topk_e<8, 2>(scores, batch, n_kv_heads, max_pages, seq_lens, page_size, k, smask, sink, local, ids, counts, st);
-  if (max_pages <= 2048) return launch_topk_e<8, 4>(scores, batch, n_kv_heads, max_pages, seq_lens, page_size, k, smask, sink, local, ids, counts, st);
-  if (max_pages <= 4096) return launch_topk_e<8, 8>(scores, batch, n_kv_heads, max_pages, seq_lens, page_size, k, smask, sink, local, ids, counts, st);
-  if (max_pages <= 8192) return launch_topk_e<8, 16>(scores, batch, n_kv_heads, max_pages, seq_lens, page_size, k, smask, sink, local, ids, counts, st);
-  if (max_pages <= 16384) return launch_topk_e<16, 16>(scores, batch, n_kv_heads, max_pages, seq_lens, page_size, k, smask, sink, local, ids, counts, st);
-  if (max_pages <= 32768) return launch_topk_e<32, 16>(scores, batch, n_kv_heads, max_pages, seq_lens, page_size, k, smask, sink, local, ids, counts, st);
-  return launch_topk_e<64, 16>(scores, batch, n_kv_heads, max_pages, seq_lens, page_size, k, smask, sink, local, ids, counts, st);
+  // ~8 pages per thread; one wave up to 512 pages, up to 16 waves above
+  const int N = max_pages;
+#define DSA_TOPK(E, NW) return launch_topk_e<E, NW>(scores, batch, n_kv_heads, max_pages, seq_lens, page_size, k, \
+                                                     smask, sink, local, ids, counts, st)
+  if (N <= 256) DSA_TOPK(4, 1);
+  if (N <= 512) DSA_TOPK(8, 1);
+  if (N <= 1024) DSA_TOPK(4, 4);
+  if (N <= 2048) DSA_TOPK(8, 4);
+  if (N <= 4096) DSA_TOPK(8, 8);
+  if (N <= 8192) DSA_TOPK(8, 16);
+  if (N <= 16384) DSA_TOPK(16, 16);
+  if (N <= 32768) DSA_TOPK(32, 16);
+  DSA_TOPK(64, 16);
+#undef DSA_TOPK
 }

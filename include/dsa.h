@@ -31,7 +31,8 @@
  *   hipStream_t; NULL = the default stream) and returns.  Buffers must stay
  *   alive until that stream work completes.  Scratch memory comes from the
  *   caller's workspace `ws` of `ws_bytes` bytes, sized by
- *   dsa_workspace_bytes().
+ *   dsa_workspace_bytes(); its content needs no initialisation, and calls
+ *   that share one workspace must not overlap in time.
  * - Return value: DSA_OK (0) or a negative DSA_ERR_* code.  All arguments
  *   are validated on the host before anything is enqueued, so an error means
  *   no work was queued.  Errors inside a kernel surface at the caller's next

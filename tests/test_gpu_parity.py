@@ -341,7 +341,7 @@ def test_graph_replay_matches_eager(gpu_lib):
     O = torch.empty((B, 8, 128), device="cuda")
     l = torch.empty((B, 8), device="cuda")
     m = torch.empty((B, 8), device="cuda")
-    ws = torch.empty(dsa.workspace_bytes(dsa.OP_SPARSE_DECODE_ATTN, kv, 8, 40), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(dsa.workspace_bytes(dsa.OP_SPARSE_DECODE_ATTN, kv, 8, 40), dtype=torch.uint8, device="cuda")
 
     def step():
         dsa.page_score(q, kv, meta, scores=sc)
