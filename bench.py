@@ -2,22 +2,30 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
-A step is the whole hot path for one batch of decode queries: page scoring
-against key min/max metadata (with the GQA group-mean query), top-k page
-selection, and sparse attention over the selected pages (split-KV partials
-and their online-softmax combine).  Page metadata is built once beforehand,
-as it is during prefill.
+A step is the whole hot path for one batch of decode queries on inputs
+already resident in HBM; page metadata is built beforehand (prefill work).
 
-Default workload: Quest-style GQA decode, batch 1, 32 q / 8 KV heads,
-head_dim 128, 32768-token context in 16-token pages, 256-page budget, bf16
-KV.  Inputs are seeded synthetic data already resident in HBM.  Each timed
-step reads a different replica of the KV pool and metadata (R copies at
-distinct addresses, R * per-step bytes > 1 GiB), so the 256 MB Infinity
-Cache cannot serve repeated steps.
+  quest_gqa_32k (default)  page_score -> page_select_topk -> sparse_decode_attn
+      batch 1, 32 q / 8 KV heads, d=128, 32768 tokens in 16-token pages, top-256, bf16
+  lserve_hier_128k         the same three calls with 64/16 hierarchical paging and
+      4 of 8 KV heads streaming (sink 128 + local 256); batch 4, 131072 tokens, top-64
+  psa_mha_64k              page_score -> page_select_progressive (threshold 0.95)
+      batch 8, 32 heads MHA, 65536 tokens
+  prr_512k                 PRR: selection on a side stream overlapped with speculative
+      attention, then repair, EMA update and the next speculative set;
+      batch 1, 32 q / 2 KV heads, 524288 tokens, top-2048, 64-step query trace
+  tiny_f32                 score, top-8, attention and PSA on one fp32 head
 
-Output: one JSON line with queries/s, the per-step algorithmic HBM bytes and
-rate, a roofline entry for the dominant kernel call (timed with HIP events
-on its stream) and the CPU oracle's rate on a bounded sample.
+Each timed step reads a different replica of the KV pool and metadata (R
+copies at distinct addresses, R * per-step bytes > 1 GiB) so the 256 MB
+Infinity Cache cannot serve repeated steps; PRR replicas run interleaved
+64-step traces.  Exactly K steps are captured in one HIP graph and replayed
+between HIP events; per-call durations come from graphs of R launches of
+one call, timed the same way.
+
+Output: one JSON line (queries/s; one query = one sequence's decode token
+through all heads of one layer), the per-step algorithmic HBM bytes and
+rate, a roofline entry for the dominant call and the CPU oracle's rate.
 """
 from __future__ import annotations
 
@@ -35,6 +43,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 METRIC = "sparse decode attn+select: queries/sec and achieved HBM GB/s (% of peak)"
+WORKLOADS = ["quest_gqa_32k", "lserve_hier_128k", "psa_mha_64k", "prr_512k", "tiny_f32"]
 
 
 def parse():
@@ -42,7 +51,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="quest_gqa_32k", choices=["quest_gqa_32k"])
+    ap.add_argument("--workload", default="quest_gqa_32k", choices=WORKLOADS)
     ap.add_argument("--replicas", type=int, default=0, help="0 = enough for > 1 GiB per rotation")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU oracle sample")
     ap.add_argument("--no-cpu", action="store_true")
@@ -62,40 +71,6 @@ def copy_calibration(nbytes: int):
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes": nbytes, "dispatches": 10}))
-
-
-def algorithmic_bytes(bt, k_pages):
-    """Bytes a step must move from HBM: every valid page's metadata for the
-    scoring, plus K and V of the selected pages."""
-    elem = 2 if bt.dtype == "bf16" else 4
-    g = bt.page_size // bt.logical_page
-    units = bt.batch * bt.n_kv_heads
-    n_pages = min(bt.max_pages, -(-int(bt.seq_lens[0]) // bt.page_size))
-    meta = units * n_pages * g * 2 * bt.head_dim * elem
-    kv = units * min(k_pages, n_pages) * bt.page_size * bt.head_dim * 2 * elem
-    return meta, kv
-
-
-def cpu_baseline(bt, k_pages, budget_s):
-    """The oracle as it stands, single-threaded: whole decode steps of the
-    same workload (score every page of every (sequence, KV head), top-k,
-    attention of the group's q heads) repeated for about `budget_s` seconds;
-    queries/s = sequences * steps / time."""
-    import oracle
-    from threadpoolctl import threadpool_limits
-    meta, has = oracle.page_meta(bt)          # prefill-time work, not timed
-    steps, t_used = 0, 0.0
-    with threadpool_limits(1):
-        while t_used < budget_s:
-            t0 = time.perf_counter()
-            scores = oracle.page_scores(bt, meta=meta, has=has)
-            ids = oracle.select_topk(bt, scores, k_pages)
-            oracle.sparse_decode(bt, ids)
-            t_used += time.perf_counter() - t0
-            steps += 1
-    return {"value": bt.batch * steps / t_used, "unit": "queries/s", "cores": 1, "kind": "oracle",
-            "sample": f"{steps} whole decode steps of the workload ({bt.batch * bt.n_kv_heads} (sequence, KV head) "
-                      f"units each), {t_used:.1f} s single-threaded fp64 numpy"}
 
 
 def profiled_traffic(kernel: str, workload: str):
@@ -119,6 +94,108 @@ def profiled_traffic(kernel: str, workload: str):
     return None
 
 
+# --------------------------------------------------------------------------
+# algorithmic bytes
+# --------------------------------------------------------------------------
+def _elem(bt):
+    return 2 if bt.dtype == "bf16" else 4
+
+
+def _units(bt):
+    """(dense units, streaming units) as (sequence, KV head) counts."""
+    n_stream = 0 if bt.streaming is None else int(np.count_nonzero(bt.streaming))
+    return bt.batch * (bt.n_kv_heads - n_stream), bt.batch * n_stream
+
+
+def meta_bytes(bt):
+    """kmin + kmax of every valid logical page of every scored (dense) unit."""
+    dense, _ = _units(bt)
+    n_pages = min(bt.max_pages, -(-int(bt.seq_lens[0]) // bt.page_size))
+    return dense * n_pages * (bt.page_size // bt.logical_page) * 2 * bt.head_dim * _elem(bt)
+
+
+def page_kv_bytes(bt, pages_per_unit, units):
+    return int(units * pages_per_unit * bt.page_size * bt.head_dim * 2 * _elem(bt))
+
+
+def streaming_bytes(bt):
+    """K and V of the pages the streaming heads read (sink + local pages)."""
+    _, streaming_units = _units(bt)
+    if not streaming_units:
+        return 0
+    L = int(bt.seq_lens[0])
+    toks = set(range(min(bt.sink, L))) | set(range(max(0, L - bt.local), L))
+    pages = len({t // bt.page_size for t in toks})
+    return page_kv_bytes(bt, pages, streaming_units)
+
+
+# --------------------------------------------------------------------------
+# CPU baseline (the oracle as it stands)
+# --------------------------------------------------------------------------
+def cpu_baseline(bt, budget_s):
+    """The oracle, single-threaded, on whole decode steps of the workload
+    (PRR: the plain selection + attention its repair reproduces), repeated
+    for about `budget_s` seconds; queries/s = sequences * steps / time.
+    Batches of more than 16 (sequence, KV head) units run a fixed sample of
+    16 units and scale by the fraction."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+    units = None
+    if bt.batch * bt.n_kv_heads > 16:
+        rng = np.random.default_rng(0)
+        all_units = [(b, h) for b in range(bt.batch) for h in range(bt.n_kv_heads)]
+        units = set(all_units[i] for i in rng.choice(len(all_units), 16, replace=False))
+    frac = 1.0 if units is None else len(units) / (bt.batch * bt.n_kv_heads)
+    meta, has = oracle.page_meta(bt, units)          # prefill-time work, not timed
+    steps, t_used = 0, 0.0
+    with threadpool_limits(1):
+        while t_used < budget_s:
+            t0 = time.perf_counter()
+            scores = oracle.page_scores(bt, meta=meta, has=has, units=units)
+            for b in range(bt.batch):
+                for h in range(bt.n_kv_heads):
+                    if units is not None and (b, h) not in units:
+                        continue
+                    if bt.topk is None:
+                        oracle.psa_progressive(bt, b, h, scores[b, h], bt.threshold, 0)
+                        continue
+                    n = oracle.n_pages(bt.seq_lens[b], bt.page_size)
+                    if bt.streaming is not None and bt.streaming[h]:
+                        ids = oracle.streaming_pages(bt.seq_lens[b], bt.page_size, bt.sink, bt.local)
+                    else:
+                        ids = oracle.topk_pages(scores[b, h], n, bt.topk)
+                    oracle.attend_pages(bt, b, h, ids)
+                    if bt.threshold is not None:
+                        oracle.psa_progressive(bt, b, h, scores[b, h], bt.threshold, 0)
+            t_used += time.perf_counter() - t0
+            steps += 1
+    sample = (f"{steps} whole decode steps" if units is None else
+              f"{steps} decode steps of {len(units)} sampled (sequence, KV head) units, scaled by "
+              f"{1 / frac:.0f},")
+    return {"value": bt.batch * steps * frac / t_used, "unit": "queries/s", "cores": 1, "kind": "oracle",
+            "sample": f"{sample} of the workload; {t_used:.1f} s single-threaded fp64 numpy"}
+
+
+# --------------------------------------------------------------------------
+# GPU timing
+# --------------------------------------------------------------------------
+def replicate(dsa, torch, bt, R):
+    """R copies of pool, page table and metadata at distinct addresses;
+    returns one PagedKV view per replica and the metadata."""
+    base = dsa.PagedKV.from_numpy(bt.k, bt.v, bt.page_table, bt.seq_lens, bt.dtype)
+    S = base.num_slots
+    kbig = base.k.repeat(R, 1, 1, 1)
+    vbig = base.v.repeat(R, 1, 1, 1)
+    pts = torch.cat([torch.where(base.page_table < 0, base.page_table, base.page_table + r * S) for r in range(R)],
+                    0).contiguous()
+    sls = base.seq_lens.repeat(R).contiguous()
+    meta = dsa.page_meta_build(dsa.PagedKV(kbig, vbig, pts, sls), bt.logical_page)
+    B = bt.batch
+    kvs = [dsa.PagedKV(kbig, vbig, pts[r * B:(r + 1) * B].contiguous(), sls[r * B:(r + 1) * B].contiguous())
+           for r in range(R)]
+    return kvs, meta
+
+
 def main():
     a = parse()
     if a.copy_calibration:
@@ -135,61 +212,130 @@ def main():
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
     bt = wl.make(a.workload)
-    k_pages = bt.topk
-    meta_b, kv_b = algorithmic_bytes(bt, k_pages)
-    step_bytes = meta_b + kv_b
-    R = a.replicas or max(1, math.ceil((1 << 30) / step_bytes))
-
-    # --- resident inputs: R replicas of pool, tables and metadata ---------
-    q = dsa.upload_q(bt.q, bt.dtype)
-    base = dsa.PagedKV.from_numpy(bt.k, bt.v, bt.page_table, bt.seq_lens, bt.dtype)
-    S = base.num_slots
-    kbig = base.k.repeat(R, 1, 1, 1)
-    vbig = base.v.repeat(R, 1, 1, 1)
-    pts = torch.cat([base.page_table + r * S for r in range(R)], 0).contiguous()
-    pts = torch.where(base.page_table.repeat(R, 1) < 0, torch.full_like(pts, -1), pts).contiguous()
-    sls = base.seq_lens.repeat(R).contiguous()
-    allkv = dsa.PagedKV(kbig, vbig, pts, sls)
-    meta = dsa.page_meta_build(allkv, bt.logical_page)
-    del base
-    B = bt.batch
-    kvs = [dsa.PagedKV(kbig, vbig, pts[r * B:(r + 1) * B].contiguous(), sls[r * B:(r + 1) * B].contiguous())
-           for r in range(R)]
-    Hq, Hkv, D, N = bt.n_q_heads, bt.n_kv_heads, bt.head_dim, bt.max_pages
-    scores = torch.empty((B, Hkv, N), dtype=torch.float32, device=dev)
-    ids = torch.empty((B, Hkv, k_pages), dtype=torch.int32, device=dev)
-    counts = torch.empty((B, Hkv), dtype=torch.int32, device=dev)
-    O = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
-    l = torch.empty((B, Hq), dtype=torch.float32, device=dev)
-    m = torch.empty((B, Hq), dtype=torch.float32, device=dev)
-    ws = torch.zeros(dsa.workspace_bytes(dsa.OP_SPARSE_DECODE_ATTN, kvs[0], Hq, k_pages), dtype=torch.uint8,
-                     device=dev)
+    B, Hq, Hkv, D, N = bt.batch, bt.n_q_heads, bt.n_kv_heads, bt.head_dim, bt.max_pages
     scale = float(bt.scale)
+    st = None if bt.streaming is None else dsa.Streaming(bt.streaming, bt.sink, bt.local)
+    dense_units, _ = _units(bt)
+    mb = meta_bytes(bt)
+    f32, i32 = torch.float32, torch.int32
+    scores = torch.empty((B, Hkv, N), dtype=f32, device=dev)
+    O = torch.empty((B, Hq, D), dtype=f32, device=dev)
+    l = torch.empty((B, Hq), dtype=f32, device=dev)
+    m = torch.empty((B, Hq), dtype=f32, device=dev)
 
-    def step(r):
-        kv = kvs[r % R]
-        dsa.page_score(q, kv, meta, bt.logical_page, scores=scores)
-        dsa.page_select_topk(scores, kv.seq_lens, bt.page_size, k_pages, ids=ids, counts=counts)
-        dsa.sparse_decode_attn(q, kv, ids, counts, scale=scale, out=(O, l, m), ws=ws)
+    # per-step byte estimate for the replica count (refined below)
+    if a.workload == "prr_512k":
+        est = mb + 2 * page_kv_bytes(bt, bt.topk, B * Hkv)
+    elif a.workload == "psa_mha_64k":
+        est = mb
+    else:
+        est = mb + page_kv_bytes(bt, bt.topk, dense_units) + streaming_bytes(bt)
+    R = a.replicas or max(1, math.ceil((1 << 30) / est))
+    kvs, meta = replicate(dsa, torch, bt, R)
+    q = dsa.upload_q(bt.q, bt.dtype)
 
-    op_fns = {
-        "page_score": lambda r: dsa.page_score(q, kvs[r % R], meta, bt.logical_page, scores=scores),
-        "page_select_topk": lambda r: dsa.page_select_topk(scores, kvs[r % R].seq_lens, bt.page_size, k_pages,
-                                                           ids=ids, counts=counts),
-        "sparse_decode_attn": lambda r: dsa.sparse_decode_attn(q, kvs[r % R], ids, counts, scale=scale,
-                                                               out=(O, l, m), ws=ws),
-    }
+    extra = {}
+    if a.workload == "prr_512k":
+        from dynamic_sparse_attention_page_amd.prr import PRRDecoder
+        a_, b_, g_ = bt.extra["ema"]
+        T = bt.extra["steps"]
+        qt = torch.from_numpy(bt.extra["q_trace"].view(np.int16)).to(dev).view(torch.bfloat16)
+        decs = [PRRDecoder(kv, meta, Hq, bt.topk, a_, b_, g_, bt.extra["delta"], scale=scale) for kv in kvs]
+
+        def step(i):   # step i: replica i mod R at trace step (i // R) mod T
+            r = i % R
+            decs[r].t = (i // R) % T
+            decs[r].step(qt[decs[r].t])
+        # one pass over the traces: predictor state and the measured miss rate
+        miss, prev_p = [], None
+        for t in range(T):
+            for r in range(R):
+                decs[r].t = t
+                decs[r].step(qt[t])
+            torch.cuda.synchronize()
+            A = decs[0].a_ids.cpu().numpy()
+            if prev_p is not None:
+                miss.append(np.mean([len(set(A[0, h].tolist()) - set(prev_p[0, h].tolist())) / bt.topk
+                                     for h in range(Hkv)]))
+            prev_p = decs[0].p_ids.cpu().numpy()
+        miss_rate = float(np.mean(miss))
+        extra["prr_miss_rate"] = {"mean": miss_rate, "min": float(np.min(miss)), "max": float(np.max(miss))}
+        kvb = page_kv_bytes(bt, bt.topk, B * Hkv)
+        step_bytes = mb + kvb + miss_rate * kvb + B * Hkv * N * (24 + 8)
+        ops = {
+            "page_score": lambda r: dsa.page_score(q, kvs[r], meta, scores=decs[r].scores),
+            "page_select_topk": lambda r: dsa.page_select_topk(decs[r].scores, kvs[r].seq_lens, bt.page_size,
+                                                               bt.topk, ids=decs[r].a_ids, counts=decs[r].a_counts),
+            "sparse_decode_attn": lambda r: dsa.sparse_decode_attn(q, kvs[r], decs[r].p_ids, decs[r].p_counts,
+                                                                   scale=scale, out=(O, l, m), ws=decs[r].ws),
+            "attn_repair": lambda r: dsa.attn_repair(q, kvs[r], decs[r].a_ids, decs[r].a_counts, decs[r].p_ids,
+                                                     decs[r].p_counts, O, l, m, scale=scale, ws=decs[r].ws),
+            "ema_predict_update": lambda r: dsa.ema_predict_update(decs[r].scores, decs[r].level, decs[r].trend,
+                                                                   decs[r].pred, a_, b_, g_),
+        }
+        op_bytes = {"page_score": mb, "sparse_decode_attn": kvb, "ema_predict_update": B * Hkv * N * 24}
+    elif bt.topk is None or a.workload == "tiny_f32":   # PSA (and the tiny workload: top-k and PSA)
+        ids_p = torch.empty((B, Hkv, N), dtype=i32, device=dev)
+        cnt_p = torch.empty((B, Hkv), dtype=i32, device=dev)
+        Op = (torch.empty_like(O), torch.empty_like(l), torch.empty_like(m))
+        ops = {
+            "page_score": lambda r: dsa.page_score(q, kvs[r], meta, scores=scores),
+            "page_select_progressive": lambda r: dsa.page_select_progressive(
+                q, kvs[r], scores, bt.threshold, 0, scale, out=(ids_p, cnt_p, *Op)),
+        }
+        if bt.topk is not None:
+            ids = torch.empty((B, Hkv, bt.topk), dtype=i32, device=dev)
+            cnt = torch.empty((B, Hkv), dtype=i32, device=dev)
+            ws = torch.zeros(dsa.workspace_bytes(dsa.OP_SPARSE_DECODE_ATTN, kvs[0], Hq, bt.topk), dtype=torch.uint8,
+                             device=dev)
+            ops["page_select_topk"] = lambda r: dsa.page_select_topk(scores, kvs[r].seq_lens, bt.page_size,
+                                                                     bt.topk, ids=ids, counts=cnt)
+            ops["sparse_decode_attn"] = lambda r: dsa.sparse_decode_attn(q, kvs[r], ids, cnt, scale=scale,
+                                                                         out=(O, l, m), ws=ws)
+
+        def step(i):
+            for fn in ops.values():
+                fn(i % R)
+        step(0)
+        torch.cuda.synchronize()
+        visited = float(cnt_p.float().mean().item())
+        extra["psa_pages_visited"] = {"mean": visited, "max": int(cnt_p.max().item())}
+        step_bytes = mb + page_kv_bytes(bt, visited, B * Hkv)
+        op_bytes = {"page_score": mb, "page_select_progressive": page_kv_bytes(bt, visited, B * Hkv)}
+        if bt.topk is not None:
+            step_bytes += page_kv_bytes(bt, bt.topk, B * Hkv)
+            op_bytes["sparse_decode_attn"] = page_kv_bytes(bt, bt.topk, B * Hkv)
+    else:   # quest_gqa_32k, lserve_hier_128k
+        k_pages = bt.topk
+        ids = torch.empty((B, Hkv, k_pages), dtype=i32, device=dev)
+        cnt = torch.empty((B, Hkv), dtype=i32, device=dev)
+        ws = torch.zeros(dsa.workspace_bytes(dsa.OP_SPARSE_DECODE_ATTN, kvs[0], Hq, k_pages), dtype=torch.uint8,
+                         device=dev)
+        ops = {
+            "page_score": lambda r: dsa.page_score(q, kvs[r], meta, bt.logical_page, streaming=st, scores=scores),
+            "page_select_topk": lambda r: dsa.page_select_topk(scores, kvs[r].seq_lens, bt.page_size, k_pages,
+                                                               streaming=st, ids=ids, counts=cnt),
+            "sparse_decode_attn": lambda r: dsa.sparse_decode_attn(q, kvs[r], ids, cnt, streaming=st, scale=scale,
+                                                                   out=(O, l, m), ws=ws),
+        }
+
+        def step(i):
+            for fn in ops.values():
+                fn(i % R)
+        kvb = page_kv_bytes(bt, k_pages, dense_units) + streaming_bytes(bt)
+        step_bytes = mb + kvb
+        op_bytes = {"page_score": mb, "sparse_decode_attn": kvb}
 
     def capture(fn, n):
-        """A HIP graph of n calls (replica r = 0..n-1); launches stay on the
-        capture stream, no memset nodes."""
+        """A HIP graph of n calls fn(0..n-1) on the capture stream (no memset nodes)."""
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            for r in range(n):
-                fn(r)
+            for i in range(n):
+                fn(i)
         return g
 
     def time_graph(g, reps):
+        torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(reps):
@@ -198,7 +344,7 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1)
 
-    # eager (host-launched) step rate, for reference
+    # eager (host-launched) steps: warmup, and the reference eager rate
     for i in range(a.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -210,56 +356,56 @@ def main():
     torch.cuda.synchronize()
     eager_ms_step = e0.elapsed_time(e1) / a.steps
 
-    # timed region: exactly K steps (replica i mod R) replayed from one graph
+    # timed region: exactly K steps replayed from one graph
     g_step = capture(step, a.steps)
     g_step.replay()                       # untimed warm replay
-    torch.cuda.synchronize()
     ms = time_graph(g_step, 1)
-    n_steps = a.steps
-    ms_step = ms / n_steps
-    reps = max(1, math.ceil(a.steps / R))
+    ms_step = ms / a.steps
 
-    # per-call durations: a graph of R launches of one call, timed with
-    # events on the stream it replays on
-    ops = {}
-    for name, fn in op_fns.items():
+    # per-call durations: graphs of R launches of one call
+    reps = max(1, math.ceil(a.steps / R))
+    op_us = {}
+    for name, fn in ops.items():
         g = capture(fn, R)
         g.replay()
-        torch.cuda.synchronize()
-        ops[name] = time_graph(g, reps) / (reps * R) * 1e3   # us per call
-    bytes_of = {"page_score": meta_b, "sparse_decode_attn": kv_b}
-    dom = max(bytes_of, key=lambda k: ops[k])
-    dur_us, dom_bytes = ops[dom], bytes_of[dom]
+        op_us[name] = time_graph(g, reps) / (reps * R) * 1e3
+    dom = max(op_bytes, key=lambda k: op_us[k])
+    dur_us, dom_bytes = op_us[dom], op_bytes[dom]
     achieved = dom_bytes / (dur_us * 1e-6) / 1e9
 
+    cfg = {"workload": a.workload, "batch": B, "n_q_heads": Hq, "n_kv_heads": Hkv, "head_dim": D,
+           "seq_len": int(bt.seq_lens[0]), "page_size": bt.page_size, "logical_page": bt.logical_page,
+           "topk_pages": bt.topk, "threshold": bt.threshold, "kv_dtype": bt.dtype, "replicas": R,
+           "parallelism": "single GPU"}
+    if bt.streaming is not None:
+        cfg.update(streaming_kv_heads=int(np.count_nonzero(bt.streaming)), sink=bt.sink, local=bt.local)
     res = {
         "metric": METRIC,
-        "value": B * n_steps / (ms * 1e-3),
+        "value": B * a.steps / (ms * 1e-3),
         "unit": "queries/s",
         "n_gpus": 1,
-        "steps": n_steps,
+        "steps": a.steps,
         "warmup": a.warmup,
         "ms_per_step": ms_step,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": bt.dtype,
         "data": "synthetic",
-        "config": {"workload": a.workload, "batch": B, "n_q_heads": Hq, "n_kv_heads": Hkv, "head_dim": D,
-                   "seq_len": int(bt.seq_lens[0]), "page_size": bt.page_size, "topk_pages": k_pages,
-                   "replicas": R, "parallelism": "single GPU"},
-        "step_bytes": step_bytes,
+        "config": cfg,
+        "step_bytes": int(step_bytes),
         "step_GBps": step_bytes / (ms_step * 1e-3) / 1e9,
         "step_hbm_frac": step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-        "op_us": {k: round(v, 3) for k, v in ops.items()},
+        "op_us": {k: round(v, 3) for k, v in op_us.items()},
         "eager_ms_per_step": eager_ms_step,
-        "timing": "HIP graph of one step per replica, replayed; events on the replay stream",
+        "timing": "HIP graph of K steps replayed once between events; per-call graphs of R launches",
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": profiled_traffic(dom, a.workload),
-                     "bytes_per_launch": dom_bytes, "avg_launch_us": dur_us},
+                     "bytes_per_launch": int(dom_bytes), "avg_launch_us": dur_us},
     }
+    res.update(extra)
     if not a.no_cpu:
-        res["cpu_baseline"] = cpu_baseline(bt, k_pages, a.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(bt, a.cpu_seconds)
     print(json.dumps(res), flush=True)
 
 

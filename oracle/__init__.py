@@ -68,12 +68,13 @@ def page_tokens(pool: np.ndarray, dtype: str, page_table, b: int, h: int, page: 
 # --------------------------------------------------------------------------
 # step 1: page key metadata  (LServe section 4.2, Figure 7; PSA section 3.1)
 # --------------------------------------------------------------------------
-def page_meta(batch) -> tuple[np.ndarray, np.ndarray]:
+def page_meta(batch, units=None) -> tuple[np.ndarray, np.ndarray]:
     """kmin/kmax of every logical page, per channel, over its valid tokens.
 
     Returns ``meta[num_slots][Hkv][g][2][D]`` (index 0 = kmin, 1 = kmax) and
     ``has[num_slots][Hkv][g]`` (True where the logical page has at least one
-    valid token).  Slots no sequence uses stay NaN / False."""
+    valid token).  Slots no sequence uses stay NaN / False.  ``units``, a
+    set of (sequence, KV head) pairs, restricts the work to those."""
     P, Pl, D = batch.page_size, batch.logical_page, batch.head_dim
     g = P // Pl
     meta = np.full((batch.num_slots, batch.n_kv_heads, g, 2, D), np.nan)
@@ -83,6 +84,8 @@ def page_meta(batch) -> tuple[np.ndarray, np.ndarray]:
         for j in range(n_pages(L, P)):
             slot = int(batch.page_table[b][j])
             for h in range(batch.n_kv_heads):
+                if units is not None and (b, h) not in units:
+                    continue
                 keys = page_tokens(batch.k, batch.dtype, batch.page_table, b, h, j, L, P)
                 for s in range(g):
                     sub = keys[s * Pl:(s + 1) * Pl]
@@ -114,12 +117,13 @@ def criticality(qbar: np.ndarray, kmin: np.ndarray, kmax: np.ndarray) -> float:
     return float(np.sum(np.maximum(qbar * kmax, qbar * kmin)))
 
 
-def page_scores(batch, meta=None, has=None, q=None, with_logical: bool = False):
+def page_scores(batch, meta=None, has=None, q=None, with_logical: bool = False, units=None):
     """Physical page scores ``[B][Hkv][max_pages]``.  A physical page's score
     is the max of its logical pages' scores; pages past the sequence end and
-    every page of a streaming head score -inf."""
+    every page of a streaming head score -inf.  ``units`` restricts the work
+    to those (sequence, KV head) pairs (the others stay -inf)."""
     if meta is None:
-        meta, has = page_meta(batch)
+        meta, has = page_meta(batch, units)
     qbar = group_query(batch, q)
     P, Pl = batch.page_size, batch.logical_page
     g = P // Pl
@@ -129,6 +133,8 @@ def page_scores(batch, meta=None, has=None, q=None, with_logical: bool = False):
     for b in range(B):
         for h in range(Hkv):
             if batch.streaming is not None and batch.streaming[h]:
+                continue
+            if units is not None and (b, h) not in units:
                 continue
             for j in range(n_pages(batch.seq_lens[b], P)):
                 slot = int(batch.page_table[b][j])
