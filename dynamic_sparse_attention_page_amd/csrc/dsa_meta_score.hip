@@ -98,13 +98,15 @@ __global__ __launch_bounds__(256) void meta_build_kernel(
 }
 
 // ============================================================ page score
-// A wave walks a contiguous range of physical pages.  One wave-wide load
-// covers 4 vectors (rows): kmin and kmax of two logical pages.  Row r holds
-// vector (r & 1) (0 = kmin, 1 = kmax) of logical page "2u + (r >> 1)" of the
-// current group of loads.  Each lane multiplies its channels by the part of
-// qbar that selects its vector (qbar >= 0 picks kmax, qbar < 0 picks kmin),
-// so the sum over the two rows of a logical page is
-// sum_c max(qbar_c*kmax_c, qbar_c*kmin_c).
+// A wave walks a contiguous range of physical pages (one page-table load
+// for the whole range).  Row r of the wave takes logical page 4u + r of the
+// range in load pair u and each of its lanes loads the same 16 B channel
+// slice of that page's kmin and kmax.  With qpos = max(qbar, 0) and
+// qneg = min(qbar, 0) the lane term sum_c qpos*kmax + qneg*kmin summed over
+// the row (4 DPP steps) is sum_c max(qbar_c*kmax_c, qbar_c*kmin_c): no
+// cross-row traffic.  Loads of invalid pages are redirected to a valid
+// address and masked, so the loop has no divergent branches.  The physical
+// max over g = 2 or 4 logical pages combines rows with two swizzles.
 template <typename T, int D, int G, int GL>
 __global__ __launch_bounds__(256) void score_kernel(
     const T* __restrict__ q, const T* __restrict__ meta, const int32_t* __restrict__ page_table,
@@ -112,8 +114,7 @@ __global__ __launch_bounds__(256) void score_kernel(
     unsigned long long streaming, int pages_per_wave, float* __restrict__ scores) {
   using L_ = Lay<T, D>;
   constexpr int CPL = L_::CPL, DW = L_::DW;
-  constexpr int LOADS_PER_64 = 64 * GL / 2;  // wave loads per 64 physical pages
-  constexpr int U = DSA_SCORE_LOADS;         // loads in flight per lane
+  constexpr int U = DSA_SCORE_LOADS / 2;     // load pairs in flight per lane
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int b = blockIdx.z, h = blockIdx.y;
   const int j0 = (blockIdx.x * 4 + wave) * pages_per_wave;
@@ -127,11 +128,11 @@ __global__ __launch_bounds__(256) void score_kernel(
     for (int j = j0 + lane; j < j1; j += 64) srow[j] = kNegInf;
     return;
   }
-
   const int r = lane >> 4, cg = lane & 15;
-  const bool is_max = r & 1;
+  // slots of this wave's pages (pages_per_wave <= 64)
+  const int my_slot = (j0 + lane < min(j1, np)) ? page_table[(size_t)b * max_pages + j0 + lane] : -1;
   // group-mean query, this lane's channels, split by sign
-  float qsel[CPL];
+  float qpos[CPL], qneg[CPL];
   {
     float acc[CPL];
 #pragma unroll
@@ -146,60 +147,46 @@ __global__ __launch_bounds__(256) void score_kernel(
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
       const float qb = acc[c] * (1.0f / G);
-      qsel[c] = is_max ? fmaxf(qb, 0.0f) : fminf(qb, 0.0f);
+      qpos[c] = fmaxf(qb, 0.0f);
+      qneg[c] = fminf(qb, 0.0f);
     }
   }
-
   const size_t head_stride = (size_t)GL * 2 * D;  // elements of one (slot, head) metadata block
-  for (int c0 = j0; c0 < j1; c0 += 64) {
-    const int pj = c0 + lane;
-    const int my_slot = (pj < np) ? page_table[(size_t)b * max_pages + pj] : -1;
-    const int n_here = min(64, j1 - c0);
-    const int n_loads = (n_here * GL + 1) / 2;
-    float best = kNegInf;  // running physical max (GL == 4 spans two loads)
-    for (int u0 = 0; u0 < n_loads; u0 += U) {
-      uint32_t w[U][DW];
-      bool ok[U];
+  const int n_pairs = ((j1 - j0) * GL + 3) / 4;    // uniform
+  for (int u0 = 0; u0 < n_pairs; u0 += U) {
+    uint32_t wmin[U][DW], wmax[U][DW];
+    bool ok[U];
 #pragma unroll
-      for (int uu = 0; uu < U; ++uu) {
-        const int u = u0 + uu;
-        const int lp = 2 * u + (r >> 1);          // logical page index within the chunk
-        const int pl = lp / GL, sub = lp % GL;    // physical page (chunk-relative), sub-page
-        const int slot = __shfl(my_slot, pl & 63, 64);
-        const int pg = c0 + pl;
-        ok[uu] = (u < n_loads) && pl < n_here && pg < np && slot >= 0 && slot < num_slots &&
-                 pg * P + sub * Pl < L;
-        if (ok[uu]) {
-          load_dw<DW>(meta + ((size_t)slot * n_kv_heads + h) * head_stride + (size_t)sub * 2 * D +
-                          (size_t)(r & 1) * D + cg * CPL,
-                      w[uu]);
-        }
+    for (int uu = 0; uu < U; ++uu) {
+      const int lp = 4 * (u0 + uu) + r;            // logical page within the range
+      const int pl = lp / GL, sub = lp % GL;
+      const int slot = __shfl(my_slot, pl & 63, 64);
+      const int pg = j0 + pl;
+      ok[uu] = pg < j1 && pg < np && slot >= 0 && slot < num_slots && pg * P + sub * Pl < L;
+      const T* src = ok[uu] ? meta + ((size_t)slot * n_kv_heads + h) * head_stride + (size_t)sub * 2 * D + cg * CPL
+                            : meta + cg * CPL;        // valid address, result discarded
+      load_dw<DW>(src, wmin[uu]);
+      load_dw<DW>(src + D, wmax[uu]);
+    }
+#pragma unroll
+    for (int uu = 0; uu < U; ++uu) {
+      float part = 0.0f;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        part = fmaf(qpos[c], chan<T>(wmax[uu], c), part);
+        part = fmaf(qneg[c], chan<T>(wmin[uu], c), part);
       }
-#pragma unroll
-      for (int uu = 0; uu < U; ++uu) {
-        const int u = u0 + uu;
-        if (u >= n_loads) break;
-        float part = 0.0f;
-        if (ok[uu]) {
-#pragma unroll
-          for (int c = 0; c < CPL; ++c) part = fmaf(qsel[c], chan<T>(w[uu], c), part);
-        }
-        float s = row_sum(part);
-        s += shfl_xor_f(s, 16);          // kmin row + kmax row of the same logical page
-        if (!ok[uu]) s = kNegInf;        // invalid sub-page takes no part in the max
-        if constexpr (GL == 1) {
-          // rows 0-1: page 2u, rows 2-3: page 2u+1
-          const int pg = c0 + 2 * u + (r >> 1);
-          if ((lane == 0 || lane == 32) && 2 * u + (r >> 1) < n_here) srow[pg] = s;
-        } else if constexpr (GL == 2) {
-          s = fmaxf(s, shfl_xor_f(s, 32));
-          if (lane == 0 && u < n_here) srow[c0 + u] = s;
-        } else {  // GL == 4: loads 2v and 2v+1 make one physical page
-          s = fmaxf(s, shfl_xor_f(s, 32));
-          best = (u & 1) ? fmaxf(best, s) : s;
-          if ((u & 1) && lane == 0 && (u >> 1) < n_here) srow[c0 + (u >> 1)] = best;
-        }
+      float sc = row_sum(part);
+      if (!ok[uu]) sc = kNegInf;                  // invalid sub-page takes no part in the max
+      const int pl = (4 * (u0 + uu) + r) / GL;
+      if constexpr (GL == 2) {
+        sc = fmaxf(sc, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(sc), 0x401F)));  // rows ^1
+      } else if constexpr (GL == 4) {
+        sc = fmaxf(sc, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(sc), 0x401F)));  // rows ^1
+        sc = fmaxf(sc, __shfl_xor(sc, 32, 64));                                                     // rows ^2
       }
+      const bool writer = cg == 0 && (r % GL) == 0;
+      if (writer && j0 + pl < j1) srow[j0 + pl] = sc;
     }
   }
 }
@@ -241,12 +228,13 @@ extern "C" int dsa_page_meta_build(const dsa_kv* kv, int32_t logical_page, void*
 template <typename T, int D, int G, int GL>
 static int launch_score_g(const void* q, const dsa_kv* kv, const void* meta, int Pl, uint64_t smask,
                           float* scores, hipStream_t st) {
-  // Aim for ~8 waves per CU over 256 CUs; each wave walks a page range.
+  // Each wave walks a range of <= 64 physical pages (one page-table load);
+  // aim for DSA_SCORE_WAVES waves over the grid.
   const long long units = (long long)kv->batch * kv->n_kv_heads;
   const long long target_waves = DSA_SCORE_WAVES;
   long long ppw = (units * kv->max_pages + target_waves - 1) / target_waves;
-  ppw = ppw < 8 ? 8 : (ppw > 2048 ? 2048 : ppw);
-  ppw = (ppw + 7) / 8 * 8;
+  ppw = ppw < 4 ? 4 : (ppw > 64 ? 64 : ppw);
+  ppw = (ppw + 3) / 4 * 4;
   const int waves = ceil_div(kv->max_pages, ppw);
   dim3 grid(ceil_div(waves, 4), kv->n_kv_heads, kv->batch);
   hipLaunchKernelGGL((score_kernel<T, D, G, GL>), grid, dim3(256), 0, st, (const T*)q, (const T*)meta,

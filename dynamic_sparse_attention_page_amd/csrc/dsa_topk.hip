@@ -2,9 +2,9 @@
 // selection stage of a dynamic sparse attention step) and the fixed
 // sink/local page lists of streaming heads (LServe, section 4.1).
 //
-// One workgroup per (sequence, KV head); thread t owns the E consecutive
-// page indices [t*E, (t+1)*E) of the score row in registers, as 32-bit keys
-// with the order of the float scores (-0 and +0 equal).  Adaptive radix
+// One workgroup per (sequence, KV head) of NT threads; thread t owns page
+// indices t, t + NT, t + 2NT, ... (coalesced loads) in registers, as 32-bit
+// keys with the order of the float scores (-0 and +0 equal).  Adaptive radix
 // select: the keys still in play span [klo, khi]; bucket (key - klo) >> s,
 // with s chosen so the span fills at most 2048 buckets, is monotone in the
 // score and equal scores share a bucket.  An LDS histogram and a block
@@ -12,8 +12,9 @@
 // higher buckets are kept, lower ones dropped, and the pass repeats on that
 // bucket (each pass removes 11 bits of span, so at most 3) until it holds
 // exactly the pages still needed or only equal keys.  Those are taken in
-// index order -- the lower-index tie rule.  A block scan then writes the
-// kept indices in ascending order.
+// index order -- the lower-index tie rule.  Index-order ranks come from
+// per-(element slot, wave) ballot counts and one block scan over them; the
+// kept indices are written in ascending order the same way.
 #include "dsa_common.hpp"
 #include "dsa_host.hpp"
 
@@ -61,11 +62,45 @@ __device__ __forceinline__ void block_minmax_u32(uint32_t& lo, uint32_t& hi, uin
   }
 }
 
+// Index-order rank of every set bit of `mask` (bit e = element e * NT + tid)
+// among all set bits of the workgroup, and their total.  Slots (e, wave) are
+// counted with ballots, one block scan orders them, lanes add their rank in
+// the ballot.  cnt: E * NW ints of LDS.
+template <int E, int NW>
+__device__ __forceinline__ int ordered_ranks(unsigned long long mask, int (&rank)[E], int* cnt, int* scan_smem);
+
 // Workgroup-wide LDS ordering point: a barrier, or for one wave a fence.
 template <int NW>
 __device__ __forceinline__ void group_sync() {
   if constexpr (NW == 1) wave_sync();
   else __syncthreads();
+}
+
+template <int NW>
+__device__ __forceinline__ void group_sync();
+
+template <int E, int NW>
+__device__ __forceinline__ int ordered_ranks(unsigned long long mask, int (&rank)[E], int* cnt, int* scan_smem) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const unsigned long long below = (1ull << lane) - 1ull;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const unsigned long long b = __ballot((mask >> e) & 1ull);
+    rank[e] = __popcll(b & below);
+    if (lane == 0) cnt[e * NW + wave] = __popcll(b);
+  }
+  group_sync<NW>();
+  // E * NW <= NT: one slot per thread, scanned in (e, wave) order
+  const int tid = threadIdx.x;
+  const int v = tid < E * NW ? cnt[tid] : 0;
+  int total;
+  const int before = block_excl_scan<NW>(v, scan_smem, total);
+  if (tid < E * NW) cnt[tid] = before;
+  group_sync<NW>();
+#pragma unroll
+  for (int e = 0; e < E; ++e) rank[e] += cnt[e * NW + wave];
+  group_sync<NW>();   // cnt is reused by the next call
+  return total;
 }
 
 // float -> uint32 with the same order; -0.0 maps like +0.0.
@@ -85,6 +120,7 @@ __global__ __launch_bounds__(NW * 64) void topk_kernel(const float* __restrict__
   constexpr int BPT = kBuckets / NT;  // buckets per thread in the suffix scan
   __shared__ unsigned hist[kBuckets];
   __shared__ int scan_smem[NW];
+  __shared__ int rank_smem[E * NW];
   __shared__ uint32_t mm_smem[2 * NW];
   __shared__ int s_bstar, s_above;
   const int h = blockIdx.x, b = blockIdx.y;
@@ -111,7 +147,7 @@ __global__ __launch_bounds__(NW * 64) void topk_kernel(const float* __restrict__
   const float* srow = scores + (size_t)unit * max_pages;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    const int idx = tid * E + e;
+    const int idx = e * NT + tid;
     key[e] = idx < np ? order_key(srow[idx]) : 0u;
     if (idx < np) actm |= 1ull << e;
   }
@@ -168,21 +204,19 @@ __global__ __launch_bounds__(NW * 64) void topk_kernel(const float* __restrict__
   // the keys still in play are equal (or exactly `need` of them are left):
   // take them in index order
   {
-    int a_tot;
-    int before = block_excl_scan<NW>(__popcll(actm), scan_smem, a_tot);
+    int rk[E];
+    ordered_ranks<E, NW>(actm, rk, rank_smem, scan_smem);
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      if ((actm >> e) & 1ull) {
-        if (before < need) selm |= 1ull << e;
-        ++before;
-      }
-    }
+    for (int e = 0; e < E; ++e)
+      if (((actm >> e) & 1ull) && rk[e] < need) selm |= 1ull << e;
   }
-  int sel_total;
-  int pos = block_excl_scan<NW>(__popcll(selm), scan_smem, sel_total);
+  {
+    int rk[E];
+    ordered_ranks<E, NW>(selm, rk, rank_smem, scan_smem);
 #pragma unroll
-  for (int e = 0; e < E; ++e)
-    if (((selm >> e) & 1ull) && pos < keff) out[pos++] = tid * E + e;
+    for (int e = 0; e < E; ++e)
+      if (((selm >> e) & 1ull) && rk[e] < keff) out[rk[e]] = e * NT + tid;
+  }
   for (int x = keff + tid; x < k; x += NT) out[x] = -1;
   if (tid == 0) counts[unit] = keff;
 }
