@@ -13,11 +13,13 @@
 //   missing set M = A \ P, the split-KV path attends over M only, and the
 //   combine folds the caller's speculative (O, l, m) in as one more partial.
 // page_select_progressive (PSA, section 3.2, with the GPU-side weight check
-//   of section 3.3): one workgroup per (sequence, KV head) sorts the pages by
-//   score, computes the (o, l, m) of 16 pages at a time in parallel, then one
-//   thread walks them in rank order applying the stop test; no host sync.
+//   of section 3.3): one workgroup per (sequence, KV head) selects the next
+//   pages by score in rounds, computes the (o, l, m) of 16 of them at a time
+//   in parallel and applies the stop test to them in rank order with prefix
+//   scans; no host sync.
 #include "dsa_attn_core.hpp"
 #include "dsa_host.hpp"
+#include "dsa_select.hpp"
 
 #ifndef DSA_SPLIT_TARGET
 #define DSA_SPLIT_TARGET 384  // target workgroups of the split-KV grid
@@ -300,7 +302,22 @@ __global__ __launch_bounds__(256) void missing_set_kernel(const int32_t* __restr
 }
 
 // ============================================================ PSA progressive
-constexpr int kPsaWaves = 16;
+// One workgroup of NWV waves per (sequence, KV head).  Pages are taken in
+// rounds: the block radix select picks the next 64 (then 256) pages by score
+// among those not yet taken, a counting sort puts them in rank order (score
+// descending, lower index first on ties), and the walk attends to them NWV
+// at a time -- wave w computes the (o, l, m) of the page at rank cs + w.
+// The stop test of each group runs as prefix scans over NWV lanes of wave
+// 0: running log-sum of the block masses and running minimum, then the first
+// rank whose test passes ends the walk.  The visited blocks are folded into
+// the output with the online-softmax merge, in rank order.
+constexpr int kPsaMaxPages = 8192;
+constexpr int kPsaFirst = 64;    // pages of the first round
+constexpr int kPsaRound = 256;   // pages of each later round
+
+// 16 waves where a wave's tile state fits 128 registers, else 8
+template <typename T, int G>
+constexpr int psa_waves() { return (G == 1 && sizeof(T) == 2) ? 16 : 8; }
 
 __device__ __forceinline__ float log_add(float a, float b) {
   const float mx = fmaxf(a, b), mn = fminf(a, b);
@@ -309,21 +326,26 @@ __device__ __forceinline__ float log_add(float a, float b) {
 }
 
 template <typename T, int D, int G>
-__global__ __launch_bounds__(1024) void psa_kernel(
+__global__ __launch_bounds__((psa_waves<T, G>() * 64)) void psa_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const int32_t* __restrict__ page_table, const int32_t* __restrict__ seq_lens, const float* __restrict__ scores,
-    int n_kv_heads, int P, int max_pages, int num_slots, int np2, int stop_mode, int never_stop, int always_stop,
+    int n_kv_heads, int P, int max_pages, int num_slots, int stop_mode, int never_stop, int always_stop,
     float ln_odds, float scale, float c, int32_t* __restrict__ ids, int32_t* __restrict__ counts,
     float* __restrict__ O, float* __restrict__ l, float* __restrict__ m) {
   using A = AttnWave<T, D, G>;
   constexpr int CPL = A::CPL, DW = A::DW;
-  extern __shared__ unsigned long long keys[];  // np2 composite keys
-  __shared__ __align__(16) float lds_rows[kPsaWaves][A::LDS_FLOATS];
-  __shared__ __align__(16) float ch_o[kPsaWaves][G][D];
-  __shared__ float ch_ml[kPsaWaves][G][2];
-  __shared__ int s_take, s_stop;
+  constexpr int NWV = psa_waves<T, G>();
+  constexpr int NT = NWV * 64;
+  constexpr int E = kPsaMaxPages / NT;
+  static_assert(G * D <= NT, "one output element per thread");
+  __shared__ SelectSmem<E, NWV> sm;
+  __shared__ unsigned long long s_key[kPsaRound];  // picks of the round: score key << 32 | ~index
+  __shared__ int s_page[kPsaRound], s_slot[kPsaRound];  // in rank order
+  __shared__ __align__(16) float lds_rows[NWV][A::LDS_FLOATS];
+  __shared__ __align__(16) float ch_o[NWV][G][D];
+  __shared__ float ch_ml[NWV][G][2];
+  __shared__ int s_take, s_stop, s_left;
   __shared__ float s_lnacc, s_lnmin;
-  __shared__ int s_left;
 
   const int h = blockIdx.x, b = blockIdx.y;
   const int unit = b * n_kv_heads + h;
@@ -331,32 +353,17 @@ __global__ __launch_bounds__(1024) void psa_kernel(
   const int L = clamp_len(seq_lens[b], max_pages, P);
   const int np = (L + P - 1) / P;
   const float* srow = scores + (size_t)unit * max_pages;
+  int32_t* irow = ids + (size_t)unit * max_pages;
 
-  // 1. rank: composite key (score order key << 32 | ~index), sorted descending
-  for (int x = tid; x < np2; x += 1024) {
-    unsigned long long key = 0ull;
-    if (x < np) {
-      uint32_t u = __float_as_uint(srow[x]);
-      if (u == 0x80000000u) u = 0u;
-      u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-      key = ((unsigned long long)u << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)x);
-    }
-    keys[x] = key;
-  }
-  __syncthreads();
-  for (int size = 2; size <= np2; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = tid; i < np2 / 2; i += 1024) {
-        const int lo = 2 * stride * (i / stride) + (i % stride), hi = lo + stride;
-        const unsigned long long a = keys[lo], bq = keys[hi];
-        const bool desc = (lo & size) == 0;
-        if (desc ? (a < bq) : (a > bq)) { keys[lo] = bq; keys[hi] = a; }
-      }
-      __syncthreads();
-    }
+  uint32_t key[E];
+  unsigned long long remm = 0ull;  // bit e: page e * NT + tid not taken yet
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int idx = e * NT + tid;
+    key[e] = idx < np ? order_key(srow[idx]) : 0u;
+    if (idx < np) remm |= 1ull << e;
   }
 
-  // 2. progressive walk, 16 pages per chunk
   A st;
   st.init(q + ((size_t)b * n_kv_heads * G + (size_t)h * G) * D, lds_rows[wave]);
   const size_t slot_stride = (size_t)n_kv_heads * P * D;
@@ -364,93 +371,132 @@ __global__ __launch_bounds__(1024) void psa_kernel(
   const int TPP = P / 16;
   float acc_o = 0.0f, acc_l = 0.0f, acc_m = kNegInf;  // thread tid < G*D owns element tid
   const int my_h = tid / D, my_c = tid % D;
-  if (tid == 0) { s_lnacc = kNegInf; s_lnmin = __builtin_huge_valf(); s_left = np; }
-  int visited = 0;
-  for (int cs = 0; cs < np; cs += kPsaWaves) {
-    const int pos = cs + wave;
-    st.reset();
-    float pm[G], pl[G];
-    if (pos < np) {
-      const int page = (int)(0xFFFFFFFFu - (uint32_t)(keys[pos] & 0xFFFFFFFFull));
-      const int slot = page_table[(size_t)b * max_pages + page];
-      if (slot >= 0 && slot < num_slots) {
-        for (int tin = 0; tin < TPP; ++tin) {
-          const int tok0 = page * P + tin * 16;
-          const int nvalid = min(16, L - tok0);
-          if (nvalid <= 0) break;
-          uint32_t kd[4][DW], vd[4][DW];
-          const size_t off = (size_t)slot * slot_stride + head_off + (size_t)tin * 16 * D;
-          A::load_tile(k + off, lane, kd);
-          A::load_tile(v + off, lane, vd);
-          st.tile(kd, vd, nvalid, false, tok0, L, 0, 0, c);
-        }
-      }
-    }
-    st.finish(pm, pl, c);
-    if (lane < 16) {
+  if (tid == 0) { s_lnacc = kNegInf; s_lnmin = __builtin_huge_valf(); s_left = np; s_stop = 0; }
+  int visited = 0, n_rem = np;
+  bool stop = false;
+  for (int round = 0; !stop && n_rem > 0; ++round) {
+    // 1. the next pages by score, in rank order
+    const int n_pick = min(round == 0 ? kPsaFirst : kPsaRound, n_rem);
+    const unsigned long long pick = block_select_top<E, NWV>(key, remm, n_rem, n_pick, sm);
+    remm &= ~pick;
+    n_rem -= n_pick;
+    {
+      int rk[E];
+      ordered_ranks<E, NWV>(pick, rk, sm.rank, sm.scan);
 #pragma unroll
-      for (int hh = 0; hh < G; ++hh)
-#pragma unroll
-        for (int cc = 0; cc < CPL; ++cc) ch_o[wave][hh][lane * CPL + cc] = st.o[hh][cc];
-    }
-    if (lane == 0) {
-#pragma unroll
-      for (int hh = 0; hh < G; ++hh) {
-        ch_ml[wave][hh][0] = (pm[hh] == kNegInf) ? kNegInf : pm[hh] * scale;
-        ch_ml[wave][hh][1] = pl[hh];
-      }
+      for (int e = 0; e < E; ++e)
+        if ((pick >> e) & 1ull)
+          s_key[rk[e]] = ((unsigned long long)key[e] << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)(e * NT + tid));
     }
     __syncthreads();
-    // on-device stop test, in rank order
-    if (tid == 0) {
-      const int n_here = min(kPsaWaves, np - cs);
-      int take = n_here, stop = 0;
-      float lnacc = s_lnacc, lnmin = s_lnmin;
-      int left = s_left;
-      for (int w = 0; w < n_here; ++w) {
-        float ln_as = kNegInf;  // block mass summed over the group's heads, log domain
+    if (tid < n_pick) {
+      const unsigned long long mine = s_key[tid];
+      int r = 0;
+      for (int x = 0; x < n_pick; ++x) r += s_key[x] > mine ? 1 : 0;   // keys are distinct
+      const int page = (int)(0xFFFFFFFFu - (uint32_t)(mine & 0xFFFFFFFFull));
+      s_page[r] = page;
+      s_slot[r] = page_table[(size_t)b * max_pages + page];
+    }
+    __syncthreads();
+
+    // 2. walk the round NWV pages at a time
+    for (int cs = 0; cs < n_pick; cs += NWV) {
+      const int pos = cs + wave;
+      st.reset();
+      float pm[G], pl[G];
+      if (pos < n_pick) {
+        const int page = s_page[pos], slot = s_slot[pos];
+        if (slot >= 0 && slot < num_slots) {
+          for (int tin = 0; tin < TPP; ++tin) {
+            const int tok0 = page * P + tin * 16;
+            const int nvalid = min(16, L - tok0);
+            if (nvalid <= 0) break;
+            uint32_t kd[4][DW], vd[4][DW];
+            const size_t off = (size_t)slot * slot_stride + head_off + (size_t)tin * 16 * D;
+            A::load_tile(k + off, lane, kd);
+            A::load_tile(v + off, lane, vd);
+            st.tile(kd, vd, nvalid, false, tok0, L, 0, 0, c);
+          }
+        }
+      }
+      st.finish(pm, pl, c);
+      if (lane < 16) {
+#pragma unroll
         for (int hh = 0; hh < G; ++hh)
-          if (ch_ml[w][hh][1] > 0.0f) ln_as = log_add(ln_as, ch_ml[w][hh][0] + logf(ch_ml[w][hh][1]));
-        lnacc = log_add(lnacc, ln_as);
-        lnmin = fminf(lnmin, ln_as);
-        --left;
+#pragma unroll
+          for (int cc = 0; cc < CPL; ++cc) ch_o[wave][hh][lane * CPL + cc] = st.o[hh][cc];
+      }
+      if (lane == 0) {
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) {
+          ch_ml[wave][hh][0] = (pm[hh] == kNegInf) ? kNegInf : pm[hh] * scale;
+          ch_ml[wave][hh][1] = pl[hh];
+        }
+      }
+      __syncthreads();
+      // stop test in rank order: lane w of wave 0 stands for rank cs + w
+      if (wave == 0) {
+        const int n_here = min(NWV, n_pick - cs);
+        const bool here = lane < n_here;
+        float ln_as = kNegInf;  // block mass summed over the group's heads, log domain
+        if (here) {
+#pragma unroll
+          for (int hh = 0; hh < G; ++hh)
+            if (ch_ml[lane][hh][1] > 0.0f) ln_as = log_add(ln_as, ch_ml[lane][hh][0] + logf(ch_ml[lane][hh][1]));
+        }
+        float pacc = ln_as, pmin = here ? ln_as : __builtin_huge_valf();
+#pragma unroll
+        for (int sh = 1; sh < NWV; sh <<= 1) {
+          const float oa = __shfl_up(pacc, sh, NWV), om = __shfl_up(pmin, sh, NWV);
+          if ((lane & (NWV - 1)) >= sh) { pacc = log_add(pacc, oa); pmin = fminf(pmin, om); }
+        }
+        const float lnacc = log_add(s_lnacc, pacc);
+        const float lnmin = fminf(s_lnmin, pmin);
+        const int left = s_left - (lane + 1);
         bool pass;
         if (never_stop) pass = false;
         else if (always_stop) pass = true;
         else if (stop_mode == 0) pass = lnacc - lnmin >= ln_odds;
         else pass = (left == 0) || (lnacc - (lnmin + logf((float)left)) >= ln_odds);
-        if (pass) { take = w + 1; stop = 1; break; }
+        const unsigned long long hit = __ballot(here && pass);
+        const int take = hit ? (__ffsll((long long)hit)) : n_here;   // 1-based rank of the first pass
+        if (lane == take - 1) {
+          s_lnacc = lnacc;
+          s_lnmin = lnmin;
+          s_left = left;
+          s_take = take;
+          s_stop = hit ? 1 : 0;
+        }
       }
-      s_take = take;
-      s_stop = stop;
-      s_lnacc = lnacc;
-      s_lnmin = lnmin;
-      s_left = left;
-    }
-    __syncthreads();
-    const int take = s_take;
-    if (tid < G * D) {
-      for (int w = 0; w < take; ++w) {
-        const float mw = ch_ml[w][my_h][0];
-        const float mn = fmaxf(acc_m, mw);
-        if (mn == kNegInf) continue;
-        const float a = (acc_m == kNegInf) ? 0.0f : expf(acc_m - mn);
-        const float bw = (mw == kNegInf) ? 0.0f : expf(mw - mn);
-        acc_o = acc_o * a + ch_o[w][my_h][my_c] * bw;
-        acc_l = acc_l * a + ch_ml[w][my_h][1] * bw;
-        acc_m = mn;
+      __syncthreads();
+      const int take = s_take;
+      if (tid < G * D) {
+        float mx = acc_m;
+        for (int w = 0; w < take; ++w) mx = fmaxf(mx, ch_ml[w][my_h][0]);
+        if (mx != kNegInf) {
+          const float a = (acc_m == kNegInf) ? 0.0f : expf(acc_m - mx);
+          acc_o *= a;
+          acc_l *= a;
+          for (int w = 0; w < take; ++w) {
+            const float mw = ch_ml[w][my_h][0];
+            if (mw == kNegInf) continue;
+            const float bw = expf(mw - mx);
+            acc_o = fmaf(ch_o[w][my_h][my_c], bw, acc_o);
+            acc_l = fmaf(ch_ml[w][my_h][1], bw, acc_l);
+          }
+          acc_m = mx;
+        }
       }
+      if (tid < take) irow[visited + tid] = s_page[cs + tid];
+      visited += take;
+      stop = s_stop != 0;
+      __syncthreads();   // ch_o / ch_ml / s_* are rewritten next
+      if (stop) break;
     }
-    visited = cs + take;
-    const int stop = s_stop;
-    __syncthreads();
-    if (stop) break;
   }
 
   // 3. outputs
-  int32_t* irow = ids + (size_t)unit * max_pages;
-  for (int x = tid; x < max_pages; x += 1024)
-    irow[x] = (x < visited) ? (int)(0xFFFFFFFFu - (uint32_t)(keys[x] & 0xFFFFFFFFull)) : -1;
+  for (int x = visited + tid; x < max_pages; x += NT) irow[x] = -1;
   if (tid == 0) counts[unit] = visited;
   if (tid < G * D) {
     const size_t row = (size_t)b * n_kv_heads * G + (size_t)h * G + my_h;
@@ -581,19 +627,13 @@ static int max_lds_per_block() {
 template <typename T, int D, int G>
 static int launch_psa_g(const void* q, const dsa_kv* kv, const float* scores, float thr, int stop_mode, float scale,
                         int32_t* ids, int32_t* counts, float* O, float* l, float* m, hipStream_t st) {
-  using A = AttnWave<T, D, G>;
-  int np2 = 2;
-  while (np2 < kv->max_pages) np2 <<= 1;
-  const size_t dyn = (size_t)np2 * sizeof(unsigned long long);
-  const size_t stat = sizeof(float) * (kPsaWaves * A::LDS_FLOATS + kPsaWaves * G * D + kPsaWaves * G * 2) + 64;
-  if ((int)(dyn + stat) > max_lds_per_block()) return DSA_ERR_UNSUPPORTED;
   const int never_stop = thr >= 1.0f;
   const int always_stop = thr <= 0.0f;
   const float ln_odds = (never_stop || always_stop) ? 0.0f : (float)log((double)thr / (1.0 - (double)thr));
   const float c = scale * kLog2e;
-  hipLaunchKernelGGL((psa_kernel<T, D, G>), dim3(kv->n_kv_heads, kv->batch), dim3(1024), dyn, st, (const T*)q,
+  hipLaunchKernelGGL((psa_kernel<T, D, G>), dim3(kv->n_kv_heads, kv->batch), dim3(psa_waves<T, G>() * 64), 0, st, (const T*)q,
                      (const T*)kv->k, (const T*)kv->v, kv->page_table, kv->seq_lens, scores, kv->n_kv_heads,
-                     kv->page_size, kv->max_pages, kv->num_slots, np2, stop_mode, never_stop, always_stop, ln_odds,
+                     kv->page_size, kv->max_pages, kv->num_slots, stop_mode, never_stop, always_stop, ln_odds,
                      scale, c, ids, counts, O, l, m);
   return launch_status();
 }
@@ -678,7 +718,7 @@ extern "C" int dsa_page_select_progressive(const void* q, int32_t n_q_heads, con
   if (rc) return rc;
   if (stop_mode != 0 && stop_mode != 1) return DSA_ERR_SHAPE;
   if (threshold != threshold) return DSA_ERR_SHAPE;
-  if (kv->max_pages > 8192) return DSA_ERR_UNSUPPORTED;
+  if (kv->max_pages > kPsaMaxPages) return DSA_ERR_UNSUPPORTED;
   if (kv->batch == 0) return DSA_OK;
   if (!scores || !ids || !counts || !O || !l || !m) return DSA_ERR_NULL;
   hipStream_t st = (hipStream_t)stream;
