@@ -340,12 +340,14 @@ __global__ __launch_bounds__((psa_waves<T, G>() * 64)) void psa_kernel(
   static_assert(G * D <= NT, "one output element per thread");
   __shared__ SelectSmem<E, NWV> sm;
   __shared__ unsigned long long s_key[kPsaRound];  // picks of the round: score key << 32 | ~index
+  __shared__ uint32_t s_keys[kPsaMaxPages];            // score keys, element order
   __shared__ int s_page[kPsaRound], s_slot[kPsaRound];  // in rank order
   __shared__ __align__(16) float lds_rows[NWV][A::LDS_FLOATS];
   __shared__ __align__(16) float ch_o[NWV][G][D];
   __shared__ float ch_ml[NWV][G][2];
   __shared__ int s_take, s_stop, s_left;
   __shared__ float s_lnacc, s_lnmin;
+  __shared__ float s_wt[NWV][G], s_alpha[G], s_accm[G];  // merge weights; running max per head
 
   const int h = blockIdx.x, b = blockIdx.y;
   const int unit = b * n_kv_heads + h;
@@ -354,13 +356,18 @@ __global__ __launch_bounds__((psa_waves<T, G>() * 64)) void psa_kernel(
   const int np = (L + P - 1) / P;
   const float* srow = scores + (size_t)unit * max_pages;
   int32_t* irow = ids + (size_t)unit * max_pages;
+  const int32_t* ptrow = page_table + (size_t)b * max_pages;
 
+  // scores are loaded up to max_pages, so the loads do not wait for seq_lens
+  float sv[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) sv[e] = (e * NT + tid < max_pages) ? srow[e * NT + tid] : 0.0f;
   uint32_t key[E];
   unsigned long long remm = 0ull;  // bit e: page e * NT + tid not taken yet
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int idx = e * NT + tid;
-    key[e] = idx < np ? order_key(srow[idx]) : 0u;
+    key[e] = order_key(sv[e]);
     if (idx < np) remm |= 1ull << e;
   }
 
@@ -369,18 +376,28 @@ __global__ __launch_bounds__((psa_waves<T, G>() * 64)) void psa_kernel(
   const size_t slot_stride = (size_t)n_kv_heads * P * D;
   const size_t head_off = (size_t)h * P * D;
   const int TPP = P / 16;
-  float acc_o = 0.0f, acc_l = 0.0f, acc_m = kNegInf;  // thread tid < G*D owns element tid
+  float acc_o = 0.0f, acc_l = 0.0f;  // thread tid < G*D owns element tid
   const int my_h = tid / D, my_c = tid % D;
   if (tid == 0) { s_lnacc = kNegInf; s_lnmin = __builtin_huge_valf(); s_left = np; s_stop = 0; }
+  if (tid < G) s_accm[tid] = kNegInf;
   int visited = 0, n_rem = np;
   bool stop = false;
   for (int round = 0; !stop && n_rem > 0; ++round) {
-    // 1. the next pages by score, in rank order
+    // 1. the next pages by score, in rank order (the keys wait in LDS
+    //    while a round is walked)
+    if (round > 0) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) key[e] = s_keys[e * NT + tid];
+    }
     const int n_pick = min(round == 0 ? kPsaFirst : kPsaRound, n_rem);
     const unsigned long long pick = block_select_top<E, NWV>(key, remm, n_rem, n_pick, sm);
     remm &= ~pick;
     n_rem -= n_pick;
     {
+      if (round == 0) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) s_keys[e * NT + tid] = key[e];
+      }
       int rk[E];
       ordered_ranks<E, NWV>(pick, rk, sm.rank, sm.scan);
 #pragma unroll
@@ -391,11 +408,12 @@ __global__ __launch_bounds__((psa_waves<T, G>() * 64)) void psa_kernel(
     __syncthreads();
     if (tid < n_pick) {
       const unsigned long long mine = s_key[tid];
+      const int page = (int)(0xFFFFFFFFu - (uint32_t)(mine & 0xFFFFFFFFull));
+      const int slot = ptrow[page];   // in flight during the ranking loop
       int r = 0;
       for (int x = 0; x < n_pick; ++x) r += s_key[x] > mine ? 1 : 0;   // keys are distinct
-      const int page = (int)(0xFFFFFFFFu - (uint32_t)(mine & 0xFFFFFFFFull));
       s_page[r] = page;
-      s_slot[r] = page_table[(size_t)b * max_pages + page];
+      s_slot[r] = slot;
     }
     __syncthreads();
 
@@ -434,32 +452,58 @@ __global__ __launch_bounds__((psa_waves<T, G>() * 64)) void psa_kernel(
         }
       }
       __syncthreads();
-      // stop test in rank order: lane w of wave 0 stands for rank cs + w
+      // stop test in rank order: lane w of row 0 of wave 0 stands for rank
+      // cs + w.  Block masses are summed over the group's heads, kept as
+      // logs; prefix sums run in the linear domain relative to the largest.
       if (wave == 0) {
         const int n_here = min(NWV, n_pick - cs);
         const bool here = lane < n_here;
-        float ln_as = kNegInf;  // block mass summed over the group's heads, log domain
-        if (here) {
+        float mh[G];
+        float ln_as = kNegInf;
+        {
+          float mx = kNegInf;
 #pragma unroll
-          for (int hh = 0; hh < G; ++hh)
-            if (ch_ml[lane][hh][1] > 0.0f) ln_as = log_add(ln_as, ch_ml[lane][hh][0] + logf(ch_ml[lane][hh][1]));
-        }
-        float pacc = ln_as, pmin = here ? ln_as : __builtin_huge_valf();
+          for (int hh = 0; hh < G; ++hh) {
+            mh[hh] = here ? ch_ml[lane & (NWV - 1)][hh][0] : kNegInf;
+            mx = fmaxf(mx, mh[hh]);
+          }
+          if (mx != kNegInf) {
+            float sum = 0.0f;
 #pragma unroll
-        for (int sh = 1; sh < NWV; sh <<= 1) {
-          const float oa = __shfl_up(pacc, sh, NWV), om = __shfl_up(pmin, sh, NWV);
-          if ((lane & (NWV - 1)) >= sh) { pacc = log_add(pacc, oa); pmin = fminf(pmin, om); }
+            for (int hh = 0; hh < G; ++hh)
+              if (mh[hh] != kNegInf) sum = fmaf(ch_ml[lane & (NWV - 1)][hh][1], __expf(mh[hh] - mx), sum);
+            ln_as = sum > 0.0f ? mx + __logf(sum) : kNegInf;
+          }
         }
-        const float lnacc = log_add(s_lnacc, pacc);
-        const float lnmin = fminf(s_lnmin, pmin);
+        const float acc0 = s_lnacc;
+        const float big = fmaxf(acc0, row_max(ln_as));
+        float lnacc = kNegInf;
+        {
+          const float x = (ln_as == kNegInf) ? 0.0f : __expf(ln_as - big);
+          const float pre = row_scan_sum(x) + ((acc0 == kNegInf) ? 0.0f : __expf(acc0 - big));
+          if (big != kNegInf && pre > 0.0f) lnacc = big + __logf(pre);
+        }
+        const float lnmin = fminf(s_lnmin, row_scan_min(here ? ln_as : __builtin_huge_valf()));
         const int left = s_left - (lane + 1);
         bool pass;
         if (never_stop) pass = false;
         else if (always_stop) pass = true;
         else if (stop_mode == 0) pass = lnacc - lnmin >= ln_odds;
-        else pass = (left == 0) || (lnacc - (lnmin + logf((float)left)) >= ln_odds);
+        else pass = (left == 0) || (lnacc - (lnmin + __logf((float)left)) >= ln_odds);
         const unsigned long long hit = __ballot(here && pass);
         const int take = hit ? (__ffsll((long long)hit)) : n_here;   // 1-based rank of the first pass
+        // merge weights of the taken blocks, per head: exp(m_w - M), M the new running max
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) {
+          const float mo = s_accm[hh];
+          const float mt = lane < take ? mh[hh] : kNegInf;
+          const float M = fmaxf(mo, row_max(mt));
+          if (lane < NWV) s_wt[lane][hh] = (mt == kNegInf) ? 0.0f : __expf(mt - M);
+          if (lane == 0) {
+            s_alpha[hh] = (mo == kNegInf) ? (M == kNegInf ? 1.0f : 0.0f) : __expf(mo - M);
+            s_accm[hh] = M;
+          }
+        }
         if (lane == take - 1) {
           s_lnacc = lnacc;
           s_lnmin = lnmin;
@@ -471,20 +515,16 @@ __global__ __launch_bounds__((psa_waves<T, G>() * 64)) void psa_kernel(
       __syncthreads();
       const int take = s_take;
       if (tid < G * D) {
-        float mx = acc_m;
-        for (int w = 0; w < take; ++w) mx = fmaxf(mx, ch_ml[w][my_h][0]);
-        if (mx != kNegInf) {
-          const float a = (acc_m == kNegInf) ? 0.0f : expf(acc_m - mx);
-          acc_o *= a;
-          acc_l *= a;
-          for (int w = 0; w < take; ++w) {
-            const float mw = ch_ml[w][my_h][0];
-            if (mw == kNegInf) continue;
-            const float bw = expf(mw - mx);
-            acc_o = fmaf(ch_o[w][my_h][my_c], bw, acc_o);
-            acc_l = fmaf(ch_ml[w][my_h][1], bw, acc_l);
+        const float a = s_alpha[my_h];
+        acc_o *= a;
+        acc_l *= a;
+#pragma unroll
+        for (int w = 0; w < NWV; ++w) {
+          if (w < take) {
+            const float wt = s_wt[w][my_h];
+            acc_o = fmaf(ch_o[w][my_h][my_c], wt, acc_o);
+            acc_l = fmaf(ch_ml[w][my_h][1], wt, acc_l);
           }
-          acc_m = mx;
         }
       }
       if (tid < take) irow[visited + tid] = s_page[cs + tid];
@@ -503,7 +543,7 @@ __global__ __launch_bounds__((psa_waves<T, G>() * 64)) void psa_kernel(
     O[row * D + my_c] = acc_l > 0.0f ? acc_o / acc_l : 0.0f;
     if (my_c == 0) {
       l[row] = acc_l;
-      m[row] = acc_l > 0.0f ? acc_m : kNegInf;
+      m[row] = acc_l > 0.0f ? s_accm[my_h] : kNegInf;
     }
   }
 }

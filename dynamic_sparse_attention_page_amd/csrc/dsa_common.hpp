@@ -83,6 +83,35 @@ __device__ __forceinline__ float row_sum(float x) {
   return x;
 }
 
+// Row-wide max (all 16 lanes get it).
+__device__ __forceinline__ float row_max(float x) {
+  x = fmaxf(x, dpp<DPP_ROW_MIRROR>(x));
+  x = fmaxf(x, dpp<DPP_ROW_HALF_MIRROR>(x));
+  x = fmaxf(x, dpp<DPP_QUAD_XOR3>(x));
+  return fmaxf(x, dpp<DPP_QUAD_XOR1>(x));
+}
+
+// DPP move whose lanes with no source in the row take `fill`.
+template <int CTRL>
+__device__ __forceinline__ float dpp_fill(float x, float fill) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(fill), __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Inclusive prefix sum / min over the 16 lanes of each row (row_shr 1, 2, 4, 8).
+__device__ __forceinline__ float row_scan_sum(float x) {
+  x += dpp_fill<0x111>(x, 0.0f);
+  x += dpp_fill<0x112>(x, 0.0f);
+  x += dpp_fill<0x114>(x, 0.0f);
+  return x + dpp_fill<0x118>(x, 0.0f);
+}
+__device__ __forceinline__ float row_scan_min(float x) {
+  const float inf = __builtin_huge_valf();
+  x = fminf(x, dpp_fill<0x111>(x, inf));
+  x = fminf(x, dpp_fill<0x112>(x, inf));
+  x = fminf(x, dpp_fill<0x114>(x, inf));
+  return fminf(x, dpp_fill<0x118>(x, inf));
+}
+
 // Max / sum over the 4 lanes j, j+4, j+8, j+12 of a row.
 __device__ __forceinline__ float ror_max4(float x) {
   x = fmaxf(x, dpp<DPP_ROW_ROR4>(x));

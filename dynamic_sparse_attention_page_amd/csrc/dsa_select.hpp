@@ -5,16 +5,18 @@
 // A workgroup of NT = NW * 64 threads holds E keys per thread; thread t owns
 // element indices t, t + NT, t + 2NT, ... (bit e of a 64-bit mask stands for
 // element e * NT + t).  Keys are 32-bit with the order of the float scores
-// (-0 and +0 equal).  Adaptive radix select: the keys still in play span
-// [lo, hi]; bucket (key - lo) >> s, with s chosen so the span fills at most
-// 2048 buckets, is monotone in the key and equal keys share a bucket.  An
-// LDS histogram and a block suffix scan find the bucket holding the wanted
+// (-0 and +0 equal).  Radix select over the elements still in play, whose
+// keys span [lo, hi]: each pass maps them to at most 2048 buckets with a
+// map that is monotone in the key (equal keys share a bucket), builds an LDS
+// histogram, and a block suffix scan finds the bucket holding the wanted
 // rank; elements in higher buckets are chosen, lower ones dropped, and the
-// pass repeats on that bucket (each pass removes 11 bits of span, so at
-// most 3) until it holds exactly the elements still needed or only equal
-// keys.  Those are taken in index order -- the lower-index tie rule.
-// Index-order ranks come from per-(element slot, wave) ballot counts and one
-// block scan over them.
+// pass repeats on that bucket.  The first pass maps the score values
+// linearly onto the buckets (when they are finite), later passes take
+// (key - lo) >> s, which removes 11 bits of span per pass.  Once at most 64
+// elements are left they are ranked directly by (key, lower index first);
+// if more are left with equal keys, they are taken in index order -- the
+// lower-index tie rule either way.  Index-order ranks come from
+// per-(element slot, wave) ballot counts and one block scan over them.
 #pragma once
 
 #include "dsa_common.hpp"
@@ -22,14 +24,18 @@
 namespace dsa {
 
 constexpr int kBuckets = 2048;
+constexpr int kSmall = 64;  // elements left that are ranked directly
 
 template <int E, int NW>
 struct SelectSmem {
-  unsigned hist[kBuckets];
-  int scan[NW];
+  unsigned hist[2][kBuckets];        // alternate passes use alternate buffers
+  unsigned long long small[kSmall];
+  int scan[NW];                      // ordered_ranks
+  int pscan[2][NW];                  // pass scans, alternating
   int rank[E * NW];
-  uint32_t mm[2 * NW];
-  int bstar, above;
+  uint32_t mm[2][2 * NW];            // pass min/max, alternating
+  int bstar, above, n_small;
+  unsigned long long kappa;
 };
 
 // Workgroup-wide LDS ordering point: a barrier, or for one wave a fence.
@@ -60,22 +66,6 @@ __device__ __forceinline__ int block_excl_scan(int x, int* smem /* NW ints */, i
     }
     __syncthreads();
     return before + incl - x;
-  }
-}
-
-template <int NW>
-__device__ __forceinline__ void block_minmax_u32(uint32_t& lo, uint32_t& hi, uint32_t* smem /* 2*NW */) {
-  lo = wave_min_u32(lo);
-  hi = wave_max_u32(hi);
-  if constexpr (NW > 1) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    if (lane == 0) { smem[2 * wave] = lo; smem[2 * wave + 1] = hi; }
-    __syncthreads();
-    lo = smem[0];
-    hi = smem[1];
-#pragma unroll
-    for (int w = 1; w < NW; ++w) { lo = min(lo, smem[2 * w]); hi = max(hi, smem[2 * w + 1]); }
-    __syncthreads();
   }
 }
 
@@ -114,10 +104,63 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Inverse of order_key (the value of -0 comes back as +0).
+__device__ __forceinline__ float key_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// Bucket map of one pass: linear in the score value, or a key shift.
+struct BucketMap {
+  bool lin;
+  float f0, inv;
+  uint32_t lo;
+  int shift;
+  __device__ __forceinline__ uint32_t linear(uint32_t k) const {
+    return (uint32_t)fminf((key_value(k) - f0) * inv, (float)(kBuckets - 1));
+  }
+  __device__ __forceinline__ uint32_t shifted(uint32_t k) const { return (k - lo) >> shift; }
+};
+
 // Among the elements whose bit is set in `actm` (n_act of them over the
 // workgroup), choose the `need` with the largest keys, equal keys going to
 // the lower index.  Returns this thread's chosen bits.  All threads call it
-// with the same n_act and need.
+// with the same n_act and need; consecutive calls on one SelectSmem must be
+// separated by a workgroup barrier.
+// Min / max over the block with one barrier (smem alternates between calls
+// that are not separated by another barrier).
+template <int NW>
+__device__ __forceinline__ void block_minmax_1b(uint32_t& lo, uint32_t& hi, uint32_t* smem /* 2*NW */) {
+  lo = wave_min_u32(lo);
+  hi = wave_max_u32(hi);
+  if constexpr (NW > 1) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) { smem[2 * wave] = lo; smem[2 * wave + 1] = hi; }
+    __syncthreads();
+    lo = smem[0];
+    hi = smem[1];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) { lo = min(lo, smem[2 * w]); hi = max(hi, smem[2 * w + 1]); }
+  }
+}
+
+// Exclusive block scan with one barrier (smem alternates like above).
+template <int NW>
+__device__ __forceinline__ int block_excl_scan_1b(int x, int* smem /* NW */) {
+  const int incl = wave_incl_scan(x);
+  if constexpr (NW == 1) {
+    return incl - x;
+  } else {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 63) smem[wave] = incl;
+    __syncthreads();
+    int before = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w)
+      if (w < wave) before += smem[w];
+    return before + incl - x;
+  }
+}
+
 template <int E, int NW>
 __device__ __forceinline__ unsigned long long block_select_top(const uint32_t (&key)[E], unsigned long long actm,
                                                                int n_act, int need, SelectSmem<E, NW>& sm) {
@@ -128,31 +171,79 @@ __device__ __forceinline__ unsigned long long block_select_top(const uint32_t (&
   if (need >= n_act) return actm;
   const int tid = threadIdx.x;
   unsigned long long selm = 0ull;
-  for (int iter = 0; iter < 4; ++iter) {
+  for (int pass = 0; pass < 5; ++pass) {
+    if (n_act == need) return selm | actm;
+    if (n_act <= kSmall) {
+      // rank the few left by (key, lower index first); the need-th largest
+      // composite value is the cut
+      if (tid == 0) sm.n_small = 0;
+      group_sync<NW>();
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        if ((actm >> e) & 1ull) {
+          const int p = atomicAdd(&sm.n_small, 1);
+          sm.small[p] = ((unsigned long long)key[e] << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)(e * NT + tid));
+        }
+      group_sync<NW>();
+      if (tid < n_act) {
+        const unsigned long long mine = sm.small[tid];
+        int r = 0;
+        for (int x = 0; x < n_act; ++x) r += sm.small[x] > mine ? 1 : 0;
+        if (r == need - 1) sm.kappa = mine;
+      }
+      group_sync<NW>();
+      const uint32_t cut_key = (uint32_t)(sm.kappa >> 32);
+      const int cut_idx = (int)(0xFFFFFFFFu - (uint32_t)(sm.kappa & 0xFFFFFFFFull));
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        if (((actm >> e) & 1ull) && (key[e] > cut_key || (key[e] == cut_key && e * NT + tid <= cut_idx)))
+          selm |= 1ull << e;
+      return selm;   // the next writer of small / kappa / n_small passes a barrier first
+    }
+    unsigned* hist = sm.hist[pass & 1];
+    for (int x = tid; x < kBuckets; x += NT) hist[x] = 0u;   // last read two passes ago
     uint32_t lo = 0xFFFFFFFFu, hi = 0u;
 #pragma unroll
     for (int e = 0; e < E; ++e)
       if ((actm >> e) & 1ull) { lo = min(lo, key[e]); hi = max(hi, key[e]); }
-    block_minmax_u32<NW>(lo, hi, sm.mm);
-    if (n_act == need || lo == hi) break;
+    block_minmax_1b<NW>(lo, hi, sm.mm[pass & 1]);   // also orders the zeroing before the atomics
+    if (lo == hi) break;
+    BucketMap map;
     const uint32_t span = hi - lo;
-    const int shift = span < (uint32_t)kBuckets ? 0 : (32 - __clz((int)span) - 11);
-    for (int x = tid; x < kBuckets; x += NT) sm.hist[x] = 0u;
-    group_sync<NW>();
+    map.lo = lo;
+    map.shift = span < (uint32_t)kBuckets ? 0 : (32 - __clz((int)span) - 11);
+    map.lin = false;
+    map.f0 = 0.0f;
+    map.inv = 0.0f;
+    if (pass == 0 && span >= (uint32_t)kBuckets) {
+      const float f0 = key_value(lo), f1 = key_value(hi);
+      const float inv = (float)(kBuckets - 1) / (f1 - f0);
+      if (__builtin_isfinite(f0) && __builtin_isfinite(f1) && __builtin_isfinite(f1 - f0) && f1 > f0 &&
+          __builtin_isfinite(inv) && inv > 0.0f) {
+        map.lin = true;
+        map.f0 = f0;
+        map.inv = inv;
+      }
+    }
+    if (map.lin) {
 #pragma unroll
-    for (int e = 0; e < E; ++e)
-      if ((actm >> e) & 1ull) atomicAdd(&sm.hist[(key[e] - lo) >> shift], 1u);
+      for (int e = 0; e < E; ++e)
+        if ((actm >> e) & 1ull) atomicAdd(&hist[map.linear(key[e])], 1u);
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        if ((actm >> e) & 1ull) atomicAdd(&hist[map.shifted(key[e])], 1u);
+    }
     group_sync<NW>();
     // suffix scan: thread t owns buckets [(NT-1-t)*BPT, +BPT), so lower t = higher buckets
     const int b0 = (NT - 1 - tid) * BPT;
     int mine = 0;
 #pragma unroll
-    for (int x = 0; x < BPT; ++x) mine += (int)sm.hist[b0 + x];
-    int tot;
-    int acc = block_excl_scan<NW>(mine, sm.scan, tot);
+    for (int x = 0; x < BPT; ++x) mine += (int)hist[b0 + x];
+    int acc = block_excl_scan_1b<NW>(mine, sm.pscan[pass & 1]);
     if (acc < need && need <= acc + mine) {
       for (int x = BPT - 1; x >= 0; --x) {
-        const int hb = (int)sm.hist[b0 + x];
+        const int hb = (int)hist[b0 + x];
         if (acc + hb >= need) { sm.bstar = b0 + x; sm.above = acc; break; }
         acc += hb;
       }
@@ -160,21 +251,25 @@ __device__ __forceinline__ unsigned long long block_select_top(const uint32_t (&
     group_sync<NW>();
     const uint32_t bstar = (uint32_t)sm.bstar;
     const int above = sm.above;
+    auto classify = [&](auto bucket) {
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const unsigned long long bit = 1ull << e;
-      if (actm & bit) {
-        const uint32_t bk = (key[e] - lo) >> shift;
-        if (bk > bstar) { selm |= bit; actm &= ~bit; }
-        else if (bk < bstar) actm &= ~bit;
+      for (int e = 0; e < E; ++e) {
+        const unsigned long long bit = 1ull << e;
+        if (actm & bit) {
+          const uint32_t bk = bucket(key[e]);
+          if (bk > bstar) { selm |= bit; actm &= ~bit; }
+          else if (bk < bstar) actm &= ~bit;
+        }
       }
-    }
+    };
+    if (map.lin) classify([&](uint32_t k) { return map.linear(k); });
+    else classify([&](uint32_t k) { return map.shifted(k); });
     need -= above;
-    n_act = (int)sm.hist[bstar];
-    group_sync<NW>();  // hist is rewritten by the next pass
+    n_act = (int)hist[bstar];
+    // no barrier: bstar / above are next written after two more barriers,
+    // and this hist buffer is next zeroed two passes later
   }
-  // the keys still in play are equal (or exactly `need` of them are left):
-  // take them in index order
+  // the keys still in play are equal: take them in index order
   int rk[E];
   ordered_ranks<E, NW>(actm, rk, sm.rank, sm.scan);
 #pragma unroll

@@ -42,11 +42,14 @@ __global__ __launch_bounds__(NW * 64) void topk_kernel(const float* __restrict__
   uint32_t key[E];
   unsigned long long actm = 0ull;  // bit e: page e * NT + tid is valid
   const float* srow = scores + (size_t)unit * max_pages;
+  // scores are loaded up to max_pages, so the loads do not wait for seq_lens
+  float sv[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) sv[e] = (e * NT + tid < max_pages) ? srow[e * NT + tid] : 0.0f;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    const int idx = e * NT + tid;
-    key[e] = idx < np ? order_key(srow[idx]) : 0u;
-    if (idx < np) actm |= 1ull << e;
+    key[e] = order_key(sv[e]);
+    if (e * NT + tid < np) actm |= 1ull << e;
   }
   const unsigned long long selm = block_select_top<E, NW>(key, actm, np, keff, sm);
   {
