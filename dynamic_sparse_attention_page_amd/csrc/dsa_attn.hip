@@ -9,15 +9,17 @@
 //   group from one read of each K/V tile, merges its waves through LDS and
 //   writes one unnormalised partial (o, l, m); the combine kernel folds the
 //   partials of a head with the online-softmax merge.
-// attn_repair (PRR, sections 3.3-3.4): an LDS bitmap of P filters A into the
-//   missing set M = A \ P, the split-KV path attends over M only, and the
-//   combine folds the caller's speculative (O, l, m) in as one more partial.
+// attn_repair (PRR, sections 3.3-3.4): the split-KV path runs over A with
+//   an LDS bitmap of P in each workgroup, so only the missing set M = A \ P
+//   is attended, and the combine folds the caller's speculative (O, l, m) in
+//   as one more partial.
 // page_select_progressive (PSA, section 3.2, with the GPU-side weight check
 //   of section 3.3): one workgroup per (sequence, KV head) selects the next
 //   pages by score in rounds, computes the (o, l, m) of 16 of them at a time
 //   in parallel and applies the stop test to them in rank order with prefix
 //   scans; no host sync.
 #include "dsa_attn_core.hpp"
+#include "dsa_attn_mfma.hpp"
 #include "dsa_host.hpp"
 #include "dsa_select.hpp"
 
@@ -30,13 +32,14 @@ namespace dsa {
 constexpr int kWgWaves = 4;
 
 // ============================================================ split-KV partial
-template <typename T, int D, int G>
+template <typename T, int D, int G, bool FILTER>
 __global__ __launch_bounds__(256) void attn_partial_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const int32_t* __restrict__ page_table, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ ids, const int32_t* __restrict__ counts, int ids_stride, int n_kv_heads, int P,
     int max_pages, int num_slots, unsigned long long streaming, int sink, int local, float scale, float c,
-    int tiles_per_split, int n_splits, float* __restrict__ part_o, float* __restrict__ part_ml) {
+    int tiles_per_split, int n_splits, const int32_t* __restrict__ skip_ids,
+    const int32_t* __restrict__ skip_counts, float* __restrict__ part_o, float* __restrict__ part_ml) {
   using A = AttnWave<T, D, G>;
   constexpr int CPL = A::CPL, DW = A::DW;
   __shared__ __align__(16) float lds_rows[kWgWaves][A::LDS_FLOATS];
@@ -70,6 +73,22 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
   const int L = clamp_len(seq_lens[b], max_pages, P);
   const int np = (L + P - 1) / P;
   const bool smask = (streaming >> h) & 1ull;
+  if constexpr (FILTER) {
+    // pages listed in skip_ids (PRR's speculative set P) are left out: an
+    // LDS bitmap of them filters this split's entries (M = A \ P in place)
+    extern __shared__ uint32_t skip_bits[];
+    const int nwords = (max_pages + 31) >> 5;
+    for (int x = threadIdx.x; x < nwords; x += 256) skip_bits[x] = 0u;
+    __syncthreads();
+    int pc = skip_counts[unit];
+    pc = pc < 0 ? 0 : (pc > ids_stride ? ids_stride : pc);
+    for (int x = threadIdx.x; x < pc; x += 256) {
+      const int pg = skip_ids[(size_t)unit * ids_stride + x];
+      if (pg >= 0 && pg < max_pages) atomicOr(&skip_bits[pg >> 5], 1u << (pg & 31));
+    }
+    __syncthreads();
+    if (pg_raw >= 0 && pg_raw < max_pages && ((skip_bits[pg_raw >> 5] >> (pg_raw & 31)) & 1u)) sl_raw = -1;
+  }
 
   A st;
   st.init(q + ((size_t)b * n_kv_heads * G + (size_t)h * G) * D, lds_rows[wave]);
@@ -180,6 +199,132 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
   }
 }
 
+// ============================================================ split-KV partial, matrix cores
+// Same split and output as attn_partial_kernel, for bf16 KV with 8 or 16 q
+// heads per KV head: each wave runs the MFMA tile of dsa_attn_mfma.hpp over
+// its tiles, and the 4 wave states meet in LDS.
+template <int D, int G, bool FILTER>
+__global__ __launch_bounds__(256) void attn_partial_mfma_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const int32_t* __restrict__ page_table, const int32_t* __restrict__ seq_lens,
+    const int32_t* __restrict__ ids, const int32_t* __restrict__ counts, int ids_stride, int n_kv_heads, int P,
+    int max_pages, int num_slots, unsigned long long streaming, int sink, int local, float scale, float c,
+    int tiles_per_split, int n_splits, const int32_t* __restrict__ skip_ids,
+    const int32_t* __restrict__ skip_counts, float* __restrict__ part_o, float* __restrict__ part_ml) {
+  using M = MfmaWave<D, G>;
+  constexpr int NK = M::NK, NB = M::NB;
+  constexpr int OS = D + 4;   // LDS row stride of the merge buffer (floats)
+  __shared__ __align__(16) uint16_t lds_v[kWgWaves][M::LDS_ELEMS];
+  __shared__ __align__(16) float lds_o[kWgWaves][G][OS];
+  __shared__ float lds_ml[kWgWaves][G][2];
+
+  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int unit = b * n_kv_heads + h;
+  const int TPP = P / 16;
+  const int t_begin = split * tiles_per_split;
+  const int first_entry = t_begin / TPP;
+  int pg_raw = -1, sl_raw = -1;
+  if (lane < tiles_per_split / TPP && first_entry + lane < ids_stride) {
+    pg_raw = ids[(size_t)unit * ids_stride + first_entry + lane];
+    if (pg_raw >= 0 && pg_raw < max_pages) sl_raw = page_table[(size_t)b * max_pages + pg_raw];
+  }
+  int cnt = counts[unit];
+  cnt = cnt < 0 ? 0 : (cnt > ids_stride ? ids_stride : cnt);
+  const int n_tiles = cnt * TPP;
+  if (t_begin >= n_tiles) return;  // whole workgroup: the combine reads only active splits
+  const int t_end = min(n_tiles, t_begin + tiles_per_split);
+  const int L = clamp_len(seq_lens[b], max_pages, P);
+  const int np = (L + P - 1) / P;
+  const bool smask = (streaming >> h) & 1ull;
+  if constexpr (FILTER) {
+    // pages listed in skip_ids (PRR's speculative set P) are left out: an
+    // LDS bitmap of them filters this split's entries (M = A \ P in place)
+    extern __shared__ uint32_t skip_bits[];
+    const int nwords = (max_pages + 31) >> 5;
+    for (int x = threadIdx.x; x < nwords; x += 256) skip_bits[x] = 0u;
+    __syncthreads();
+    int pc = skip_counts[unit];
+    pc = pc < 0 ? 0 : (pc > ids_stride ? ids_stride : pc);
+    for (int x = threadIdx.x; x < pc; x += 256) {
+      const int pg = skip_ids[(size_t)unit * ids_stride + x];
+      if (pg >= 0 && pg < max_pages) atomicOr(&skip_bits[pg >> 5], 1u << (pg & 31));
+    }
+    __syncthreads();
+    if (pg_raw >= 0 && pg_raw < max_pages && ((skip_bits[pg_raw >> 5] >> (pg_raw & 31)) & 1u)) sl_raw = -1;
+  }
+
+  M st;
+  st.init(q + ((size_t)b * n_kv_heads * G + (size_t)h * G) * D, lds_v[wave]);
+
+  const int n_entries = (t_end - 1) / TPP - first_entry + 1;
+  int my_page = -1, my_slot = -1;
+  if (lane < n_entries && pg_raw >= 0 && pg_raw < np && sl_raw >= 0 && sl_raw < num_slots) {
+    my_page = pg_raw;
+    my_slot = sl_raw;
+  }
+  const size_t slot_stride = (size_t)n_kv_heads * P * D;
+  const size_t head_off = (size_t)h * P * D;
+
+  uint4 ka[NK], va[NK], kb[NK], vb[NK];
+  int nva = 0, tka = 0, nvb = 0, tkb = 0;
+  auto fetch = [&](int t, uint4 (&kd)[NK], uint4 (&vd)[NK], int& nvalid, int& tok0) {
+    nvalid = 0;
+    tok0 = 0;
+    if (t >= t_end) return;
+    const int e = t / TPP - first_entry, tin = t % TPP;
+    const int page = __builtin_amdgcn_readlane(my_page, e);
+    const int slot = __builtin_amdgcn_readlane(my_slot, e);
+    if (slot < 0) return;
+    tok0 = page * P + tin * 16;
+    nvalid = min(16, L - tok0);
+    const size_t off = (size_t)slot * slot_stride + head_off + (size_t)tin * 16 * D;
+    M::load_k(k + off, lane, kd);
+    M::load_v(v + off, lane, vd);
+  };
+  int t = t_begin + wave;
+  fetch(t, ka, va, nva, tka);
+  while (t < t_end) {
+    fetch(t + kWgWaves, kb, vb, nvb, tkb);
+    if (nva > 0) st.tile(ka, va, nva, smask, tka, L, sink, local, c);
+    t += kWgWaves;
+    if (t >= t_end) break;
+    fetch(t + kWgWaves, ka, va, nva, tka);
+    if (nvb > 0) st.tile(kb, vb, nvb, smask, tkb, L, sink, local, c);
+    t += kWgWaves;
+  }
+
+  // wave states meet in LDS: lane holds O[head h][16n + 4g + j]
+  const float lsum = st.total_l();
+  if (st.h < G) {
+#pragma unroll
+    for (int n = 0; n < NB; ++n)
+      *reinterpret_cast<float4*>(&lds_o[wave][st.h][16 * n + 4 * st.g]) =
+          make_float4(st.acc[n][0], st.acc[n][1], st.acc[n][2], st.acc[n][3]);
+    if (st.g == 0) { lds_ml[wave][st.h][0] = st.m; lds_ml[wave][st.h][1] = lsum; }
+  }
+  __syncthreads();
+  const size_t pbase = ((size_t)unit * n_splits + split) * G;
+  for (int idx = threadIdx.x; idx < G * D; idx += 256) {
+    const int hh = idx / D, cc = idx % D;
+    float mm = kNegInf;
+#pragma unroll
+    for (int w = 0; w < kWgWaves; ++w) mm = fmaxf(mm, lds_ml[w][hh][0]);
+    float acc = 0.0f, ls = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWgWaves; ++w) {
+      const float wt = exp2_diff(lds_ml[w][hh][0], mm, c);
+      acc = fmaf(lds_o[w][hh][cc], wt, acc);
+      ls = fmaf(lds_ml[w][hh][1], wt, ls);
+    }
+    part_o[(pbase + hh) * D + cc] = acc;
+    if (cc == 0) {
+      part_ml[(pbase + hh) * 2 + 0] = (mm == kNegInf) ? kNegInf : mm * scale;  // natural-log units
+      part_ml[(pbase + hh) * 2 + 1] = ls;
+    }
+  }
+}
+
 // ============================================================ combine
 // One workgroup (4 waves) per (sequence, q head).  The active splits' maxima
 // are reduced first; then wave w sums splits w, w+4, ... with weights
@@ -254,51 +399,6 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(
       m[row] = L > 0.0f ? M : kNegInf;
     }
   }
-}
-
-// ============================================================ repair filter
-// M = entries of A not in P, in A's order (one workgroup per unit).
-__global__ __launch_bounds__(256) void missing_set_kernel(const int32_t* __restrict__ a_ids,
-                                                          const int32_t* __restrict__ a_counts,
-                                                          const int32_t* __restrict__ p_ids,
-                                                          const int32_t* __restrict__ p_counts, int ids_stride,
-                                                          int max_pages, int32_t* __restrict__ m_ids,
-                                                          int32_t* __restrict__ m_counts) {
-  extern __shared__ uint32_t bits[];  // ceil(max_pages / 32) words
-  __shared__ int wave_tot[4];
-  const int unit = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nwords = (max_pages + 31) / 32;
-  for (int x = tid; x < nwords; x += 256) bits[x] = 0u;
-  __syncthreads();
-  int pc = p_counts[unit];
-  pc = pc < 0 ? 0 : (pc > ids_stride ? ids_stride : pc);
-  for (int x = tid; x < pc; x += 256) {
-    const int pg = p_ids[(size_t)unit * ids_stride + x];
-    if (pg >= 0 && pg < max_pages) atomicOr(&bits[pg >> 5], 1u << (pg & 31));
-  }
-  __syncthreads();
-  int ac = a_counts[unit];
-  ac = ac < 0 ? 0 : (ac > ids_stride ? ids_stride : ac);
-  int base = 0;
-  for (int x0 = 0; x0 < ac; x0 += 256) {
-    const int x = x0 + tid;
-    int pg = -1;
-    bool keep = false;
-    if (x < ac) {
-      pg = a_ids[(size_t)unit * ids_stride + x];
-      keep = pg >= 0 && pg < max_pages && !((bits[pg >> 5] >> (pg & 31)) & 1u);
-    }
-    const unsigned long long mask = __ballot(keep);
-    const int before = __popcll(mask & ((1ull << lane) - 1ull));
-    if (lane == 0) wave_tot[wave] = __popcll(mask);
-    __syncthreads();
-    int off = base;
-    for (int w = 0; w < wave; ++w) off += wave_tot[w];
-    if (keep) m_ids[(size_t)unit * ids_stride + off + before] = pg;
-    base += wave_tot[0] + wave_tot[1] + wave_tot[2] + wave_tot[3];
-    __syncthreads();
-  }
-  if (tid == 0) m_counts[unit] = base;
 }
 
 // ============================================================ PSA progressive
@@ -589,17 +689,28 @@ inline size_t partial_bytes(const dsa_kv* kv, int G, int ids_stride) {
 template <typename T, int D, int G>
 static int launch_attn_g(const void* q, const dsa_kv* kv, const int32_t* ids, const int32_t* counts,
                          int ids_stride, uint64_t smask, int sink, int local, float scale, float* O, float* l,
-                         float* m, void* ws, int fold, hipStream_t st) {
+                         float* m, void* ws, int fold, const int32_t* skip_ids, const int32_t* skip_counts,
+                         hipStream_t st) {
   const SplitPlan p = plan_splits(kv, ids_stride, __builtin_popcountll(smask));
   const size_t units = (size_t)kv->batch * kv->n_kv_heads;
   float* part_o = (float*)ws;
   float* part_ml = (float*)((char*)ws + align256(units * max_splits_of(kv, ids_stride) * G * D * sizeof(float)));
   const float c = scale * kLog2e;
   dim3 grid(p.n_splits, kv->n_kv_heads, kv->batch);
-  hipLaunchKernelGGL((attn_partial_kernel<T, D, G>), grid, dim3(256), 0, st, (const T*)q, (const T*)kv->k,
-                     (const T*)kv->v, kv->page_table, kv->seq_lens, ids, counts, ids_stride, kv->n_kv_heads,
-                     kv->page_size, kv->max_pages, kv->num_slots, (unsigned long long)smask, sink, local, scale, c,
-                     p.tiles_per_split, p.n_splits, part_o, part_ml);
+  const size_t dyn = skip_ids ? (size_t)((kv->max_pages + 31) / 32) * sizeof(uint32_t) : 0;
+#define DSA_PARTIAL(KERNEL, TT, ...)                                                                             \
+  hipLaunchKernelGGL((KERNEL<__VA_ARGS__>), grid, dim3(256), dyn, st, (const TT*)q, (const TT*)kv->k,           \
+                     (const TT*)kv->v, kv->page_table, kv->seq_lens, ids, counts, ids_stride, kv->n_kv_heads,   \
+                     kv->page_size, kv->max_pages, kv->num_slots, (unsigned long long)smask, sink, local, scale, \
+                     c, p.tiles_per_split, p.n_splits, skip_ids, skip_counts, part_o, part_ml)
+  if constexpr (sizeof(T) == 2 && G >= 8) {
+    if (skip_ids) DSA_PARTIAL(attn_partial_mfma_kernel, uint16_t, D, G, true);
+    else DSA_PARTIAL(attn_partial_mfma_kernel, uint16_t, D, G, false);
+  } else {
+    if (skip_ids) DSA_PARTIAL(attn_partial_kernel, T, T, D, G, true);
+    else DSA_PARTIAL(attn_partial_kernel, T, T, D, G, false);
+  }
+#undef DSA_PARTIAL
   int rc = launch_status();
   if (rc) return rc;
   hipLaunchKernelGGL((attn_combine_kernel<D>), dim3(kv->n_kv_heads * G, kv->batch), dim3(256), 0, st, part_o,
@@ -611,26 +722,28 @@ static int launch_attn_g(const void* q, const dsa_kv* kv, const int32_t* ids, co
 template <typename T, int D>
 static int launch_attn_d(const void* q, int G, const dsa_kv* kv, const int32_t* ids, const int32_t* counts,
                          int ids_stride, uint64_t smask, int sink, int local, float scale, float* O, float* l,
-                         float* m, void* ws, int fold, hipStream_t st) {
+                         float* m, void* ws, int fold, const int32_t* skip_ids, const int32_t* skip_counts,
+                         hipStream_t st) {
   switch (G) {
-    case 1: return launch_attn_g<T, D, 1>(q, kv, ids, counts, ids_stride, smask, sink, local, scale, O, l, m, ws, fold, st);
-    case 2: return launch_attn_g<T, D, 2>(q, kv, ids, counts, ids_stride, smask, sink, local, scale, O, l, m, ws, fold, st);
-    case 4: return launch_attn_g<T, D, 4>(q, kv, ids, counts, ids_stride, smask, sink, local, scale, O, l, m, ws, fold, st);
-    case 8: return launch_attn_g<T, D, 8>(q, kv, ids, counts, ids_stride, smask, sink, local, scale, O, l, m, ws, fold, st);
-    case 16: return launch_attn_g<T, D, 16>(q, kv, ids, counts, ids_stride, smask, sink, local, scale, O, l, m, ws, fold, st);
+    case 1: return launch_attn_g<T, D, 1>(q, kv, ids, counts, ids_stride, smask, sink, local, scale, O, l, m, ws, fold, skip_ids, skip_counts, st);
+    case 2: return launch_attn_g<T, D, 2>(q, kv, ids, counts, ids_stride, smask, sink, local, scale, O, l, m, ws, fold, skip_ids, skip_counts, st);
+    case 4: return launch_attn_g<T, D, 4>(q, kv, ids, counts, ids_stride, smask, sink, local, scale, O, l, m, ws, fold, skip_ids, skip_counts, st);
+    case 8: return launch_attn_g<T, D, 8>(q, kv, ids, counts, ids_stride, smask, sink, local, scale, O, l, m, ws, fold, skip_ids, skip_counts, st);
+    case 16: return launch_attn_g<T, D, 16>(q, kv, ids, counts, ids_stride, smask, sink, local, scale, O, l, m, ws, fold, skip_ids, skip_counts, st);
   }
   return DSA_ERR_UNSUPPORTED;
 }
 
 static int launch_attn(const void* q, int G, const dsa_kv* kv, const int32_t* ids, const int32_t* counts,
                        int ids_stride, uint64_t smask, int sink, int local, float scale, float* O, float* l,
-                       float* m, void* ws, int fold, hipStream_t st) {
+                       float* m, void* ws, int fold, const int32_t* skip_ids, const int32_t* skip_counts,
+                       hipStream_t st) {
   const bool bf = kv->dtype == DSA_BF16;
   if (kv->head_dim == 128)
-    return bf ? launch_attn_d<uint16_t, 128>(q, G, kv, ids, counts, ids_stride, smask, sink, local, scale, O, l, m, ws, fold, st)
-              : launch_attn_d<float, 128>(q, G, kv, ids, counts, ids_stride, smask, sink, local, scale, O, l, m, ws, fold, st);
-  return bf ? launch_attn_d<uint16_t, 64>(q, G, kv, ids, counts, ids_stride, smask, sink, local, scale, O, l, m, ws, fold, st)
-            : launch_attn_d<float, 64>(q, G, kv, ids, counts, ids_stride, smask, sink, local, scale, O, l, m, ws, fold, st);
+    return bf ? launch_attn_d<uint16_t, 128>(q, G, kv, ids, counts, ids_stride, smask, sink, local, scale, O, l, m, ws, fold, skip_ids, skip_counts, st)
+              : launch_attn_d<float, 128>(q, G, kv, ids, counts, ids_stride, smask, sink, local, scale, O, l, m, ws, fold, skip_ids, skip_counts, st);
+  return bf ? launch_attn_d<uint16_t, 64>(q, G, kv, ids, counts, ids_stride, smask, sink, local, scale, O, l, m, ws, fold, skip_ids, skip_counts, st)
+            : launch_attn_d<float, 64>(q, G, kv, ids, counts, ids_stride, smask, sink, local, scale, O, l, m, ws, fold, skip_ids, skip_counts, st);
 }
 
 static int check_attn_common(const void* q, int n_q_heads, const dsa_kv* kv, float scale, int* G) {
@@ -645,11 +758,6 @@ static int check_attn_common(const void* q, int n_q_heads, const dsa_kv* kv, flo
     if (!aligned16(q)) return DSA_ERR_ALIGN;
   }
   return DSA_OK;
-}
-
-static size_t repair_ids_bytes(const dsa_kv* kv, int ids_stride) {
-  const size_t units = (size_t)kv->batch * kv->n_kv_heads;
-  return align256(units * ids_stride * sizeof(int32_t)) + align256(units * sizeof(int32_t));
 }
 
 static int max_lds_per_block() {
@@ -700,7 +808,7 @@ extern "C" size_t dsa_workspace_bytes(int32_t op, const dsa_kv* kv, int32_t n_q_
   if (!pow2_group(G)) return 0;
   const size_t part = partial_bytes(kv, G, ids_stride);
   if (op == DSA_OP_SPARSE_DECODE_ATTN) return part;
-  if (op == DSA_OP_ATTN_REPAIR) return repair_ids_bytes(kv, ids_stride) + part;
+  if (op == DSA_OP_ATTN_REPAIR) return part;
   return 0;
 }
 
@@ -720,8 +828,8 @@ extern "C" int dsa_sparse_decode_attn(const void* q, int32_t n_q_heads, const ds
   if (!ws || ws_bytes < need) return DSA_ERR_WORKSPACE;
   if (!aligned16(ws)) return DSA_ERR_ALIGN;
   const int sink = stream_cfg ? stream_cfg->sink : 0, local = stream_cfg ? stream_cfg->local : 0;
-  return launch_attn(q, G, kv, ids, counts, ids_stride, smask, sink, local, scale, O, l, m, ws, 0,
-                     (hipStream_t)stream);
+  return launch_attn(q, G, kv, ids, counts, ids_stride, smask, sink, local, scale, O, l, m, ws, 0, nullptr,
+                     nullptr, (hipStream_t)stream);
 }
 
 extern "C" int dsa_attn_repair(const void* q, int32_t n_q_heads, const dsa_kv* kv, const int32_t* a_ids,
@@ -738,16 +846,9 @@ extern "C" int dsa_attn_repair(const void* q, int32_t n_q_heads, const dsa_kv* k
   if (!ws || ws_bytes < need) return DSA_ERR_WORKSPACE;
   if (!aligned16(ws)) return DSA_ERR_ALIGN;
   const size_t lds = (size_t)((kv->max_pages + 31) / 32) * sizeof(uint32_t);
-  if ((int)lds + 64 > max_lds_per_block()) return DSA_ERR_UNSUPPORTED;
-  hipStream_t st = (hipStream_t)stream;
-  const size_t units = (size_t)kv->batch * kv->n_kv_heads;
-  int32_t* m_ids = (int32_t*)ws;
-  int32_t* m_counts = (int32_t*)((char*)ws + align256(units * ids_stride * sizeof(int32_t)));
-  void* part = (char*)ws + repair_ids_bytes(kv, ids_stride);
-  hipLaunchKernelGGL(missing_set_kernel, dim3((unsigned)units), dim3(256), lds, st, a_ids, a_counts, p_ids, p_counts,
-                     ids_stride, kv->max_pages, m_ids, m_counts);
-  if ((rc = launch_status())) return rc;
-  return launch_attn(q, G, kv, m_ids, m_counts, ids_stride, 0, 0, 0, scale, O, l, m, part, 1, st);
+  if ((int)lds + 52 * 1024 > max_lds_per_block()) return DSA_ERR_UNSUPPORTED;
+  return launch_attn(q, G, kv, a_ids, a_counts, ids_stride, 0, 0, 0, scale, O, l, m, ws, 1, p_ids, p_counts,
+                     (hipStream_t)stream);
 }
 
 extern "C" int dsa_page_select_progressive(const void* q, int32_t n_q_heads, const dsa_kv* kv, const float* scores,

@@ -231,7 +231,9 @@ static int launch_score_g(const void* q, const dsa_kv* kv, const void* meta, int
   // Each wave walks a range of <= 64 physical pages (one page-table load);
   // aim for DSA_SCORE_WAVES waves over the grid.
   const long long units = (long long)kv->batch * kv->n_kv_heads;
-  const long long target_waves = DSA_SCORE_WAVES;
+  // every wave forms the group-mean query itself: with many heads per group
+  // fewer, longer waves read less of it
+  const long long target_waves = (long long)DSA_SCORE_WAVES * 4 / (G > 4 ? G : 4);
   long long ppw = (units * kv->max_pages + target_waves - 1) / target_waves;
   ppw = ppw < 4 ? 4 : (ppw > 64 ? 64 : ppw);
   ppw = (ppw + 3) / 4 * 4;

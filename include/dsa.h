@@ -229,7 +229,9 @@ int dsa_sparse_decode_attn(const void *q, int32_t n_q_heads, const dsa_kv *kv,
  * that into (O, l, m) in place:
  *   m' = max(m, m~), l' = e^(m-m') l + e^(m~-m') l~,
  *   O' = (e^(m-m') l O + e^(m~-m') l~ O~) / l'
- * so the result is attention over P u A.  Work and traffic scale with |M|.
+ * so the result is attention over P u A.  KV traffic scales with |M|; each
+ * workgroup of the split over A also reads p_ids once into an LDS bitmap of
+ * max_pages bits (DSA_ERR_UNSUPPORTED if that bitmap does not fit in LDS).
  * a_ids, p_ids: device int32 [batch][n_kv_heads][ids_stride] with page ids
  * < max_pages.  Streaming heads are not supported here.
  * ws: device scratch of dsa_workspace_bytes(DSA_OP_ATTN_REPAIR, ...).

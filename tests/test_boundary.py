@@ -94,7 +94,7 @@ def test_validation_errors(dsa):
                                     ok_ptr, ok_ptr, need - 1, None) == -5
     assert L.dsa_sparse_decode_attn(ok_ptr, 4, ctypes.byref(kv), ok_ptr, ok_ptr, 8, None, -1.0, ok_ptr, ok_ptr,
                                     ok_ptr, ok_ptr, need, None) == -2
-    assert L.dsa_workspace_bytes(2, ctypes.byref(kv), 4, 8) > need
+    assert L.dsa_workspace_bytes(2, ctypes.byref(kv), 4, 8) >= need
     assert L.dsa_workspace_bytes(9, ctypes.byref(kv), 4, 8) == 0
     # progressive: bad stop mode, too many pages, G=8 unsupported
     assert L.dsa_page_select_progressive(ok_ptr, 4, ctypes.byref(kv), ok_ptr, ctypes.c_float(0.9), 2,

@@ -155,6 +155,7 @@ def test_topk_streaming_lists(gpu_lib):
 # ---------------------------------------------------------------- attention
 @pytest.mark.parametrize("dtype,D,P,G", [("bf16", 128, 16, 1), ("bf16", 128, 16, 4), ("bf16", 128, 16, 16),
                                          ("bf16", 64, 16, 2), ("bf16", 128, 64, 4), ("bf16", 128, 32, 8),
+                                         ("bf16", 128, 16, 8), ("bf16", 64, 16, 8), ("bf16", 64, 64, 16),
                                          ("f32", 64, 16, 1), ("f32", 128, 16, 4), ("f32", 64, 64, 16)])
 def test_sparse_decode_attn(gpu_lib, dtype, D, P, G):
     dsa = gpu_lib
@@ -190,9 +191,10 @@ def test_attention_all_pages_is_dense(gpu_lib):
     check_attention("bf16", np_(O), np_(l), np_(m), rO, rl, rm, "dense")
 
 
-def test_attention_streaming_heads(gpu_lib):
+@pytest.mark.parametrize("G", [2, 8])
+def test_attention_streaming_heads(gpu_lib, G):
     dsa = gpu_lib
-    bt = wl.random_batch(53, [64 * 20 + 30, 64 * 8, 200], n_q_heads=8, n_kv_heads=4, head_dim=128, page_size=64,
+    bt = wl.random_batch(53, [64 * 20 + 30, 64 * 8, 200], n_q_heads=4 * G, n_kv_heads=4, head_dim=128, page_size=64,
                          logical_page=16, streaming=[1, 0, 0, 1], sink=128, local=256)
     q, kv, st = to_device(dsa, bt)
     meta = dsa.page_meta_build(kv, 16)
