@@ -235,6 +235,7 @@ def main():
     q = dsa.upload_q(bt.q, bt.dtype)
 
     extra = {}
+    step_end = None
     if a.workload == "prr_512k":
         from dynamic_sparse_attention_page_amd.prr import PRRDecoder
         a_, b_, g_ = bt.extra["ema"]
@@ -242,16 +243,21 @@ def main():
         qt = torch.from_numpy(bt.extra["q_trace"].view(np.int16)).to(dev).view(torch.bfloat16)
         decs = [PRRDecoder(kv, meta, Hq, bt.topk, a_, b_, g_, bt.extra["delta"], scale=scale) for kv in kvs]
 
-        def step(i):   # step i: replica i mod R at trace step (i // R) mod T
+        def step(i):   # step i: replica i mod R at trace step 1 + (i // R) mod (T - 1), a speculative step
             r = i % R
-            decs[r].t = (i // R) % T
+            decs[r].t = 1 + (i // R) % (T - 1)
             decs[r].step(qt[decs[r].t])
+
+        def step_end():   # the side streams' last predictor updates join the caller's stream
+            for d in decs:
+                d.join()
         # one pass over the traces: predictor state and the measured miss rate
         miss, prev_p = [], None
         for t in range(T):
             for r in range(R):
                 decs[r].t = t
                 decs[r].step(qt[t])
+            step_end()
             torch.cuda.synchronize()
             A = decs[0].a_ids.cpu().numpy()
             if prev_p is not None:
@@ -326,12 +332,17 @@ def main():
         step_bytes = mb + kvb
         op_bytes = {"page_score": mb, "sparse_decode_attn": kvb}
 
-    def capture(fn, n):
+    def capture(fn, n, end=None):
         """A HIP graph of n calls fn(0..n-1) on the capture stream (no memset nodes)."""
+        torch.cuda.synchronize()
+        if end is not None:
+            end()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for i in range(n):
                 fn(i)
+            if end is not None:
+                end()
         return g
 
     def time_graph(g, reps):
@@ -352,12 +363,14 @@ def main():
     e0.record()
     for i in range(a.steps):
         step(i)
+    if step_end is not None:
+        step_end()
     e1.record()
     torch.cuda.synchronize()
     eager_ms_step = e0.elapsed_time(e1) / a.steps
 
     # timed region: exactly K steps replayed from one graph
-    g_step = capture(step, a.steps)
+    g_step = capture(step, a.steps, step_end)
     g_step.replay()                       # untimed warm replay
     ms = time_graph(g_step, 1)
     ms_step = ms / a.steps

@@ -1,5 +1,6 @@
-"""PRR decode step orchestration: selection overlapped with speculative
-attention on two HIP streams, then repair and the EMA predictor.
+"""PRR decode step orchestration: the exact selection and the predictor run
+on a side stream while the speculative attention runs on the caller's
+stream; the repair joins them.
 
 "Predict, Reuse, and Repair", sections 1-3: in a plain dynamic-sparse step
 the page selection must finish before attention starts.  PRR predicts the
@@ -8,8 +9,15 @@ predicted set P while the real selection A is computed, then repairs the
 result with the pages of A that P missed (section 3.3), and feeds the new
 scores back into the predictor.
 
+The predictor update and the next step's speculative set P^{t+1} depend
+only on this step's scores IS^t, not on attention, so they follow the
+selection on the side stream and overlap the repair; the caller's stream
+waits for P^{t+1} only at the next step's speculative attention.  P is
+double-buffered: the side stream writes P^{t+1} while the caller's stream
+still reads P^t.
+
 This module only sequences calls of the C ABI (through the binding) on two
-streams joined by an event; every step of the arithmetic runs in the HIP
+streams joined by events; every step of the arithmetic runs in the HIP
 library.  Stream priorities stay at the default.
 """
 from __future__ import annotations
@@ -24,10 +32,11 @@ from . import (OP_ATTN_REPAIR, PagedKV, attn_repair, ema_predict_update, page_sc
 
 class PRRDecoder:
     """Per-layer PRR state for one batch of sequences: EMA level/trend per
-    (sequence, KV head, page), the speculative set for the next step, and
-    the buffers of one step.  `step(q)` enqueues one decode step on the
-    current stream (plus a side stream for the selection) and returns
-    (O, l, m); nothing is synchronised with the host."""
+    (sequence, KV head, page), the speculative sets, and the buffers of one
+    step.  `step(q)` enqueues one decode step on the current stream (plus a
+    side stream for the selection and the predictor) and returns (O, l, m);
+    nothing is synchronised with the host.  After a step, `a_ids` holds A^t
+    and `p_ids` the prediction P^{t+1} for the next step."""
 
     def __init__(self, kv: PagedKV, meta: torch.Tensor, n_q_heads: int, k: int, alpha: float, beta: float,
                  gamma: float, delta: float = 1.0, logical_page: int | None = None, scale: float | None = None):
@@ -43,8 +52,9 @@ class PRRDecoder:
         self.scores = torch.empty((B, H, N), dtype=f32, device=dev)
         self.a_ids = torch.full((B, H, self.stride), -1, dtype=i32, device=dev)
         self.a_counts = torch.zeros((B, H), dtype=i32, device=dev)
-        self.p_ids = torch.full((B, H, self.stride), -1, dtype=i32, device=dev)
-        self.p_counts = torch.zeros((B, H), dtype=i32, device=dev)
+        self._p = [(torch.full((B, H, self.stride), -1, dtype=i32, device=dev),
+                    torch.zeros((B, H), dtype=i32, device=dev)) for _ in range(2)]
+        self._cur = 0                      # buffer holding P^t of the coming step
         self.level = torch.zeros(B * H * N, dtype=f32, device=dev)
         self.trend = torch.zeros(B * H * N, dtype=f32, device=dev)
         self.pred = torch.zeros((B, H, N), dtype=f32, device=dev)
@@ -54,7 +64,25 @@ class PRRDecoder:
         self.ws = torch.zeros(workspace_bytes(OP_ATTN_REPAIR, kv, n_q_heads, self.stride), dtype=torch.uint8,
                               device=dev)
         self.side = torch.cuda.Stream(device=dev)      # default priority
+        self._p_ready = None               # event: P^t written (side stream of the previous step)
         self.t = 0
+
+    def join(self):
+        """Make the current stream wait for the side stream's last work (the
+        predictor update of the last step); needed before graph capture ends
+        and before timing the caller's stream."""
+        if self._p_ready is not None:
+            torch.cuda.current_stream().wait_event(self._p_ready)
+            self._p_ready = None
+
+    @property
+    def p_ids(self):
+        """The latest prediction (P^{t+1} after step t)."""
+        return self._p[self._cur][0]
+
+    @property
+    def p_counts(self):
+        return self._p[self._cur][1]
 
     def _select(self, q):
         """IS^t = page scores; A^t = top-k of IS^t (written into a_ids)."""
@@ -68,40 +96,50 @@ class PRRDecoder:
             self.a_ids[..., :self.k].copy_(ids)
             self.a_counts.copy_(counts)
 
-    def _predict_next(self, init: bool):
-        """EMA update with IS^t (or initialisation) and P^{t+1} = top of the prediction."""
+    def _predict_next(self, init: bool, buf: int):
+        """EMA update with IS^t (or initialisation) and P^{t+1} = top of the prediction, into buffer buf."""
         ema_predict_update(self.scores, self.level, self.trend, self.pred, self.alpha, self.beta, self.gamma,
                            init=init)
+        p_ids, p_counts = self._p[buf]
         if self.stride == self.k_spec:
-            page_select_topk(self.pred, self.kv.seq_lens, self.kv.page_size, self.k_spec, ids=self.p_ids,
-                             counts=self.p_counts)
+            page_select_topk(self.pred, self.kv.seq_lens, self.kv.page_size, self.k_spec, ids=p_ids,
+                             counts=p_counts)
         else:
             ids, counts = page_select_topk(self.pred, self.kv.seq_lens, self.kv.page_size, self.k_spec)
-            self.p_ids.fill_(-1)
-            self.p_ids[..., :self.k_spec].copy_(ids)
-            self.p_counts.copy_(counts)
+            p_ids.fill_(-1)
+            p_ids[..., :self.k_spec].copy_(ids)
+            p_counts.copy_(counts)
 
     def step(self, q: torch.Tensor):
         out = (self.O, self.l, self.m)
+        main = torch.cuda.current_stream()
+        cur, nxt = self._cur, 1 - self._cur
         if self.t == 0:
             # no prediction yet: a plain selection-then-attention step
             self._select(q)
             sparse_decode_attn(q, self.kv, self.a_ids, self.a_counts, scale=self.scale, out=out, ws=self.ws)
-            self._predict_next(init=True)
+            self._predict_next(init=True, buf=nxt)
         else:
-            main = torch.cuda.current_stream()
+            # the side stream starts once everything enqueued so far on the
+            # caller's stream (the previous step, which read a_ids and P^{t-1})
+            # is done
             fork = torch.cuda.Event()
             fork.record(main)
             with torch.cuda.stream(self.side):
                 self.side.wait_event(fork)
-                self._select(q)                       # selection ...
-                joined = torch.cuda.Event()
-                joined.record(self.side)
-            # ... overlapped with speculative attention over P^t
-            sparse_decode_attn(q, self.kv, self.p_ids, self.p_counts, scale=self.scale, out=out, ws=self.ws)
-            main.wait_event(joined)
-            attn_repair(q, self.kv, self.a_ids, self.a_counts, self.p_ids, self.p_counts, *out, scale=self.scale,
-                        ws=self.ws)
-            self._predict_next(init=False)
+                self._select(q)                              # IS^t, A^t ...
+                a_ready = torch.cuda.Event()
+                a_ready.record(self.side)
+                self._predict_next(init=False, buf=nxt)      # ... then EMA and P^{t+1}
+                p_ready = torch.cuda.Event()
+                p_ready.record(self.side)
+            # speculative attention over P^t, overlapped with the selection
+            self.join()
+            p_ids, p_counts = self._p[cur]
+            sparse_decode_attn(q, self.kv, p_ids, p_counts, scale=self.scale, out=out, ws=self.ws)
+            main.wait_event(a_ready)
+            attn_repair(q, self.kv, self.a_ids, self.a_counts, p_ids, p_counts, *out, scale=self.scale, ws=self.ws)
+            self._p_ready = p_ready
+        self._cur = nxt
         self.t += 1
         return out
