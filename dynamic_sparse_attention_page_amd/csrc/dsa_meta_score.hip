@@ -158,6 +158,7 @@ __global__ __launch_bounds__(256) void score_kernel(
     bool ok[U];
 #pragma unroll
     for (int uu = 0; uu < U; ++uu) {
+      if (u0 + uu >= n_pairs) break;                 // uniform: no loads past the range
       const int lp = 4 * (u0 + uu) + r;            // logical page within the range
       const int pl = lp / GL, sub = lp % GL;
       const int slot = __shfl(my_slot, pl & 63, 64);
@@ -170,6 +171,7 @@ __global__ __launch_bounds__(256) void score_kernel(
     }
 #pragma unroll
     for (int uu = 0; uu < U; ++uu) {
+      if (u0 + uu >= n_pairs) break;
       float part = 0.0f;
 #pragma unroll
       for (int c = 0; c < CPL; ++c) {
