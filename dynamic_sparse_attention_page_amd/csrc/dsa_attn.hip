@@ -326,73 +326,104 @@ __global__ __launch_bounds__(256) void attn_partial_mfma_kernel(
 }
 
 // ============================================================ combine
-// One workgroup (4 waves) per (sequence, q head).  The active splits' maxima
-// are reduced first; then wave w sums splits w, w+4, ... with weights
-// exp(m_s - M) (lanes over channels, loads independent across splits), and
-// the 4 wave sums meet in LDS.  For repair the caller's (O, l, m) is one more
-// term.  Writes normalised O.
+// One workgroup (4 waves) per (sequence, q head).  Wave w folds splits w,
+// w+4, ... with the online-softmax merge, lanes over channels; the partials
+// of all n_splits splits are loaded without waiting for the count (entries
+// of inactive splits are never written and are selected away, not
+// multiplied), so the count, the (m, l) pairs and the outputs arrive in one
+// round trip.  The 4 wave states meet in LDS.  For repair the caller's
+// (O, l, m) is one more term.  Writes normalised O.
 template <int D>
 __global__ __launch_bounds__(256) void attn_combine_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_ml, const int32_t* __restrict__ counts,
     int ids_stride, int n_kv_heads, int G, int TPP, int tiles_per_split, int n_splits, int fold,
     float* __restrict__ O, float* __restrict__ l, float* __restrict__ m) {
   constexpr int CPT = D / 64;
-  __shared__ float s_red[4];
   __shared__ float s_acc[4][D];
-  __shared__ float s_l[4];
+  __shared__ float s_ml[4][2];
   const int hq = blockIdx.x, b = blockIdx.y;
   const int Hq = n_kv_heads * G;
   const int h = hq / G, g = hq % G;
   const int unit = b * n_kv_heads + h;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int cnt = counts[unit];
-  cnt = cnt < 0 ? 0 : (cnt > ids_stride ? ids_stride : cnt);
-  const int active = min(n_splits, (cnt * TPP + tiles_per_split - 1) / tiles_per_split);
   const size_t row = (size_t)b * Hq + hq;
-  const float* ml = part_ml + ((size_t)unit * n_splits * G + g) * 2;   // split s at ml[s * 2G]
-
-  float mx = kNegInf;
-  for (int s = tid; s < active; s += 256) mx = fmaxf(mx, ml[(size_t)s * 2 * G]);
-  for (int d = 32; d >= 1; d >>= 1) mx = fmaxf(mx, __shfl_xor(mx, d, 64));
-  if (lane == 0) s_red[wave] = mx;
-  float m_in = kNegInf, l_in = 0.0f;
-  if (fold) {
+  float m_in = kNegInf, l_in = 0.0f, o_in[CPT];
+  if (fold && wave == 0) {
     m_in = m[row];
     l_in = l[row];
-    if (!(l_in > 0.0f)) m_in = kNegInf;
+#pragma unroll
+    for (int x = 0; x < CPT; ++x) o_in[x] = O[row * D + lane + 64 * x];
   }
-  __syncthreads();
-  const float M = fmaxf(fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3])), m_in);
+  cnt = cnt < 0 ? 0 : (cnt > ids_stride ? ids_stride : cnt);
+  const int active = min(n_splits, (cnt * TPP + tiles_per_split - 1) / tiles_per_split);
 
-  float acc[CPT], ls = 0.0f;
+  float mw = kNegInf, lw = 0.0f, acc[CPT];
 #pragma unroll
   for (int x = 0; x < CPT; ++x) acc[x] = 0.0f;
-#pragma unroll 4
-  for (int s = wave; s < active; s += 4) {
-    const size_t pi = ((size_t)unit * n_splits + s) * G + g;
-    const float ms = part_ml[pi * 2], lsp = part_ml[pi * 2 + 1];
-    const float wt = (ms == kNegInf) ? 0.0f : expf(ms - M);
-    ls = fmaf(lsp, wt, ls);
+  constexpr int NB = 8;   // splits per batch and wave: all loads of a batch are in flight together
+  for (int s0 = wave; s0 < n_splits; s0 += 4 * NB) {
+    float ms[NB], lsp[NB], os[NB][CPT];
 #pragma unroll
-    for (int x = 0; x < CPT; ++x) acc[x] = fmaf(part_o[pi * D + lane + 64 * x], wt, acc[x]);
+    for (int u = 0; u < NB; ++u) {
+      const int sp = min(s0 + 4 * u, n_splits - 1);   // in bounds; duplicates are masked below
+      const size_t pi = ((size_t)unit * n_splits + sp) * G + g;
+      ms[u] = part_ml[pi * 2];
+      lsp[u] = part_ml[pi * 2 + 1];
+#pragma unroll
+      for (int x = 0; x < CPT; ++x) os[u][x] = part_o[pi * D + lane + 64 * x];
+    }
+    float mb = kNegInf;
+    bool ok[NB];
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      ok[u] = s0 + 4 * u < active && ms[u] != kNegInf && lsp[u] > 0.0f;   // inactive or empty splits drop out
+      if (ok[u]) mb = fmaxf(mb, ms[u]);
+    }
+    if (mb == kNegInf) continue;                      // uniform across the wave
+    const float mn = fmaxf(mw, mb);
+    const float a = (mw == kNegInf) ? 0.0f : expf(mw - mn);
+    lw *= a;
+#pragma unroll
+    for (int x = 0; x < CPT; ++x) acc[x] *= a;
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      const float wt = ok[u] ? expf(ms[u] - mn) : 0.0f;
+      lw = fmaf(ok[u] ? lsp[u] : 0.0f, wt, lw);
+#pragma unroll
+      for (int x = 0; x < CPT; ++x) acc[x] = fmaf(ok[u] ? os[u][x] : 0.0f, wt, acc[x]);
+    }
+    mw = mn;
   }
-  if (wave == 0 && fold && m_in != kNegInf) {
-    const float wt = expf(m_in - M) * l_in;
-    ls += wt;
+  if (wave == 0 && fold && l_in > 0.0f && m_in != kNegInf) {   // the caller's (O, l, m): O is normalised
+    const float mn = fmaxf(mw, m_in);
+    const float a = (mw == kNegInf) ? 0.0f : expf(mw - mn);
+    const float wt = expf(m_in - mn) * l_in;
+    lw = fmaf(lw, a, wt);
 #pragma unroll
-    for (int x = 0; x < CPT; ++x) acc[x] = fmaf(O[row * D + lane + 64 * x], wt, acc[x]);
+    for (int x = 0; x < CPT; ++x) acc[x] = fmaf(acc[x], a, o_in[x] * wt);
+    mw = mn;
   }
 #pragma unroll
   for (int x = 0; x < CPT; ++x) s_acc[wave][lane + 64 * x] = acc[x];
-  if (lane == 0) s_l[wave] = ls;
+  if (lane == 0) { s_ml[wave][0] = mw; s_ml[wave][1] = lw; }
   __syncthreads();
   if (wave == 0) {
-    const float L = s_l[0] + s_l[1] + s_l[2] + s_l[3];
+    const float M = fmaxf(fmaxf(s_ml[0][0], s_ml[1][0]), fmaxf(s_ml[2][0], s_ml[3][0]));
+    float wts[4], L = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      wts[w] = (s_ml[w][0] == kNegInf) ? 0.0f : expf(s_ml[w][0] - M);
+      L = fmaf(s_ml[w][1], wts[w], L);
+    }
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
 #pragma unroll
     for (int x = 0; x < CPT; ++x) {
       const int c = lane + 64 * x;
-      O[row * D + c] = (s_acc[0][c] + s_acc[1][c] + s_acc[2][c] + s_acc[3][c]) * inv;
+      float o = 0.0f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) o = fmaf(s_acc[w][c], wts[w], o);
+      O[row * D + c] = o * inv;
     }
     if (lane == 0) {
       l[row] = L;
