@@ -5,9 +5,11 @@
 A step is the whole hot path for one batch of decode queries on inputs
 already resident in HBM; page metadata is built beforehand (prefill work).
 
-  quest_gqa_32k (default)  page_score -> page_select_topk -> sparse_decode_attn
+  quest_gqa_32k (default)  page_score -> sparse_decode_attn_topk (top-k selection + sparse
+      attention in one call; the separate page_select_topk and sparse_decode_attn are
+      timed beside it)
       batch 1, 32 q / 8 KV heads, d=128, 32768 tokens in 16-token pages, top-256, bf16
-  lserve_hier_128k         the same three calls with 64/16 hierarchical paging and
+  lserve_hier_128k         the same calls with 64/16 hierarchical paging and
       4 of 8 KV heads streaming (sink 128 + local 256); batch 4, 131072 tokens, top-64
   psa_mha_64k              page_score -> page_select_progressive (threshold 0.95)
       batch 8, 32 heads MHA, 65536 tokens
@@ -319,18 +321,21 @@ def main():
                          device=dev)
         ops = {
             "page_score": lambda r: dsa.page_score(q, kvs[r], meta, bt.logical_page, streaming=st, scores=scores),
+            "sparse_decode_attn_topk": lambda r: dsa.sparse_decode_attn_topk(
+                q, kvs[r], scores, k_pages, streaming=st, scale=scale, out=(O, l, m), ids=ids, counts=cnt, ws=ws),
+            # the two calls the fused one stands for, timed on their own (not part of the step)
             "page_select_topk": lambda r: dsa.page_select_topk(scores, kvs[r].seq_lens, bt.page_size, k_pages,
                                                                streaming=st, ids=ids, counts=cnt),
             "sparse_decode_attn": lambda r: dsa.sparse_decode_attn(q, kvs[r], ids, cnt, streaming=st, scale=scale,
                                                                    out=(O, l, m), ws=ws),
         }
 
-        def step(i):
-            for fn in ops.values():
-                fn(i % R)
+        def step(i):   # score -> top-k selection + sparse attention (one call)
+            ops["page_score"](i % R)
+            ops["sparse_decode_attn_topk"](i % R)
         kvb = page_kv_bytes(bt, k_pages, dense_units) + streaming_bytes(bt)
         step_bytes = mb + kvb
-        op_bytes = {"page_score": mb, "sparse_decode_attn": kvb}
+        op_bytes = {"page_score": mb, "sparse_decode_attn_topk": kvb + 4 * N * B * Hkv, "sparse_decode_attn": kvb}
 
     def capture(fn, n, end=None):
         """A HIP graph of n calls fn(0..n-1) on the capture stream (no memset nodes)."""

@@ -5,7 +5,7 @@ function below marshals torch tensors into the C ABI call of the same name
 and launches on the current HIP stream.  Every step of the computation runs
 in the library's HIP kernels; torch only provides device memory and streams.
 Importing this module fails loudly if the library has not been built
-(``python -m dynamic_sparse_attention_page_amd.build``).
+(``python dynamic_sparse_attention_page_amd/build.py``).
 """
 from __future__ import annotations
 
@@ -19,7 +19,7 @@ import torch
 __all__ = [
     "DsaError", "PagedKV", "Streaming", "lib", "LIB_PATH",
     "page_meta_build", "page_score", "page_select_topk", "page_select_progressive",
-    "sparse_decode_attn", "attn_repair", "ema_predict_update", "workspace_bytes",
+    "sparse_decode_attn", "sparse_decode_attn_topk", "attn_repair", "ema_predict_update", "workspace_bytes",
     "OP_SPARSE_DECODE_ATTN", "OP_ATTN_REPAIR", "EXPORTED",
 ]
 
@@ -29,8 +29,8 @@ DSA_F32, DSA_BF16 = 0, 1
 OP_SPARSE_DECODE_ATTN, OP_ATTN_REPAIR = 1, 2
 EXPORTED = (
     "dsa_status_str", "dsa_version", "dsa_page_meta_build", "dsa_page_score", "dsa_page_select_topk",
-    "dsa_page_select_progressive", "dsa_sparse_decode_attn", "dsa_attn_repair", "dsa_ema_predict_update",
-    "dsa_workspace_bytes",
+    "dsa_page_select_progressive", "dsa_sparse_decode_attn", "dsa_sparse_decode_attn_topk", "dsa_attn_repair",
+    "dsa_ema_predict_update", "dsa_workspace_bytes",
 )
 
 
@@ -56,7 +56,7 @@ class _Stream(ctypes.Structure):
 def _load(path: str = LIB_PATH):
     if not os.path.exists(path):
         raise ImportError(f"{path} is missing: build it with "
-                          "`python -m dynamic_sparse_attention_page_amd.build` (hipcc, gfx950)")
+                          "`python dynamic_sparse_attention_page_amd/build.py` (hipcc, gfx950)")
     L = ctypes.CDLL(path)
     P, I32, I64, F32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
     KV, ST = ctypes.POINTER(_KV), ctypes.POINTER(_Stream)
@@ -68,6 +68,7 @@ def _load(path: str = LIB_PATH):
         "dsa_page_select_topk": (ctypes.c_int, [P, I32, I32, I32, P, I32, I32, ST, P, P, P]),
         "dsa_page_select_progressive": (ctypes.c_int, [P, I32, KV, P, F32, I32, F32, P, P, P, P, P, P]),
         "dsa_sparse_decode_attn": (ctypes.c_int, [P, I32, KV, P, P, I32, ST, F32, P, P, P, P, SZ, P]),
+        "dsa_sparse_decode_attn_topk": (ctypes.c_int, [P, I32, KV, P, I32, ST, F32, P, P, P, P, P, P, SZ, P]),
         "dsa_attn_repair": (ctypes.c_int, [P, I32, KV, P, P, P, P, I32, F32, P, P, P, P, SZ, P]),
         "dsa_ema_predict_update": (ctypes.c_int, [P, P, P, P, I64, F32, F32, F32, I32, P]),
         "dsa_workspace_bytes": (SZ, [I32, KV, I32, I32]),
@@ -279,6 +280,32 @@ def sparse_decode_attn(q: torch.Tensor, kv: PagedKV, ids: torch.Tensor, counts: 
         _ptr(q), Hq, ctypes.byref(kv.c()), _ptr(ids), _ptr(counts), stride, _stream_arg(streaming), sc,
         _ptr(O), _ptr(l), _ptr(m), _ptr(ws), ws.numel() * ws.element_size(), _stream()))
     return O, l, m
+
+
+def sparse_decode_attn_topk(q: torch.Tensor, kv: PagedKV, scores: torch.Tensor, k: int,
+                            streaming: Streaming | None = None, scale: float | None = None, out=None, ids=None,
+                            counts=None, ws: torch.Tensor | None = None):
+    """Top-k selection from `scores` and attention over the selected pages in
+    one call: (ids [B][Hkv][k], counts [B][Hkv], O, l, m)."""
+    B, Hq = q.shape[0], q.shape[1]
+    dev = kv.k.device
+    if out is None:
+        out = (torch.empty((B, Hq, kv.head_dim), dtype=torch.float32, device=dev),
+               torch.empty((B, Hq), dtype=torch.float32, device=dev),
+               torch.empty((B, Hq), dtype=torch.float32, device=dev))
+    if ids is None:
+        ids = torch.empty((kv.batch, kv.n_kv_heads, k), dtype=torch.int32, device=dev)
+    if counts is None:
+        counts = torch.empty((kv.batch, kv.n_kv_heads), dtype=torch.int32, device=dev)
+    O, l, m = out
+    need = workspace_bytes(OP_SPARSE_DECODE_ATTN, kv, Hq, k)
+    if ws is None:
+        ws = _workspace(need, dev)
+    sc = _default_scale(kv.head_dim) if scale is None else scale
+    _check("dsa_sparse_decode_attn_topk", lib.dsa_sparse_decode_attn_topk(
+        _ptr(q), Hq, ctypes.byref(kv.c()), _ptr(scores), k, _stream_arg(streaming), sc, _ptr(ids), _ptr(counts),
+        _ptr(O), _ptr(l), _ptr(m), _ptr(ws), ws.numel() * ws.element_size(), _stream()))
+    return ids, counts, O, l, m
 
 
 def attn_repair(q: torch.Tensor, kv: PagedKV, a_ids, a_counts, p_ids, p_counts, O, l, m,

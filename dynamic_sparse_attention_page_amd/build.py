@@ -1,6 +1,9 @@
 """Builds libdsa.so (the HIP library behind include/dsa.h) in-tree for gfx950.
 
-    python -m dynamic_sparse_attention_page_amd.build [--jobs N]
+    python dynamic_sparse_attention_page_amd/build.py [--jobs N]
+
+(run as a file, not as a module of the package: importing the package loads
+the library this script builds)
 
 Every csrc/*.hip file is compiled separately (in parallel) to an object under
 _build/, then linked into dynamic_sparse_attention_page_amd/libdsa.so.

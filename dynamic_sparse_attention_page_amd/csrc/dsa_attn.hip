@@ -31,15 +31,27 @@ namespace dsa {
 
 constexpr int kWgWaves = 4;
 
+// Fused selection (dsa_sparse_decode_attn_topk): each split workgroup ranks
+// its row of scores itself and takes the entries of its range; split 0
+// writes the ids and count.  e == 0: ids/counts are inputs.
+struct SelectArgs {
+  const float* scores;
+  int k;
+  int32_t* ids_out;
+  int32_t* counts_out;
+  int e;   // scores per thread: max_pages <= 256 * e
+};
+
 // ============================================================ split-KV partial
-template <typename T, int D, int G, bool FILTER>
+template <typename T, int D, int G, bool FILTER, int SEL_E>
 __global__ __launch_bounds__(256) void attn_partial_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const int32_t* __restrict__ page_table, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ ids, const int32_t* __restrict__ counts, int ids_stride, int n_kv_heads, int P,
     int max_pages, int num_slots, unsigned long long streaming, int sink, int local, float scale, float c,
     int tiles_per_split, int n_splits, const int32_t* __restrict__ skip_ids,
-    const int32_t* __restrict__ skip_counts, float* __restrict__ part_o, float* __restrict__ part_ml) {
+    const int32_t* __restrict__ skip_counts, SelectArgs sel, float* __restrict__ part_o,
+    float* __restrict__ part_ml) {
   using A = AttnWave<T, D, G>;
   constexpr int CPL = A::CPL, DW = A::DW;
   __shared__ __align__(16) float lds_rows[kWgWaves][A::LDS_FLOATS];
@@ -57,16 +69,70 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
   const int TPP = P / 16;
   const int t_begin = split * tiles_per_split;
   const int first_entry = t_begin / TPP;
-  // The id and its slot are fetched together with the count (the count only
-  // decides later which of them are used): entry -> page -> slot is one
-  // dependent hop instead of two.
   int pg_raw = -1, sl_raw = -1;
-  if (lane < tiles_per_split / TPP && first_entry + lane < ids_stride) {
-    pg_raw = ids[(size_t)unit * ids_stride + first_entry + lane];
+  int cnt;
+  if constexpr (SEL_E > 0) {
+    // the selection of dsa_page_select_topk, recomputed by every split of
+    // the row (no cross-workgroup traffic); entries are in ascending order
+    __shared__ SelectSmem<SEL_E, kWgWaves> ssm;
+    __shared__ int s_pages[64];
+    const int tid = threadIdx.x;
+    const int L0 = clamp_len(seq_lens[b], max_pages, P);
+    const int np0 = (L0 + P - 1) / P;
+    const int nslot = tiles_per_split / TPP;
+    int32_t* out = sel.ids_out + (size_t)unit * sel.k;
+    if ((streaming >> h) & 1ull) {
+      const int n_sink = min(np0, (min(sink, L0) + P - 1) / P);
+      const int l_first = max(n_sink, (local > 0 && L0 > 0) ? max(0, L0 - local) / P : np0);
+      cnt = min(sel.k, n_sink + (np0 - l_first));
+      const int x = first_entry + lane;
+      if (lane < nslot && x < cnt) pg_raw = x < n_sink ? x : l_first + (x - n_sink);
+      if (split == 0) {
+        for (int y = tid; y < sel.k; y += 256) out[y] = y < cnt ? (y < n_sink ? y : l_first + (y - n_sink)) : -1;
+        if (tid == 0) sel.counts_out[unit] = cnt;
+      }
+    } else {
+      cnt = min(sel.k, np0);
+      const float* srow = sel.scores + (size_t)unit * max_pages;
+      float sv[SEL_E];
+#pragma unroll
+      for (int e = 0; e < SEL_E; ++e) sv[e] = (e * 256 + tid < max_pages) ? srow[e * 256 + tid] : 0.0f;
+      uint32_t key[SEL_E];
+      unsigned long long actm = 0ull;
+#pragma unroll
+      for (int e = 0; e < SEL_E; ++e) {
+        key[e] = order_key(sv[e]);
+        if (e * 256 + tid < np0) actm |= 1ull << e;
+      }
+      const unsigned long long selm = block_select_top<SEL_E, kWgWaves>(key, actm, np0, cnt, ssm);
+      int rk[SEL_E];
+      ordered_ranks<SEL_E, kWgWaves>(selm, rk, ssm.rank, ssm.scan);
+#pragma unroll
+      for (int e = 0; e < SEL_E; ++e)
+        if ((selm >> e) & 1ull) {
+          const int r = rk[e];
+          if (r >= first_entry && r < first_entry + nslot) s_pages[r - first_entry] = e * 256 + tid;
+          if (split == 0 && r < cnt) out[r] = e * 256 + tid;
+        }
+      if (split == 0) {
+        for (int y = cnt + tid; y < sel.k; y += 256) out[y] = -1;
+        if (tid == 0) sel.counts_out[unit] = cnt;
+      }
+      __syncthreads();
+      if (lane < nslot && first_entry + lane < cnt) pg_raw = s_pages[lane];
+    }
     if (pg_raw >= 0 && pg_raw < max_pages) sl_raw = page_table[(size_t)b * max_pages + pg_raw];
+  } else {
+    // The id and its slot are fetched together with the count (the count
+    // only decides later which of them are used): entry -> page -> slot is
+    // one dependent hop instead of two.
+    if (lane < tiles_per_split / TPP && first_entry + lane < ids_stride) {
+      pg_raw = ids[(size_t)unit * ids_stride + first_entry + lane];
+      if (pg_raw >= 0 && pg_raw < max_pages) sl_raw = page_table[(size_t)b * max_pages + pg_raw];
+    }
+    cnt = counts[unit];
+    cnt = cnt < 0 ? 0 : (cnt > ids_stride ? ids_stride : cnt);
   }
-  int cnt = counts[unit];
-  cnt = cnt < 0 ? 0 : (cnt > ids_stride ? ids_stride : cnt);
   const int n_tiles = cnt * TPP;
   if (t_begin >= n_tiles) return;  // whole workgroup: the combine reads only active splits
   const int t_end = min(n_tiles, t_begin + tiles_per_split);
@@ -210,7 +276,8 @@ __global__ __launch_bounds__(256) void attn_partial_mfma_kernel(
     const int32_t* __restrict__ ids, const int32_t* __restrict__ counts, int ids_stride, int n_kv_heads, int P,
     int max_pages, int num_slots, unsigned long long streaming, int sink, int local, float scale, float c,
     int tiles_per_split, int n_splits, const int32_t* __restrict__ skip_ids,
-    const int32_t* __restrict__ skip_counts, float* __restrict__ part_o, float* __restrict__ part_ml) {
+    const int32_t* __restrict__ skip_counts, SelectArgs, float* __restrict__ part_o,
+    float* __restrict__ part_ml) {
   using M = MfmaWave<D, G>;
   constexpr int NK = M::NK, NB = M::NB;
   constexpr int OS = D + 4;   // LDS row stride of the merge buffer (floats)
@@ -721,7 +788,7 @@ template <typename T, int D, int G>
 static int launch_attn_g(const void* q, const dsa_kv* kv, const int32_t* ids, const int32_t* counts,
                          int ids_stride, uint64_t smask, int sink, int local, float scale, float* O, float* l,
                          float* m, void* ws, int fold, const int32_t* skip_ids, const int32_t* skip_counts,
-                         hipStream_t st) {
+                         const SelectArgs& sel, hipStream_t st) {
   const SplitPlan p = plan_splits(kv, ids_stride, __builtin_popcountll(smask));
   const size_t units = (size_t)kv->batch * kv->n_kv_heads;
   float* part_o = (float*)ws;
@@ -733,19 +800,23 @@ static int launch_attn_g(const void* q, const dsa_kv* kv, const int32_t* ids, co
   hipLaunchKernelGGL((KERNEL<__VA_ARGS__>), grid, dim3(256), dyn, st, (const TT*)q, (const TT*)kv->k,           \
                      (const TT*)kv->v, kv->page_table, kv->seq_lens, ids, counts, ids_stride, kv->n_kv_heads,   \
                      kv->page_size, kv->max_pages, kv->num_slots, (unsigned long long)smask, sink, local, scale, \
-                     c, p.tiles_per_split, p.n_splits, skip_ids, skip_counts, part_o, part_ml)
+                     c, p.tiles_per_split, p.n_splits, skip_ids, skip_counts, sel, part_o, part_ml)
   if constexpr (sizeof(T) == 2 && G >= 8) {
+    if (sel.e) return DSA_ERR_UNSUPPORTED;
     if (skip_ids) DSA_PARTIAL(attn_partial_mfma_kernel, uint16_t, D, G, true);
     else DSA_PARTIAL(attn_partial_mfma_kernel, uint16_t, D, G, false);
   } else {
-    if (skip_ids) DSA_PARTIAL(attn_partial_kernel, T, T, D, G, true);
-    else DSA_PARTIAL(attn_partial_kernel, T, T, D, G, false);
+    if (sel.e == 8) DSA_PARTIAL(attn_partial_kernel, T, T, D, G, false, 8);
+    else if (sel.e == 16) DSA_PARTIAL(attn_partial_kernel, T, T, D, G, false, 16);
+    else if (sel.e) return DSA_ERR_UNSUPPORTED;
+    else if (skip_ids) DSA_PARTIAL(attn_partial_kernel, T, T, D, G, true, 0);
+    else DSA_PARTIAL(attn_partial_kernel, T, T, D, G, false, 0);
   }
 #undef DSA_PARTIAL
   int rc = launch_status();
   if (rc) return rc;
   hipLaunchKernelGGL((attn_combine_kernel<D>), dim3(kv->n_kv_heads * G, kv->batch), dim3(256), 0, st, part_o,
-                     part_ml, counts, ids_stride, kv->n_kv_heads, G, p.TPP, p.tiles_per_split, p.n_splits, fold, O,
+                     part_ml, sel.e ? sel.counts_out : counts, ids_stride, kv->n_kv_heads, G, p.TPP, p.tiles_per_split, p.n_splits, fold, O,
                      l, m);
   return launch_status();
 }
@@ -754,13 +825,13 @@ template <typename T, int D>
 static int launch_attn_d(const void* q, int G, const dsa_kv* kv, const int32_t* ids, const int32_t* counts,
                          int ids_stride, uint64_t smask, int sink, int local, float scale, float* O, float* l,
                          float* m, void* ws, int fold, const int32_t* skip_ids, const int32_t* skip_counts,
-                         hipStream_t st) {
+                         const SelectArgs& sel, hipStream_t st) {
   switch (G) {
-    case 1: return launch_attn_g<T, D, 1>(q, kv, ids, counts, ids_stride, smask, sink, local, scale, O, l, m, ws, fold, skip_ids, skip_counts, st);
-    case 2: return launch_attn_g<T, D, 2>(q, kv, ids, counts, ids_stride, smask, sink, local, scale, O, l, m, ws, fold, skip_ids, skip_counts, st);
-    case 4: return launch_attn_g<T, D, 4>(q, kv, ids, counts, ids_stride, smask, sink, local, scale, O, l, m, ws, fold, skip_ids, skip_counts, st);
-    case 8: return launch_attn_g<T, D, 8>(q, kv, ids, counts, ids_stride, smask, sink, local, scale, O, l, m, ws, fold, skip_ids, skip_counts, st);
-    case 16: return launch_attn_g<T, D, 16>(q, kv, ids, counts, ids_stride, smask, sink, local, scale, O, l, m, ws, fold, skip_ids, skip_counts, st);
+    case 1: return launch_attn_g<T, D, 1>(q, kv, ids, counts, ids_stride, smask, sink, local, scale, O, l, m, ws, fold, skip_ids, skip_counts, sel, st);
+    case 2: return launch_attn_g<T, D, 2>(q, kv, ids, counts, ids_stride, smask, sink, local, scale, O, l, m, ws, fold, skip_ids, skip_counts, sel, st);
+    case 4: return launch_attn_g<T, D, 4>(q, kv, ids, counts, ids_stride, smask, sink, local, scale, O, l, m, ws, fold, skip_ids, skip_counts, sel, st);
+    case 8: return launch_attn_g<T, D, 8>(q, kv, ids, counts, ids_stride, smask, sink, local, scale, O, l, m, ws, fold, skip_ids, skip_counts, sel, st);
+    case 16: return launch_attn_g<T, D, 16>(q, kv, ids, counts, ids_stride, smask, sink, local, scale, O, l, m, ws, fold, skip_ids, skip_counts, sel, st);
   }
   return DSA_ERR_UNSUPPORTED;
 }
@@ -768,13 +839,13 @@ static int launch_attn_d(const void* q, int G, const dsa_kv* kv, const int32_t* 
 static int launch_attn(const void* q, int G, const dsa_kv* kv, const int32_t* ids, const int32_t* counts,
                        int ids_stride, uint64_t smask, int sink, int local, float scale, float* O, float* l,
                        float* m, void* ws, int fold, const int32_t* skip_ids, const int32_t* skip_counts,
-                       hipStream_t st) {
+                       const SelectArgs& sel, hipStream_t st) {
   const bool bf = kv->dtype == DSA_BF16;
   if (kv->head_dim == 128)
-    return bf ? launch_attn_d<uint16_t, 128>(q, G, kv, ids, counts, ids_stride, smask, sink, local, scale, O, l, m, ws, fold, skip_ids, skip_counts, st)
-              : launch_attn_d<float, 128>(q, G, kv, ids, counts, ids_stride, smask, sink, local, scale, O, l, m, ws, fold, skip_ids, skip_counts, st);
-  return bf ? launch_attn_d<uint16_t, 64>(q, G, kv, ids, counts, ids_stride, smask, sink, local, scale, O, l, m, ws, fold, skip_ids, skip_counts, st)
-            : launch_attn_d<float, 64>(q, G, kv, ids, counts, ids_stride, smask, sink, local, scale, O, l, m, ws, fold, skip_ids, skip_counts, st);
+    return bf ? launch_attn_d<uint16_t, 128>(q, G, kv, ids, counts, ids_stride, smask, sink, local, scale, O, l, m, ws, fold, skip_ids, skip_counts, sel, st)
+              : launch_attn_d<float, 128>(q, G, kv, ids, counts, ids_stride, smask, sink, local, scale, O, l, m, ws, fold, skip_ids, skip_counts, sel, st);
+  return bf ? launch_attn_d<uint16_t, 64>(q, G, kv, ids, counts, ids_stride, smask, sink, local, scale, O, l, m, ws, fold, skip_ids, skip_counts, sel, st)
+            : launch_attn_d<float, 64>(q, G, kv, ids, counts, ids_stride, smask, sink, local, scale, O, l, m, ws, fold, skip_ids, skip_counts, sel, st);
 }
 
 static int check_attn_common(const void* q, int n_q_heads, const dsa_kv* kv, float scale, int* G) {
@@ -860,7 +931,45 @@ extern "C" int dsa_sparse_decode_attn(const void* q, int32_t n_q_heads, const ds
   if (!aligned16(ws)) return DSA_ERR_ALIGN;
   const int sink = stream_cfg ? stream_cfg->sink : 0, local = stream_cfg ? stream_cfg->local : 0;
   return launch_attn(q, G, kv, ids, counts, ids_stride, smask, sink, local, scale, O, l, m, ws, 0, nullptr,
-                     nullptr, (hipStream_t)stream);
+                     nullptr, SelectArgs{}, (hipStream_t)stream);
+}
+
+extern "C" int dsa_sparse_decode_attn_topk(const void* q, int32_t n_q_heads, const dsa_kv* kv, const float* scores,
+                                           int32_t k, const dsa_stream_cfg* stream_cfg, float scale, int32_t* ids,
+                                           int32_t* counts, float* O, float* l, float* m, void* ws, size_t ws_bytes,
+                                           void* stream) {
+  int G = 0;
+  int rc = check_attn_common(q, n_q_heads, kv, scale, &G);
+  if (rc) return rc;
+  if (k < 1) return DSA_ERR_SHAPE;
+  uint64_t smask;
+  if ((rc = streaming_mask(stream_cfg, kv->n_kv_heads, &smask))) return rc;
+  if (smask) {
+    // the sink/local page list of a streaming head must fit in k
+    long long worst = (stream_cfg->sink + (long long)kv->page_size - 1) / kv->page_size +
+                      (stream_cfg->local + (long long)kv->page_size - 1) / kv->page_size + 1;
+    if (worst > kv->max_pages) worst = kv->max_pages;
+    if (worst > k) return DSA_ERR_SHAPE;
+  }
+  if (kv->batch == 0) return DSA_OK;
+  if (!scores || !ids || !counts || !O || !l || !m) return DSA_ERR_NULL;
+  const size_t need = dsa_workspace_bytes(DSA_OP_SPARSE_DECODE_ATTN, kv, n_q_heads, k);
+  if (!ws || ws_bytes < need) return DSA_ERR_WORKSPACE;
+  if (!aligned16(ws)) return DSA_ERR_ALIGN;
+  const int sink = stream_cfg ? stream_cfg->sink : 0, local = stream_cfg ? stream_cfg->local : 0;
+  hipStream_t st = (hipStream_t)stream;
+  const int e = kv->max_pages <= 2048 ? 8 : (kv->max_pages <= 4096 ? 16 : 0);
+  if (G <= 4 && e) {
+    const SelectArgs sel{scores, k, ids, counts, e};
+    return launch_attn(q, G, kv, nullptr, nullptr, k, smask, sink, local, scale, O, l, m, ws, 0, nullptr, nullptr,
+                       sel, st);
+  }
+  // large rows or large groups: the two calls in sequence
+  if ((rc = dsa_page_select_topk(scores, kv->batch, kv->n_kv_heads, kv->max_pages, kv->seq_lens, kv->page_size, k,
+                                 stream_cfg, ids, counts, stream)))
+    return rc;
+  return launch_attn(q, G, kv, ids, counts, k, smask, sink, local, scale, O, l, m, ws, 0, nullptr, nullptr,
+                     SelectArgs{}, st);
 }
 
 extern "C" int dsa_attn_repair(const void* q, int32_t n_q_heads, const dsa_kv* kv, const int32_t* a_ids,
@@ -879,7 +988,7 @@ extern "C" int dsa_attn_repair(const void* q, int32_t n_q_heads, const dsa_kv* k
   const size_t lds = (size_t)((kv->max_pages + 31) / 32) * sizeof(uint32_t);
   if ((int)lds + 52 * 1024 > max_lds_per_block()) return DSA_ERR_UNSUPPORTED;
   return launch_attn(q, G, kv, a_ids, a_counts, ids_stride, 0, 0, 0, scale, O, l, m, ws, 1, p_ids, p_counts,
-                     (hipStream_t)stream);
+                     SelectArgs{}, (hipStream_t)stream);
 }
 
 extern "C" int dsa_page_select_progressive(const void* q, int32_t n_q_heads, const dsa_kv* kv, const float* scores,

@@ -219,6 +219,26 @@ int dsa_sparse_decode_attn(const void *q, int32_t n_q_heads, const dsa_kv *kv,
                            float *m, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * dsa_sparse_decode_attn_topk -- dsa_page_select_topk followed by
+ * dsa_sparse_decode_attn over the pages it selects, in one call ([PSA]
+ * section 2.2 / [PRR] section 2: the selection stage feeding the sparse
+ * attention of a dynamic sparse attention step).
+ *
+ * Results are those of the two calls with ids_stride = k: ids[b][h][0..k)
+ * (ascending, -1 padded) and counts[b][h] are written, and O, l, m are
+ * attention over those pages.  For groups of at most 4 q heads and
+ * max_pages <= 4096 every attention workgroup ranks its row of scores itself
+ * (no separate selection launch); otherwise the two launches run in order.
+ * Arguments as for the two calls; ws: device scratch of
+ * dsa_workspace_bytes(DSA_OP_SPARSE_DECODE_ATTN, kv, n_q_heads, k).
+ * Errors: those of either call.
+ */
+int dsa_sparse_decode_attn_topk(const void *q, int32_t n_q_heads, const dsa_kv *kv,
+                                const float *scores, int32_t k, const dsa_stream_cfg *stream_cfg,
+                                float scale, int32_t *ids, int32_t *counts, float *O, float *l,
+                                float *m, void *ws, size_t ws_bytes, void *stream);
+
+/*
  * dsa_attn_repair -- PRR incremental repair ([PRR] section 3.3, the repair
  * kernel's online-softmax recurrence; section 3.4, the missing set M = A\P).
  *

@@ -1,0 +1,77 @@
+"""GPU parity of dsa_sparse_decode_attn_topk (selection recomputed inside
+the attention workgroups) against the two separate calls it replaces and
+against the fp64 oracle: ids and counts bit-exact with dsa_page_select_topk
+(same fp32 scores), (O, l, m) to the attention tolerance of the oracle over
+those pages.  Covers both row widths of the fused path (<= 2048 and <= 4096
+pages), streaming heads, k above the valid page count, empty sequences,
+fp32 KV, and the fallback (16 heads per KV head; rows above 4096 pages)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from parity_util import check_attention, ids_lists, np_, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _banner(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def _run(dsa, bt, k, st=None):
+    q, kv, st0 = to_device(dsa, bt)
+    st = st or st0
+    meta = dsa.page_meta_build(kv, bt.logical_page)
+    sc = dsa.page_score(q, kv, meta, bt.logical_page, streaming=st)
+    ids_f, cnt_f, O, l, m = dsa.sparse_decode_attn_topk(q, kv, sc, k, streaming=st)
+    ids_s, cnt_s = dsa.page_select_topk(sc, kv.seq_lens, bt.page_size, k, streaming=st)
+    O2, l2, m2 = dsa.sparse_decode_attn(q, kv, ids_s, cnt_s, streaming=st)
+    torch.cuda.synchronize()
+    assert np.array_equal(np_(cnt_f), np_(cnt_s)), "counts differ from dsa_page_select_topk"
+    assert np.array_equal(np_(ids_f), np_(ids_s)), "ids differ from dsa_page_select_topk"
+    # same pages, same kernels: the outputs of the two routes agree to rounding
+    np.testing.assert_allclose(np_(O), np_(O2), rtol=0, atol=1e-6)
+    rO, rl, rm = oracle.sparse_decode(bt, ids_lists(np_(ids_f), np_(cnt_f)))
+    check_attention(bt.dtype, np_(O), np_(l), np_(m), rO, rl, rm, "fused")
+
+
+@pytest.mark.parametrize("dtype,D,P,G,max_pages,k", [
+    ("bf16", 128, 16, 4, 2048, 256),     # quest shape, 8 scores per thread
+    ("bf16", 128, 16, 4, 3000, 100),     # 16 scores per thread
+    ("bf16", 64, 16, 2, 500, 37),
+    ("f32", 64, 16, 1, 700, 64),
+    ("bf16", 128, 16, 16, 600, 48),      # fallback: two launches
+    ("bf16", 128, 16, 4, 5000, 64),      # fallback: row above 4096 pages
+])
+def test_fused_topk_attention(gpu_lib, dtype, D, P, G, max_pages, k):
+    dsa = gpu_lib
+    _banner(f"fused {dtype} D={D} P={P} G={G} N={max_pages} k={k}")
+    lens = [0, 5, P * 3 + 1, P * (max_pages // 3) + 7, P * max_pages]
+    bt = wl.random_batch(81, lens, n_q_heads=2 * G, n_kv_heads=2, head_dim=D, page_size=P, dtype=dtype,
+                         max_pages=max_pages)
+    _run(dsa, bt, k)
+
+
+def test_fused_streaming_heads(gpu_lib):
+    dsa = gpu_lib
+    _banner("fused streaming heads")
+    bt = wl.random_batch(82, [64 * 20 + 30, 64 * 8, 200, 64 * 300], n_q_heads=8, n_kv_heads=4, head_dim=128,
+                         page_size=64, logical_page=16, streaming=[1, 0, 0, 1], sink=128, local=256)
+    _run(dsa, bt, 8)
+
+
+def test_fused_quest_workload(gpu_lib):
+    dsa = gpu_lib
+    _banner("fused quest_gqa_32k")
+    bt = wl.make("quest_gqa_32k")
+    _run(dsa, bt, bt.topk)
+
+
+def test_fused_exact_ties(gpu_lib):
+    dsa = gpu_lib
+    _banner("fused exact score ties")
+    bt = wl.random_batch(83, [16 * 900 + 5, 16 * 400], n_q_heads=8, n_kv_heads=2, head_dim=128, max_pages=1000,
+                         dup_pages=40)
+    _run(dsa, bt, 30)
