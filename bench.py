@@ -13,8 +13,9 @@ already resident in HBM; page metadata is built beforehand (prefill work).
       4 of 8 KV heads streaming (sink 128 + local 256); batch 4, 131072 tokens, top-64
   psa_mha_64k              page_score -> page_select_progressive (threshold 0.95)
       batch 8, 32 heads MHA, 65536 tokens
-  prr_512k                 PRR: selection on a side stream overlapped with speculative
-      attention, then repair, EMA update and the next speculative set;
+  prr_512k                 PRR: score and one launch selecting A and (after the EMA
+      update) the next speculative set, on a side stream overlapped with the
+      speculative attention; then the repair;
       batch 1, 32 q / 2 KV heads, 524288 tokens, top-2048, 64-step query trace
   tiny_f32                 score, top-8, attention and PSA on one fp32 head
 
@@ -280,6 +281,10 @@ def main():
                                                      decs[r].p_counts, O, l, m, scale=scale, ws=decs[r].ws),
             "ema_predict_update": lambda r: dsa.ema_predict_update(decs[r].scores, decs[r].level, decs[r].trend,
                                                                    decs[r].pred, a_, b_, g_),
+            "prr_select": lambda r: dsa.prr_select(decs[r].scores, kvs[r].seq_lens, bt.page_size, bt.topk,
+                                                   decs[r].level, decs[r].trend, decs[r].pred, a_, b_, g_, False,
+                                                   decs[r].k_spec, decs[r].a_ids, decs[r].a_counts,
+                                                   decs[r].p_ids, decs[r].p_counts),
         }
         op_bytes = {"page_score": mb, "sparse_decode_attn": kvb, "ema_predict_update": B * Hkv * N * 24}
     elif bt.topk is None or a.workload == "tiny_f32":   # PSA (and the tiny workload: top-k and PSA)

@@ -19,7 +19,8 @@ import torch
 __all__ = [
     "DsaError", "PagedKV", "Streaming", "lib", "LIB_PATH",
     "page_meta_build", "page_score", "page_select_topk", "page_select_progressive",
-    "sparse_decode_attn", "sparse_decode_attn_topk", "attn_repair", "ema_predict_update", "workspace_bytes",
+    "sparse_decode_attn", "sparse_decode_attn_topk", "attn_repair", "ema_predict_update", "prr_select",
+    "workspace_bytes",
     "OP_SPARSE_DECODE_ATTN", "OP_ATTN_REPAIR", "EXPORTED",
 ]
 
@@ -30,7 +31,7 @@ OP_SPARSE_DECODE_ATTN, OP_ATTN_REPAIR = 1, 2
 EXPORTED = (
     "dsa_status_str", "dsa_version", "dsa_page_meta_build", "dsa_page_score", "dsa_page_select_topk",
     "dsa_page_select_progressive", "dsa_sparse_decode_attn", "dsa_sparse_decode_attn_topk", "dsa_attn_repair",
-    "dsa_ema_predict_update", "dsa_workspace_bytes",
+    "dsa_ema_predict_update", "dsa_prr_select", "dsa_workspace_bytes",
 )
 
 
@@ -71,6 +72,7 @@ def _load(path: str = LIB_PATH):
         "dsa_sparse_decode_attn_topk": (ctypes.c_int, [P, I32, KV, P, I32, ST, F32, P, P, P, P, P, P, SZ, P]),
         "dsa_attn_repair": (ctypes.c_int, [P, I32, KV, P, P, P, P, I32, F32, P, P, P, P, SZ, P]),
         "dsa_ema_predict_update": (ctypes.c_int, [P, P, P, P, I64, F32, F32, F32, I32, P]),
+        "dsa_prr_select": (ctypes.c_int, [P, I32, I32, I32, P, I32, I32, P, P, P, P, P, F32, F32, F32, I32, I32, P, P, P]),
         "dsa_workspace_bytes": (SZ, [I32, KV, I32, I32]),
     }
     for name, (res, args) in sig.items():
@@ -333,3 +335,17 @@ def ema_predict_update(is_true, level: torch.Tensor, trend: torch.Tensor, pred: 
         _ptr(is_true), _ptr(level), _ptr(trend), _ptr(pred), n, float(alpha), float(beta), float(gamma),
         int(bool(init)), _stream()))
     return pred
+
+
+def prr_select(scores: torch.Tensor, seq_lens: torch.Tensor, page_size: int, k: int, level: torch.Tensor,
+               trend: torch.Tensor, pred: torch.Tensor, alpha: float, beta: float, gamma: float, init: bool,
+               k_spec: int, a_ids: torch.Tensor, a_counts: torch.Tensor, p_ids: torch.Tensor,
+               p_counts: torch.Tensor):
+    """A = top-k of scores; EMA update with scores; P = top-k_spec of the new
+    prediction -- one launch (see dsa_prr_select)."""
+    B, H, N = scores.shape
+    _check("dsa_prr_select", lib.dsa_prr_select(
+        _ptr(scores), B, H, N, _ptr(seq_lens), page_size, k, _ptr(a_ids), _ptr(a_counts), _ptr(level), _ptr(trend),
+        _ptr(pred), float(alpha), float(beta), float(gamma), 1 if init else 0, k_spec, _ptr(p_ids), _ptr(p_counts),
+        _stream()))
+    return a_ids, a_counts, p_ids, p_counts

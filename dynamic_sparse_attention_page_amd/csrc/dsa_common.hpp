@@ -226,6 +226,17 @@ __device__ __forceinline__ float lane_dot(const uint32_t* k, const uint32_t* q) 
   return acc;
 }
 
+// One EMA step of PRR's predictor ("Predict, Reuse, and Repair", section
+// 3.1): trend and level both read the previous level; the prediction
+// extrapolates the new level by gamma times the new trend.
+// Written with explicit fmaf so every kernel rounds it the same way.
+__device__ __forceinline__ void ema_step(float is, float lv, float tr, float alpha, float beta, float gamma,
+                                         float& nl, float& nt, float& pr) {
+  nt = fmaf(beta, is - lv, (1.0f - beta) * tr);
+  nl = fmaf(alpha, is, (1.0f - alpha) * lv);
+  pr = fmaf(gamma, nt, nl);
+}
+
 __device__ __forceinline__ int clamp_len(int L, int max_pages, int P) {
   const long long cap = (long long)max_pages * P;
   return L < 0 ? 0 : (L > cap ? (int)cap : L);

@@ -21,12 +21,11 @@ __device__ __forceinline__ void ema_one(const float* is_true, float* level, floa
     pred[x] = is;
     return;
   }
-  const float lv = level[x], tr = trend[x];
-  const float nt = beta * (is - lv) + (1.0f - beta) * tr;
-  const float nl = alpha * is + (1.0f - alpha) * lv;
+  float nl, nt, pr;
+  ema_step(is, level[x], trend[x], alpha, beta, gamma, nl, nt, pr);
   level[x] = nl;
   trend[x] = nt;
-  pred[x] = fmaf(gamma, nt, nl);
+  pred[x] = pr;
 }
 
 __global__ __launch_bounds__(256) void ema_kernel(const float* __restrict__ is_true, float* __restrict__ level,
@@ -50,19 +49,10 @@ __global__ __launch_bounds__(256) void ema_kernel(const float* __restrict__ is_t
           tr = make_float4(0.f, 0.f, 0.f, 0.f);
           pr = is;
         } else {
-          float4 nt, nl;
-          nt.x = beta * (is.x - lv.x) + (1.0f - beta) * tr.x;
-          nt.y = beta * (is.y - lv.y) + (1.0f - beta) * tr.y;
-          nt.z = beta * (is.z - lv.z) + (1.0f - beta) * tr.z;
-          nt.w = beta * (is.w - lv.w) + (1.0f - beta) * tr.w;
-          nl.x = alpha * is.x + (1.0f - alpha) * lv.x;
-          nl.y = alpha * is.y + (1.0f - alpha) * lv.y;
-          nl.z = alpha * is.z + (1.0f - alpha) * lv.z;
-          nl.w = alpha * is.w + (1.0f - alpha) * lv.w;
-          lv = nl;
-          tr = nt;
-          pr = make_float4(fmaf(gamma, nt.x, nl.x), fmaf(gamma, nt.y, nl.y), fmaf(gamma, nt.z, nl.z),
-                           fmaf(gamma, nt.w, nl.w));
+          ema_step(is.x, lv.x, tr.x, alpha, beta, gamma, lv.x, tr.x, pr.x);
+          ema_step(is.y, lv.y, tr.y, alpha, beta, gamma, lv.y, tr.y, pr.y);
+          ema_step(is.z, lv.z, tr.z, alpha, beta, gamma, lv.z, tr.z, pr.z);
+          ema_step(is.w, lv.w, tr.w, alpha, beta, gamma, lv.w, tr.w, pr.w);
         }
         reinterpret_cast<float4*>(level)[x] = lv;
         reinterpret_cast<float4*>(trend)[x] = tr;

@@ -12,6 +12,28 @@
 
 namespace dsa {
 
+// Top keff of the valid elements (index < np) of one row held in registers,
+// written ascending into out[0..k) with -1 after, and the count.
+template <int E, int NW>
+__device__ __forceinline__ void select_and_write(const uint32_t (&key)[E], int np, int keff, int k,
+                                                 int32_t* __restrict__ out, int32_t* __restrict__ count,
+                                                 SelectSmem<E, NW>& sm) {
+  constexpr int NT = NW * 64;
+  const int tid = threadIdx.x;
+  unsigned long long actm = 0ull;  // bit e: element e * NT + tid is valid
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    if (e * NT + tid < np) actm |= 1ull << e;
+  const unsigned long long selm = block_select_top<E, NW>(key, actm, np, keff, sm);
+  int rk[E];
+  ordered_ranks<E, NW>(selm, rk, sm.rank, sm.scan);
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    if (((selm >> e) & 1ull) && rk[e] < keff) out[rk[e]] = e * NT + tid;
+  for (int x = keff + tid; x < k; x += NT) out[x] = -1;
+  if (tid == 0) *count = keff;
+}
+
 template <int E, int NW>
 __global__ __launch_bounds__(NW * 64) void topk_kernel(const float* __restrict__ scores,
                                                          const int32_t* __restrict__ seq_lens, int n_kv_heads,
@@ -40,27 +62,43 @@ __global__ __launch_bounds__(NW * 64) void topk_kernel(const float* __restrict__
 
   const int keff = min(k, np);
   uint32_t key[E];
-  unsigned long long actm = 0ull;  // bit e: page e * NT + tid is valid
   const float* srow = scores + (size_t)unit * max_pages;
   // scores are loaded up to max_pages, so the loads do not wait for seq_lens
   float sv[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) sv[e] = (e * NT + tid < max_pages) ? srow[e * NT + tid] : 0.0f;
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    key[e] = order_key(sv[e]);
-    if (e * NT + tid < np) actm |= 1ull << e;
-  }
-  const unsigned long long selm = block_select_top<E, NW>(key, actm, np, keff, sm);
-  {
-    int rk[E];
-    ordered_ranks<E, NW>(selm, rk, sm.rank, sm.scan);
+  for (int e = 0; e < E; ++e) key[e] = order_key(sv[e]);
+  select_and_write<E, NW>(key, np, keff, k, out, counts + unit, sm);
+}
+
+// PRR's two selections side by side ("Predict, Reuse, and Repair",
+// sections 2 and 3.1): blockIdx.z == 0 selects A^t = top-k of the scores
+// IS^t, blockIdx.z == 1 selects P^{t+1} = top-k_spec of the prediction
+// (already updated with IS^t).
+template <int E, int NW>
+__global__ __launch_bounds__(NW * 64) void prr_select_kernel(
+    const float* __restrict__ scores, const float* __restrict__ pred, const int32_t* __restrict__ seq_lens,
+    int n_kv_heads, int max_pages, int P, int k, int32_t* __restrict__ a_ids, int32_t* __restrict__ a_counts,
+    int k_spec, int32_t* __restrict__ p_ids, int32_t* __restrict__ p_counts) {
+  constexpr int NT = NW * 64;
+  __shared__ SelectSmem<E, NW> sm;
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int unit = b * n_kv_heads + h;
+  const int tid = threadIdx.x;
+  const int L = clamp_len(seq_lens[b], max_pages, P);
+  const int np = (L + P - 1) / P;
+  const bool spec = blockIdx.z != 0;
+  const float* src = (spec ? pred : scores) + (size_t)unit * max_pages;
+  const int kk = spec ? k_spec : k;
+  float sv[E];
 #pragma unroll
-    for (int e = 0; e < E; ++e)
-      if (((selm >> e) & 1ull) && rk[e] < keff) out[rk[e]] = e * NT + tid;
-  }
-  for (int x = keff + tid; x < k; x += NT) out[x] = -1;
-  if (tid == 0) counts[unit] = keff;
+  for (int e = 0; e < E; ++e) sv[e] = (e * NT + tid < max_pages) ? src[e * NT + tid] : 0.0f;
+  uint32_t key[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) key[e] = order_key(sv[e]);
+  select_and_write<E, NW>(key, np, min(kk, np), kk, (spec ? p_ids : a_ids) + (size_t)unit * kk,
+                          (spec ? p_counts : a_counts) + unit, sm);
 }
 
 template <int E, int NW>
@@ -71,9 +109,50 @@ static int launch_topk_e(const float* scores, int B, int Hkv, int max_pages, con
   return launch_status();
 }
 
+template <int E, int NW>
+static int launch_prr_select_e(const float* scores, const float* pred, int B, int Hkv, int max_pages,
+                               const int32_t* seq_lens, int P, int k, int32_t* a_ids, int32_t* a_counts, int k_spec,
+                               int32_t* p_ids, int32_t* p_counts, hipStream_t st) {
+  hipLaunchKernelGGL((prr_select_kernel<E, NW>), dim3(Hkv, B, 2), dim3(NW * 64), 0, st, scores, pred, seq_lens, Hkv,
+                     max_pages, P, k, a_ids, a_counts, k_spec, p_ids, p_counts);
+  return launch_status();
+}
+
 }  // namespace dsa
 
 using namespace dsa;
+
+extern "C" int dsa_prr_select(const float* scores, int32_t batch, int32_t n_kv_heads, int32_t max_pages,
+                              const int32_t* seq_lens, int32_t page_size, int32_t k, int32_t* a_ids,
+                              int32_t* a_counts, float* level, float* trend, float* pred, float alpha, float beta,
+                              float gamma, int32_t init, int32_t k_spec, int32_t* p_ids, int32_t* p_counts,
+                              void* stream) {
+  if (batch < 0 || n_kv_heads < 1 || max_pages < 1 || page_size < 1 || k < 1 || k_spec < 1) return DSA_ERR_SHAPE;
+  if (max_pages > 65536) return DSA_ERR_UNSUPPORTED;
+  if (batch == 0) return DSA_OK;
+  if (!scores || !seq_lens || !a_ids || !a_counts || !level || !trend || !pred || !p_ids || !p_counts)
+    return DSA_ERR_NULL;
+  if (pred == level || pred == trend || level == trend) return DSA_ERR_SHAPE;
+  // the EMA update is elementwise and spread over the whole GPU; the two
+  // selections then run in one grid
+  int rc = dsa_ema_predict_update(scores, level, trend, pred, (int64_t)batch * n_kv_heads * max_pages, alpha, beta,
+                                  gamma, init, stream);
+  if (rc) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  const int N = max_pages;
+#define DSA_PRR(E, NW) return launch_prr_select_e<E, NW>(scores, pred, batch, n_kv_heads, max_pages, seq_lens, \
+                                                          page_size, k, a_ids, a_counts, k_spec, p_ids, p_counts, st)
+  if (N <= 256) DSA_PRR(4, 1);
+  if (N <= 512) DSA_PRR(8, 1);
+  if (N <= 1024) DSA_PRR(4, 4);
+  if (N <= 2048) DSA_PRR(8, 4);
+  if (N <= 4096) DSA_PRR(8, 8);
+  if (N <= 8192) DSA_PRR(8, 16);
+  if (N <= 16384) DSA_PRR(16, 16);
+  if (N <= 32768) DSA_PRR(32, 16);
+  DSA_PRR(64, 16);
+#undef DSA_PRR
+}
 
 extern "C" int dsa_page_select_topk(const float* scores, int32_t batch, int32_t n_kv_heads, int32_t max_pages,
                                     const int32_t* seq_lens, int32_t page_size, int32_t k,

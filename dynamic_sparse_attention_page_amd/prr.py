@@ -10,9 +10,10 @@ result with the pages of A that P missed (section 3.3), and feeds the new
 scores back into the predictor.
 
 The predictor update and the next step's speculative set P^{t+1} depend
-only on this step's scores IS^t, not on attention, so they follow the
-selection on the side stream and overlap the repair; the caller's stream
-waits for P^{t+1} only at the next step's speculative attention.  P is
+only on this step's scores IS^t, not on attention or on A^t, so one launch
+(dsa_prr_select) selects A^t and, in other workgroups of the same grid,
+updates the EMA and selects P^{t+1}; the caller's stream waits for P^{t+1}
+only at the next step's speculative attention.  P is
 double-buffered: the side stream writes P^{t+1} while the caller's stream
 still reads P^t.
 
@@ -27,7 +28,7 @@ import math
 import torch
 
 from . import (OP_ATTN_REPAIR, PagedKV, attn_repair, ema_predict_update, page_score, page_select_topk,
-               sparse_decode_attn, workspace_bytes)
+               prr_select, sparse_decode_attn, workspace_bytes)
 
 
 class PRRDecoder:
@@ -110,15 +111,28 @@ class PRRDecoder:
             p_ids[..., :self.k_spec].copy_(ids)
             p_counts.copy_(counts)
 
+    def _select_and_predict(self, q, init: bool, buf: int):
+        """IS^t, A^t, the EMA update and P^{t+1} (into buffer buf): one
+        score launch and one launch that runs both selections side by side
+        when |A| = |P|, else the separate calls."""
+        if self.k == self.k_spec:
+            page_score(q, self.kv, self.meta, self.lp, scores=self.scores)
+            p_ids, p_counts = self._p[buf]
+            prr_select(self.scores, self.kv.seq_lens, self.kv.page_size, self.k, self.level, self.trend,
+                       self.pred.view(-1), self.alpha, self.beta, self.gamma, init, self.k_spec, self.a_ids,
+                       self.a_counts, p_ids, p_counts)
+        else:
+            self._select(q)
+            self._predict_next(init=init, buf=buf)
+
     def step(self, q: torch.Tensor):
         out = (self.O, self.l, self.m)
         main = torch.cuda.current_stream()
         cur, nxt = self._cur, 1 - self._cur
         if self.t == 0:
             # no prediction yet: a plain selection-then-attention step
-            self._select(q)
+            self._select_and_predict(q, init=True, buf=nxt)
             sparse_decode_attn(q, self.kv, self.a_ids, self.a_counts, scale=self.scale, out=out, ws=self.ws)
-            self._predict_next(init=True, buf=nxt)
         else:
             # the side stream starts once everything enqueued so far on the
             # caller's stream (the previous step, which read a_ids and P^{t-1})
@@ -127,12 +141,18 @@ class PRRDecoder:
             fork.record(main)
             with torch.cuda.stream(self.side):
                 self.side.wait_event(fork)
-                self._select(q)                              # IS^t, A^t ...
-                a_ready = torch.cuda.Event()
-                a_ready.record(self.side)
-                self._predict_next(init=False, buf=nxt)      # ... then EMA and P^{t+1}
-                p_ready = torch.cuda.Event()
-                p_ready.record(self.side)
+                if self.k == self.k_spec:
+                    self._select_and_predict(q, init=False, buf=nxt)   # IS^t, A^t, EMA, P^{t+1}
+                    a_ready = torch.cuda.Event()
+                    a_ready.record(self.side)
+                    p_ready = a_ready
+                else:
+                    self._select(q)                              # IS^t, A^t ...
+                    a_ready = torch.cuda.Event()
+                    a_ready.record(self.side)
+                    self._predict_next(init=False, buf=nxt)      # ... then EMA and P^{t+1}
+                    p_ready = torch.cuda.Event()
+                    p_ready.record(self.side)
             # speculative attention over P^t, overlapped with the selection
             self.join()
             p_ids, p_counts = self._p[cur]

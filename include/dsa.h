@@ -277,6 +277,29 @@ int dsa_ema_predict_update(const float *is_true, float *level, float *trend, flo
                            void *stream);
 
 /*
+ * dsa_prr_select -- PRR's selection stage ([PRR] section 2:
+ * the exact selection A^t; section 3.1: the EMA update with IS^t and the
+ * next speculative set P^{t+1} = top-k_spec of the prediction).
+ *
+ * Equivalent to, in order:
+ *   dsa_page_select_topk(scores, ..., k, NULL, a_ids, a_counts)
+ *   dsa_ema_predict_update(scores, level, trend, pred, batch*n_kv_heads*max_pages,
+ *                          alpha, beta, gamma, init)
+ *   dsa_page_select_topk(pred, ..., k_spec, NULL, p_ids, p_counts)
+ * as two launches: the elementwise EMA update over the whole GPU, then one
+ * grid in which the two selections run side by side.
+ * scores: IS^t, device float [batch][n_kv_heads][max_pages]; level, trend,
+ * pred: device float arrays of the same shape, distinct; a_ids: int32
+ * [batch][n_kv_heads][k]; p_ids: int32 [batch][n_kv_heads][k_spec]; ids
+ * ascending, -1 padded.  No streaming heads.  max_pages <= 65536.
+ */
+int dsa_prr_select(const float *scores, int32_t batch, int32_t n_kv_heads, int32_t max_pages,
+                   const int32_t *seq_lens, int32_t page_size, int32_t k, int32_t *a_ids,
+                   int32_t *a_counts, float *level, float *trend, float *pred, float alpha,
+                   float beta, float gamma, int32_t init, int32_t k_spec, int32_t *p_ids,
+                   int32_t *p_counts, void *stream);
+
+/*
  * dsa_workspace_bytes -- scratch needed by dsa_sparse_decode_attn (op
  * DSA_OP_SPARSE_DECODE_ATTN) or dsa_attn_repair (DSA_OP_ATTN_REPAIR) for
  * this pool, n_q_heads and ids_stride.  Returns 0 for invalid arguments.
