@@ -751,10 +751,15 @@ struct SplitPlan {
   int tiles_per_split, n_splits, TPP;
 };
 
-// Tiles per workgroup so that ~1024 workgroups cover the largest possible
-// selection (counts live on the device, so the grid is sized for ids_stride).
-inline SplitPlan plan_splits(const dsa_kv* kv, int ids_stride, int n_streaming_heads) {
+// Tiles per workgroup so that about DSA_SPLIT_TARGET workgroups cover the
+// largest possible selection (counts live on the device, so the grid is
+// sized for ids_stride).  The matrix-core tile (8+ heads) is cheap enough
+// for twice the tiles per workgroup; the smaller grid also leaves CUs to a
+// kernel running beside it (PRR's selection runs beside its speculative
+// attention).
+inline SplitPlan plan_splits(const dsa_kv* kv, int ids_stride, int n_streaming_heads, int G) {
   SplitPlan p;
+  const long long target = G >= 8 ? DSA_SPLIT_TARGET / 2 : DSA_SPLIT_TARGET;
   p.TPP = kv->page_size / 16;
   const long long tiles_max = (long long)ids_stride * p.TPP;
   const int dense_heads = kv->n_kv_heads - n_streaming_heads;
@@ -762,7 +767,7 @@ inline SplitPlan plan_splits(const dsa_kv* kv, int ids_stride, int n_streaming_h
   // a split's pages must fit the 64 lanes that resolve them
   const long long cap = 64LL * p.TPP < 128 ? 64LL * p.TPP : 128;
   long long tps = 2 * kWgWaves;
-  while (tps < cap && total / tps > DSA_SPLIT_TARGET) tps <<= 1;
+  while (tps < cap && total / tps > target) tps <<= 1;
   p.tiles_per_split = (int)tps;
   p.n_splits = (int)((tiles_max + tps - 1) / tps);
   if (p.n_splits < 1) p.n_splits = 1;
@@ -789,7 +794,7 @@ static int launch_attn_g(const void* q, const dsa_kv* kv, const int32_t* ids, co
                          int ids_stride, uint64_t smask, int sink, int local, float scale, float* O, float* l,
                          float* m, void* ws, int fold, const int32_t* skip_ids, const int32_t* skip_counts,
                          const SelectArgs& sel, hipStream_t st) {
-  const SplitPlan p = plan_splits(kv, ids_stride, __builtin_popcountll(smask));
+  const SplitPlan p = plan_splits(kv, ids_stride, __builtin_popcountll(smask), G);
   const size_t units = (size_t)kv->batch * kv->n_kv_heads;
   float* part_o = (float*)ws;
   float* part_ml = (float*)((char*)ws + align256(units * max_splits_of(kv, ids_stride) * G * D * sizeof(float)));
