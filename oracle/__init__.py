@@ -29,6 +29,7 @@ against closed forms, brute force or hand-built inputs.
 """
 from __future__ import annotations
 
+import dataclasses
 import math
 
 import numpy as np
@@ -95,6 +96,42 @@ def page_meta(batch, units=None) -> tuple[np.ndarray, np.ndarray]:
                     meta[slot, h, s, 1] = sub.max(axis=0)
                     has[slot, h, s] = True
     return meta, has
+
+
+# --------------------------------------------------------------------------
+# decode-time append  (PSA section 3.1, system design: the KV cache manager
+# writes each new token's K/V into its GPU block, and block metadata stays in
+# GPU memory; LServe section 4.2, Figure 7: a physical page's kmin/kmax come
+# from the prefill and the earlier decode steps)
+# --------------------------------------------------------------------------
+def append_token(batch, k_new, v_new):
+    """One new token per sequence, at position p = seq_lens[b]: its rows
+    k_new[b][h], v_new[b][h] (stored format) go to row p % P of the slot that
+    holds page p // P, and the sequence grows by one.  A sequence whose page
+    lies past max_pages, or whose page-table entry is no slot, is left as it
+    is (the slot of a new page is allocated by the caller beforehand).
+
+    Returns (grown batch, appended flags).  The key metadata of the grown
+    cache is, by definition, page_meta() of the returned batch: an
+    incremental update must reach exactly that, since min and max are
+    exact."""
+    P = batch.page_size
+    out = dataclasses.replace(batch, k=batch.k.copy(), v=batch.v.copy(),
+                              seq_lens=np.array(batch.seq_lens, dtype=np.int32, copy=True))
+    done = np.zeros(batch.batch, bool)
+    for b in range(batch.batch):
+        p = int(batch.seq_lens[b])
+        j = p // P
+        if p < 0 or j >= batch.max_pages:
+            continue
+        slot = int(batch.page_table[b][j])
+        if not 0 <= slot < batch.num_slots:
+            continue
+        out.k[slot, :, p % P] = k_new[b]
+        out.v[slot, :, p % P] = v_new[b]
+        out.seq_lens[b] = p + 1
+        done[b] = True
+    return out, done
 
 
 # --------------------------------------------------------------------------

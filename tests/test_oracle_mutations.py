@@ -31,6 +31,10 @@ MUTATIONS = [
      "return np.asarray(level, float) + np.asarray(trend, float)"),
     ("set(range(max(0, L - local), L))", "set(range(max(0, L - local + page_size), L))"),
     ("int(math.floor(delta * a_size))", "int(math.ceil(delta * a_size))"),
+    ("out.k[slot, :, p % P] = k_new[b]", "out.k[slot, :, (p + 1) % P] = k_new[b]"),
+    ("out.v[slot, :, p % P] = v_new[b]", "out.v[slot, :, p % P] = k_new[b]"),
+    ("if p < 0 or j >= batch.max_pages:", "if p < 0 or j > batch.max_pages:"),
+    ("out.seq_lens[b] = p + 1", "out.seq_lens[b] = p + 1 if p % P else p"),
 ]
 
 

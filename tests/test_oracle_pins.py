@@ -83,6 +83,95 @@ def test_meta_is_the_attained_per_channel_box(dtype, P, Pl):
                     assert np.all((sub == kmin).any(axis=0)) and np.all((sub == kmax).any(axis=0))
 
 
+# ---------------------------------------------------------------- decode-time append
+def free_slots(bt):
+    return sorted(set(range(bt.num_slots)) - set(int(x) for x in bt.page_table[bt.page_table >= 0]))
+
+
+def stored(x, dtype):
+    return (wl.from_bf16_bits(x) if dtype == "bf16" else np.asarray(x, np.float32)).astype(np.float64)
+
+
+@pytest.mark.parametrize("dtype,P,Pl", [("bf16", 16, 16), ("bf16", 64, 16), ("f32", 32, 16)])
+def test_append_writes_the_next_token_and_nothing_else(dtype, P, Pl):
+    """By direct pool indexing: after one append every sequence reads back
+    its old tokens followed by the new row (in both pools), and exactly one
+    row per (sequence, KV head) of each pool changed.  Sequence 1's new token
+    opens page 1, whose slot the test allocates first."""
+    bt = wl.random_batch(11, [5, P, 3 * P - 1], n_q_heads=2, n_kv_heads=2, head_dim=16, page_size=P,
+                         logical_page=Pl, dtype=dtype, max_pages=4, spare_slots=4)
+    bt.page_table[1][1] = free_slots(bt)[0]
+    kn, vn = wl.append_stream(5, 3, 2, 16, 1, dtype)
+    nb, done = oracle.append_token(bt, kn[0], vn[0])
+    assert done.all() and list(nb.seq_lens) == [6, P + 1, 3 * P]
+    for b in range(3):
+        for h in range(2):
+            for pool0, pool1, new in ((bt.k, nb.k, kn), (bt.v, nb.v, vn)):
+                before, after = token_major(bt, pool0, b, h), token_major(nb, pool1, b, h)
+                np.testing.assert_array_equal(after[:-1], before)
+                np.testing.assert_array_equal(after[-1], stored(new[0, b, h], dtype))
+    for pool0, pool1 in ((bt.k, nb.k), (bt.v, nb.v)):
+        assert int((pool0 != pool1).any(axis=-1).sum()) == 3 * 2
+
+
+def test_append_skips_full_and_unallocated_sequences():
+    """A sequence at max_pages * P tokens and one whose next page has no slot
+    (page-table entry -1) are left exactly as they were."""
+    bt = wl.random_batch(12, [64, 32, 7], n_q_heads=2, n_kv_heads=2, head_dim=16, page_size=16,
+                         dtype="f32", max_pages=4, spare_slots=2)
+    kn, vn = wl.append_stream(6, 3, 2, 16, 1, "f32")
+    nb, done = oracle.append_token(bt, kn[0], vn[0])
+    assert list(done) == [False, False, True]
+    assert list(nb.seq_lens) == [64, 32, 8]
+    for b in (0, 1):
+        for h in range(2):
+            np.testing.assert_array_equal(token_major(nb, nb.k, b, h), token_major(bt, bt.k, b, h))
+    assert int((nb.k != bt.k).any(axis=-1).sum()) == 2
+
+
+@pytest.mark.parametrize("dtype,P,Pl", [("bf16", 64, 16), ("f32", 16, 16)])
+def test_append_meta_is_the_running_min_max(dtype, P, Pl):
+    """Metadata of the grown cache, by the per-channel identities of min and
+    max: in the new token's logical page, a token that opens it gives
+    kmin = kmax = token, any other gives kmin' = min(kmin, token) and
+    kmax' = max(kmax, token); every other logical page keeps its box.  The
+    appends walk across logical-page and page boundaries."""
+    bt = wl.random_batch(13, [1, Pl - 1, P - 1], n_q_heads=2, n_kv_heads=2, head_dim=16, page_size=P,
+                         logical_page=Pl, dtype=dtype, max_pages=3, spare_slots=6)
+    spare = free_slots(bt)
+    kn, vn = wl.append_stream(7, 3, 2, 16, Pl + 2, dtype)
+    for t in range(Pl + 2):
+        for b in range(3):
+            L = int(bt.seq_lens[b])
+            if L % P == 0 and bt.page_table[b][L // P] < 0:
+                bt.page_table[b][L // P] = spare.pop()
+        m0, h0 = oracle.page_meta(bt)
+        nb, done = oracle.append_token(bt, kn[t], vn[t])
+        assert done.all()
+        m1, h1 = oracle.page_meta(nb)
+        touched = set()
+        for b in range(3):
+            p = int(bt.seq_lens[b])
+            slot, s = int(bt.page_table[b][p // P]), (p % P) // Pl
+            touched.add((slot, s))
+            for h in range(2):
+                x = stored(kn[t, b, h], dtype)
+                assert h1[slot, h, s]
+                if p % Pl == 0:
+                    assert not h0[slot, h, s]
+                    np.testing.assert_array_equal(m1[slot, h, s, 0], x)
+                    np.testing.assert_array_equal(m1[slot, h, s, 1], x)
+                else:
+                    np.testing.assert_array_equal(m1[slot, h, s, 0], np.minimum(m0[slot, h, s, 0], x))
+                    np.testing.assert_array_equal(m1[slot, h, s, 1], np.maximum(m0[slot, h, s, 1], x))
+        for slot in range(bt.num_slots):
+            for s in range(P // Pl):
+                if (slot, s) not in touched:
+                    assert (h0[slot, :, s] == h1[slot, :, s]).all()
+                    np.testing.assert_array_equal(m0[slot, :, s][h0[slot, :, s]], m1[slot, :, s][h1[slot, :, s]])
+        bt = nb
+
+
 # ---------------------------------------------------------------- steps 2-4: scores
 def test_criticality_is_max_over_box_corners():
     """max_i-separable bound == maximum of q.x over the 2^D corners of the box

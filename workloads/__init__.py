@@ -32,7 +32,7 @@ import numpy as np
 __all__ = [
     "Batch", "to_bf16_bits", "from_bf16_bits",
     "tiny_heavy", "quest_gqa", "lserve_hier", "psa_mha", "prr_trace",
-    "random_batch", "WORKLOADS", "make",
+    "random_batch", "append_stream", "WORKLOADS", "make",
 ]
 
 
@@ -382,6 +382,15 @@ def random_batch(seed: int, seq_lens, n_q_heads: int = 4, n_kv_heads: int = 2, h
     return Batch("random", dtype, B, n_q_heads, n_kv_heads, head_dim, page_size,
                  logical_page or page_size, max_pages, q, k, v, pt, seq_lens, streaming=st,
                  sink=sink, local=local)
+
+
+def append_stream(seed: int, batch: int, n_kv_heads: int, head_dim: int, steps: int, dtype: str = "bf16"):
+    """K and V rows of `steps` newly generated tokens per sequence, N(0,1),
+    stored format: two arrays [steps][batch][n_kv_heads][head_dim]."""
+    rk, rv = (np.random.default_rng(s) for s in np.random.SeedSequence(seed).spawn(2))
+    shape = (steps, batch, n_kv_heads, head_dim)
+    return (_store(rk.standard_normal(shape, dtype=np.float32), dtype),
+            _store(rv.standard_normal(shape, dtype=np.float32), dtype))
 
 
 # Full-size workloads, by what they are.
