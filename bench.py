@@ -342,6 +342,23 @@ def main():
         step_bytes = mb + kvb
         op_bytes = {"page_score": mb, "sparse_decode_attn_topk": kvb + 4 * N * B * Hkv, "sparse_decode_attn": kvb}
 
+    # decode-time append, timed on its own (it precedes the step and is not
+    # part of it): each sequence's last token is written again at its own
+    # position (lengths one short, new lengths into a side buffer), which
+    # leaves the cache as it was
+    P_, Pl_ = bt.page_size, bt.logical_page
+    app_lens = torch.empty((B,), dtype=i32, device=dev)
+    app = []
+    for kv_r in kvs:
+        lens = kv_r.seq_lens.cpu().numpy()
+        pt = kv_r.page_table.cpu().numpy()
+        rows = [(int(pt[b, (int(L) - 1) // P_]), (int(L) - 1) % P_) for b, L in enumerate(lens)]
+        kn = torch.stack([kv_r.k[s, :, o] for s, o in rows]).contiguous()
+        vn = torch.stack([kv_r.v[s, :, o] for s, o in rows]).contiguous()
+        app.append((dsa.PagedKV(kv_r.k, kv_r.v, kv_r.page_table, (kv_r.seq_lens - 1).contiguous()), kn, vn))
+    ops["kv_append"] = lambda r: dsa.kv_append(app[r][0], app[r][1], app[r][2], meta, Pl_, new_seq_lens=app_lens)
+    op_bytes["kv_append"] = B * Hkv * 8 * D * _elem(bt)   # k/v rows in and out, kmin/kmax read and written
+
     def capture(fn, n, end=None):
         """A HIP graph of n calls fn(0..n-1) on the capture stream (no memset nodes)."""
         torch.cuda.synchronize()

@@ -18,7 +18,7 @@ import torch
 
 __all__ = [
     "DsaError", "PagedKV", "Streaming", "lib", "LIB_PATH",
-    "page_meta_build", "page_score", "page_select_topk", "page_select_progressive",
+    "page_meta_build", "kv_append", "page_score", "page_select_topk", "page_select_progressive",
     "sparse_decode_attn", "sparse_decode_attn_topk", "attn_repair", "ema_predict_update", "prr_select",
     "workspace_bytes",
     "OP_SPARSE_DECODE_ATTN", "OP_ATTN_REPAIR", "EXPORTED",
@@ -29,7 +29,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsa.so")
 DSA_F32, DSA_BF16 = 0, 1
 OP_SPARSE_DECODE_ATTN, OP_ATTN_REPAIR = 1, 2
 EXPORTED = (
-    "dsa_status_str", "dsa_version", "dsa_page_meta_build", "dsa_page_score", "dsa_page_select_topk",
+    "dsa_status_str", "dsa_version", "dsa_page_meta_build", "dsa_kv_append", "dsa_page_score", "dsa_page_select_topk",
     "dsa_page_select_progressive", "dsa_sparse_decode_attn", "dsa_sparse_decode_attn_topk", "dsa_attn_repair",
     "dsa_ema_predict_update", "dsa_prr_select", "dsa_workspace_bytes",
 )
@@ -65,6 +65,7 @@ def _load(path: str = LIB_PATH):
         "dsa_status_str": (ctypes.c_char_p, [ctypes.c_int]),
         "dsa_version": (ctypes.c_int, []),
         "dsa_page_meta_build": (ctypes.c_int, [KV, I32, P, I32, I32, P]),
+        "dsa_kv_append": (ctypes.c_int, [KV, I32, P, P, P, P, P, P]),
         "dsa_page_score": (ctypes.c_int, [P, I32, KV, P, I32, ST, P, P]),
         "dsa_page_select_topk": (ctypes.c_int, [P, I32, I32, I32, P, I32, I32, ST, P, P, P]),
         "dsa_page_select_progressive": (ctypes.c_int, [P, I32, KV, P, F32, I32, F32, P, P, P, P, P, P]),
@@ -215,6 +216,24 @@ def page_meta_build(kv: PagedKV, logical_page: int | None = None, meta: torch.Te
     _check("dsa_page_meta_build", lib.dsa_page_meta_build(ctypes.byref(kv.c()), lp, _ptr(meta), first_page,
                                                           n_pages, _stream()))
     return meta
+
+
+def kv_append(kv: PagedKV, k_new: torch.Tensor, v_new: torch.Tensor, meta: torch.Tensor,
+              logical_page: int | None = None, new_seq_lens: torch.Tensor | None = None,
+              status: torch.Tensor | None = None) -> torch.Tensor:
+    """One token per sequence: k_new/v_new [batch][n_kv_heads][head_dim] go to
+    position seq_lens[b], the page's kmin/kmax follow.  Returns the new
+    lengths (by default written over kv.seq_lens, in place)."""
+    lp = logical_page or kv.page_size
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        if t.dtype != kv.k.dtype or tuple(t.shape) != (kv.batch, kv.n_kv_heads, kv.head_dim) or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [batch][n_kv_heads][head_dim] tensor of the pool dtype")
+    if new_seq_lens is None:
+        new_seq_lens = kv.seq_lens
+    _check("dsa_kv_append", lib.dsa_kv_append(ctypes.byref(kv.c()), lp, _ptr(k_new), _ptr(v_new), _ptr(meta),
+                                              _ptr(new_seq_lens), _ptr(status),
+                                              _stream()))
+    return new_seq_lens
 
 
 def page_score(q: torch.Tensor, kv: PagedKV, meta: torch.Tensor, logical_page: int | None = None,

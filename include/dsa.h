@@ -4,6 +4,8 @@
  *
  * One decode step of dynamic sparse attention over a paged KV cache:
  *   page_meta_build        per-page key min/max metadata
+ *   kv_append              one new token per sequence into its page, with
+ *                          that page's min/max kept current
  *   page_score             page criticality against that metadata, with a
  *                          group-mean query and a logical->physical max
  *   page_select_topk       fixed top-k pages (ties to the lower index)
@@ -132,6 +134,37 @@ int dsa_version(void);
  */
 int dsa_page_meta_build(const dsa_kv *kv, int32_t logical_page, void *meta,
                         int32_t first_page, int32_t n_pages, void *stream);
+
+/*
+ * dsa_kv_append -- decode-time append of one token per sequence ([PSA]
+ * section 3.1: the KV cache manager writes each newly generated token's K/V
+ * into its block on the GPU and the block metadata stays in GPU memory;
+ * [LServe] section 4.2 and Figure 7: a physical page's kmin/kmax vectors
+ * come from the prefill and the earlier decoding steps).
+ *
+ * For every sequence b, with p = kv->seq_lens[b], page j = p / page_size,
+ * row o = p % page_size and slot = page_table[b][j]:
+ *   k[slot][h][o][:] = k_new[b][h][:] and v[slot][h][o][:] = v_new[b][h][:]
+ *   for every KV head h, and in the logical sub-page s = o / logical_page:
+ *     o % logical_page == 0:  meta[slot][h][s][0] = meta[slot][h][s][1] = k_new[b][h]
+ *     otherwise:              meta[slot][h][s][0] = min(meta[slot][h][s][0], k_new[b][h]),
+ *                             meta[slot][h][s][1] = max(meta[slot][h][s][1], k_new[b][h])
+ *   (per channel); new_seq_lens[b] = p + 1; status[b] = 1.
+ * The metadata before the call must describe the sub-page's earlier tokens
+ * (as dsa_page_meta_build or earlier appends wrote it); afterwards it equals
+ * dsa_page_meta_build of the grown page exactly.  A sequence whose page j is
+ * not below max_pages, or whose page-table entry lies outside
+ * [0, num_slots), is skipped: nothing is written for it, new_seq_lens[b] = p
+ * and status[b] = 0.  Giving a new page its slot is the caller's job.
+ * k_new, v_new: device [batch][n_kv_heads][head_dim] in kv->dtype, 16-byte
+ * aligned, not overlapping the pool.  meta: layout of dsa_page_meta_build
+ * with the same logical_page.  new_seq_lens: device int32 [batch]; it may be
+ * kv->seq_lens itself (each length is read before it is rewritten).
+ * status: device int32 [batch] or NULL.  This call writes through kv->k and
+ * kv->v.  NaN keys are not supported.
+ */
+int dsa_kv_append(const dsa_kv *kv, int32_t logical_page, const void *k_new, const void *v_new,
+                  void *meta, int32_t *new_seq_lens, int32_t *status, void *stream);
 
 /*
  * dsa_page_score -- page criticality ([LServe] section 4.2, importance of a

@@ -102,6 +102,13 @@ def test_validation_errors(dsa):
     assert L.dsa_page_select_progressive(ok_ptr, 4, ctypes.byref(_kv(dsa, max_pages=9000)), ok_ptr,
                                          ctypes.c_float(0.9), 0, ctypes.c_float(0.088), ok_ptr, ok_ptr, ok_ptr,
                                          ok_ptr, ok_ptr, None) == -4
+    # append: null new rows / lengths, misaligned rows or metadata, bad logical page
+    assert L.dsa_kv_append(ctypes.byref(kv), 16, None, ok_ptr, ok_ptr, ok_ptr, None, None) == -1
+    assert L.dsa_kv_append(ctypes.byref(kv), 16, ok_ptr, ok_ptr, ok_ptr, None, None, None) == -1
+    assert L.dsa_kv_append(ctypes.byref(kv), 16, P(4100), ok_ptr, ok_ptr, ok_ptr, None, None) == -6
+    assert L.dsa_kv_append(ctypes.byref(kv), 16, ok_ptr, ok_ptr, P(4100), ok_ptr, None, None) == -6
+    assert L.dsa_kv_append(ctypes.byref(kv), 32, ok_ptr, ok_ptr, ok_ptr, ok_ptr, None, None) == -2
+    assert L.dsa_kv_append(ctypes.byref(_kv(dsa, k=0)), 16, ok_ptr, ok_ptr, ok_ptr, ok_ptr, None, None) == -1
     # EMA: negative n, aliasing
     assert L.dsa_ema_predict_update(None, ok_ptr, P(8192), ok_ptr, 10, 0.6, 0.3, 0.25, 0, None) == -2
     assert L.dsa_ema_predict_update(None, ok_ptr, P(8192), P(12288), -1, 0.6, 0.3, 0.25, 0, None) == -2
@@ -113,6 +120,8 @@ def test_empty_inputs_are_noops(dsa):
     kv = _kv(dsa, batch=0, page_table=0, seq_lens=0)
     P = ctypes.c_void_p
     assert L.dsa_page_meta_build(ctypes.byref(kv), 16, None, 0, -1, None) == 0
+    assert L.dsa_kv_append(ctypes.byref(_kv(dsa, batch=0, page_table=0, seq_lens=0)), 16, None, None, None, None,
+                           None, None) == 0
     assert L.dsa_page_score(None, 4, ctypes.byref(kv), None, 16, None, None, None) == 0
     assert L.dsa_page_select_topk(None, 0, 2, 4, None, 16, 4, None, None, None, None) == 0
     assert L.dsa_ema_predict_update(None, None, None, None, 0, 0.6, 0.3, 0.25, 0, None) == 0
