@@ -441,6 +441,85 @@ def ema_update(is_true, level, trend, alpha: float, beta: float):
     return new_level, new_trend
 
 
+# --------------------------------------------------------------------------
+# online predictor calibration  (PRR section 3.2 of the page = the paper's
+# section 4.2: score-weighted hit rate H(theta; IS) over a prefill score
+# trace, maximised over the printed 4 x 5 x 4 grid)
+# --------------------------------------------------------------------------
+CALIB_ALPHAS = (0.2, 0.4, 0.6, 0.8)
+CALIB_BETAS = (0.1, 0.2, 0.3, 0.4, 0.5)
+CALIB_GAMMAS = (0.0, 0.25, 0.5, 0.75)
+
+
+def calibration_grid() -> list:
+    """The 80 candidates (alpha, beta, gamma), alpha slowest, gamma fastest."""
+    return [(a, b, g) for a in CALIB_ALPHAS for b in CALIB_BETAS for g in CALIB_GAMMAS]
+
+
+def ema_step_f32(is_true, level, trend, alpha: float, beta: float):
+    """ema_update in float32 with every product and sum rounded on its own,
+    in the order trend' = beta*(IS - level) + (1-beta)*trend, level' =
+    alpha*IS + (1-alpha)*level.  The calibration ranks pages by the
+    prediction, so the reference takes that decision in the precision and
+    rounding of the kernel (float32, no fused multiply-add)."""
+    f = np.float32
+    is_true, level, trend = (np.asarray(x, f) for x in (is_true, level, trend))
+    a, b = f(alpha), f(beta)
+    new_trend = b * (is_true - level) + (f(1) - b) * trend
+    new_level = a * is_true + (f(1) - a) * level
+    return new_level, new_trend
+
+
+def ema_predict_f32(level, trend, gamma: float):
+    """ema_predict in float32: level + (gamma * trend), each rounded."""
+    f = np.float32
+    return np.asarray(level, f) + f(gamma) * np.asarray(trend, f)
+
+
+def hit_rate(pred_row, is_row, n_valid: int, k: int, m: int) -> float:
+    """One term of H: the IS-weighted share of A = top-k(IS) covered by
+    P = top-m(prediction), over the n_valid valid pages.  An empty A (or one
+    of zero total weight) leaves nothing to miss: 1."""
+    A = topk_pages(np.asarray(is_row, float), n_valid, k)
+    P = topk_pages(np.asarray(pred_row, float), n_valid, m)
+    w = np.asarray(is_row, float)
+    den = float(w[A].sum())
+    if len(A) == 0 or den == 0.0:
+        return 1.0
+    return float(w[np.intersect1d(P, A)].sum()) / den
+
+
+def calibrate(trace, n_valid, k: int, m: int, candidates=None) -> np.ndarray:
+    """H[u][c] for trace[T][units][N] (float32 scores of T consecutive steps).
+
+    Per unit and candidate the EMA starts at level = IS_0, trend = 0; every
+    later step phi is first predicted from the state so far, scored as
+    hit_rate(pred_phi, IS_phi), then absorbed into the state.  H is the mean
+    over the T - 1 predicted steps.  `candidates` (indices into
+    calibration_grid()) restricts the columns computed; the rest are NaN."""
+    trace = np.asarray(trace, np.float32)
+    T, U, N = trace.shape
+    grid = calibration_grid()
+    cols = range(len(grid)) if candidates is None else candidates
+    H = np.full((U, len(grid)), np.nan)
+    for u in range(U):
+        nv = int(n_valid[u])
+        for c in cols:
+            alpha, beta, gamma = grid[c]
+            level, trend = trace[0, u].copy(), np.zeros(N, np.float32)
+            acc = 0.0
+            for phi in range(1, T):
+                acc += hit_rate(ema_predict_f32(level, trend, gamma), trace[phi, u], nv, k, m)
+                level, trend = ema_step_f32(trace[phi, u], level, trend, alpha, beta)
+            H[u, c] = acc / (T - 1)
+    return H
+
+
+def best_candidate(H_row) -> int:
+    """argmax over the candidates, the lowest index among equal maxima."""
+    return int(np.argmax(np.asarray(H_row, float)))
+
+
 def speculative_set(pred_row: np.ndarray, n_valid: int, a_size: int, delta: float) -> np.ndarray:
     """P = the floor(delta*|A|) pages with the highest prediction, ascending
     (PRR section 3.4: |P| is bounded by delta*|A|)."""

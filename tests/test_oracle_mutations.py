@@ -35,6 +35,13 @@ MUTATIONS = [
     ("out.v[slot, :, p % P] = v_new[b]", "out.v[slot, :, p % P] = k_new[b]"),
     ("if p < 0 or j >= batch.max_pages:", "if p < 0 or j > batch.max_pages:"),
     ("out.seq_lens[b] = p + 1", "out.seq_lens[b] = p + 1 if p % P else p"),
+    ("H[u, c] = acc / (T - 1)", "H[u, c] = acc / T"),
+    ("for phi in range(1, T):\n                acc", "for phi in range(2, T):\n                acc"),
+    ("return float(w[np.intersect1d(P, A)].sum()) / den", "return float(w[np.union1d(P, A)].sum()) / den"),
+    ("new_trend = b * (is_true - level) + (f(1) - b) * trend", "new_trend = b * (is_true - level) + (f(1) - a) * trend"),
+    ("return np.asarray(level, f) + f(gamma) * np.asarray(trend, f)", "return np.asarray(level, f) + np.asarray(trend, f)"),
+    ("A = topk_pages(np.asarray(is_row, float), n_valid, k)\n    P = topk_pages(np.asarray(pred_row, float), n_valid, m)",
+     "A = topk_pages(np.asarray(is_row, float), n_valid, k)\n    P = topk_pages(np.asarray(pred_row, float), n_valid, k)"),
 ]
 
 

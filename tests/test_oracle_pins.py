@@ -509,11 +509,111 @@ def test_speculative_set_size():
 
 def test_calibration_grid_has_80_candidates():
     """PRR section 3.2 grid: alpha 0.2..0.8 step 0.2, beta 0.1..0.5 step 0.1,
-    gamma 0..0.75 step 0.25 -> the page states 80 candidates."""
+    gamma 0..0.75 step 0.25 -> the page states 80 candidates; the oracle's
+    grid is exactly that product, alpha slowest and gamma fastest."""
     alphas = np.arange(0.2, 0.8 + 1e-9, 0.2)
     betas = np.arange(0.1, 0.5 + 1e-9, 0.1)
     gammas = np.arange(0.0, 0.75 + 1e-9, 0.25)
     assert len(alphas) * len(betas) * len(gammas) == 80
+    grid = oracle.calibration_grid()
+    assert len(grid) == 80 and len(set(grid)) == 80
+    for ia, a in enumerate(alphas):
+        for ib, b in enumerate(betas):
+            for ig, g in enumerate(gammas):
+                assert grid[(ia * 5 + ib) * 4 + ig] == pytest.approx((a, b, g), abs=1e-12)
+
+
+# ---------------------------------------------------------------- calibration (PRR section 3.2)
+def test_f32_ema_is_the_ema():
+    """The float32 predictor of the calibration agrees with the pinned fp64
+    update and prediction to float32 rounding, on random states and on the
+    hand step (level 2, trend 1, IS 5 -> 3.8, 1.6, prediction 4.2)."""
+    rng = np.random.default_rng(21)
+    is_, lv, tr = (rng.standard_normal(1000).astype(np.float32) * 10 for _ in range(3))
+    for a, b, g in oracle.calibration_grid()[::7]:
+        l32, t32 = oracle.ema_step_f32(is_, lv, tr, a, b)
+        l64, t64 = oracle.ema_update(is_, lv, tr, a, b)
+        assert np.allclose(l32, l64, rtol=0, atol=1e-5 * 30) and np.allclose(t32, t64, rtol=0, atol=1e-5 * 30)
+        p32 = oracle.ema_predict_f32(l32, t32, g)
+        assert np.allclose(p32, oracle.ema_predict(l64, t64, g), rtol=0, atol=1e-4)
+        assert l32.dtype == np.float32 and p32.dtype == np.float32
+    l, t_ = oracle.ema_step_f32([5.0], [2.0], [1.0], 0.6, 0.3)
+    assert l[0] == pytest.approx(3.8, rel=1e-6) and t_[0] == pytest.approx(1.6, rel=1e-6)
+    assert oracle.ema_predict_f32(l, t_, 0.25)[0] == pytest.approx(4.2, rel=1e-6)
+
+
+def test_hit_rate_hand_built():
+    """IS = [5, 1, 4, 3, 2], k = 2: A = {0, 2}, weight 9.  A prediction that
+    ranks pages 0 and 1 highest covers 5 of it; all five pages cover it all;
+    no page covers nothing; an empty A has nothing to miss."""
+    is_ = np.array([5.0, 1.0, 4.0, 3.0, 2.0])
+    pred = np.array([9.0, 8.0, 0.0, 1.0, 2.0])
+    assert oracle.hit_rate(pred, is_, 5, 2, 2) == pytest.approx(5 / 9)
+    assert oracle.hit_rate(pred, is_, 5, 2, 5) == 1.0
+    assert oracle.hit_rate(pred, is_, 5, 2, 0) == 0.0
+    assert oracle.hit_rate(pred, is_, 5, 0, 2) == 1.0
+    assert oracle.hit_rate(pred, is_, 3, 2, 1) == pytest.approx(5 / 9)   # pages 0..2 valid: A = {0, 2}, P = {0}
+
+
+def _ramp_trace(T=12, N=40, U=2, seed=22):
+    """Pages on straight lines that cross: base ~ U(0, 50), slope ~ U(0, 6)."""
+    rng = np.random.default_rng(seed)
+    base = rng.uniform(0, 50, (U, N))
+    slope = rng.uniform(0, 6, (U, N))
+    return np.stack([base + slope * phi for phi in range(T)]).astype(np.float32)
+
+
+def test_calibrate_bounds_and_degenerate_budgets():
+    """0 <= H <= 1; a constant trace is predicted exactly (H = 1 for every
+    candidate); P over all valid pages covers A (H = 1); an empty P covers
+    nothing (H = 0)."""
+    tr = _ramp_trace()
+    nv = [40, 33]
+    H = oracle.calibrate(tr, nv, 8, 8)
+    assert np.all((H >= 0) & (H <= 1)) and not np.all(H == 1)
+    const = np.repeat(tr[:1], 6, axis=0)
+    assert np.all(oracle.calibrate(const, nv, 8, 8) == 1.0)
+    assert np.all(oracle.calibrate(tr[:5], nv, 8, 40) == 1.0)
+    assert np.all(oracle.calibrate(tr[:5], nv, 8, 0) == 0.0)
+
+
+def test_calibrate_prefers_fast_extrapolation_on_ramps():
+    """On crossing straight lines the EMA lags each page by about
+    slope * (1 - gamma) / alpha (the linear-series closed form), so rising
+    pages are under-ranked: the highest alpha and gamma of the grid win, and
+    more extrapolation never hurts at fixed (alpha, beta)."""
+    tr = _ramp_trace(T=16, N=60, U=1, seed=23)
+    H = oracle.calibrate(tr, [60], 10, 10)[0]
+    grid = oracle.calibration_grid()
+    a, _, g = grid[oracle.best_candidate(H)]
+    assert a == 0.8 and g == 0.75
+    assert H[0] < H[oracle.best_candidate(H)]
+    for c in range(0, 80, 4):   # gamma = 0, 0.25, 0.5, 0.75 at one (alpha, beta)
+        assert H[c] <= H[c + 1] <= H[c + 2] <= H[c + 3]
+
+
+def test_calibrate_matches_a_direct_loop():
+    """On a trace whose scores are spaced widely enough that float32 and
+    float64 rank alike, H of a few candidates equals a direct loop over the
+    fp64 EMA, top-k selections and the weighted hit share."""
+    rng = np.random.default_rng(24)
+    T, U, N, k, m = 7, 2, 30, 6, 5
+    tr = (rng.permutation(np.arange(T * U * N)).reshape(T, U, N) * 8.0 + 64.0).astype(np.float32)
+    grid = oracle.calibration_grid()
+    cols = [0, 17, 42, 79]
+    H = oracle.calibrate(tr, [N, N - 4], k, m, candidates=cols)
+    for u, nv in enumerate([N, N - 4]):
+        for c in cols:
+            a, b, g = grid[c]
+            level, trend, total = tr[0, u].astype(float), np.zeros(N), 0.0
+            for phi in range(1, T):
+                pred = oracle.ema_predict(level, trend, g)
+                is_ = tr[phi, u].astype(float)
+                A = set(np.argsort(-is_[:nv], kind="stable")[:k].tolist())
+                P = set(np.argsort(-pred[:nv], kind="stable")[:m].tolist())
+                total += sum(is_[j] for j in A & P) / sum(is_[j] for j in A)
+                level, trend = oracle.ema_update(is_, level, trend, a, b)
+            assert H[u, c] == pytest.approx(total / (T - 1), rel=1e-12)
 
 
 # ---------------------------------------------------------------- workload checks
