@@ -19,7 +19,7 @@ import torch
 __all__ = [
     "DsaError", "PagedKV", "Streaming", "lib", "LIB_PATH",
     "page_meta_build", "kv_append", "page_score", "page_select_topk", "page_select_progressive",
-    "sparse_decode_attn", "sparse_decode_attn_topk", "attn_repair", "ema_predict_update", "prr_select",
+    "sparse_decode_attn", "sparse_decode_attn_topk", "attn_repair", "ema_predict_update", "prr_select", "prr_calibrate",
     "workspace_bytes",
     "OP_SPARSE_DECODE_ATTN", "OP_ATTN_REPAIR", "EXPORTED",
 ]
@@ -31,7 +31,8 @@ OP_SPARSE_DECODE_ATTN, OP_ATTN_REPAIR = 1, 2
 EXPORTED = (
     "dsa_status_str", "dsa_version", "dsa_page_meta_build", "dsa_kv_append", "dsa_page_score", "dsa_page_select_topk",
     "dsa_page_select_progressive", "dsa_sparse_decode_attn", "dsa_sparse_decode_attn_topk", "dsa_attn_repair",
-    "dsa_ema_predict_update", "dsa_prr_select", "dsa_workspace_bytes",
+    "dsa_ema_predict_update", "dsa_prr_select", "dsa_prr_calibrate", "dsa_prr_calibrate_workspace_bytes",
+    "dsa_workspace_bytes",
 )
 
 
@@ -74,6 +75,8 @@ def _load(path: str = LIB_PATH):
         "dsa_attn_repair": (ctypes.c_int, [P, I32, KV, P, P, P, P, I32, F32, P, P, P, P, SZ, P]),
         "dsa_ema_predict_update": (ctypes.c_int, [P, P, P, P, I64, F32, F32, F32, I32, P]),
         "dsa_prr_select": (ctypes.c_int, [P, I32, I32, I32, P, I32, I32, P, P, P, P, P, F32, F32, F32, I32, I32, P, P, P]),
+        "dsa_prr_calibrate": (ctypes.c_int, [P, I32, I32, I32, P, I32, I32, P, P, P, SZ, P]),
+        "dsa_prr_calibrate_workspace_bytes": (SZ, [I32, I32, I32]),
         "dsa_workspace_bytes": (SZ, [I32, KV, I32, I32]),
     }
     for name, (res, args) in sig.items():
@@ -368,3 +371,26 @@ def prr_select(scores: torch.Tensor, seq_lens: torch.Tensor, page_size: int, k: 
         _ptr(pred), float(alpha), float(beta), float(gamma), 1 if init else 0, k_spec, _ptr(p_ids), _ptr(p_counts),
         _stream()))
     return a_ids, a_counts, p_ids, p_counts
+
+
+CALIB_CANDIDATES = 80
+
+
+def prr_calibrate(trace: torch.Tensor, n_valid: torch.Tensor, k: int, m: int, H: torch.Tensor | None = None,
+                  best: torch.Tensor | None = None, ws: torch.Tensor | None = None):
+    """PRR's EMA calibration over a score trace [steps][units][n] (float32):
+    (H [units][80], best [units]); candidate c = (ia*5 + ib)*4 + ig."""
+    if trace.dtype != torch.float32 or trace.dim() != 3 or not trace.is_contiguous():
+        raise ValueError("trace must be a contiguous float32 [steps][units][n] tensor")
+    T, U, N = trace.shape
+    dev = trace.device
+    if H is None:
+        H = torch.empty((U, CALIB_CANDIDATES), dtype=torch.float32, device=dev)
+    if best is None:
+        best = torch.empty((U,), dtype=torch.int32, device=dev)
+    need = int(lib.dsa_prr_calibrate_workspace_bytes(T, U, N))
+    if ws is None:
+        ws = _workspace(need, dev)
+    _check("dsa_prr_calibrate", lib.dsa_prr_calibrate(_ptr(trace), T, U, N, _ptr(n_valid), k, m, _ptr(H), _ptr(best),
+                                                      _ptr(ws), ws.numel() * ws.element_size(), _stream()))
+    return H, best

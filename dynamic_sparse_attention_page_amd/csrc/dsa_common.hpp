@@ -228,13 +228,24 @@ __device__ __forceinline__ float lane_dot(const uint32_t* k, const uint32_t* q) 
 
 // One EMA step of PRR's predictor ("Predict, Reuse, and Repair", section
 // 3.1): trend and level both read the previous level; the prediction
-// extrapolates the new level by gamma times the new trend.
-// Written with explicit fmaf so every kernel rounds it the same way.
+// extrapolates the new level by gamma times the new trend.  Every product
+// and sum is rounded to fp32 on its own (no fused multiply-add), in this
+// order, so that any kernel -- and a float32 reference -- rounds the
+// predictor the same way:
+//   trend' = beta*(IS - level) + (1 - beta)*trend
+//   level' = alpha*IS + (1 - alpha)*level
+//   pred   = level' + gamma*trend'
+__device__ __forceinline__ float ema_predict(float lv, float tr, float gamma) {
+#pragma clang fp contract(off)
+  return lv + gamma * tr;
+}
+
 __device__ __forceinline__ void ema_step(float is, float lv, float tr, float alpha, float beta, float gamma,
                                          float& nl, float& nt, float& pr) {
-  nt = fmaf(beta, is - lv, (1.0f - beta) * tr);
-  nl = fmaf(alpha, is, (1.0f - alpha) * lv);
-  pr = fmaf(gamma, nt, nl);
+#pragma clang fp contract(off)
+  nt = beta * (is - lv) + (1.0f - beta) * tr;
+  nl = alpha * is + (1.0f - alpha) * lv;
+  pr = ema_predict(nl, nt, gamma);
 }
 
 __device__ __forceinline__ int clamp_len(int L, int max_pages, int P) {

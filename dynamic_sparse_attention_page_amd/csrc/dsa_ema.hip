@@ -11,7 +11,7 @@ namespace dsa {
 __device__ __forceinline__ void ema_one(const float* is_true, float* level, float* trend, float* pred, long long x,
                                         float alpha, float beta, float gamma, int init) {
   if (!is_true) {
-    pred[x] = fmaf(gamma, trend[x], level[x]);
+    pred[x] = ema_predict(level[x], trend[x], gamma);
     return;
   }
   const float is = is_true[x];
@@ -40,8 +40,8 @@ __global__ __launch_bounds__(256) void ema_kernel(const float* __restrict__ is_t
       float4 tr = reinterpret_cast<float4*>(trend)[x];
       float4 pr;
       if (!is_true) {
-        pr = make_float4(fmaf(gamma, tr.x, lv.x), fmaf(gamma, tr.y, lv.y), fmaf(gamma, tr.z, lv.z),
-                         fmaf(gamma, tr.w, lv.w));
+        pr = make_float4(ema_predict(lv.x, tr.x, gamma), ema_predict(lv.y, tr.y, gamma),
+                         ema_predict(lv.z, tr.z, gamma), ema_predict(lv.w, tr.w, gamma));
       } else {
         const float4 is = reinterpret_cast<const float4*>(is_true)[x];
         if (init) {

@@ -16,6 +16,8 @@
  *   attn_repair            folds the pages of A that the speculative set P
  *                          missed into a speculative (O, l, m)
  *   ema_predict_update     PRR's EMA page-score predictor
+ *   prr_calibrate          PRR's search of the EMA hyper-parameters over a
+ *                          score trace
  *
  * Sources, cited by page title and section:
  *   [PSA]    "PSA: Progressive Sparse Attention -- Algorithm and System
@@ -303,7 +305,9 @@ int dsa_attn_repair(const void *q, int32_t n_q_heads, const dsa_kv *kv, const in
  *   otherwise:        trend' = beta*(IS - level) + (1-beta)*trend,
  *                     level' = alpha*IS + (1-alpha)*level   (both read the old level),
  *                     pred = level' + gamma * trend'        (the next step's prediction)
- * level and trend are updated in place; pred may not alias them.
+ * level and trend are updated in place; pred may not alias them.  Every
+ * product and sum is rounded to fp32 on its own, in the order written (no
+ * fused multiply-add), so a float32 reference reproduces it bit for bit.
  */
 int dsa_ema_predict_update(const float *is_true, float *level, float *trend, float *pred,
                            int64_t n, float alpha, float beta, float gamma, int32_t init,
@@ -331,6 +335,41 @@ int dsa_prr_select(const float *scores, int32_t batch, int32_t n_kv_heads, int32
                    int32_t *a_counts, float *level, float *trend, float *pred, float alpha,
                    float beta, float gamma, int32_t init, int32_t k_spec, int32_t *p_ids,
                    int32_t *p_counts, void *stream);
+
+/*
+ * dsa_prr_calibrate -- PRR online predictor calibration ([PRR] section 3.2:
+ * the EMA hyper-parameters are chosen per prompt by the score-weighted hit
+ * rate H(theta; IS) over a prefill score trace, maximised over the printed
+ * grid alpha in {0.2, 0.4, 0.6, 0.8}, beta in {0.1, 0.2, 0.3, 0.4, 0.5},
+ * gamma in {0, 0.25, 0.5, 0.75}: 80 candidates).
+ *
+ * trace: device float [steps][units][n], the scores IS_phi of `steps`
+ * consecutive steps of each unit (for instance one (sequence, KV head) row
+ * of dsa_page_score per step); the pages j < n_valid[u] of unit u are valid
+ * (n_valid: device int32 [units], clamped to [0, n]).  Candidate
+ * c = (ia*5 + ib)*4 + ig has alpha = {0.2, 0.4, 0.6, 0.8}[ia],
+ * beta = {0.1, ..., 0.5}[ib], gamma = 0.25*ig (as float).  Per unit and
+ * candidate the EMA starts at level = IS_0, trend = 0, and every step
+ * phi = 1 .. steps-1 is
+ *   predicted:  pred = level + gamma*trend (rounded as dsa_ema_predict_update),
+ *   scored:     h_phi = sum_{b in P & A} IS_phi,b / sum_{b in A} IS_phi,b with
+ *               A = top-k(IS_phi), P = top-m(pred) over the valid pages
+ *               (ties to the lower index; h_phi = 1 when A is empty or
+ *               weighs 0),
+ *   absorbed:   trend and level updated with IS_phi as in dsa_ema_predict_update.
+ * H[u][c] = mean of h_phi over the steps - 1 predicted steps (device float
+ * [units][80]); best[u] = the c of the largest H[u][c], the lowest c among
+ * equal values (device int32 [units]; may be NULL).
+ * ws: device scratch of dsa_prr_calibrate_workspace_bytes(steps, units, n)
+ * bytes.  Requires steps >= 2, 1 <= n <= 65536, k >= 0, m >= 0.  NaN scores
+ * are not supported.
+ */
+int dsa_prr_calibrate(const float *trace, int32_t steps, int32_t units, int32_t n,
+                      const int32_t *n_valid, int32_t k, int32_t m, float *H, int32_t *best,
+                      void *ws, size_t ws_bytes, void *stream);
+
+/* Scratch bytes dsa_prr_calibrate needs (0 for invalid sizes). */
+size_t dsa_prr_calibrate_workspace_bytes(int32_t steps, int32_t units, int32_t n);
 
 /*
  * dsa_workspace_bytes -- scratch needed by dsa_sparse_decode_attn (op

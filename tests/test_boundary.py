@@ -109,6 +109,17 @@ def test_validation_errors(dsa):
     assert L.dsa_kv_append(ctypes.byref(kv), 16, ok_ptr, ok_ptr, P(4100), ok_ptr, None, None) == -6
     assert L.dsa_kv_append(ctypes.byref(kv), 32, ok_ptr, ok_ptr, ok_ptr, ok_ptr, None, None) == -2
     assert L.dsa_kv_append(ctypes.byref(_kv(dsa, k=0)), 16, ok_ptr, ok_ptr, ok_ptr, ok_ptr, None, None) == -1
+    # calibration: too few steps, too many pages, null outputs, small workspace
+    wsz = L.dsa_prr_calibrate_workspace_bytes(4, 2, 1000)
+    assert wsz > 0 and L.dsa_prr_calibrate_workspace_bytes(1, 2, 1000) == 0
+    assert L.dsa_prr_calibrate_workspace_bytes(4, 2, 70000) == 0
+    assert L.dsa_prr_calibrate(ok_ptr, 1, 2, 1000, ok_ptr, 8, 8, ok_ptr, None, ok_ptr, wsz, None) == -2
+    assert L.dsa_prr_calibrate(ok_ptr, 4, 2, 70000, ok_ptr, 8, 8, ok_ptr, None, ok_ptr, wsz, None) == -4
+    assert L.dsa_prr_calibrate(ok_ptr, 4, 2, 1000, ok_ptr, -1, 8, ok_ptr, None, ok_ptr, wsz, None) == -2
+    assert L.dsa_prr_calibrate(ok_ptr, 4, 2, 1000, None, 8, 8, ok_ptr, None, ok_ptr, wsz, None) == -1
+    assert L.dsa_prr_calibrate(ok_ptr, 4, 2, 1000, ok_ptr, 8, 8, None, None, ok_ptr, wsz, None) == -1
+    assert L.dsa_prr_calibrate(ok_ptr, 4, 2, 1000, ok_ptr, 8, 8, ok_ptr, None, ok_ptr, wsz - 1, None) == -5
+    assert L.dsa_prr_calibrate(None, 4, 0, 1000, None, 8, 8, None, None, None, 0, None) == 0
     # EMA: negative n, aliasing
     assert L.dsa_ema_predict_update(None, ok_ptr, P(8192), ok_ptr, 10, 0.6, 0.3, 0.25, 0, None) == -2
     assert L.dsa_ema_predict_update(None, ok_ptr, P(8192), P(12288), -1, 0.6, 0.3, 0.25, 0, None) == -2

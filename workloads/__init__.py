@@ -32,7 +32,7 @@ import numpy as np
 __all__ = [
     "Batch", "to_bf16_bits", "from_bf16_bits",
     "tiny_heavy", "quest_gqa", "lserve_hier", "psa_mha", "prr_trace",
-    "random_batch", "append_stream", "WORKLOADS", "make",
+    "random_batch", "append_stream", "score_trace", "WORKLOADS", "make",
 ]
 
 
@@ -391,6 +391,23 @@ def append_stream(seed: int, batch: int, n_kv_heads: int, head_dim: int, steps: 
     shape = (steps, batch, n_kv_heads, head_dim)
     return (_store(rk.standard_normal(shape, dtype=np.float32), dtype),
             _store(rv.standard_normal(shape, dtype=np.float32), dtype))
+
+
+def score_trace(seed: int, steps: int, units: int, n: int, mean: float = 100.0, spread: float = 3.0,
+                drift: float = 0.5, noise: float = 0.3, ties: bool = False) -> np.ndarray:
+    """Page-score trace [steps][units][n] (float32) standing in for the
+    scores of consecutive prefill steps: every page has a base level
+    N(mean, spread), a constant drift N(0, drift) per step and fresh N(0,
+    noise) noise at every step.  ``ties`` rounds the scores to integers,
+    which makes equal scores common."""
+    rb, rd, rn = (np.random.default_rng(s) for s in np.random.SeedSequence(seed).spawn(3))
+    base = rb.normal(mean, spread, (units, n))
+    vel = rd.normal(0.0, drift, (units, n))
+    phi = np.arange(steps, dtype=np.float64)[:, None, None]
+    tr = base[None] + vel[None] * phi + rn.normal(0.0, noise, (steps, units, n))
+    if ties:
+        tr = np.round(tr)
+    return tr.astype(np.float32)
 
 
 # Full-size workloads, by what they are.
