@@ -534,3 +534,27 @@ def quest_step(batch, k: int, q=None):
     scores = page_scores(batch, q=q)
     ids = select_topk(batch, scores, k)
     return scores, ids, sparse_decode(batch, ids, q)
+
+
+# --------------------------------------------------------------------------
+# reusable page selector  (LServe section 4.3: the selector runs only at the
+# start of each chunk of C consecutive decode tokens -- 4 by default -- and
+# the chunk's later tokens reuse the first token's pages)
+# --------------------------------------------------------------------------
+def chunk_start(t: int, chunk: int) -> int:
+    """The decode step whose selection step t uses."""
+    return (t // chunk) * chunk
+
+
+def reuse_decode(batch, q_trace, k: int, chunk: int):
+    """For each step t of q_trace [T][B][Hq][D] (stored format): the pages
+    selected for the query of step chunk_start(t), and the attention of step
+    t's own query over them.  Returns ([ids per step], [(O, l, m) per step])."""
+    ids_of, out_ids, outs = {}, [], []
+    for t in range(len(q_trace)):
+        s = chunk_start(t, chunk)
+        if s not in ids_of:
+            ids_of[s] = select_topk(batch, page_scores(batch, q=q_trace[s]), k)
+        out_ids.append(ids_of[s])
+        outs.append(sparse_decode(batch, ids_of[s], q_trace[t]))
+    return out_ids, outs

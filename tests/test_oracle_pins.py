@@ -617,6 +617,48 @@ def test_calibrate_matches_a_direct_loop():
 
 
 # ---------------------------------------------------------------- workload checks
+# ---------------------------------------------------------------- reusable selector (LServe section 4.3)
+def test_reuse_chunk_starts():
+    """Chunk size 4: steps 0-3 use step 0's selection, 4-7 step 4's, ...;
+    chunk size 1 selects at every step."""
+    assert [oracle.chunk_start(t, 4) for t in range(10)] == [0, 0, 0, 0, 4, 4, 4, 4, 8, 8]
+    assert [oracle.chunk_start(t, 1) for t in range(5)] == [0, 1, 2, 3, 4]
+
+
+def test_reuse_decode_against_fresh_selection():
+    """Chunk 1 is the plain per-step pipeline; with chunk 4 every step uses
+    the pages of its chunk's first query and attends with its own query, and
+    a query that repeats within a chunk reproduces the fresh step exactly."""
+    bt = wl.random_batch(31, [200, 77], n_q_heads=4, n_kv_heads=2, head_dim=16, page_size=16)
+    qs = wl.query_drift(32, bt.q, 6, 0.3, bt.dtype)
+    ids1, out1 = oracle.reuse_decode(bt, qs, 3, 1)
+    ids4, out4 = oracle.reuse_decode(bt, qs, 3, 4)
+    for t in range(6):
+        _, ref_ids, ref = oracle.quest_step(bt, 3, q=qs[t])
+        assert all(np.array_equal(a, b) for ra, rb in zip(ids1[t], ref_ids) for a, b in zip(ra, rb))
+        for x, y in zip(out1[t], ref):
+            np.testing.assert_array_equal(x, y)
+        s = oracle.chunk_start(t, 4)
+        _, start_ids, _ = oracle.quest_step(bt, 3, q=qs[s])
+        assert all(np.array_equal(a, b) for ra, rb in zip(ids4[t], start_ids) for a, b in zip(ra, rb))
+        for x, y in zip(out4[t], oracle.sparse_decode(bt, start_ids, qs[t])):
+            np.testing.assert_array_equal(x, y)
+    same = np.stack([qs[0]] * 3)
+    _, o_same = oracle.reuse_decode(bt, same, 3, 4)
+    for x, y in zip(o_same[2], oracle.quest_step(bt, 3, q=qs[0])[2]):
+        np.testing.assert_array_equal(x, y)
+
+
+def test_query_drift_keeps_the_norm_scale():
+    """theta = 0 repeats q0; a drifting step is a rotation-like mix whose
+    cosine with the previous query is about cos(theta) for wide heads."""
+    bt = wl.random_batch(33, [40], n_q_heads=2, n_kv_heads=1, head_dim=128, page_size=16, dtype="f32")
+    assert np.array_equal(wl.query_drift(1, bt.q, 3, 0.0, "f32")[2], bt.q)
+    qs = wl.query_drift(2, bt.q, 2, 0.3, "f32").astype(np.float64)
+    c = (qs[0] * qs[1]).sum(-1) / np.linalg.norm(qs[0], axis=-1) / np.linalg.norm(qs[1], axis=-1)
+    assert np.all(np.abs(c - math.cos(0.3)) < 0.1)
+
+
 def test_quest_bias_pages_have_cosine_0_4_and_rank_high():
     bt = wl.quest_gqa(seq_len=4096, n_kv_heads=2, n_q_heads=8)
     qbar = oracle.group_query(bt)

@@ -32,7 +32,7 @@ import numpy as np
 __all__ = [
     "Batch", "to_bf16_bits", "from_bf16_bits",
     "tiny_heavy", "quest_gqa", "lserve_hier", "psa_mha", "prr_trace",
-    "random_batch", "append_stream", "score_trace", "WORKLOADS", "make",
+    "random_batch", "append_stream", "score_trace", "query_drift", "WORKLOADS", "make",
 ]
 
 
@@ -408,6 +408,20 @@ def score_trace(seed: int, steps: int, units: int, n: int, mean: float = 100.0, 
     if ties:
         tr = np.round(tr)
     return tr.astype(np.float32)
+
+
+def query_drift(seed: int, q0: np.ndarray, steps: int, theta: float, dtype: str = "bf16") -> np.ndarray:
+    """Queries of `steps` consecutive decode tokens starting from q0 (stored
+    format [B][Hq][D]): q_t = cos(theta) q_{t-1} + sin(theta) xi_t with xi_t
+    ~ N(0, I), the recursion in float64, each step stored rounded.  Returns
+    [steps][B][Hq][D]; step 0 is q0 itself."""
+    rng = np.random.default_rng(seed)
+    cur = _stored_as_f64(q0, dtype)
+    out = [np.array(q0, copy=True)]
+    for _ in range(1, steps):
+        cur = math.cos(theta) * cur + math.sin(theta) * rng.standard_normal(cur.shape)
+        out.append(_store(cur.astype(np.float32), dtype))
+    return np.stack(out)
 
 
 # Full-size workloads, by what they are.
