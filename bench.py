@@ -50,6 +50,7 @@ METRIC = "sparse decode attn+select: queries/sec and achieved HBM GB/s (% of pea
 # dominant call of the step only
 SIDE_OPS = {"kv_append", "prr_calibrate"}
 T_CAL = 32   # steps of the score trace the PRR calibration searches over
+REUSE_CHUNK = 4   # LServe's default selector-reuse interval
 WORKLOADS = ["quest_gqa_32k", "lserve_hier_128k", "psa_mha_64k", "prr_512k", "tiny_f32"]
 
 
@@ -186,6 +187,32 @@ def cpu_baseline(bt, budget_s):
 # --------------------------------------------------------------------------
 # GPU timing
 # --------------------------------------------------------------------------
+def reuse_coverage(dsa, torch, wl, bt, kv, meta, st, q, steps=8, theta=0.1):
+    """Share of a fresh top-k that the reused pages cover, on a drifting
+    query trace (angle theta per step), averaged over the steps that reuse;
+    dense heads only."""
+    qs = wl.query_drift(91, bt.q, steps, theta, bt.dtype)
+    from dynamic_sparse_attention_page_amd.reuse import ChunkedReuseDecoder
+    dec = ChunkedReuseDecoder(kv, meta, bt.n_q_heads, bt.topk, chunk=REUSE_CHUNK, logical_page=bt.logical_page,
+                              streaming=st)
+    cov = []
+    for t in range(steps):
+        qt = dsa.upload_q(qs[t], bt.dtype)
+        dec.step(qt)
+        sc = dsa.page_score(qt, kv, meta, bt.logical_page, streaming=st)
+        ids_f, cnt_f = dsa.page_select_topk(sc, kv.seq_lens, bt.page_size, bt.topk, streaming=st)
+        if t % REUSE_CHUNK == 0:
+            continue
+        a, ca, r, cr = (x.cpu().numpy() for x in (ids_f, cnt_f, dec.ids, dec.counts))
+        for b in range(bt.batch):
+            for h in range(bt.n_kv_heads):
+                if bt.streaming is not None and bt.streaming[h]:
+                    continue
+                fresh = set(a[b, h, :ca[b, h]].tolist())
+                cov.append(len(fresh & set(r[b, h, :cr[b, h]].tolist())) / max(1, len(fresh)))
+    return {"theta_per_step": theta, "mean": float(np.mean(cov)), "min": float(np.min(cov))}
+
+
 def replicate(dsa, torch, bt, R):
     """R copies of pool, page table and metadata at distinct addresses;
     returns one PagedKV view per replica and the metadata."""
@@ -243,6 +270,7 @@ def main():
 
     extra = {}
     step_end = None
+    reuse_step = None
     if a.workload == "prr_512k":
         from dynamic_sparse_attention_page_amd.prr import PRRDecoder
         a_, b_, g_ = bt.extra["ema"]
@@ -353,6 +381,17 @@ def main():
         def step(i):   # score -> top-k selection + sparse attention (one call)
             ops["page_score"](i % R)
             ops["sparse_decode_attn_topk"](i % R)
+
+        # LServe's reusable selector (section 4.3): the selector runs on the
+        # first token of every chunk of REUSE_CHUNK steps, later tokens reuse
+        # its pages; timed over a whole number of chunks per replica
+        from dynamic_sparse_attention_page_amd.reuse import ChunkedReuseDecoder
+        reuse_decs = [ChunkedReuseDecoder(kv_r, meta, Hq, k_pages, chunk=REUSE_CHUNK, logical_page=bt.logical_page,
+                                          streaming=st, scale=scale) for kv_r in kvs]
+        reuse_steps = REUSE_CHUNK * R * max(1, round(a.steps / (REUSE_CHUNK * R)))
+
+        def reuse_step(i):
+            reuse_decs[i % R].step(q)
         kvb = page_kv_bytes(bt, k_pages, dense_units) + streaming_bytes(bt)
         step_bytes = mb + kvb
         op_bytes = {"page_score": mb, "sparse_decode_attn_topk": kvb + 4 * N * B * Hkv, "sparse_decode_attn": kvb}
@@ -416,6 +455,16 @@ def main():
     g_step.replay()                       # untimed warm replay
     ms = time_graph(g_step, 1)
     ms_step = ms / a.steps
+
+    if reuse_step is not None:
+        g_reuse = capture(reuse_step, reuse_steps)
+        g_reuse.replay()
+        ms_reuse = time_graph(g_reuse, 1)
+        extra["chunked_reuse"] = {"chunk": REUSE_CHUNK, "steps": reuse_steps,
+                                  "ms_per_step": ms_reuse / reuse_steps,
+                                  "queries_per_s": B * reuse_steps / (ms_reuse * 1e-3),
+                                  "speedup_vs_step": ms_step / (ms_reuse / reuse_steps),
+                                  "coverage": reuse_coverage(dsa, torch, wl, bt, kvs[0], meta, st, q)}
 
     # per-call durations: graphs of R launches of one call
     reps = max(1, math.ceil(a.steps / R))
