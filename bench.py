@@ -213,6 +213,33 @@ def reuse_coverage(dsa, torch, wl, bt, kv, meta, st, q, steps=8, theta=0.1):
     return {"theta_per_step": theta, "mean": float(np.mean(cov)), "min": float(np.min(cov))}
 
 
+def host_signal_latency(dsa, torch, ops, counts, iters=30):
+    """Host wall time from enqueueing a PSA step (scores + progressive
+    selection) to holding its page counts: through the zero-copy signal
+    (dsa_signal_host + polling a pinned flag) vs a synchronising copy.
+    Medians in microseconds."""
+    import time
+    host = torch.zeros(counts.numel(), dtype=torch.int32, pin_memory=True)
+    flag = torch.zeros(1, dtype=torch.int32, pin_memory=True)
+    res = {}
+    for kind in ("signal", "sync_copy"):
+        ts = []
+        for it in range(iters):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            ops["page_score"](0)
+            ops["page_select_progressive"](0)
+            if kind == "signal":
+                dsa.signal_host(counts.view(-1), host, flag, 1000 + it)
+                if not dsa.wait_host_flag(flag, 1000 + it, timeout_s=10.0):
+                    raise RuntimeError("host signal never arrived")
+            else:
+                counts.view(-1).cpu()
+            ts.append((time.perf_counter() - t0) * 1e6)
+        res[kind + "_us"] = float(np.median(ts))
+    return res
+
+
 def replicate(dsa, torch, bt, R):
     """R copies of pool, page table and metadata at distinct addresses;
     returns one PagedKV view per replica and the metadata."""
@@ -330,6 +357,10 @@ def main():
         ops["prr_calibrate"] = lambda r: dsa.prr_calibrate(cal_trace, cal_nv, bt.topk, decs[r].k_spec, H=cal_H,
                                                            best=cal_best, ws=cal_ws)
         op_bytes["prr_calibrate"] = T_CAL * B * Hkv * N * 4
+        # section 3.4: the offline profile behind the speculation budget
+        from dynamic_sparse_attention_page_amd.prr import profile_delta_table
+        _, extra["prr_delta_profile"] = profile_delta_table(n_q_heads=Hq, n_kv_heads=Hkv, head_dim=D,
+                                                            page_size=bt.page_size)
     elif bt.topk is None or a.workload == "tiny_f32":   # PSA (and the tiny workload: top-k and PSA)
         ids_p = torch.empty((B, Hkv, N), dtype=i32, device=dev)
         cnt_p = torch.empty((B, Hkv), dtype=i32, device=dev)
@@ -356,6 +387,7 @@ def main():
         torch.cuda.synchronize()
         visited = float(cnt_p.float().mean().item())
         extra["psa_pages_visited"] = {"mean": visited, "max": int(cnt_p.max().item())}
+        extra["psa_host_signal"] = host_signal_latency(dsa, torch, ops, cnt_p)
         step_bytes = mb + page_kv_bytes(bt, visited, B * Hkv)
         op_bytes = {"page_score": mb, "page_select_progressive": page_kv_bytes(bt, visited, B * Hkv)}
         if bt.topk is not None:

@@ -19,7 +19,7 @@ import torch
 __all__ = [
     "DsaError", "PagedKV", "Streaming", "lib", "LIB_PATH",
     "page_meta_build", "kv_append", "page_score", "page_select_topk", "page_select_progressive",
-    "sparse_decode_attn", "sparse_decode_attn_topk", "attn_repair", "ema_predict_update", "prr_select", "prr_calibrate",
+    "sparse_decode_attn", "sparse_decode_attn_topk", "attn_repair", "ema_predict_update", "prr_select", "prr_calibrate", "signal_host",
     "workspace_bytes",
     "OP_SPARSE_DECODE_ATTN", "OP_ATTN_REPAIR", "EXPORTED",
 ]
@@ -32,6 +32,7 @@ EXPORTED = (
     "dsa_status_str", "dsa_version", "dsa_page_meta_build", "dsa_kv_append", "dsa_page_score", "dsa_page_select_topk",
     "dsa_page_select_progressive", "dsa_sparse_decode_attn", "dsa_sparse_decode_attn_topk", "dsa_attn_repair",
     "dsa_ema_predict_update", "dsa_prr_select", "dsa_prr_calibrate", "dsa_prr_calibrate_workspace_bytes",
+    "dsa_signal_host",
     "dsa_workspace_bytes",
 )
 
@@ -77,6 +78,7 @@ def _load(path: str = LIB_PATH):
         "dsa_prr_select": (ctypes.c_int, [P, I32, I32, I32, P, I32, I32, P, P, P, P, P, F32, F32, F32, I32, I32, P, P, P]),
         "dsa_prr_calibrate": (ctypes.c_int, [P, I32, I32, I32, P, I32, I32, P, P, P, SZ, P]),
         "dsa_prr_calibrate_workspace_bytes": (SZ, [I32, I32, I32]),
+        "dsa_signal_host": (ctypes.c_int, [P, I32, P, P, I32, P]),
         "dsa_workspace_bytes": (SZ, [I32, KV, I32, I32]),
     }
     for name, (res, args) in sig.items():
@@ -394,3 +396,27 @@ def prr_calibrate(trace: torch.Tensor, n_valid: torch.Tensor, k: int, m: int, H:
     _check("dsa_prr_calibrate", lib.dsa_prr_calibrate(_ptr(trace), T, U, N, _ptr(n_valid), k, m, _ptr(H), _ptr(best),
                                                       _ptr(ws), ws.numel() * ws.element_size(), _stream()))
     return H, best
+
+
+def signal_host(src: torch.Tensor, host_dst: torch.Tensor, host_flag: torch.Tensor, seq: int):
+    """Enqueue the zero-copy notification: src (device int32) into host_dst,
+    then seq into host_flag[0]; both host tensors pinned int32."""
+    for name, t in (("host_dst", host_dst), ("host_flag", host_flag)):
+        if t.device.type != "cpu" or not t.is_pinned() or t.dtype != torch.int32:
+            raise ValueError(f"{name} must be a pinned int32 host tensor")
+    if src.dtype != torch.int32 or not src.is_contiguous() or host_dst.numel() < src.numel():
+        raise ValueError("src must be contiguous int32 and fit in host_dst")
+    _check("dsa_signal_host", lib.dsa_signal_host(_ptr(src), src.numel(), _ptr(host_dst), _ptr(host_flag), seq,
+                                                  _stream()))
+
+
+def wait_host_flag(host_flag: torch.Tensor, seq: int, timeout_s: float = 10.0) -> bool:
+    """Poll a pinned flag written by signal_host until it equals seq (no
+    device synchronisation); False on timeout."""
+    import time
+    view = host_flag.numpy()
+    t_end = time.monotonic() + timeout_s
+    while int(view[0]) != seq:
+        if time.monotonic() > t_end:
+            return False
+    return True

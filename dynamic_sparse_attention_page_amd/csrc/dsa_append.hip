@@ -8,7 +8,7 @@
 //   come from the prefill and from the earlier decoding steps, i.e. they are
 //   maintained token by token.
 //
-// One workgroup per sequence.  Its threads own 16-byte chunks of the
+// One workgroup per sequence, one thread per 16-byte chunk of the
 // (KV head, channel) rows: each chunk is one load of k_new, v_new and of the
 // logical page's kmin/kmax, and one store of each; the min/max update is the
 // only arithmetic.  The sequence length is read by every thread before the
@@ -52,7 +52,7 @@ __device__ __forceinline__ void chunk_minmax<uint16_t>(const uint4& a, const uin
 }
 
 template <typename T>
-__global__ __launch_bounds__(256) void append_kernel(
+__global__ __launch_bounds__(1024) void append_kernel(
     T* __restrict__ k, T* __restrict__ v, const int32_t* __restrict__ page_table, const int32_t* seq_lens,
     int n_kv_heads, int P, int Pl, int D, int max_pages, int num_slots, const T* __restrict__ k_new,
     const T* __restrict__ v_new, T* __restrict__ meta, int32_t* new_lens, int32_t* __restrict__ status) {
@@ -106,13 +106,17 @@ extern "C" int dsa_kv_append(const dsa_kv* kv, int32_t logical_page, const void*
   if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(meta)) return DSA_ERR_ALIGN;
   hipStream_t st = (hipStream_t)stream;
   const dim3 grid(kv->batch);
+  // one thread per 16-byte chunk of a sequence's rows, so all of its loads
+  // are in flight at once (up to 1024 threads)
+  const long long chunks = (long long)kv->n_kv_heads * kv->head_dim * (kv->dtype == DSA_BF16 ? 2 : 4) / 16;
+  const dim3 block((unsigned)(chunks >= 1024 ? 1024 : (chunks + 63) / 64 * 64));
   if (kv->dtype == DSA_BF16)
-    hipLaunchKernelGGL((append_kernel<uint16_t>), grid, dim3(256), 0, st, (uint16_t*)kv->k, (uint16_t*)kv->v,
+    hipLaunchKernelGGL((append_kernel<uint16_t>), grid, block, 0, st, (uint16_t*)kv->k, (uint16_t*)kv->v,
                        kv->page_table, kv->seq_lens, kv->n_kv_heads, kv->page_size, logical_page, kv->head_dim,
                        kv->max_pages, kv->num_slots, (const uint16_t*)k_new, (const uint16_t*)v_new,
                        (uint16_t*)meta, new_seq_lens, status);
   else
-    hipLaunchKernelGGL((append_kernel<float>), grid, dim3(256), 0, st, (float*)kv->k, (float*)kv->v,
+    hipLaunchKernelGGL((append_kernel<float>), grid, block, 0, st, (float*)kv->k, (float*)kv->v,
                        kv->page_table, kv->seq_lens, kv->n_kv_heads, kv->page_size, logical_page, kv->head_dim,
                        kv->max_pages, kv->num_slots, (const float*)k_new, (const float*)v_new, (float*)meta,
                        new_seq_lens, status);

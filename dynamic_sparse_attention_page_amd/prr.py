@@ -17,13 +17,20 @@ only at the next step's speculative attention.  P is
 double-buffered: the side stream writes P^{t+1} while the caller's stream
 still reads P^t.
 
+The speculation budget |P| = floor(delta * |A|) comes from an offline
+profile indexed by context length (section 3.4): the largest delta whose
+speculative attention still fits in the selection window
+(profile_delta_table, DeltaTable).
+
 This module only sequences calls of the C ABI (through the binding) on two
 streams joined by events; every step of the arithmetic runs in the HIP
 library.  Stream priorities stay at the default.
 """
 from __future__ import annotations
 
+import bisect
 import math
+from dataclasses import dataclass, field
 
 import torch
 
@@ -40,7 +47,10 @@ class PRRDecoder:
     and `p_ids` the prediction P^{t+1} for the next step."""
 
     def __init__(self, kv: PagedKV, meta: torch.Tensor, n_q_heads: int, k: int, alpha: float, beta: float,
-                 gamma: float, delta: float = 1.0, logical_page: int | None = None, scale: float | None = None):
+                 gamma: float, delta: float = 1.0, logical_page: int | None = None, scale: float | None = None,
+                 delta_table: "DeltaTable | None" = None, context_tokens: int | None = None):
+        if delta_table is not None:   # section 3.4: delta by context length
+            delta = delta_table.lookup(context_tokens or kv.max_pages * kv.page_size)
         self.kv, self.meta, self.k = kv, meta, k
         self.alpha, self.beta, self.gamma, self.delta = alpha, beta, gamma, delta
         self.lp = logical_page or kv.page_size
@@ -163,3 +173,96 @@ class PRRDecoder:
         self._cur = nxt
         self.t += 1
         return out
+
+
+# --------------------------------------------------------------------------
+# dynamic speculation budget (section 3.4): min |A \ P| subject to
+# |P| <= delta |A|, with delta the largest value whose speculative attention
+# fits in the selection window, profiled offline per context length
+# --------------------------------------------------------------------------
+DELTA_GRID = (0.25, 0.5, 0.75, 1.0, 1.25, 1.5, 2.0)
+PROFILE_CONTEXTS = (4096, 8192, 16384, 32768, 65536)
+
+
+def choose_delta(t_select_us: float, t_spec_us: dict) -> float:
+    """The largest delta whose speculative attention takes no longer than
+    the selection it overlaps; the smallest profiled delta when none fits."""
+    fit = [d for d, t in t_spec_us.items() if t <= t_select_us]
+    return max(fit) if fit else min(t_spec_us)
+
+
+@dataclass
+class DeltaTable:
+    """(context tokens, delta) pairs, ascending in context."""
+    entries: list = field(default_factory=list)
+
+    def lookup(self, context_tokens: int) -> float:
+        """delta of the longest profiled context not above context_tokens
+        (of the shortest one for shorter contexts)."""
+        if not self.entries:
+            raise ValueError("empty delta table")
+        ctx = [c for c, _ in self.entries]
+        i = bisect.bisect_right(ctx, int(context_tokens)) - 1
+        return self.entries[max(i, 0)][1]
+
+
+def _time_us(fn, reps: int, trials: int = 7) -> float:
+    """Duration of fn() from a HIP graph of `reps` calls: the median over
+    `trials` replays of the per-call average."""
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    out = []
+    for _ in range(trials):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1) * 1e3 / reps)
+    return sorted(out)[len(out) // 2]
+
+
+def profile_delta_table(n_q_heads: int = 32, n_kv_heads: int = 2, head_dim: int = 128, page_size: int = 16,
+                        contexts=PROFILE_CONTEXTS, deltas=DELTA_GRID, sparsity: int = 16, reps: int = 20,
+                        seed: int = 0):
+    """Offline profile of section 3.4 on a seeded bf16 pool (batch 1): per
+    context length, the selection window (page scores, then dsa_prr_select:
+    the exact selection, the EMA and the next speculative selection) and the
+    speculative attention over floor(delta * k) pages for every delta, with
+    k = pages / sparsity.  Returns (DeltaTable, {context: timings})."""
+    from . import PagedKV as _KV, page_meta_build
+    dev = torch.device("cuda", torch.cuda.current_device())
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    entries, report = [], {}
+    for L in sorted(contexts):
+        N = -(-L // page_size)
+        k = max(1, N // sparsity)
+        pool = (N, n_kv_heads, page_size, head_dim)
+        kv = _KV(torch.randn(pool, generator=gen, device=dev).to(torch.bfloat16),
+                 torch.randn(pool, generator=gen, device=dev).to(torch.bfloat16),
+                 torch.arange(N, dtype=torch.int32, device=dev)[None, :].contiguous(),
+                 torch.full((1,), L, dtype=torch.int32, device=dev))
+        meta = page_meta_build(kv)
+        q = torch.randn((1, n_q_heads, head_dim), generator=gen, device=dev).to(torch.bfloat16)
+        dec = PRRDecoder(kv, meta, n_q_heads, k, 0.6, 0.3, 0.25)
+        dec._select_and_predict(q, init=True, buf=0)
+        t_sel = _time_us(lambda: dec._select_and_predict(q, init=False, buf=1), reps)
+        t_spec = {}
+        for d in deltas:
+            kd = max(1, min(N, int(math.floor(d * k))))
+            ids = torch.arange(kd, dtype=torch.int32, device=dev).view(1, 1, kd).expand(1, n_kv_heads, kd).contiguous()
+            cnt = torch.full((1, n_kv_heads), kd, dtype=torch.int32, device=dev)
+            ws = torch.zeros(workspace_bytes(OP_ATTN_REPAIR, kv, n_q_heads, kd), dtype=torch.uint8, device=dev)
+            out = (dec.O, dec.l, dec.m)
+            t_spec[d] = _time_us(lambda: sparse_decode_attn(q, kv, ids, cnt, out=out, ws=ws), reps)
+        delta = choose_delta(t_sel, t_spec)
+        entries.append((L, delta))
+        report[L] = {"pages": N, "k": k, "select_us": round(t_sel, 3),
+                     "spec_us": {str(d): round(v, 3) for d, v in t_spec.items()}, "delta": delta}
+    return DeltaTable(entries), report

@@ -18,6 +18,7 @@
  *   ema_predict_update     PRR's EMA page-score predictor
  *   prr_calibrate          PRR's search of the EMA hyper-parameters over a
  *                          score trace
+ *   signal_host            zero-copy notification of the host (PSA)
  *
  * Sources, cited by page title and section:
  *   [PSA]    "PSA: Progressive Sparse Attention -- Algorithm and System
@@ -367,6 +368,23 @@ int dsa_prr_select(const float *scores, int32_t batch, int32_t n_kv_heads, int32
 int dsa_prr_calibrate(const float *trace, int32_t steps, int32_t units, int32_t n,
                       const int32_t *n_valid, int32_t k, int32_t m, float *H, int32_t *best,
                       void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * dsa_signal_host -- zero-copy notification of the host ([PSA] section 3.3:
+ * after the threshold test passes, the GPU writes a signal variable into
+ * pinned host memory, so the CPU learns of it asynchronously).
+ *
+ * Enqueued on `stream` after the producing calls (for instance after
+ * dsa_page_select_progressive with src = its counts): copies src[0..n)
+ * (device int32) to host_dst[0..n) and then writes seq to *host_flag, both
+ * with system-scope stores, the flag last with release ordering.  A host
+ * thread that reads *host_flag == seq then reads the n values as written,
+ * with no stream or device synchronisation.  host_dst and host_flag must be
+ * pinned host memory the device can address (hipHostMalloc, or a pinned
+ * torch tensor); host_dst may be NULL when n == 0.
+ */
+int dsa_signal_host(const int32_t *src, int32_t n, int32_t *host_dst, int32_t *host_flag, int32_t seq,
+                    void *stream);
 
 /* Scratch bytes dsa_prr_calibrate needs (0 for invalid sizes). */
 size_t dsa_prr_calibrate_workspace_bytes(int32_t steps, int32_t units, int32_t n);

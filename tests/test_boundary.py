@@ -120,6 +120,10 @@ def test_validation_errors(dsa):
     assert L.dsa_prr_calibrate(ok_ptr, 4, 2, 1000, ok_ptr, 8, 8, None, None, ok_ptr, wsz, None) == -1
     assert L.dsa_prr_calibrate(ok_ptr, 4, 2, 1000, ok_ptr, 8, 8, ok_ptr, None, ok_ptr, wsz - 1, None) == -5
     assert L.dsa_prr_calibrate(None, 4, 0, 1000, None, 8, 8, None, None, None, 0, None) == 0
+    # host signal: negative count, missing flag or destination
+    assert L.dsa_signal_host(ok_ptr, -1, ok_ptr, ok_ptr, 1, None) == -2
+    assert L.dsa_signal_host(ok_ptr, 4, ok_ptr, None, 1, None) == -1
+    assert L.dsa_signal_host(ok_ptr, 4, None, ok_ptr, 1, None) == -1
     # EMA: negative n, aliasing
     assert L.dsa_ema_predict_update(None, ok_ptr, P(8192), ok_ptr, 10, 0.6, 0.3, 0.25, 0, None) == -2
     assert L.dsa_ema_predict_update(None, ok_ptr, P(8192), P(12288), -1, 0.6, 0.3, 0.25, 0, None) == -2
