@@ -537,6 +537,39 @@ def quest_step(batch, k: int, q=None):
 
 
 # --------------------------------------------------------------------------
+# block-sparse prefill  (LServe section 2.3: every T_Q x T_K tile is either
+# skipped or computed as causal attention; section 3.3 / Figure 5: dense and
+# streaming heads in one kernel; section 4.1: a streaming head keeps the
+# Lambda mask of sink and local tokens)
+# --------------------------------------------------------------------------
+def prefill_keys(i: int, L: int, streaming: bool, sink: int, local: int) -> np.ndarray:
+    """Keys query i attends to: j <= i (causal), and for a streaming head
+    only the sink tokens j < sink and the local ones j > i - local (the
+    decode rule with the sequence ending at i)."""
+    j = np.arange(min(i + 1, L))
+    if streaming:
+        j = j[(j < sink) | (j > i - local)]
+    return j
+
+
+def prefill_attention(q, k, v, dtype: str, scale: float, streaming=None, sink: int = 0, local: int = 0):
+    """(O[L][Hq][D], l[L][Hq], m[L][Hq]) of one sequence: q [L][Hq][D],
+    k, v [L][Hkv][D] (stored format); q head hq reads KV head hq // G."""
+    qf, kf, vf = (widen(x, dtype) for x in (q, k, v))
+    L, Hq, D = qf.shape
+    Hkv = kf.shape[1]
+    G = Hq // Hkv
+    O, l, m = np.zeros((L, Hq, D)), np.zeros((L, Hq)), np.full((L, Hq), NEG_INF)
+    for hq in range(Hq):
+        h = hq // G
+        st = streaming is not None and bool(streaming[h])
+        for i in range(L):
+            j = prefill_keys(i, L, st, sink, local)
+            O[i, hq], l[i, hq], m[i, hq] = attention(qf[i, hq], kf[j, h], vf[j, h], scale)
+    return O, l, m
+
+
+# --------------------------------------------------------------------------
 # reusable page selector  (LServe section 4.3: the selector runs only at the
 # start of each chunk of C consecutive decode tokens -- 4 by default -- and
 # the chunk's later tokens reuse the first token's pages)

@@ -36,6 +36,8 @@ MUTATIONS = [
     ("if p < 0 or j >= batch.max_pages:", "if p < 0 or j > batch.max_pages:"),
     ("out.seq_lens[b] = p + 1", "out.seq_lens[b] = p + 1 if p % P else p"),
     ("H[u, c] = acc / (T - 1)", "H[u, c] = acc / T"),
+    ("j = np.arange(min(i + 1, L))", "j = np.arange(min(i, L))"),
+    ("j = j[(j < sink) | (j > i - local)]", "j = j[(j < sink) | (j >= i - local)]"),
     ("return (t // chunk) * chunk", "return t - t % chunk + (1 if t % chunk else 0)"),
     ("outs.append(sparse_decode(batch, ids_of[s], q_trace[t]))", "outs.append(sparse_decode(batch, ids_of[s], q_trace[s]))"),
     ("for phi in range(1, T):\n                acc", "for phi in range(2, T):\n                acc"),

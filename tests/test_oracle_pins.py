@@ -617,6 +617,41 @@ def test_calibrate_matches_a_direct_loop():
 
 
 # ---------------------------------------------------------------- workload checks
+# ---------------------------------------------------------------- block-sparse prefill (LServe sections 2.3, 4.1)
+def test_prefill_dense_is_textbook_causal_softmax():
+    """Dense heads: query i is softmax(scale * K[:i+1] q_i) V[:i+1], by scipy."""
+    L, Hq, Hkv, D = 23, 4, 2, 8
+    q, k, v = wl.prefill_inputs(41, L, Hq, Hkv, D, "f32", q_gain=2.0)
+    sc = 0.35
+    O, l, m = oracle.prefill_attention(q, k, v, "f32", sc)
+    for hq in range(Hq):
+        h = hq // 2
+        for i in range(L):
+            s = sc * (k[:i + 1, h].astype(float) @ q[i, hq].astype(float))
+            np.testing.assert_allclose(O[i, hq], softmax(s) @ v[:i + 1, h].astype(float), rtol=1e-12, atol=1e-12)
+            assert m[i, hq] == pytest.approx(s.max()) and l[i, hq] == pytest.approx(np.exp(s - s.max()).sum())
+
+
+def test_prefill_streaming_lambda_mask():
+    """A streaming head attends to the sink tokens and the last `local`
+    tokens up to i (the decode rule at length i + 1); with sink + local
+    covering everything it is the dense head; the keys are a subset of the
+    causal ones and always include i itself when local >= 1."""
+    L, sink, local = 40, 3, 5
+    for i in range(L):
+        j = oracle.prefill_keys(i, L, True, sink, local)
+        expect = [x for x in range(i + 1) if x < sink or x >= i + 1 - local]
+        assert list(j) == expect and i in j
+        assert list(oracle.prefill_keys(i, L, False, sink, local)) == list(range(i + 1))
+    q, k, v = wl.prefill_inputs(42, 17, 2, 1, 8, "bf16")
+    a = oracle.prefill_attention(q, k, v, "bf16", 0.3, streaming=[1], sink=4, local=13)
+    b = oracle.prefill_attention(q, k, v, "bf16", 0.3)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+    c = oracle.prefill_attention(q, k, v, "bf16", 0.3, streaming=[1], sink=2, local=3)
+    assert not np.allclose(c[0][10:], b[0][10:])
+
+
 # ---------------------------------------------------------------- reusable selector (LServe section 4.3)
 def test_reuse_chunk_starts():
     """Chunk size 4: steps 0-3 use step 0's selection, 4-7 step 4's, ...;

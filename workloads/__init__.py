@@ -32,7 +32,7 @@ import numpy as np
 __all__ = [
     "Batch", "to_bf16_bits", "from_bf16_bits",
     "tiny_heavy", "quest_gqa", "lserve_hier", "psa_mha", "prr_trace",
-    "random_batch", "append_stream", "score_trace", "query_drift", "WORKLOADS", "make",
+    "random_batch", "append_stream", "score_trace", "query_drift", "prefill_inputs", "WORKLOADS", "make",
 ]
 
 
@@ -422,6 +422,18 @@ def query_drift(seed: int, q0: np.ndarray, steps: int, theta: float, dtype: str 
         cur = math.cos(theta) * cur + math.sin(theta) * rng.standard_normal(cur.shape)
         out.append(_store(cur.astype(np.float32), dtype))
     return np.stack(out)
+
+
+def prefill_inputs(seed: int, L: int, n_q_heads: int, n_kv_heads: int, head_dim: int, dtype: str = "bf16",
+                   q_gain: float = 1.0):
+    """q [L][n_q_heads][D], k, v [L][n_kv_heads][D] of one prompt (stored
+    format), N(0, 1); q is multiplied by q_gain (larger gains give peakier
+    attention)."""
+    rq, rk, rv = (np.random.default_rng(s) for s in np.random.SeedSequence(seed).spawn(3))
+    q = rq.standard_normal((L, n_q_heads, head_dim), dtype=np.float32) * np.float32(q_gain)
+    k = rk.standard_normal((L, n_kv_heads, head_dim), dtype=np.float32)
+    v = rv.standard_normal((L, n_kv_heads, head_dim), dtype=np.float32)
+    return _store(q, dtype), _store(k, dtype), _store(v, dtype)
 
 
 # Full-size workloads, by what they are.
