@@ -49,6 +49,8 @@ METRIC = "sparse decode attn+select: queries/sec and achieved HBM GB/s (% of pea
 # calls timed beside the step but not part of it: the roofline names the
 # dominant call of the step only
 SIDE_OPS = {"kv_append", "prr_calibrate"}
+PREFILL = "lserve_prefill_16k"   # the block-sparse prefill workload
+MFMA_BF16_TFLOPS = 2500.0        # dense bf16 matrix-core peak
 T_CAL = 32   # steps of the score trace the PRR calibration searches over
 REUSE_CHUNK = 4   # LServe's default selector-reuse interval
 WORKLOADS = ["quest_gqa_32k", "lserve_hier_128k", "psa_mha_64k", "prr_512k", "tiny_f32"]
@@ -59,7 +61,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="quest_gqa_32k", choices=WORKLOADS)
+    ap.add_argument("--workload", default="quest_gqa_32k", choices=list(WORKLOADS) + [PREFILL])
     ap.add_argument("--replicas", type=int, default=0, help="0 = enough for > 1 GiB per rotation")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU oracle sample")
     ap.add_argument("--no-cpu", action="store_true")
@@ -257,6 +259,79 @@ def replicate(dsa, torch, bt, R):
     return kvs, meta
 
 
+def prefill_pairs(L: int, streaming, sink: int, local: int, G: int) -> int:
+    """(query, key) pairs the prefill attends to, over all q heads."""
+    i = np.arange(L, dtype=np.int64)
+    dense = int(((i + 1)).sum())
+    lam = np.minimum(i + 1, sink) + np.maximum(0, i - np.maximum(sink, i - local + 1) + 1)
+    return G * sum(int(lam.sum()) if s else dense for s in streaming)
+
+
+def run_prefill(a, dsa, torch, wl):
+    """LServe's block-sparse prefill on the 16K-token prompt: prefill tokens
+    per second, against the bf16 matrix-core peak on the attended pairs."""
+    import time
+    cfg = wl.PREFILL_16K
+    L, Hq, Hkv, D = cfg["L"], cfg["n_q_heads"], cfg["n_kv_heads"], cfg["head_dim"]
+    q, k, v = wl.prefill_inputs(cfg["seed"], L, Hq, Hkv, D, "bf16")
+    qd, kd, vd = (dsa.upload_q(x, "bf16") for x in (q, k, v))
+    st = dsa.Streaming(cfg["streaming"], cfg["sink"], cfg["local"])
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    out = dsa.block_sparse_prefill(qd, kd, vd, streaming=st, scale=scale)
+    for _ in range(a.warmup):
+        dsa.block_sparse_prefill(qd, kd, vd, streaming=st, scale=scale, out=out)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(a.steps):
+            dsa.block_sparse_prefill(qd, kd, vd, streaming=st, scale=scale, out=out)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / a.steps
+    G = Hq // Hkv
+    pairs = prefill_pairs(L, cfg["streaming"], cfg["sink"], cfg["local"], G)
+    flops = 4.0 * D * pairs                      # q.k and p.v, 2 flops per multiply-add
+    n_qt = -(-L // 64)
+    dense_tiles = n_qt * (n_qt + 1) // 2
+    res = {
+        "metric": "block-sparse prefill: prompt tokens/s",
+        "value": L / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": PREFILL, "seq_len": L, "n_q_heads": Hq, "n_kv_heads": Hkv, "head_dim": D,
+                   "streaming_kv_heads": int(np.count_nonzero(cfg["streaming"])), "sink": cfg["sink"],
+                   "local": cfg["local"], "tile": 64, "parallelism": "single GPU"},
+        "attended_pairs": pairs,
+        "block_sparsity_vs_causal": 1.0 - pairs / (G * Hkv * L * (L + 1) / 2),
+        "dense_head_tiles": dense_tiles,
+        "roofline": {"bound": "mfma", "kernel": "block_sparse_prefill", "achieved": flops / (ms * 1e-3) / 1e12,
+                     "peak": MFMA_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": flops / (ms * 1e-3) / 1e12 / MFMA_BF16_TFLOPS, "traffic": None,
+                     "flops_per_launch": flops, "avg_launch_us": ms * 1e3},
+    }
+    if not a.no_cpu:   # the oracle on a bounded sample of queries (all heads of each)
+        import oracle
+        qf, kf, vf = (oracle.widen(x, "bf16") for x in (q, k, v))
+        rng = np.random.default_rng(0)
+        t0, n = time.perf_counter(), 0
+        while time.perf_counter() - t0 < a.cpu_seconds:
+            i = int(rng.integers(0, L))
+            for hq in range(Hq):
+                hk = hq // G
+                j = oracle.prefill_keys(i, L, bool(cfg["streaming"][hk]), cfg["sink"], cfg["local"])
+                oracle.attention(qf[i, hq], kf[j, hk], vf[j, hk], scale)
+            n += 1
+        dt = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": n / dt, "unit": "tokens/s (uniformly sampled query positions)",
+                               "cores": 1, "kind": "oracle", "sample": f"{n} query tokens x {Hq} heads"}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     a = parse()
     if a.copy_calibration:
@@ -272,6 +347,9 @@ def main():
 
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
+    if a.workload == PREFILL:
+        run_prefill(a, dsa, torch, wl)
+        return
     bt = wl.make(a.workload)
     B, Hq, Hkv, D, N = bt.batch, bt.n_q_heads, bt.n_kv_heads, bt.head_dim, bt.max_pages
     scale = float(bt.scale)

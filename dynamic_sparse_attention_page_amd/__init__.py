@@ -19,7 +19,7 @@ import torch
 __all__ = [
     "DsaError", "PagedKV", "Streaming", "lib", "LIB_PATH",
     "page_meta_build", "kv_append", "page_score", "page_select_topk", "page_select_progressive",
-    "sparse_decode_attn", "sparse_decode_attn_topk", "attn_repair", "ema_predict_update", "prr_select", "prr_calibrate", "signal_host",
+    "sparse_decode_attn", "sparse_decode_attn_topk", "attn_repair", "ema_predict_update", "prr_select", "prr_calibrate", "signal_host", "block_sparse_prefill",
     "workspace_bytes",
     "OP_SPARSE_DECODE_ATTN", "OP_ATTN_REPAIR", "EXPORTED",
 ]
@@ -32,7 +32,7 @@ EXPORTED = (
     "dsa_status_str", "dsa_version", "dsa_page_meta_build", "dsa_kv_append", "dsa_page_score", "dsa_page_select_topk",
     "dsa_page_select_progressive", "dsa_sparse_decode_attn", "dsa_sparse_decode_attn_topk", "dsa_attn_repair",
     "dsa_ema_predict_update", "dsa_prr_select", "dsa_prr_calibrate", "dsa_prr_calibrate_workspace_bytes",
-    "dsa_signal_host",
+    "dsa_signal_host", "dsa_block_sparse_prefill",
     "dsa_workspace_bytes",
 )
 
@@ -79,6 +79,7 @@ def _load(path: str = LIB_PATH):
         "dsa_prr_calibrate": (ctypes.c_int, [P, I32, I32, I32, P, I32, I32, P, P, P, SZ, P]),
         "dsa_prr_calibrate_workspace_bytes": (SZ, [I32, I32, I32]),
         "dsa_signal_host": (ctypes.c_int, [P, I32, P, P, I32, P]),
+        "dsa_block_sparse_prefill": (ctypes.c_int, [P, P, P, I32, I32, I32, I32, ST, F32, P, P, P, P]),
         "dsa_workspace_bytes": (SZ, [I32, KV, I32, I32]),
     }
     for name, (res, args) in sig.items():
@@ -420,3 +421,25 @@ def wait_host_flag(host_flag: torch.Tensor, seq: int, timeout_s: float = 10.0) -
         if time.monotonic() > t_end:
             return False
     return True
+
+
+def block_sparse_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, streaming: Streaming | None = None,
+                         scale: float | None = None, out=None):
+    """Prefill attention of one sequence: q [L][Hq][D], k, v [L][Hkv][D]
+    (bf16) -> (O [L][Hq][D], l [L][Hq], m [L][Hq]) in float32."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != torch.bfloat16 or t.dim() != 3 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous bf16 [L][heads][head_dim] tensor")
+    L, Hq, D = q.shape
+    Hkv = k.shape[1]
+    if tuple(k.shape) != (L, Hkv, D) or tuple(v.shape) != (L, Hkv, D):
+        raise ValueError("k and v must be [L][n_kv_heads][head_dim] with q's L and head_dim")
+    if out is None:
+        out = (torch.empty((L, Hq, D), dtype=torch.float32, device=q.device),
+               torch.empty((L, Hq), dtype=torch.float32, device=q.device),
+               torch.empty((L, Hq), dtype=torch.float32, device=q.device))
+    O, l, m = out
+    sc = _default_scale(D) if scale is None else scale
+    _check("dsa_block_sparse_prefill", lib.dsa_block_sparse_prefill(
+        _ptr(q), _ptr(k), _ptr(v), L, Hq, Hkv, D, _stream_arg(streaming), sc, _ptr(O), _ptr(l), _ptr(m), _stream()))
+    return O, l, m

@@ -19,6 +19,7 @@
  *   prr_calibrate          PRR's search of the EMA hyper-parameters over a
  *                          score trace
  *   signal_host            zero-copy notification of the host (PSA)
+ *   block_sparse_prefill   LServe's prefill attention with tile skipping
  *
  * Sources, cited by page title and section:
  *   [PSA]    "PSA: Progressive Sparse Attention -- Algorithm and System
@@ -368,6 +369,28 @@ int dsa_prr_select(const float *scores, int32_t batch, int32_t n_kv_heads, int32
 int dsa_prr_calibrate(const float *trace, int32_t steps, int32_t units, int32_t n,
                       const int32_t *n_valid, int32_t k, int32_t m, float *H, int32_t *best,
                       void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * dsa_block_sparse_prefill -- block-sparse prefill attention of one
+ * sequence ([LServe] section 2.3: every T_Q x T_K tile is skipped or
+ * computed like causal attention; section 3.3 and Figure 5: dense and
+ * streaming heads in one kernel that visits only the needed tiles; section
+ * 4.1: the Lambda mask of a streaming head).
+ *
+ * q: device bf16 [L][n_q_heads][head_dim]; k, v: device bf16
+ * [L][n_kv_heads][head_dim] (the prompt's projections, token-major); q head
+ * hq reads KV head hq / G.  Query i attends to the keys j <= i; for a KV
+ * head flagged streaming in stream_cfg (may be NULL) only to j < sink or
+ * j > i - local.  Outputs per (token, q head), as in the decode calls:
+ * O device float [L][n_q_heads][head_dim] (normalised), l and m device float
+ * [L][n_q_heads] (m in scaled-logit units; an empty key set gives O = 0,
+ * l = 0, m = -inf).  Tiles of 64 queries x 64 keys without an attended pair
+ * are not visited.  Requires head_dim 64 or 128 and a finite scale > 0;
+ * q, k, v and O 16-byte aligned.
+ */
+int dsa_block_sparse_prefill(const void *q, const void *k, const void *v, int32_t L, int32_t n_q_heads,
+                             int32_t n_kv_heads, int32_t head_dim, const dsa_stream_cfg *stream_cfg,
+                             float scale, float *O, float *l, float *m, void *stream);
 
 /*
  * dsa_signal_host -- zero-copy notification of the host ([PSA] section 3.3:

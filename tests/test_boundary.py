@@ -120,6 +120,17 @@ def test_validation_errors(dsa):
     assert L.dsa_prr_calibrate(ok_ptr, 4, 2, 1000, ok_ptr, 8, 8, None, None, ok_ptr, wsz, None) == -1
     assert L.dsa_prr_calibrate(ok_ptr, 4, 2, 1000, ok_ptr, 8, 8, ok_ptr, None, ok_ptr, wsz - 1, None) == -5
     assert L.dsa_prr_calibrate(None, 4, 0, 1000, None, 8, 8, None, None, None, 0, None) == 0
+    # prefill: inconsistent heads, head_dim, scale, null output
+    F = ctypes.c_float
+    assert L.dsa_block_sparse_prefill(ok_ptr, ok_ptr, ok_ptr, 64, 6, 4, 128, None, F(0.1), ok_ptr, ok_ptr, ok_ptr,
+                                      None) == -2
+    assert L.dsa_block_sparse_prefill(ok_ptr, ok_ptr, ok_ptr, 64, 8, 4, 96, None, F(0.1), ok_ptr, ok_ptr, ok_ptr,
+                                      None) == -4
+    assert L.dsa_block_sparse_prefill(ok_ptr, ok_ptr, ok_ptr, 64, 8, 4, 128, None, F(0.0), ok_ptr, ok_ptr, ok_ptr,
+                                      None) == -2
+    assert L.dsa_block_sparse_prefill(ok_ptr, ok_ptr, ok_ptr, 64, 8, 4, 128, None, F(0.1), None, ok_ptr, ok_ptr,
+                                      None) == -1
+    assert L.dsa_block_sparse_prefill(None, None, None, 0, 8, 4, 128, None, F(0.1), None, None, None, None) == 0
     # host signal: negative count, missing flag or destination
     assert L.dsa_signal_host(ok_ptr, -1, ok_ptr, ok_ptr, 1, None) == -2
     assert L.dsa_signal_host(ok_ptr, 4, ok_ptr, None, 1, None) == -1

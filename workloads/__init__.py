@@ -32,7 +32,7 @@ import numpy as np
 __all__ = [
     "Batch", "to_bf16_bits", "from_bf16_bits",
     "tiny_heavy", "quest_gqa", "lserve_hier", "psa_mha", "prr_trace",
-    "random_batch", "append_stream", "score_trace", "query_drift", "prefill_inputs", "WORKLOADS", "make",
+    "random_batch", "append_stream", "score_trace", "query_drift", "prefill_inputs", "PREFILL_16K", "WORKLOADS", "make",
 ]
 
 
@@ -434,6 +434,13 @@ def prefill_inputs(seed: int, L: int, n_q_heads: int, n_kv_heads: int, head_dim:
     k = rk.standard_normal((L, n_kv_heads, head_dim), dtype=np.float32)
     v = rv.standard_normal((L, n_kv_heads, head_dim), dtype=np.float32)
     return _store(q, dtype), _store(k, dtype), _store(v, dtype)
+
+
+# The block-sparse prefill workload: one 16K-token prompt, 32 q / 8 KV heads,
+# head_dim 128, bf16, every other KV head streaming (sink 128, local 256
+# tokens): the LServe shape of the decode workload, at prefill.
+PREFILL_16K = {"seed": 106, "L": 16384, "n_q_heads": 32, "n_kv_heads": 8, "head_dim": 128,
+               "streaming": np.array([0, 1, 0, 1, 0, 1, 0, 1], np.uint8), "sink": 128, "local": 256}
 
 
 # Full-size workloads, by what they are.
