@@ -5,26 +5,40 @@
 // kernel whose iterator visits only the tiles it needs; section 4.1 -- a
 // streaming head keeps the Lambda mask of sink and local tokens.
 //
-// One workgroup per (64-query tile, q head); wave w owns queries
-// 16w .. 16w+15 of the tile.  The key tiles (64 keys) the tile needs are
-// visited in order: all of 0 .. qt for a dense head (causal), the sink tiles
-// and the tiles of the local window for a streaming head; a skipped tile
-// holds no attended (query, key) pair.  Inside a visited tile the token mask
+// One workgroup of NWQ waves per (query tile of 16 QS NWQ queries, q head);
+// wave w owns QS sets of 16 consecutive queries, and every K or V read from
+// LDS feeds the matrix-core products of all its sets.  The key tiles (64 keys)
+// the query tile needs are visited in order: every tile up to the one of the
+// last query for a dense head (causal), the sink tiles and the tiles of the
+// local window for a streaming head; a skipped tile holds no attended
+// (query, key) pair.  Inside a visited tile the token mask
 // is exact.  Per tile the workgroup stages K (row-major) and V (transposed)
 // in LDS, and every wave runs the online-softmax recurrence on the matrix
 // cores with the layouts of the decode tile (dsa_attn_mfma.hpp), queries in
 // place of heads:
 //   S^T = K Q^T      v_mfma_f32_16x16x32_bf16, D/32 steps per 16 keys;
 //                    lane (h = l%16, g = l/16) holds S[query h][keys 4g+j]
-//   O^T += V^T P^T   v_mfma_f32_16x16x16_bf16, P as bf16 hi + lo parts;
-//                    A = V^T is one 8-byte read of the transposed V tile
+//   O^T += V^T P^T   v_mfma_f32_16x16x32_bf16 over 32 keys, P as bf16 hi +
+//                    lo parts; the k index 8g + j stands for key 4g + j of
+//                    the chunk's first 16 keys (j < 4) and 16 + 4g + j - 4 of
+//                    its second, so B is the lane's own logits and A two
+//                    8-byte reads of the transposed V tile
+// Tiles below the diagonal of a dense head (and sink tiles below it) need
+// no token mask.
 // Heaviest query tiles (most key tiles) are launched first.
 #include "dsa_attn_mfma.hpp"
 #include "dsa_host.hpp"
 
 namespace dsa {
 
-constexpr int kPfTile = 64;   // T_Q = T_K
+#ifndef DSA_PREFILL_WAVES
+#define DSA_PREFILL_WAVES 8   // waves per workgroup
+#endif
+#ifndef DSA_PREFILL_QSETS
+#define DSA_PREFILL_QSETS 1   // sets of 16 queries per wave (each LDS read feeds all)
+#endif
+
+constexpr int kPfTile = 64;   // T_K
 
 template <int D>
 struct PrefillSmem {
@@ -39,13 +53,18 @@ __device__ __forceinline__ uint32_t bf16_at(const uint4& x, int i) {
   return (i & 1) ? (w >> 16) : (w & 0xFFFFu);
 }
 
-template <int D>
-__global__ __launch_bounds__(256) void prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+template <int D, int NWQ, int QS>
+__global__ __launch_bounds__(NWQ * 64) void prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                                       const uint16_t* __restrict__ v, int L, int Hq, int Hkv,
                                                       unsigned long long streaming, int sink, int local, float scale,
                                                       float c, float* __restrict__ O, float* __restrict__ lout,
                                                       float* __restrict__ mout) {
   constexpr int NK = D / 32, NB = D / 16;
+  constexpr int NT = NWQ * 64, QT = 16 * QS * NWQ;   // threads; queries per tile
+  constexpr int KCH = D / (8 * NWQ);           // K chunks per thread
+  constexpr int VCH = D / (16 * NWQ) > 0 ? D / (16 * NWQ) : 1;   // V chunks per half-wave
+  constexpr int VHW = D / (8 * VCH);           // half-waves that stage V
+  static_assert(KCH * NT * 8 == kPfTile * D, "K staging");
   using S = PrefillSmem<D>;
   __shared__ S sm;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -53,127 +72,181 @@ __global__ __launch_bounds__(256) void prefill_kernel(const uint16_t* __restrict
   const int qt = gridDim.x - 1 - blockIdx.x;   // heaviest tiles first
   const int hq = blockIdx.y, G = Hq / Hkv, hk = hq / G;
   const bool smask = (streaming >> hk) & 1ull;
-  const int iq = qt * kPfTile + wave * 16 + h;  // this lane's query
+  const int q_first = qt * QT;
+  int iq[QS];                                  // this lane's query in each set
+#pragma unroll
+  for (int u = 0; u < QS; ++u) iq[u] = q_first + (wave * QS + u) * 16 + h;
   const size_t kv_row = (size_t)Hkv * D;
 
-  // Q^T operand: query iq, channels 32i + 8g
-  bf16x8_t qb[NK];
+  // Q^T operands: query iq[u], channels 32i + 8g
+  bf16x8_t qb[QS][NK];
+  f32x4_t acc[QS][NB];
+  float m[QS], lpart[QS];
 #pragma unroll
-  for (int i = 0; i < NK; ++i) {
-    uint4 w = make_uint4(0u, 0u, 0u, 0u);
-    if (iq < L) w = *reinterpret_cast<const uint4*>(q + ((size_t)iq * Hq + hq) * D + 32 * i + 8 * g);
-    qb[i] = __builtin_bit_cast(bf16x8_t, w);
+  for (int u = 0; u < QS; ++u) {
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+      uint4 w = make_uint4(0u, 0u, 0u, 0u);
+      if (iq[u] < L) w = *reinterpret_cast<const uint4*>(q + ((size_t)iq[u] * Hq + hq) * D + 32 * i + 8 * g);
+      qb[u][i] = __builtin_bit_cast(bf16x8_t, w);
+    }
+#pragma unroll
+    for (int n = 0; n < NB; ++n) acc[u][n] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    m[u] = kNegInf;
+    lpart[u] = 0.0f;
   }
-  f32x4_t acc[NB];
-#pragma unroll
-  for (int n = 0; n < NB; ++n) acc[n] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  float m = kNegInf, lpart = 0.0f;
 
-  // key tiles: dense [0, qt]; streaming: sink tiles, then the local window's
-  int n_first = qt + 1, lo2 = qt + 1;
+  // key tiles: dense [0, kb_max]; streaming: sink tiles, then the local window's
+  const int kb_max = (min(L, q_first + QT) - 1) / kPfTile;
+  int n_first = kb_max + 1, lo2 = kb_max + 1;
   if (smask) {
-    n_first = min(qt + 1, (sink + kPfTile - 1) / kPfTile);
-    lo2 = local > 0 ? max(n_first, max(0, qt * kPfTile + 1 - local) / kPfTile) : qt + 1;
+    n_first = min(kb_max + 1, (sink + kPfTile - 1) / kPfTile);
+    lo2 = local > 0 ? max(n_first, max(0, q_first + 1 - local) / kPfTile) : kb_max + 1;
   }
-  const int n_iter = n_first + max(0, qt + 1 - lo2);
+  const int n_iter = n_first + max(0, kb_max + 1 - lo2);
+
+  // Global -> register staging of a key tile; the next tile's loads are in
+  // flight while the current one is computed.  K: 16-byte chunk tid + 256x
+  // of the row-major tile.  V: a half-wave takes keys (2p, 2p+1), p =
+  // lane % 32, and D/64 channel chunks (written transposed, one 32-bit word
+  // per channel row).
+  const int hw = tid >> 5, pp = tid & 31;
+  uint4 kr[KCH], va[VCH], vb[VCH];
+  auto fetch = [&](int key0) {
+#pragma unroll
+    for (int x = 0; x < KCH; ++x) {
+      const int chunk = tid + NT * x;
+      const int row = chunk / (D / 8), col = (chunk % (D / 8)) * 8;
+      kr[x] = make_uint4(0u, 0u, 0u, 0u);
+      if (key0 + row < L) kr[x] = *reinterpret_cast<const uint4*>(k + (size_t)(key0 + row) * kv_row + (size_t)hk * D + col);
+    }
+#pragma unroll
+    for (int x = 0; x < VCH; ++x) {
+      const int col = (hw * VCH + x) * 8;
+      const int t0 = key0 + 2 * pp;
+      va[x] = make_uint4(0u, 0u, 0u, 0u);
+      vb[x] = va[x];
+      if (hw >= VHW) continue;
+      if (t0 < L) va[x] = *reinterpret_cast<const uint4*>(v + (size_t)t0 * kv_row + (size_t)hk * D + col);
+      if (t0 + 1 < L) vb[x] = *reinterpret_cast<const uint4*>(v + (size_t)(t0 + 1) * kv_row + (size_t)hk * D + col);
+    }
+  };
+  auto tile_of = [&](int it) { return it < n_first ? it : lo2 + (it - n_first); };
+  if (n_iter > 0) fetch(tile_of(0) * kPfTile);
 
   for (int it = 0; it < n_iter; ++it) {
-    const int kb = it < n_first ? it : lo2 + (it - n_first);
+    const int kb = tile_of(it);
     const int key0 = kb * kPfTile;
     __syncthreads();   // the previous tile's LDS reads are done
-    // K tile, row-major: 16-byte chunk tid + 256x
 #pragma unroll
-    for (int x = 0; x < D / 32; ++x) {
-      const int chunk = tid + 256 * x;
+    for (int x = 0; x < KCH; ++x) {
+      const int chunk = tid + NT * x;
       const int row = chunk / (D / 8), col = (chunk % (D / 8)) * 8;
-      uint4 w = make_uint4(0u, 0u, 0u, 0u);
-      if (key0 + row < L) w = *reinterpret_cast<const uint4*>(k + (size_t)(key0 + row) * kv_row + (size_t)hk * D + col);
-      *reinterpret_cast<uint4*>(sm.k + row * S::KS + col) = w;
+      *reinterpret_cast<uint4*>(sm.k + row * S::KS + col) = kr[x];
     }
-    // V tile, transposed: a half-wave takes keys (2p, 2p+1), p = lane % 32,
-    // and D/64 channel chunks; each channel row gets one 32-bit word
-    {
-      const int hw = tid >> 5, p = tid & 31;
 #pragma unroll
-      for (int x = 0; x < D / 64; ++x) {
-        const int col = (hw * (D / 64) + x) * 8;
-        uint4 a = make_uint4(0u, 0u, 0u, 0u), b = a;
-        const int t0 = key0 + 2 * p;
-        if (t0 < L) a = *reinterpret_cast<const uint4*>(v + (size_t)t0 * kv_row + (size_t)hk * D + col);
-        if (t0 + 1 < L) b = *reinterpret_cast<const uint4*>(v + (size_t)(t0 + 1) * kv_row + (size_t)hk * D + col);
+    for (int x = 0; x < VCH; ++x) {
+      const int col = (hw * VCH + x) * 8;
+      if (hw >= VHW) continue;
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-          *reinterpret_cast<uint32_t*>(sm.vt + (col + i) * S::VS + 2 * p) = bf16_at(a, i) | (bf16_at(b, i) << 16);
-      }
+      for (int i = 0; i < 8; ++i)
+        *reinterpret_cast<uint32_t*>(sm.vt + (col + i) * S::VS + 2 * pp) = bf16_at(va[x], i) | (bf16_at(vb[x], i) << 16);
     }
     __syncthreads();
+    if (it + 1 < n_iter) fetch(tile_of(it + 1) * kPfTile);
 
-    // logits of 4 sub-tiles of 16 keys
-    f32x4_t s[4];
+    // logits of 4 sub-tiles of 16 keys; one K read serves every query set
+    f32x4_t s[QS][4];
 #pragma unroll
     for (int sub = 0; sub < 4; ++sub) {
-      s[sub] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int u = 0; u < QS; ++u) s[u][sub] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int i = 0; i < NK; ++i) {
         const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(sm.k + (16 * sub + h) * S::KS + 32 * i + 8 * g);
-        s[sub] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[i], s[sub], 0, 0, 0);
+#pragma unroll
+        for (int u = 0; u < QS; ++u) s[u][sub] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[u][i], s[u][sub], 0, 0, 0);
       }
     }
-    float tm = kNegInf;
+    // every pair of a tile below the diagonal is attended (for a streaming
+    // head only if the tile is all sink); others are masked per token
+    const bool full = key0 + kPfTile <= q_first && (!smask || key0 + kPfTile <= sink);
+    float alpha[QS], mn[QS], psum[QS];
 #pragma unroll
-    for (int sub = 0; sub < 4; ++sub)
+    for (int u = 0; u < QS; ++u) {
+      float tm = kNegInf;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int key = key0 + 16 * sub + 4 * g + j;
-        const bool ok = key <= iq && key < L && (!smask || key < sink || key > iq - local);
-        if (!ok) s[sub][j] = kNegInf;
-        tm = fmaxf(tm, s[sub][j]);
+      for (int sub = 0; sub < 4; ++sub)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (!full) {
+            const int key = key0 + 16 * sub + 4 * g + j;
+            const bool ok = key <= iq[u] && key < L && (!smask || key < sink || key > iq[u] - local);
+            if (!ok) s[u][sub][j] = kNegInf;
+          }
+          tm = fmaxf(tm, s[u][sub][j]);
+        }
+      tm = fmaxf(tm, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(tm), 0x401F)));  // lanes ^ 16
+      tm = fmaxf(tm, shfl_xor_f(tm, 32));
+      mn[u] = fmaxf(m[u], tm);
+      alpha[u] = (mn[u] == kNegInf) ? 1.0f : fast_exp2((m[u] - mn[u]) * c);
+      if (__builtin_amdgcn_read_exec() & __ballot(alpha[u] != 1.0f)) {
+#pragma unroll
+        for (int n = 0; n < NB; ++n) acc[u][n] *= alpha[u];
       }
-    tm = fmaxf(tm, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(tm), 0x401F)));  // lanes ^ 16
-    tm = fmaxf(tm, shfl_xor_f(tm, 32));
-    const float mn = fmaxf(m, tm);
-    const float alpha = (mn == kNegInf) ? 1.0f : fast_exp2((m - mn) * c);
-    if (__builtin_amdgcn_read_exec() & __ballot(alpha != 1.0f)) {
-#pragma unroll
-      for (int n = 0; n < NB; ++n) acc[n] *= alpha;
+      psum[u] = 0.0f;
     }
-    float psum = 0.0f;
 #pragma unroll
-    for (int sub = 0; sub < 4; ++sub) {
-      float p[4];
+    for (int ch = 0; ch < 2; ++ch) {   // 32-key chunks: sub-tiles 2ch and 2ch + 1
+      bf16x8_t bhi[QS], blo[QS];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        p[j] = exp2_diff(s[sub][j], mn, c);
-        psum += p[j];
+      for (int u = 0; u < QS; ++u) {
+        uint32_t hw[4], lw[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {  // words: keys (4g, 4g+1), (4g+2, 4g+3) of each sub-tile
+          const int sub = 2 * ch + (x >> 1), j = 2 * (x & 1);
+          const float p0 = exp2_diff(s[u][sub][j], mn[u], c), p1 = exp2_diff(s[u][sub][j + 1], mn[u], c);
+          psum[u] += p0 + p1;
+          hw[x] = pack_bf16(p0, p1);
+          lw[x] = pack_bf16(p0 - bf_lo(hw[x]), p1 - bf_hi(hw[x]));
+        }
+        bhi[u] = __builtin_bit_cast(bf16x8_t, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+        blo[u] = __builtin_bit_cast(bf16x8_t, make_uint4(lw[0], lw[1], lw[2], lw[3]));
       }
-      const uint32_t h01 = pack_bf16(p[0], p[1]), h23 = pack_bf16(p[2], p[3]);
-      const uint32_t l01 = pack_bf16(p[0] - bf_lo(h01), p[1] - bf_hi(h01));
-      const uint32_t l23 = pack_bf16(p[2] - bf_lo(h23), p[3] - bf_hi(h23));
-      const s16x4_t bhi = __builtin_bit_cast(s16x4_t, make_uint2(h01, h23));
-      const s16x4_t blo = __builtin_bit_cast(s16x4_t, make_uint2(l01, l23));
 #pragma unroll
       for (int n = 0; n < NB; ++n) {
-        const s16x4_t a = *reinterpret_cast<const s16x4_t*>(sm.vt + (16 * n + h) * S::VS + 16 * sub + 4 * g);
-        acc[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, bhi, acc[n], 0, 0, 0);
-        acc[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, blo, acc[n], 0, 0, 0);
+        const uint16_t* vr = sm.vt + (16 * n + h) * S::VS + 32 * ch + 4 * g;
+        const uint2 a0 = *reinterpret_cast<const uint2*>(vr), a1 = *reinterpret_cast<const uint2*>(vr + 16);
+        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, make_uint4(a0.x, a0.y, a1.x, a1.y));
+#pragma unroll
+        for (int u = 0; u < QS; ++u) {
+          acc[u][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bhi[u], acc[u][n], 0, 0, 0);
+          acc[u][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, blo[u], acc[u][n], 0, 0, 0);
+        }
       }
     }
-    lpart = fmaf(lpart, alpha, psum);
-    m = mn;
+#pragma unroll
+    for (int u = 0; u < QS; ++u) {
+      lpart[u] = fmaf(lpart[u], alpha[u], psum[u]);
+      m[u] = mn[u];
+    }
   }
 
-  float lt = lpart + __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(lpart), 0x401F));
-  lt += shfl_xor_f(lt, 32);
-  if (iq < L) {
-    const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
-    float* orow = O + ((size_t)iq * Hq + hq) * D;
 #pragma unroll
-    for (int n = 0; n < NB; ++n)
-      *reinterpret_cast<float4*>(orow + 16 * n + 4 * g) =
-          make_float4(acc[n][0] * inv, acc[n][1] * inv, acc[n][2] * inv, acc[n][3] * inv);
-    if (g == 0) {
-      lout[(size_t)iq * Hq + hq] = lt;
-      mout[(size_t)iq * Hq + hq] = lt > 0.0f ? m * scale : kNegInf;
+  for (int u = 0; u < QS; ++u) {
+    float lt = lpart[u] + __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(lpart[u]), 0x401F));
+    lt += shfl_xor_f(lt, 32);
+    if (iq[u] < L) {
+      const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+      float* orow = O + ((size_t)iq[u] * Hq + hq) * D;
+#pragma unroll
+      for (int n = 0; n < NB; ++n)
+        *reinterpret_cast<float4*>(orow + 16 * n + 4 * g) =
+            make_float4(acc[u][n][0] * inv, acc[u][n][1] * inv, acc[u][n][2] * inv, acc[u][n][3] * inv);
+      if (g == 0) {
+        lout[(size_t)iq[u] * Hq + hq] = lt;
+        mout[(size_t)iq[u] * Hq + hq] = lt > 0.0f ? m[u] * scale : kNegInf;
+      }
     }
   }
 }
@@ -196,14 +269,15 @@ extern "C" int dsa_block_sparse_prefill(const void* q, const void* k, const void
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(O)) return DSA_ERR_ALIGN;
   const int sink = stream_cfg ? stream_cfg->sink : 0, local = stream_cfg ? stream_cfg->local : 0;
   const float c = scale * kLog2e;
-  const dim3 grid((L + kPfTile - 1) / kPfTile, n_q_heads);
+  constexpr int NWQ = DSA_PREFILL_WAVES, QS = DSA_PREFILL_QSETS, QT = 16 * QS * NWQ;
+  const dim3 grid((L + QT - 1) / QT, n_q_heads);
   hipStream_t st = (hipStream_t)stream;
   if (head_dim == 128)
-    hipLaunchKernelGGL((prefill_kernel<128>), grid, dim3(256), 0, st, (const uint16_t*)q, (const uint16_t*)k,
+    hipLaunchKernelGGL((prefill_kernel<128, NWQ, QS>), grid, dim3(NWQ * 64), 0, st, (const uint16_t*)q, (const uint16_t*)k,
                        (const uint16_t*)v, (int)L, (int)n_q_heads, (int)n_kv_heads, (unsigned long long)smask, sink,
                        local, scale, c, O, l, m);
   else
-    hipLaunchKernelGGL((prefill_kernel<64>), grid, dim3(256), 0, st, (const uint16_t*)q, (const uint16_t*)k,
+    hipLaunchKernelGGL((prefill_kernel<64, NWQ, QS>), grid, dim3(NWQ * 64), 0, st, (const uint16_t*)q, (const uint16_t*)k,
                        (const uint16_t*)v, (int)L, (int)n_q_heads, (int)n_kv_heads, (unsigned long long)smask, sink,
                        local, scale, c, O, l, m);
   return launch_status();
