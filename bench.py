@@ -65,6 +65,8 @@ def parse():
     ap.add_argument("--replicas", type=int, default=0, help="0 = enough for > 1 GiB per rotation")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU oracle sample")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--delta-profile", action="store_true",
+                    help="prr_512k: also run PRR's offline speculation-budget profile (4K-64K contexts)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run 10 plain device copies of BYTES (HBM counter calibration) and exit")
     return ap.parse_args()
@@ -435,10 +437,11 @@ def main():
         ops["prr_calibrate"] = lambda r: dsa.prr_calibrate(cal_trace, cal_nv, bt.topk, decs[r].k_spec, H=cal_H,
                                                            best=cal_best, ws=cal_ws)
         op_bytes["prr_calibrate"] = T_CAL * B * Hkv * N * 4
-        # section 3.4: the offline profile behind the speculation budget
-        from dynamic_sparse_attention_page_amd.prr import profile_delta_table
-        _, extra["prr_delta_profile"] = profile_delta_table(n_q_heads=Hq, n_kv_heads=Hkv, head_dim=D,
-                                                            page_size=bt.page_size)
+        if a.delta_profile:   # section 3.4: the offline profile behind the speculation budget (opt-in: it
+            # launches the attention kernels at other shapes, which would blend into their trace averages)
+            from dynamic_sparse_attention_page_amd.prr import profile_delta_table
+            _, extra["prr_delta_profile"] = profile_delta_table(n_q_heads=Hq, n_kv_heads=Hkv, head_dim=D,
+                                                                page_size=bt.page_size)
     elif bt.topk is None or a.workload == "tiny_f32":   # PSA (and the tiny workload: top-k and PSA)
         ids_p = torch.empty((B, Hkv, N), dtype=i32, device=dev)
         cnt_p = torch.empty((B, Hkv), dtype=i32, device=dev)
