@@ -75,7 +75,8 @@ def _load(path: str = LIB_PATH):
         "dsa_sparse_decode_attn_topk": (ctypes.c_int, [P, I32, KV, P, I32, ST, F32, P, P, P, P, P, P, SZ, P]),
         "dsa_attn_repair": (ctypes.c_int, [P, I32, KV, P, P, P, P, I32, F32, P, P, P, P, SZ, P]),
         "dsa_ema_predict_update": (ctypes.c_int, [P, P, P, P, I64, F32, F32, F32, I32, P]),
-        "dsa_prr_select": (ctypes.c_int, [P, I32, I32, I32, P, I32, I32, P, P, P, P, P, F32, F32, F32, I32, I32, P, P, P]),
+        "dsa_prr_select": (ctypes.c_int, [P, I32, I32, I32, P, I32, I32, P, P, P, P, P, F32, F32, F32, I32, I32, P, P,
+                                          P, P, P, P, P]),
         "dsa_prr_calibrate": (ctypes.c_int, [P, I32, I32, I32, P, I32, I32, P, P, P, SZ, P]),
         "dsa_prr_calibrate_workspace_bytes": (SZ, [I32, I32, I32]),
         "dsa_signal_host": (ctypes.c_int, [P, I32, P, P, I32, P]),
@@ -337,10 +338,13 @@ def sparse_decode_attn_topk(q: torch.Tensor, kv: PagedKV, scores: torch.Tensor, 
 
 def attn_repair(q: torch.Tensor, kv: PagedKV, a_ids, a_counts, p_ids, p_counts, O, l, m,
                 scale: float | None = None, ws: torch.Tensor | None = None):
-    """Fold attention over A \\ P into the speculative (O, l, m) in place."""
+    """Fold attention over A \\ P into the speculative (O, l, m) in place;
+    with p_ids = p_counts = None, a_ids is the missing set itself."""
     Hq = q.shape[1]
     stride = a_ids.shape[-1]
-    if p_ids.shape[-1] != stride:
+    if (p_ids is None) != (p_counts is None):
+        raise ValueError("give both p_ids and p_counts, or neither")
+    if p_ids is not None and p_ids.shape[-1] != stride:
         raise ValueError("a_ids and p_ids must share the same stride")
     need = workspace_bytes(OP_ATTN_REPAIR, kv, Hq, stride)
     if ws is None:
@@ -365,14 +369,18 @@ def ema_predict_update(is_true, level: torch.Tensor, trend: torch.Tensor, pred: 
 def prr_select(scores: torch.Tensor, seq_lens: torch.Tensor, page_size: int, k: int, level: torch.Tensor,
                trend: torch.Tensor, pred: torch.Tensor, alpha: float, beta: float, gamma: float, init: bool,
                k_spec: int, a_ids: torch.Tensor, a_counts: torch.Tensor, p_ids: torch.Tensor,
-               p_counts: torch.Tensor):
+               p_counts: torch.Tensor, p_cur: tuple | None = None, m_out: tuple | None = None):
     """A = top-k of scores; EMA update with scores; P = top-k_spec of the new
-    prediction -- one launch (see dsa_prr_select)."""
+    prediction -- one launch (see dsa_prr_select).  With p_cur = (ids, counts)
+    of this step's speculative set and m_out = (ids, counts), also the
+    missing set M = A \\ P_cur."""
     B, H, N = scores.shape
+    pc_i, pc_c = p_cur if p_cur is not None else (None, None)
+    m_i, m_c = m_out if m_out is not None else (None, None)
     _check("dsa_prr_select", lib.dsa_prr_select(
         _ptr(scores), B, H, N, _ptr(seq_lens), page_size, k, _ptr(a_ids), _ptr(a_counts), _ptr(level), _ptr(trend),
         _ptr(pred), float(alpha), float(beta), float(gamma), 1 if init else 0, k_spec, _ptr(p_ids), _ptr(p_counts),
-        _stream()))
+        _ptr(pc_i), _ptr(pc_c), _ptr(m_i), _ptr(m_c), _stream()))
     return a_ids, a_counts, p_ids, p_counts
 
 

@@ -39,7 +39,8 @@ struct SelectArgs {
   int k;
   int32_t* ids_out;
   int32_t* counts_out;
-  int e;   // scores per thread: max_pages <= 256 * e
+  int e;      // scores per thread: max_pages <= 256 * e
+  int fine;   // split as finely as possible: the ids are a short prefix of a long row
 };
 
 // ============================================================ split-KV partial
@@ -429,11 +430,14 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(
 #pragma unroll
   for (int x = 0; x < CPT; ++x) acc[x] = 0.0f;
   constexpr int NB = 8;   // splits per batch and wave: all loads of a batch are in flight together
-  for (int s0 = wave; s0 < n_splits; s0 += 4 * NB) {
+  // one batch covers up to 4 * NB splits without waiting for the count;
+  // beyond that only the active splits are visited
+  const int lim = n_splits <= 4 * NB ? n_splits : active;
+  for (int s0 = wave; s0 < lim; s0 += 4 * NB) {
     float ms[NB], lsp[NB], os[NB][CPT];
 #pragma unroll
     for (int u = 0; u < NB; ++u) {
-      const int sp = min(s0 + 4 * u, n_splits - 1);   // in bounds; duplicates are masked below
+      const int sp = min(s0 + 4 * u, max(lim, 1) - 1);   // in bounds; duplicates are masked below
       const size_t pi = ((size_t)unit * n_splits + sp) * G + g;
       ms[u] = part_ml[pi * 2];
       lsp[u] = part_ml[pi * 2 + 1];
@@ -794,7 +798,11 @@ static int launch_attn_g(const void* q, const dsa_kv* kv, const int32_t* ids, co
                          int ids_stride, uint64_t smask, int sink, int local, float scale, float* O, float* l,
                          float* m, void* ws, int fold, const int32_t* skip_ids, const int32_t* skip_counts,
                          const SelectArgs& sel, hipStream_t st) {
-  const SplitPlan p = plan_splits(kv, ids_stride, __builtin_popcountll(smask), G);
+  SplitPlan p = plan_splits(kv, ids_stride, __builtin_popcountll(smask), G);
+  if (sel.fine) {   // the smallest split: a short id list still spreads over many workgroups
+    p.tiles_per_split = 2 * kWgWaves;
+    p.n_splits = (int)max_splits_of(kv, ids_stride);
+  }
   const size_t units = (size_t)kv->batch * kv->n_kv_heads;
   float* part_o = (float*)ws;
   float* part_ml = (float*)((char*)ws + align256(units * max_splits_of(kv, ids_stride) * G * D * sizeof(float)));
@@ -986,14 +994,21 @@ extern "C" int dsa_attn_repair(const void* q, int32_t n_q_heads, const dsa_kv* k
   if (rc) return rc;
   if (ids_stride < 1) return DSA_ERR_SHAPE;
   if (kv->batch == 0) return DSA_OK;
-  if (!a_ids || !a_counts || !p_ids || !p_counts || !O || !l || !m) return DSA_ERR_NULL;
+  if (!a_ids || !a_counts || !O || !l || !m) return DSA_ERR_NULL;
+  if (!p_ids != !p_counts) return DSA_ERR_NULL;
   const size_t need = dsa_workspace_bytes(DSA_OP_ATTN_REPAIR, kv, n_q_heads, ids_stride);
   if (!ws || ws_bytes < need) return DSA_ERR_WORKSPACE;
   if (!aligned16(ws)) return DSA_ERR_ALIGN;
-  const size_t lds = (size_t)((kv->max_pages + 31) / 32) * sizeof(uint32_t);
-  if ((int)lds + 52 * 1024 > max_lds_per_block()) return DSA_ERR_UNSUPPORTED;
-  return launch_attn(q, G, kv, a_ids, a_counts, ids_stride, 0, 0, 0, scale, O, l, m, ws, 1, p_ids, p_counts,
-                     SelectArgs{}, (hipStream_t)stream);
+  if (p_ids) {
+    const size_t lds = (size_t)((kv->max_pages + 31) / 32) * sizeof(uint32_t);
+    if ((int)lds + 52 * 1024 > max_lds_per_block()) return DSA_ERR_UNSUPPORTED;
+  }
+  // without P the a_ids are M already (usually a short prefix of the row):
+  // the plain split-KV path at the finest split, folded
+  SelectArgs sel{};
+  sel.fine = p_ids ? 0 : 1;
+  return launch_attn(q, G, kv, a_ids, a_counts, ids_stride, 0, 0, 0, scale, O, l, m, ws, 1, p_ids, p_counts, sel,
+                     (hipStream_t)stream);
 }
 
 extern "C" int dsa_page_select_progressive(const void* q, int32_t n_q_heads, const dsa_kv* kv, const float* scores,

@@ -63,6 +63,9 @@ class PRRDecoder:
         self.scores = torch.empty((B, H, N), dtype=f32, device=dev)
         self.a_ids = torch.full((B, H, self.stride), -1, dtype=i32, device=dev)
         self.a_counts = torch.zeros((B, H), dtype=i32, device=dev)
+        # M^t = A^t \ P^t, written by the selection launch when |A| = |P|
+        self.m_ids = torch.full((B, H, self.stride), -1, dtype=i32, device=dev)
+        self.m_counts = torch.zeros((B, H), dtype=i32, device=dev)
         self._p = [(torch.full((B, H, self.stride), -1, dtype=i32, device=dev),
                     torch.zeros((B, H), dtype=i32, device=dev)) for _ in range(2)]
         self._cur = 0                      # buffer holding P^t of the coming step
@@ -121,16 +124,19 @@ class PRRDecoder:
             p_ids[..., :self.k_spec].copy_(ids)
             p_counts.copy_(counts)
 
-    def _select_and_predict(self, q, init: bool, buf: int):
+    def _select_and_predict(self, q, init: bool, buf: int, cur: int | None = None):
         """IS^t, A^t, the EMA update and P^{t+1} (into buffer buf): one
         score launch and one launch that runs both selections side by side
-        when |A| = |P|, else the separate calls."""
+        when |A| = |P| -- which also writes M^t = A^t \\ P^t when P^t is in
+        buffer cur -- else the separate calls."""
         if self.k == self.k_spec:
             page_score(q, self.kv, self.meta, self.lp, scores=self.scores)
             p_ids, p_counts = self._p[buf]
+            with_m = cur is not None
             prr_select(self.scores, self.kv.seq_lens, self.kv.page_size, self.k, self.level, self.trend,
                        self.pred.view(-1), self.alpha, self.beta, self.gamma, init, self.k_spec, self.a_ids,
-                       self.a_counts, p_ids, p_counts)
+                       self.a_counts, p_ids, p_counts, p_cur=self._p[cur] if with_m else None,
+                       m_out=(self.m_ids, self.m_counts) if with_m else None)
         else:
             self._select(q)
             self._predict_next(init=init, buf=buf)
@@ -152,7 +158,7 @@ class PRRDecoder:
             with torch.cuda.stream(self.side):
                 self.side.wait_event(fork)
                 if self.k == self.k_spec:
-                    self._select_and_predict(q, init=False, buf=nxt)   # IS^t, A^t, EMA, P^{t+1}
+                    self._select_and_predict(q, init=False, buf=nxt, cur=cur)   # IS^t, A^t, M^t, EMA, P^{t+1}
                     a_ready = torch.cuda.Event()
                     a_ready.record(self.side)
                     p_ready = a_ready
@@ -168,7 +174,11 @@ class PRRDecoder:
             p_ids, p_counts = self._p[cur]
             sparse_decode_attn(q, self.kv, p_ids, p_counts, scale=self.scale, out=out, ws=self.ws)
             main.wait_event(a_ready)
-            attn_repair(q, self.kv, self.a_ids, self.a_counts, p_ids, p_counts, *out, scale=self.scale, ws=self.ws)
+            if self.k == self.k_spec:   # M^t came with A^t
+                attn_repair(q, self.kv, self.m_ids, self.m_counts, None, None, *out, scale=self.scale, ws=self.ws)
+            else:
+                attn_repair(q, self.kv, self.a_ids, self.a_counts, p_ids, p_counts, *out, scale=self.scale,
+                            ws=self.ws)
             self._p_ready = p_ready
         self._cur = nxt
         self.t += 1

@@ -289,6 +289,8 @@ int dsa_sparse_decode_attn_topk(const void *q, int32_t n_q_heads, const dsa_kv *
  * so the result is attention over P u A.  KV traffic scales with |M|; each
  * workgroup of the split over A also reads p_ids once into an LDS bitmap of
  * max_pages bits (DSA_ERR_UNSUPPORTED if that bitmap does not fit in LDS).
+ * p_ids and p_counts may both be NULL: then a_ids already lists M (as
+ * dsa_prr_select writes it) and is attended as it is.
  * a_ids, p_ids: device int32 [batch][n_kv_heads][ids_stride] with page ids
  * < max_pages.  Streaming heads are not supported here.
  * ws: device scratch of dsa_workspace_bytes(DSA_OP_ATTN_REPAIR, ...).
@@ -326,7 +328,13 @@ int dsa_ema_predict_update(const float *is_true, float *level, float *trend, flo
  *                          alpha, beta, gamma, init)
  *   dsa_page_select_topk(pred, ..., k_spec, NULL, p_ids, p_counts)
  * as two launches: the elementwise EMA update over the whole GPU, then one
- * grid in which the two selections run side by side.
+ * grid in which the two selections run side by side.  With m_ids non-NULL
+ * the call also writes the repair's missing set ([PRR] section 3.4)
+ * M^t = A^t \ P^t, where P^t = p_cur_ids[b][h][0..p_cur_counts) (row
+ * stride k_spec) is this step's speculative set: m_ids int32
+ * [batch][n_kv_heads][k] ascending, -1 padded, m_counts[b][h] = |M|.
+ * p_cur_ids/p_cur_counts must not be p_ids/p_counts; all four M pointers may
+ * be NULL.
  * scores: IS^t, device float [batch][n_kv_heads][max_pages]; level, trend,
  * pred: device float arrays of the same shape, distinct; a_ids: int32
  * [batch][n_kv_heads][k]; p_ids: int32 [batch][n_kv_heads][k_spec]; ids
@@ -336,7 +344,8 @@ int dsa_prr_select(const float *scores, int32_t batch, int32_t n_kv_heads, int32
                    const int32_t *seq_lens, int32_t page_size, int32_t k, int32_t *a_ids,
                    int32_t *a_counts, float *level, float *trend, float *pred, float alpha,
                    float beta, float gamma, int32_t init, int32_t k_spec, int32_t *p_ids,
-                   int32_t *p_counts, void *stream);
+                   int32_t *p_counts, const int32_t *p_cur_ids, const int32_t *p_cur_counts,
+                   int32_t *m_ids, int32_t *m_counts, void *stream);
 
 /*
  * dsa_prr_calibrate -- PRR online predictor calibration ([PRR] section 3.2:

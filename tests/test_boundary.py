@@ -131,6 +131,14 @@ def test_validation_errors(dsa):
     assert L.dsa_block_sparse_prefill(ok_ptr, ok_ptr, ok_ptr, 64, 8, 4, 128, None, F(0.1), None, ok_ptr, ok_ptr,
                                       None) == -1
     assert L.dsa_block_sparse_prefill(None, None, None, 0, 8, 4, 128, None, F(0.1), None, None, None, None) == 0
+    # PRR selection: missing set without this step's P, or with P aliasing the next one
+    args = [ok_ptr, 1, 2, 64, ok_ptr, 16, 8, ok_ptr, ok_ptr, P(8192), P(12288), P(16384), F(0.6), F(0.3), F(0.25), 0, 8,
+            ok_ptr, ok_ptr]
+    assert L.dsa_prr_select(*args, None, None, ok_ptr, ok_ptr, None) == -1
+    assert L.dsa_prr_select(*args, ok_ptr, P(20480), ok_ptr, ok_ptr, None) == -2
+    # repair: P ids without counts
+    assert L.dsa_attn_repair(ok_ptr, 4, ctypes.byref(kv), ok_ptr, ok_ptr, ok_ptr, None, 8, F(0.088), ok_ptr, ok_ptr,
+                             ok_ptr, ok_ptr, 1 << 30, None) == -1
     # host signal: negative count, missing flag or destination
     assert L.dsa_signal_host(ok_ptr, -1, ok_ptr, ok_ptr, 1, None) == -2
     assert L.dsa_signal_host(ok_ptr, 4, ok_ptr, None, 1, None) == -1

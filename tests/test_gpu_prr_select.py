@@ -53,3 +53,27 @@ def test_prr_select_matches_separate_calls(gpu_lib, max_pages, k, k_spec):
             for h in range(H):
                 assert np.array_equal(np_(a1)[b, h, :np_(ac1)[b, h]], oracle.topk_pages(scn[b, h], n_valid, k))
                 assert np.array_equal(np_(p1)[b, h, :np_(pc1)[b, h]], oracle.topk_pages(prn[b, h], n_valid, k_spec))
+        # with this step's speculative set: M = A \ P_cur, the rest unchanged
+        hr = np.random.default_rng(11)
+        pcur = np.full((B, H, k_spec), -1, np.int32)
+        pcnt = np.zeros((B, H), np.int32)
+        for b in range(B):
+            n_valid = oracle.n_pages(bt.seq_lens[b], P)
+            for h in range(H):
+                c = max(0, min(k_spec, n_valid) - 3)
+                pcur[b, h, :c] = np.sort(hr.choice(n_valid, c, replace=False))
+                pcnt[b, h] = c
+        lv3, tr3, pr3 = lvl0.clone(), trd0.clone(), torch.empty(B * H * N, device="cuda")
+        a3, ac3 = torch.empty_like(a1), torch.empty_like(ac1)
+        p3, pc3 = torch.empty_like(p1), torch.empty_like(pc1)
+        m3, mc3 = torch.full((B, H, k), -7, dtype=i32, device="cuda"), torch.empty((B, H), dtype=i32, device="cuda")
+        dsa.prr_select(sc, kv.seq_lens, P, k, lv3, tr3, pr3, 0.6, 0.3, 0.25, init, k_spec, a3, ac3, p3, pc3,
+                       p_cur=(torch.from_numpy(pcur).cuda(), torch.from_numpy(pcnt).cuda()), m_out=(m3, mc3))
+        torch.cuda.synchronize()
+        assert torch.equal(a3, a1) and torch.equal(ac3, ac1) and torch.equal(p3, p1) and torch.equal(pr3, pr1)
+        for b in range(B):
+            for h in range(H):
+                ref = oracle.missing_pages(np_(a1)[b, h, :np_(ac1)[b, h]], pcur[b, h, :pcnt[b, h]])
+                n = int(np_(mc3)[b, h])
+                assert n == len(ref) and np.array_equal(np_(m3)[b, h, :n], ref), f"M differs ({b}, {h})"
+                assert np.all(np_(m3)[b, h, n:] == -1)
