@@ -66,7 +66,7 @@ struct AttnWave {
   __device__ __forceinline__ static void load_tile(const T* __restrict__ tile, int lane_, uint32_t (&d)[4][DW]) {
     const int rr = lane_ >> 4, jj = lane_ & 15;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) load_dw<DW>(tile + (size_t)(4 * i + rr) * D + jj * CPL, d[i]);
+    for (int i = 0; i < 4; ++i) load_dw_kv<DW>(tile + (size_t)(4 * i + rr) * D + jj * CPL, d[i]);
   }
 
   // Token t (0..15) of the tile takes part iff t < nvalid and, for a

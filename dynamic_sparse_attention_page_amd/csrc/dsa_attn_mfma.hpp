@@ -75,12 +75,12 @@ struct MfmaWave {
   __device__ __forceinline__ static void load_k(const uint16_t* __restrict__ tile, int lane, uint4 (&kd)[NK]) {
     const int hh = lane & 15, gg = lane >> 4;
 #pragma unroll
-    for (int i = 0; i < NK; ++i) kd[i] = *reinterpret_cast<const uint4*>(tile + (size_t)hh * D + 32 * i + 8 * gg);
+    for (int i = 0; i < NK; ++i) kd[i] = ld16_kv(tile + (size_t)hh * D + 32 * i + 8 * gg);
   }
   // V flat: 16-byte chunk lane + 64i of the tile (fully coalesced).
   __device__ __forceinline__ static void load_v(const uint16_t* __restrict__ tile, int lane, uint4 (&vd)[NK]) {
 #pragma unroll
-    for (int i = 0; i < NK; ++i) vd[i] = reinterpret_cast<const uint4*>(tile)[lane + 64 * i];
+    for (int i = 0; i < NK; ++i) vd[i] = ld16_kv(reinterpret_cast<const uint4*>(tile) + lane + 64 * i);
   }
 
   __device__ __forceinline__ static bool tok_ok(int t, int nvalid, bool smask, int tok0, int L, int sink,

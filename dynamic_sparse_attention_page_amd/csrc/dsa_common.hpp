@@ -204,6 +204,49 @@ __device__ __forceinline__ void load_dw(const void* p, uint32_t* out) {
   }
 }
 
+// Non-temporal variants for data read once per call (page metadata, the
+// K/V rows of selected pages): the loads carry the streaming cache hint, so
+// they do not displace reused lines, and HBM serves them at a higher rate.
+using u32x2_t = unsigned int __attribute__((ext_vector_type(2)));
+using u32x4_t = unsigned int __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld16_stream(const void* p) {
+  const u32x4_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(x.x, x.y, x.z, x.w);
+}
+#ifndef DSA_KV_NT
+#define DSA_KV_NT 1  // 1: K/V rows of selected pages load with the non-temporal hint
+#endif
+template <int DW>
+__device__ __forceinline__ void load_dw_stream(const void* p, uint32_t* out) {
+  if constexpr (DW == 2) {
+    const u32x2_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+    out[0] = x.x; out[1] = x.y;
+  } else {
+#pragma unroll
+    for (int u = 0; u < DW / 4; ++u) {
+      const uint4 x = ld16_stream(reinterpret_cast<const uint4*>(p) + u);
+      out[4 * u + 0] = x.x; out[4 * u + 1] = x.y; out[4 * u + 2] = x.z; out[4 * u + 3] = x.w;
+    }
+  }
+}
+
+// Loads of K/V rows.
+template <int DW>
+__device__ __forceinline__ void load_dw_kv(const void* p, uint32_t* out) {
+#if DSA_KV_NT
+  load_dw_stream<DW>(p, out);
+#else
+  load_dw<DW>(p, out);
+#endif
+}
+__device__ __forceinline__ uint4 ld16_kv(const void* p) {
+#if DSA_KV_NT
+  return ld16_stream(p);
+#else
+  return *reinterpret_cast<const uint4*>(p);
+#endif
+}
+
 // Channel c (0 <= c < CPL) of a lane's raw dwords as float.
 template <typename T>
 __device__ __forceinline__ float chan(const uint32_t* w, int c) {

@@ -9,15 +9,23 @@
 //   vector per KV head (here the mean of the group's q heads).
 //
 // Both kernels stream their input once with coalesced 16 B loads; the score
-// kernel is HBM-bound (one multiply-add per metadata element).
+// kernel is HBM-bound (one multiply-add per metadata element): its metadata
+// loads carry the non-temporal hint and are software-pipelined (the next
+// rows load while the current rows are scored).
 #include "dsa_common.hpp"
 #include "dsa_host.hpp"
 
 #ifndef DSA_SCORE_LOADS
 #define DSA_SCORE_LOADS 8  // metadata loads in flight per lane
 #endif
+#ifndef DSA_SCORE_PIPE
+#define DSA_SCORE_PIPE 1  // 1: the next rows' loads overlap the current rows' scores
+#endif
 #ifndef DSA_SCORE_WAVES
 #define DSA_SCORE_WAVES 8192  // target waves of the score grid
+#endif
+#ifndef DSA_SCORE_NT
+#define DSA_SCORE_NT 1  // 1: metadata loads are non-temporal (read once per step)
 #endif
 
 namespace dsa {
@@ -153,9 +161,8 @@ __global__ __launch_bounds__(256) void score_kernel(
   }
   const size_t head_stride = (size_t)GL * 2 * D;  // elements of one (slot, head) metadata block
   const int n_pairs = ((j1 - j0) * GL + 3) / 4;    // uniform
-  for (int u0 = 0; u0 < n_pairs; u0 += U) {
-    uint32_t wmin[U][DW], wmax[U][DW];
-    bool ok[U];
+  // loads of U rows (kmin and kmax per lane) ...
+  auto issue = [&](int u0, uint32_t (&wmin)[U][DW], uint32_t (&wmax)[U][DW], bool (&ok)[U]) {
 #pragma unroll
     for (int uu = 0; uu < U; ++uu) {
       if (u0 + uu >= n_pairs) break;                 // uniform: no loads past the range
@@ -166,9 +173,17 @@ __global__ __launch_bounds__(256) void score_kernel(
       ok[uu] = pg < j1 && pg < np && slot >= 0 && slot < num_slots && pg * P + sub * Pl < L;
       const T* src = ok[uu] ? meta + ((size_t)slot * n_kv_heads + h) * head_stride + (size_t)sub * 2 * D + cg * CPL
                             : meta + cg * CPL;        // valid address, result discarded
+#if DSA_SCORE_NT
+      load_dw_stream<DW>(src, wmin[uu]);
+      load_dw_stream<DW>(src + D, wmax[uu]);
+#else
       load_dw<DW>(src, wmin[uu]);
       load_dw<DW>(src + D, wmax[uu]);
+#endif
     }
+  };
+  // ... and their scores
+  auto consume = [&](int u0, const uint32_t (&wmin)[U][DW], const uint32_t (&wmax)[U][DW], const bool (&ok)[U]) {
 #pragma unroll
     for (int uu = 0; uu < U; ++uu) {
       if (u0 + uu >= n_pairs) break;
@@ -190,7 +205,27 @@ __global__ __launch_bounds__(256) void score_kernel(
       const bool writer = cg == 0 && (r % GL) == 0;
       if (writer && j0 + pl < j1) srow[j0 + pl] = sc;
     }
+  };
+#if DSA_SCORE_PIPE
+  // two register sets: the next U rows are loading while the current are scored
+  uint32_t amin[U][DW], amax[U][DW], bmin[U][DW], bmax[U][DW];
+  bool aok[U], bok[U];
+  issue(0, amin, amax, aok);
+  for (int u0 = 0; u0 < n_pairs; u0 += 2 * U) {
+    if (u0 + U < n_pairs) issue(u0 + U, bmin, bmax, bok);
+    consume(u0, amin, amax, aok);
+    if (u0 + U >= n_pairs) break;
+    if (u0 + 2 * U < n_pairs) issue(u0 + 2 * U, amin, amax, aok);
+    consume(u0 + U, bmin, bmax, bok);
   }
+#else
+  for (int u0 = 0; u0 < n_pairs; u0 += U) {
+    uint32_t wmin[U][DW], wmax[U][DW];
+    bool ok[U];
+    issue(u0, wmin, wmax, ok);
+    consume(u0, wmin, wmax, ok);
+  }
+#endif
 }
 
 }  // namespace dsa
