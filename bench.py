@@ -410,6 +410,7 @@ def main():
         extra["prr_miss_rate"] = {"mean": miss_rate, "min": float(np.min(miss)), "max": float(np.max(miss))}
         kvb = page_kv_bytes(bt, bt.topk, B * Hkv)
         step_bytes = mb + kvb + miss_rate * kvb + B * Hkv * N * (24 + 8)
+        sel_ws = torch.empty(dsa.prr_select_workspace_bytes(B, Hkv, N), dtype=torch.uint8, device=dev)
         ops = {
             "page_score": lambda r: dsa.page_score(q, kvs[r], meta, scores=decs[r].scores),
             "page_select_topk": lambda r: dsa.page_select_topk(decs[r].scores, kvs[r].seq_lens, bt.page_size,
@@ -423,7 +424,12 @@ def main():
             "prr_select": lambda r: dsa.prr_select(decs[r].scores, kvs[r].seq_lens, bt.page_size, bt.topk,
                                                    decs[r].level, decs[r].trend, decs[r].pred, a_, b_, g_, False,
                                                    decs[r].k_spec, decs[r].a_ids, decs[r].a_counts,
-                                                   decs[r].p_ids, decs[r].p_counts),
+                                                   decs[r].p_ids, decs[r].p_counts, split=False),
+            # the same call with a workspace: the split-row selection (many CUs)
+            "prr_select_split": lambda r: dsa.prr_select(decs[r].scores, kvs[r].seq_lens, bt.page_size, bt.topk,
+                                                         decs[r].level, decs[r].trend, decs[r].pred, a_, b_, g_,
+                                                         False, decs[r].k_spec, decs[r].a_ids, decs[r].a_counts,
+                                                         decs[r].p_ids, decs[r].p_counts, ws=sel_ws),
         }
         op_bytes = {"page_score": mb, "sparse_decode_attn": kvb, "ema_predict_update": B * Hkv * N * 24}
         # online calibration of (alpha, beta, gamma) over the 80-candidate grid

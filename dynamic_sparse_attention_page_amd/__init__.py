@@ -21,7 +21,7 @@ __all__ = [
     "page_meta_build", "kv_append", "page_score", "page_select_topk", "page_select_progressive",
     "sparse_decode_attn", "sparse_decode_attn_topk", "attn_repair", "ema_predict_update", "prr_select", "prr_calibrate", "signal_host", "block_sparse_prefill",
     "workspace_bytes",
-    "OP_SPARSE_DECODE_ATTN", "OP_ATTN_REPAIR", "EXPORTED",
+    "OP_SPARSE_DECODE_ATTN", "OP_ATTN_REPAIR", "EXPORTED", "prr_select_workspace_bytes",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsa.so")
@@ -31,7 +31,8 @@ OP_SPARSE_DECODE_ATTN, OP_ATTN_REPAIR = 1, 2
 EXPORTED = (
     "dsa_status_str", "dsa_version", "dsa_page_meta_build", "dsa_kv_append", "dsa_page_score", "dsa_page_select_topk",
     "dsa_page_select_progressive", "dsa_sparse_decode_attn", "dsa_sparse_decode_attn_topk", "dsa_attn_repair",
-    "dsa_ema_predict_update", "dsa_prr_select", "dsa_prr_calibrate", "dsa_prr_calibrate_workspace_bytes",
+    "dsa_ema_predict_update", "dsa_prr_select", "dsa_prr_select_workspace_bytes", "dsa_prr_calibrate",
+    "dsa_prr_calibrate_workspace_bytes",
     "dsa_signal_host", "dsa_block_sparse_prefill",
     "dsa_workspace_bytes",
 )
@@ -76,7 +77,8 @@ def _load(path: str = LIB_PATH):
         "dsa_attn_repair": (ctypes.c_int, [P, I32, KV, P, P, P, P, I32, F32, P, P, P, P, SZ, P]),
         "dsa_ema_predict_update": (ctypes.c_int, [P, P, P, P, I64, F32, F32, F32, I32, P]),
         "dsa_prr_select": (ctypes.c_int, [P, I32, I32, I32, P, I32, I32, P, P, P, P, P, F32, F32, F32, I32, I32, P, P,
-                                          P, P, P, P, P]),
+                                          P, P, P, P, P, SZ, P]),
+        "dsa_prr_select_workspace_bytes": (SZ, [I32, I32, I32]),
         "dsa_prr_calibrate": (ctypes.c_int, [P, I32, I32, I32, P, I32, I32, P, P, P, SZ, P]),
         "dsa_prr_calibrate_workspace_bytes": (SZ, [I32, I32, I32]),
         "dsa_signal_host": (ctypes.c_int, [P, I32, P, P, I32, P]),
@@ -369,19 +371,31 @@ def ema_predict_update(is_true, level: torch.Tensor, trend: torch.Tensor, pred: 
 def prr_select(scores: torch.Tensor, seq_lens: torch.Tensor, page_size: int, k: int, level: torch.Tensor,
                trend: torch.Tensor, pred: torch.Tensor, alpha: float, beta: float, gamma: float, init: bool,
                k_spec: int, a_ids: torch.Tensor, a_counts: torch.Tensor, p_ids: torch.Tensor,
-               p_counts: torch.Tensor, p_cur: tuple | None = None, m_out: tuple | None = None):
+               p_counts: torch.Tensor, p_cur: tuple | None = None, m_out: tuple | None = None,
+               ws: torch.Tensor | None = None, split: bool = True):
     """A = top-k of scores; EMA update with scores; P = top-k_spec of the new
-    prediction -- one launch (see dsa_prr_select).  With p_cur = (ids, counts)
-    of this step's speculative set and m_out = (ids, counts), also the
-    missing set M = A \\ P_cur."""
+    prediction (see dsa_prr_select).  With p_cur = (ids, counts) of this
+    step's speculative set and m_out = (ids, counts), also the missing set
+    M = A \\ P_cur.  Long rows use the split-row selection with `ws` (a
+    shared scratch tensor when None); split=False passes no workspace, so
+    each row takes one workgroup."""
     B, H, N = scores.shape
     pc_i, pc_c = p_cur if p_cur is not None else (None, None)
     m_i, m_c = m_out if m_out is not None else (None, None)
+    nb = prr_select_workspace_bytes(B, H, N) if split else 0
+    if nb and ws is None:
+        ws = _workspace(nb, scores.device)
+    if not nb:
+        ws = None
     _check("dsa_prr_select", lib.dsa_prr_select(
         _ptr(scores), B, H, N, _ptr(seq_lens), page_size, k, _ptr(a_ids), _ptr(a_counts), _ptr(level), _ptr(trend),
         _ptr(pred), float(alpha), float(beta), float(gamma), 1 if init else 0, k_spec, _ptr(p_ids), _ptr(p_counts),
-        _ptr(pc_i), _ptr(pc_c), _ptr(m_i), _ptr(m_c), _stream()))
+        _ptr(pc_i), _ptr(pc_c), _ptr(m_i), _ptr(m_c), _ptr(ws), ws.numel() if ws is not None else 0, _stream()))
     return a_ids, a_counts, p_ids, p_counts
+
+
+def prr_select_workspace_bytes(batch: int, n_kv_heads: int, max_pages: int) -> int:
+    return int(lib.dsa_prr_select_workspace_bytes(batch, n_kv_heads, max_pages))
 
 
 CALIB_CANDIDATES = 80

@@ -26,6 +26,15 @@
 #ifndef DSA_SPLIT_TARGET
 #define DSA_SPLIT_TARGET 384  // target workgroups of the split-KV grid
 #endif
+#ifndef DSA_MFMA_SPLIT_DIV
+#define DSA_MFMA_SPLIT_DIV 2  // the matrix-core grid targets DSA_SPLIT_TARGET / this
+#endif
+#ifndef DSA_MFMA_DEPTH
+#define DSA_MFMA_DEPTH 2  // K/V tiles in flight per wave (matrix-core kernel)
+#endif
+#ifndef DSA_COMBINE_NB
+#define DSA_COMBINE_NB 8  // splits per batch and wave in the combine
+#endif
 
 namespace dsa {
 
@@ -334,8 +343,6 @@ __global__ __launch_bounds__(256) void attn_partial_mfma_kernel(
   const size_t slot_stride = (size_t)n_kv_heads * P * D;
   const size_t head_off = (size_t)h * P * D;
 
-  uint4 ka[NK], va[NK], kb[NK], vb[NK];
-  int nva = 0, tka = 0, nvb = 0, tkb = 0;
   auto fetch = [&](int t, uint4 (&kd)[NK], uint4 (&vd)[NK], int& nvalid, int& tok0) {
     nvalid = 0;
     tok0 = 0;
@@ -350,16 +357,23 @@ __global__ __launch_bounds__(256) void attn_partial_mfma_kernel(
     M::load_k(k + off, lane, kd);
     M::load_v(v + off, lane, vd);
   };
-  int t = t_begin + wave;
-  fetch(t, ka, va, nva, tka);
-  while (t < t_end) {
-    fetch(t + kWgWaves, kb, vb, nvb, tkb);
-    if (nva > 0) st.tile(ka, va, nva, smask, tka, L, sink, local, c);
-    t += kWgWaves;
-    if (t >= t_end) break;
-    fetch(t + kWgWaves, ka, va, nva, tka);
-    if (nvb > 0) st.tile(kb, vb, nvb, smask, tkb, L, sink, local, c);
-    t += kWgWaves;
+  // a ring of DEPTH tiles per wave: slot d is refilled right after its tile
+  // is computed, so DEPTH - 1 loads stay in flight behind the computation
+  constexpr int DEPTH = DSA_MFMA_DEPTH;
+  uint4 kr[DEPTH][NK], vr[DEPTH][NK];
+  int nv[DEPTH], tk[DEPTH];
+  const int t0 = t_begin + wave;
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) fetch(t0 + d * kWgWaves, kr[d], vr[d], nv[d], tk[d]);
+  for (int t = t0; t < t_end; t += DEPTH * kWgWaves) {
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+      const int td = t + d * kWgWaves;
+      if (td < t_end) {
+        if (nv[d] > 0) st.tile(kr[d], vr[d], nv[d], smask, tk[d], L, sink, local, c);
+        fetch(td + DEPTH * kWgWaves, kr[d], vr[d], nv[d], tk[d]);
+      }
+    }
   }
 
   // wave states meet in LDS: lane holds O[head h][16n + 4g + j]
@@ -429,7 +443,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(
   float mw = kNegInf, lw = 0.0f, acc[CPT];
 #pragma unroll
   for (int x = 0; x < CPT; ++x) acc[x] = 0.0f;
-  constexpr int NB = 8;   // splits per batch and wave: all loads of a batch are in flight together
+  constexpr int NB = DSA_COMBINE_NB;   // splits per batch and wave: all loads of a batch are in flight together
   // one batch covers up to 4 * NB splits without waiting for the count;
   // beyond that only the active splits are visited
   const int lim = n_splits <= 4 * NB ? n_splits : active;
@@ -763,7 +777,7 @@ struct SplitPlan {
 // attention).
 inline SplitPlan plan_splits(const dsa_kv* kv, int ids_stride, int n_streaming_heads, int G) {
   SplitPlan p;
-  const long long target = G >= 8 ? DSA_SPLIT_TARGET / 2 : DSA_SPLIT_TARGET;
+  const long long target = G >= 8 ? DSA_SPLIT_TARGET / DSA_MFMA_SPLIT_DIV : DSA_SPLIT_TARGET;
   p.TPP = kv->page_size / 16;
   const long long tiles_max = (long long)ids_stride * p.TPP;
   const int dense_heads = kv->n_kv_heads - n_streaming_heads;

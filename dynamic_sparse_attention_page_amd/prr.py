@@ -10,10 +10,14 @@ result with the pages of A that P missed (section 3.3), and feeds the new
 scores back into the predictor.
 
 The predictor update and the next step's speculative set P^{t+1} depend
-only on this step's scores IS^t, not on attention or on A^t, so one launch
+only on this step's scores IS^t, not on attention or on A^t, so one call
 (dsa_prr_select) selects A^t and, in other workgroups of the same grid,
 updates the EMA and selects P^{t+1}; the caller's stream waits for P^{t+1}
-only at the next step's speculative attention.  P is
+only at the next step's speculative attention.  The call gets no
+workspace, so each row's selections take one workgroup each: the split-row
+selection would be faster on its own, but it spreads over many CUs, and
+beside the speculative attention the step is faster with the selection
+kept to a few CUs.  P is
 double-buffered: the side stream writes P^{t+1} while the caller's stream
 still reads P^t.
 
@@ -136,7 +140,7 @@ class PRRDecoder:
             prr_select(self.scores, self.kv.seq_lens, self.kv.page_size, self.k, self.level, self.trend,
                        self.pred.view(-1), self.alpha, self.beta, self.gamma, init, self.k_spec, self.a_ids,
                        self.a_counts, p_ids, p_counts, p_cur=self._p[cur] if with_m else None,
-                       m_out=(self.m_ids, self.m_counts) if with_m else None)
+                       m_out=(self.m_ids, self.m_counts) if with_m else None, split=False)
         else:
             self._select(q)
             self._predict_next(init=init, buf=buf)

@@ -327,8 +327,7 @@ int dsa_ema_predict_update(const float *is_true, float *level, float *trend, flo
  *   dsa_ema_predict_update(scores, level, trend, pred, batch*n_kv_heads*max_pages,
  *                          alpha, beta, gamma, init)
  *   dsa_page_select_topk(pred, ..., k_spec, NULL, p_ids, p_counts)
- * as two launches: the elementwise EMA update over the whole GPU, then one
- * grid in which the two selections run side by side.  With m_ids non-NULL
+ * as two launches (see ws below for how they are split).  With m_ids non-NULL
  * the call also writes the repair's missing set ([PRR] section 3.4)
  * M^t = A^t \ P^t, where P^t = p_cur_ids[b][h][0..p_cur_counts) (row
  * stride k_spec) is this step's speculative set: m_ids int32
@@ -339,13 +338,28 @@ int dsa_ema_predict_update(const float *is_true, float *level, float *trend, flo
  * pred: device float arrays of the same shape, distinct; a_ids: int32
  * [batch][n_kv_heads][k]; p_ids: int32 [batch][n_kv_heads][k_spec]; ids
  * ascending, -1 padded.  No streaming heads.  max_pages <= 65536.
+ * ws: device scratch of dsa_prr_select_workspace_bytes(batch, n_kv_heads,
+ * max_pages) bytes (16-byte aligned), or NULL.  Rows longer than 4096 pages
+ * given a workspace are split into chunks of 2048 pages, one workgroup each,
+ * in two launches (chunk histograms, then the cut and the writes; the EMA
+ * update happens inside them); otherwise, and always without a workspace,
+ * one workgroup takes a whole row after the elementwise EMA launch.  The
+ * results are the same either way.  DSA_ERR_WORKSPACE if ws is given but
+ * smaller than required.
  */
 int dsa_prr_select(const float *scores, int32_t batch, int32_t n_kv_heads, int32_t max_pages,
                    const int32_t *seq_lens, int32_t page_size, int32_t k, int32_t *a_ids,
                    int32_t *a_counts, float *level, float *trend, float *pred, float alpha,
                    float beta, float gamma, int32_t init, int32_t k_spec, int32_t *p_ids,
                    int32_t *p_counts, const int32_t *p_cur_ids, const int32_t *p_cur_counts,
-                   int32_t *m_ids, int32_t *m_counts, void *stream);
+                   int32_t *m_ids, int32_t *m_counts, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * dsa_prr_select_workspace_bytes -- scratch bytes dsa_prr_select uses for
+ * rows of max_pages pages (0 when its rows are short enough for one
+ * workgroup each, or the shape is invalid).
+ */
+size_t dsa_prr_select_workspace_bytes(int32_t batch, int32_t n_kv_heads, int32_t max_pages);
 
 /*
  * dsa_prr_calibrate -- PRR online predictor calibration ([PRR] section 3.2:

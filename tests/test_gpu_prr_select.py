@@ -1,6 +1,6 @@
-"""GPU parity of dsa_prr_select (A^t, the EMA update and P^{t+1} in one
-launch) against the calls it stands for: dsa_page_select_topk on the
-scores, dsa_ema_predict_update, dsa_page_select_topk on the prediction.
+"""GPU parity of dsa_prr_select (A^t, the EMA update and P^{t+1}) against
+the calls it stands for: dsa_page_select_topk on the scores,
+dsa_ema_predict_update, dsa_page_select_topk on the prediction.
 ids and counts bit-exact; level, trend and pred equal to the separate EMA
 call (same float arithmetic); and the selections exact against the oracle
 on the GPU's own scores / predictions."""
@@ -77,3 +77,90 @@ def test_prr_select_matches_separate_calls(gpu_lib, max_pages, k, k_spec):
                 n = int(np_(mc3)[b, h])
                 assert n == len(ref) and np.array_equal(np_(m3)[b, h, :n], ref), f"M differs ({b}, {h})"
                 assert np.all(np_(m3)[b, h, n:] == -1)
+
+
+def _prr_run(dsa, sc, lens_t, P, k, k_spec, lvl0, trd0, init, pcur, pcnt, split):
+    B, H, N = sc.shape
+    i32 = torch.int32
+    lv, tr, pr = lvl0.clone(), trd0.clone(), torch.empty(B * H * N, device="cuda")
+    a, ac = torch.full((B, H, k), -7, dtype=i32, device="cuda"), torch.empty((B, H), dtype=i32, device="cuda")
+    p, pc = torch.full((B, H, k_spec), -7, dtype=i32, device="cuda"), torch.empty((B, H), dtype=i32, device="cuda")
+    m, mc = torch.full((B, H, k), -7, dtype=i32, device="cuda"), torch.empty((B, H), dtype=i32, device="cuda")
+    dsa.prr_select(sc, lens_t, P, k, lv, tr, pr, 0.6, 0.3, 0.25, init, k_spec, a, ac, p, pc,
+                   p_cur=(pcur, pcnt), m_out=(m, mc), split=split)
+    torch.cuda.synchronize()
+    return {n: np_(t) for n, t in (("a", a), ("ac", ac), ("p", p), ("pc", pc), ("m", m), ("mc", mc), ("lv", lv),
+                                   ("tr", tr), ("pr", pr))}
+
+
+@pytest.mark.parametrize("kind", ["normal", "few_values", "all_equal", "infinities"])
+def test_prr_select_split_rows(gpu_lib, kind):
+    """Long rows (over 4096 pages) take the split-row selection when a
+    workspace is given: 2048-page chunks over many workgroups, the cut from
+    the bucket holding the k-th score.  Its A, P, M, counts and EMA state
+    equal the one-workgroup path's bit for bit and the oracle's top-k, on
+    ragged rows (a partial last chunk, a 1-page row, an empty row, budgets
+    above the valid count) and on scores with long runs of ties (few
+    distinct values, all equal: the cut then falls among thousands of equal
+    keys), and with +-inf scores."""
+    dsa = gpu_lib
+    print(f"[case] prr_select split rows kind={kind}", flush=True)
+    P, N = 16, 20000
+    lens = [P * N, P * 12345 + 3, 5, 0]
+    B, H = len(lens), 2
+    k, k_spec = 1500, 1200
+    rng = np.random.default_rng(123)
+    if kind == "normal":
+        s = rng.standard_normal((B, H, N)).astype(np.float32)
+    elif kind == "few_values":
+        s = rng.integers(0, 4, (B, H, N)).astype(np.float32)
+    elif kind == "all_equal":
+        s = np.full((B, H, N), 0.5, np.float32)
+    else:
+        s = rng.standard_normal((B, H, N)).astype(np.float32)
+        s[:, :, ::97] = np.inf
+        s[:, :, 5::89] = -np.inf
+    sc = torch.from_numpy(s).cuda()
+    lens_t = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    lvl = rng.standard_normal(B * H * N).astype(np.float32)
+    trd = rng.standard_normal(B * H * N).astype(np.float32)
+    if kind == "all_equal":   # equal predictions too
+        lvl[:] = 0.25
+        trd[:] = 0.0
+    lvl0, trd0 = torch.from_numpy(lvl).cuda(), torch.from_numpy(trd).cuda()
+    pcur = np.full((B, H, k_spec), -1, np.int32)
+    pcnt = np.zeros((B, H), np.int32)
+    for b in range(B):
+        nv = oracle.n_pages(lens[b], P)
+        for h in range(H):
+            c = min(k_spec, nv)
+            pcur[b, h, :c] = np.sort(rng.choice(nv, c, replace=False))
+            pcnt[b, h] = c
+    pcur_t, pcnt_t = torch.from_numpy(pcur).cuda(), torch.from_numpy(pcnt).cuda()
+    for init in (False, True):
+        one = _prr_run(dsa, sc, lens_t, P, k, k_spec, lvl0, trd0, init, pcur_t, pcnt_t, split=False)
+        spl = _prr_run(dsa, sc, lens_t, P, k, k_spec, lvl0, trd0, init, pcur_t, pcnt_t, split=True)
+        for name in one:
+            assert np.array_equal(one[name], spl[name], equal_nan=True), f"{name} differs (init={init})"
+        # the EMA state and prediction: the oracle's float32 update, bit for bit
+        if init:
+            lv_ref, tr_ref, pr_ref = s.reshape(-1), np.zeros_like(trd), s.reshape(-1)
+        else:
+            lv_ref, tr_ref = oracle.ema_step_f32(s.reshape(-1), lvl, trd, 0.6, 0.3)
+            pr_ref = oracle.ema_predict_f32(lv_ref, tr_ref, 0.25)
+        assert np.array_equal(spl["lv"], lv_ref) and np.array_equal(spl["tr"], tr_ref)
+        assert np.array_equal(spl["pr"], pr_ref)
+        prn = pr_ref.astype(np.float64).reshape(B, H, N)
+        for b in range(B):
+            nv = oracle.n_pages(lens[b], P)
+            for h in range(H):
+                a = spl["a"][b, h, :spl["ac"][b, h]]
+                assert np.array_equal(a, oracle.topk_pages(s[b, h].astype(np.float64), nv, k))
+                assert np.all(spl["a"][b, h, spl["ac"][b, h]:] == -1)
+                p = spl["p"][b, h, :spl["pc"][b, h]]
+                assert np.array_equal(p, oracle.topk_pages(prn[b, h], nv, k_spec))
+                assert np.all(spl["p"][b, h, spl["pc"][b, h]:] == -1)
+                ref = oracle.missing_pages(a, pcur[b, h, :pcnt[b, h]])
+                n = int(spl["mc"][b, h])
+                assert n == len(ref) and np.array_equal(spl["m"][b, h, :n], ref)
+                assert np.all(spl["m"][b, h, n:] == -1)
