@@ -7,7 +7,8 @@ the library this script builds)
 
 Every csrc/*.hip file is compiled separately (in parallel) to an object under
 _build/, then linked into dynamic_sparse_attention_page_amd/libdsa.so.
-Packed-FP32 instructions are disabled for all device code.
+Packed-FP32 instructions are disabled for all device code; matrix-core
+instructions take their accumulators in VGPRs.
 """
 from __future__ import annotations
 
@@ -30,6 +31,10 @@ HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
     "-Wno-unused-command-line-argument",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core accumulators in ordinary VGPRs: the decode attention's
+    # online-softmax rescale then needs no per-tile copies out of and back
+    # into the accumulation registers
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
 

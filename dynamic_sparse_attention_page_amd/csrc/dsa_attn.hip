@@ -74,7 +74,8 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
   __shared__ float lds_ml[NWS][G][2];
 
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // the wave index is uniform: loop bounds and branches derived from it stay scalar
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int unit = b * n_kv_heads + h;
   const int TPP = P / 16;
   const int t_begin = split * tiles_per_split;
@@ -296,7 +297,8 @@ __global__ __launch_bounds__(256) void attn_partial_mfma_kernel(
   __shared__ float lds_ml[kWgWaves][G][2];
 
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // the wave index is uniform: loop bounds and branches derived from it stay scalar
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int unit = b * n_kv_heads + h;
   const int TPP = P / 16;
   const int t_begin = split * tiles_per_split;

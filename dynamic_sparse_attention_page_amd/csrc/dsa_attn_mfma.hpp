@@ -109,11 +109,14 @@ struct MfmaWave {
 #pragma unroll
     for (int i = 0; i < NK; ++i)
       s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kd[i]), qb[i], s, 0, 0, 0);
-    bool ok[4];
+    bool ok[4] = {true, true, true, true};
+    const bool partial = nvalid < 16 || smask;   // uniform: full tiles skip the token mask
+    if (partial) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      ok[j] = tok_ok(4 * g + j, nvalid, smask, tok0, L, sink, local);
-      if (!ok[j]) s[j] = kNegInf;
+      for (int j = 0; j < 4; ++j) {
+        ok[j] = tok_ok(4 * g + j, nvalid, smask, tok0, L, sink, local);
+        if (!ok[j]) s[j] = kNegInf;
+      }
     }
     float tm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
     tm = fmaxf(tm, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(tm), 0x401F)));  // lanes ^ 16
@@ -137,7 +140,7 @@ struct MfmaWave {
     }
     // masked tokens' V may be non-finite garbage: keep 0 * v finite
     uint32_t keep01 = 0xFFFFFFFFu, keep23 = 0xFFFFFFFFu;
-    if (nvalid < 16 || smask) {
+    if (partial) {
       keep01 = (ok[0] ? 0x0000FFFFu : 0u) | (ok[1] ? 0xFFFF0000u : 0u);
       keep23 = (ok[2] ? 0x0000FFFFu : 0u) | (ok[3] ? 0xFFFF0000u : 0u);
     }

@@ -40,7 +40,7 @@ __global__ __launch_bounds__(256) void meta_build_kernel(
     T* __restrict__ meta) {
   using L_ = Lay<T, D>;
   constexpr int CPL = L_::CPL, DW = L_::DW;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int b = blockIdx.z, h = blockIdx.y;
   const int j = first_page + blockIdx.x * 4 + wave;
   const int L = clamp_len(seq_lens[b], max_pages, P);
@@ -123,7 +123,7 @@ __global__ __launch_bounds__(256) void score_kernel(
   using L_ = Lay<T, D>;
   constexpr int CPL = L_::CPL, DW = L_::DW;
   constexpr int U = DSA_SCORE_LOADS / 2;     // load pairs in flight per lane
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int b = blockIdx.z, h = blockIdx.y;
   const int j0 = (blockIdx.x * 4 + wave) * pages_per_wave;
   if (j0 >= max_pages) return;
