@@ -18,7 +18,7 @@ import torch
 
 __all__ = [
     "DsaError", "PagedKV", "Streaming", "lib", "LIB_PATH",
-    "page_meta_build", "kv_append", "page_score", "page_select_topk", "page_select_progressive",
+    "page_meta_build", "kv_append", "page_score", "page_score_ema", "page_select_topk", "page_select_progressive",
     "sparse_decode_attn", "sparse_decode_attn_topk", "attn_repair", "ema_predict_update", "prr_select", "prr_calibrate", "signal_host", "block_sparse_prefill",
     "workspace_bytes",
     "OP_SPARSE_DECODE_ATTN", "OP_ATTN_REPAIR", "EXPORTED", "prr_select_workspace_bytes",
@@ -29,7 +29,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsa.so")
 DSA_F32, DSA_BF16 = 0, 1
 OP_SPARSE_DECODE_ATTN, OP_ATTN_REPAIR = 1, 2
 EXPORTED = (
-    "dsa_status_str", "dsa_version", "dsa_page_meta_build", "dsa_kv_append", "dsa_page_score", "dsa_page_select_topk",
+    "dsa_status_str", "dsa_version", "dsa_page_meta_build", "dsa_kv_append", "dsa_page_score", "dsa_page_score_ema",
+    "dsa_page_select_topk",
     "dsa_page_select_progressive", "dsa_sparse_decode_attn", "dsa_sparse_decode_attn_topk", "dsa_attn_repair",
     "dsa_ema_predict_update", "dsa_prr_select", "dsa_prr_select_workspace_bytes", "dsa_prr_calibrate",
     "dsa_prr_calibrate_workspace_bytes",
@@ -70,6 +71,7 @@ def _load(path: str = LIB_PATH):
         "dsa_page_meta_build": (ctypes.c_int, [KV, I32, P, I32, I32, P]),
         "dsa_kv_append": (ctypes.c_int, [KV, I32, P, P, P, P, P, P]),
         "dsa_page_score": (ctypes.c_int, [P, I32, KV, P, I32, ST, P, P]),
+        "dsa_page_score_ema": (ctypes.c_int, [P, I32, KV, P, I32, ST, P, P, P, P, F32, F32, F32, I32, P]),
         "dsa_page_select_topk": (ctypes.c_int, [P, I32, I32, I32, P, I32, I32, ST, P, P, P]),
         "dsa_page_select_progressive": (ctypes.c_int, [P, I32, KV, P, F32, I32, F32, P, P, P, P, P, P]),
         "dsa_sparse_decode_attn": (ctypes.c_int, [P, I32, KV, P, P, I32, ST, F32, P, P, P, P, SZ, P]),
@@ -256,6 +258,20 @@ def page_score(q: torch.Tensor, kv: PagedKV, meta: torch.Tensor, logical_page: i
     return scores
 
 
+def page_score_ema(q: torch.Tensor, kv: PagedKV, meta: torch.Tensor, level: torch.Tensor, trend: torch.Tensor,
+                   pred: torch.Tensor, alpha: float, beta: float, gamma: float, init: bool = False,
+                   logical_page: int | None = None, streaming: Streaming | None = None,
+                   scores: torch.Tensor | None = None) -> torch.Tensor:
+    """page_score with PRR's EMA update of level/trend/pred in the same launch."""
+    lp = logical_page or kv.page_size
+    if scores is None:
+        scores = torch.empty((kv.batch, kv.n_kv_heads, kv.max_pages), dtype=torch.float32, device=kv.k.device)
+    _check("dsa_page_score_ema", lib.dsa_page_score_ema(
+        _ptr(q), q.shape[1], ctypes.byref(kv.c()), _ptr(meta), lp, _stream_arg(streaming), _ptr(scores), _ptr(level),
+        _ptr(trend), _ptr(pred), float(alpha), float(beta), float(gamma), 1 if init else 0, _stream()))
+    return scores
+
+
 def page_select_topk(scores: torch.Tensor, seq_lens: torch.Tensor, page_size: int, k: int,
                      streaming: Streaming | None = None, ids: torch.Tensor | None = None,
                      counts: torch.Tensor | None = None):
@@ -368,15 +384,16 @@ def ema_predict_update(is_true, level: torch.Tensor, trend: torch.Tensor, pred: 
     return pred
 
 
-def prr_select(scores: torch.Tensor, seq_lens: torch.Tensor, page_size: int, k: int, level: torch.Tensor,
-               trend: torch.Tensor, pred: torch.Tensor, alpha: float, beta: float, gamma: float, init: bool,
+def prr_select(scores: torch.Tensor, seq_lens: torch.Tensor, page_size: int, k: int, level: torch.Tensor | None,
+               trend: torch.Tensor | None, pred: torch.Tensor, alpha: float, beta: float, gamma: float, init: bool,
                k_spec: int, a_ids: torch.Tensor, a_counts: torch.Tensor, p_ids: torch.Tensor,
                p_counts: torch.Tensor, p_cur: tuple | None = None, m_out: tuple | None = None,
                ws: torch.Tensor | None = None, split: bool = True):
     """A = top-k of scores; EMA update with scores; P = top-k_spec of the new
     prediction (see dsa_prr_select).  With p_cur = (ids, counts) of this
     step's speculative set and m_out = (ids, counts), also the missing set
-    M = A \\ P_cur.  Long rows use the split-row selection with `ws` (a
+    M = A \\ P_cur.  level = trend = None: pred already holds the updated
+    prediction (page_score_ema).  Long rows use the split-row selection with `ws` (a
     shared scratch tensor when None); split=False passes no workspace, so
     each row takes one workgroup."""
     B, H, N = scores.shape

@@ -7,6 +7,8 @@
 //   sum_c max(q_c*kmax_c, q_c*kmin_c), a physical page takes the max of its
 //   logical pages; PRR, section 5 -- with GQA the query is one representative
 //   vector per KV head (here the mean of the group's q heads).
+// page_score_ema: the same, with PRR's EMA update (section 3.1) applied to
+//   each page's new score in the lane that writes it.
 //
 // Both kernels stream their input once with coalesced 16 B loads; the score
 // kernel is HBM-bound (one multiply-add per metadata element): its metadata
@@ -105,6 +107,18 @@ __global__ __launch_bounds__(256) void meta_build_kernel(
   }
 }
 
+// PRR's EMA update fused into the score launch: the lane that writes a
+// page's score also updates its level and trend and writes the prediction
+// (the same float operations as dsa_ema_predict_update).  level == nullptr:
+// scores only.
+struct EmaArgs {
+  float* level;
+  float* trend;
+  float* pred;
+  float alpha, beta, gamma;
+  int init;
+};
+
 // ============================================================ page score
 // A wave walks a contiguous range of physical pages (one page-table load
 // for the whole range).  Row r of the wave takes logical page 4u + r of the
@@ -119,7 +133,7 @@ template <typename T, int D, int G, int GL>
 __global__ __launch_bounds__(256) void score_kernel(
     const T* __restrict__ q, const T* __restrict__ meta, const int32_t* __restrict__ page_table,
     const int32_t* __restrict__ seq_lens, int n_kv_heads, int P, int Pl, int max_pages, int num_slots,
-    unsigned long long streaming, int pages_per_wave, float* __restrict__ scores) {
+    unsigned long long streaming, int pages_per_wave, float* __restrict__ scores, EmaArgs ema) {
   using L_ = Lay<T, D>;
   constexpr int CPL = L_::CPL, DW = L_::DW;
   constexpr int U = DSA_SCORE_LOADS / 2;     // load pairs in flight per lane
@@ -132,8 +146,20 @@ __global__ __launch_bounds__(256) void score_kernel(
   const int L = clamp_len(seq_lens[b], max_pages, P);
   const int np = (L + P - 1) / P;
 
+  const size_t rowbase = ((size_t)b * n_kv_heads + h) * max_pages;
+  auto put = [&](int j, float sc) {
+    srow[j] = sc;
+    if (ema.level) {
+      const size_t x = rowbase + j;
+      float nl = sc, nt = 0.0f, pr = sc;
+      if (!ema.init) ema_step(sc, ema.level[x], ema.trend[x], ema.alpha, ema.beta, ema.gamma, nl, nt, pr);
+      ema.level[x] = nl;
+      ema.trend[x] = nt;
+      ema.pred[x] = pr;
+    }
+  };
   if ((streaming >> h) & 1ull) {
-    for (int j = j0 + lane; j < j1; j += 64) srow[j] = kNegInf;
+    for (int j = j0 + lane; j < j1; j += 64) put(j, kNegInf);
     return;
   }
   const int r = lane >> 4, cg = lane & 15;
@@ -203,7 +229,7 @@ __global__ __launch_bounds__(256) void score_kernel(
         sc = fmaxf(sc, __shfl_xor(sc, 32, 64));                                                     // rows ^2
       }
       const bool writer = cg == 0 && (r % GL) == 0;
-      if (writer && j0 + pl < j1) srow[j0 + pl] = sc;
+      if (writer && j0 + pl < j1) put(j0 + pl, sc);
     }
   };
 #if DSA_SCORE_PIPE
@@ -264,7 +290,7 @@ extern "C" int dsa_page_meta_build(const dsa_kv* kv, int32_t logical_page, void*
 
 template <typename T, int D, int G, int GL>
 static int launch_score_g(const void* q, const dsa_kv* kv, const void* meta, int Pl, uint64_t smask,
-                          float* scores, hipStream_t st) {
+                          float* scores, const EmaArgs& ema, hipStream_t st) {
   // Each wave walks a range of <= 64 physical pages (one page-table load);
   // aim for DSA_SCORE_WAVES waves over the grid.
   const long long units = (long long)kv->batch * kv->n_kv_heads;
@@ -278,37 +304,36 @@ static int launch_score_g(const void* q, const dsa_kv* kv, const void* meta, int
   dim3 grid(ceil_div(waves, 4), kv->n_kv_heads, kv->batch);
   hipLaunchKernelGGL((score_kernel<T, D, G, GL>), grid, dim3(256), 0, st, (const T*)q, (const T*)meta,
                      kv->page_table, kv->seq_lens, kv->n_kv_heads, kv->page_size, Pl, kv->max_pages,
-                     kv->num_slots, (unsigned long long)smask, (int)ppw, scores);
+                     kv->num_slots, (unsigned long long)smask, (int)ppw, scores, ema);
   return launch_status();
 }
 
 template <typename T, int D, int G>
 static int launch_score_gl(const void* q, const dsa_kv* kv, const void* meta, int Pl, uint64_t smask,
-                           float* scores, hipStream_t st) {
+                           float* scores, const EmaArgs& ema, hipStream_t st) {
   switch (kv->page_size / Pl) {
-    case 1: return launch_score_g<T, D, G, 1>(q, kv, meta, Pl, smask, scores, st);
-    case 2: return launch_score_g<T, D, G, 2>(q, kv, meta, Pl, smask, scores, st);
-    case 4: return launch_score_g<T, D, G, 4>(q, kv, meta, Pl, smask, scores, st);
+    case 1: return launch_score_g<T, D, G, 1>(q, kv, meta, Pl, smask, scores, ema, st);
+    case 2: return launch_score_g<T, D, G, 2>(q, kv, meta, Pl, smask, scores, ema, st);
+    case 4: return launch_score_g<T, D, G, 4>(q, kv, meta, Pl, smask, scores, ema, st);
   }
   return DSA_ERR_UNSUPPORTED;
 }
 
 template <typename T, int D>
 static int launch_score_d(const void* q, int G, const dsa_kv* kv, const void* meta, int Pl, uint64_t smask,
-                          float* scores, hipStream_t st) {
+                          float* scores, const EmaArgs& ema, hipStream_t st) {
   switch (G) {
-    case 1: return launch_score_gl<T, D, 1>(q, kv, meta, Pl, smask, scores, st);
-    case 2: return launch_score_gl<T, D, 2>(q, kv, meta, Pl, smask, scores, st);
-    case 4: return launch_score_gl<T, D, 4>(q, kv, meta, Pl, smask, scores, st);
-    case 8: return launch_score_gl<T, D, 8>(q, kv, meta, Pl, smask, scores, st);
-    case 16: return launch_score_gl<T, D, 16>(q, kv, meta, Pl, smask, scores, st);
+    case 1: return launch_score_gl<T, D, 1>(q, kv, meta, Pl, smask, scores, ema, st);
+    case 2: return launch_score_gl<T, D, 2>(q, kv, meta, Pl, smask, scores, ema, st);
+    case 4: return launch_score_gl<T, D, 4>(q, kv, meta, Pl, smask, scores, ema, st);
+    case 8: return launch_score_gl<T, D, 8>(q, kv, meta, Pl, smask, scores, ema, st);
+    case 16: return launch_score_gl<T, D, 16>(q, kv, meta, Pl, smask, scores, ema, st);
   }
   return DSA_ERR_UNSUPPORTED;
 }
 
-extern "C" int dsa_page_score(const void* q, int32_t n_q_heads, const dsa_kv* kv, const void* meta,
-                              int32_t logical_page, const dsa_stream_cfg* stream_cfg, float* scores,
-                              void* stream) {
+static int page_score_impl(const void* q, int32_t n_q_heads, const dsa_kv* kv, const void* meta, int32_t logical_page,
+                           const dsa_stream_cfg* stream_cfg, float* scores, const EmaArgs& ema, void* stream) {
   int rc = check_kv(kv, false);
   if (rc) return rc;
   if ((rc = check_logical(kv, logical_page))) return rc;
@@ -323,8 +348,26 @@ extern "C" int dsa_page_score(const void* q, int32_t n_q_heads, const dsa_kv* kv
   hipStream_t st = (hipStream_t)stream;
   const bool bf = kv->dtype == DSA_BF16;
   if (kv->head_dim == 128)
-    return bf ? launch_score_d<uint16_t, 128>(q, G, kv, meta, logical_page, smask, scores, st)
-              : launch_score_d<float, 128>(q, G, kv, meta, logical_page, smask, scores, st);
-  return bf ? launch_score_d<uint16_t, 64>(q, G, kv, meta, logical_page, smask, scores, st)
-            : launch_score_d<float, 64>(q, G, kv, meta, logical_page, smask, scores, st);
+    return bf ? launch_score_d<uint16_t, 128>(q, G, kv, meta, logical_page, smask, scores, ema, st)
+              : launch_score_d<float, 128>(q, G, kv, meta, logical_page, smask, scores, ema, st);
+  return bf ? launch_score_d<uint16_t, 64>(q, G, kv, meta, logical_page, smask, scores, ema, st)
+            : launch_score_d<float, 64>(q, G, kv, meta, logical_page, smask, scores, ema, st);
+}
+
+extern "C" int dsa_page_score(const void* q, int32_t n_q_heads, const dsa_kv* kv, const void* meta,
+                              int32_t logical_page, const dsa_stream_cfg* stream_cfg, float* scores,
+                              void* stream) {
+  const EmaArgs none{nullptr, nullptr, nullptr, 0.0f, 0.0f, 0.0f, 0};
+  return page_score_impl(q, n_q_heads, kv, meta, logical_page, stream_cfg, scores, none, stream);
+}
+
+extern "C" int dsa_page_score_ema(const void* q, int32_t n_q_heads, const dsa_kv* kv, const void* meta,
+                                  int32_t logical_page, const dsa_stream_cfg* stream_cfg, float* scores, float* level,
+                                  float* trend, float* pred, float alpha, float beta, float gamma, int32_t init,
+                                  void* stream) {
+  if (!level || !trend || !pred) return DSA_ERR_NULL;
+  if (pred == level || pred == trend || level == trend || scores == pred || scores == level || scores == trend)
+    return DSA_ERR_SHAPE;
+  const EmaArgs ema{level, trend, pred, alpha, beta, gamma, init ? 1 : 0};
+  return page_score_impl(q, n_q_heads, kv, meta, logical_page, stream_cfg, scores, ema, stream);
 }

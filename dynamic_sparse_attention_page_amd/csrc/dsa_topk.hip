@@ -175,11 +175,13 @@ constexpr uint32_t kKeyNegInf = 0x007FFFFFu;
 // EMA update with it (level', trend' and the prediction).
 struct SrRow {
   const float* is;
-  const float* level;
+  const float* level;   // nullptr: the prediction is already in pred_in
   const float* trend;
+  const float* pred_in;
   float alpha, beta, gamma;
   int pred, init;
   __device__ __forceinline__ float value(int j, float& nl, float& nt) const {
+    if (pred && !level) { nl = nt = 0.0f; return pred_in[j]; }
     const float x = is[j];
     if (!pred || init) { nl = x; nt = 0.0f; return x; }
     float pr;
@@ -232,6 +234,7 @@ inline SrWs sr_ws(void* ws, size_t rows, int N) {
 __global__ __launch_bounds__(kSrNT) void sr_hist_kernel(const float* __restrict__ scores,
                                                         const float* __restrict__ level,
                                                         const float* __restrict__ trend,
+                                                        const float* __restrict__ pred,
                                                         const int32_t* __restrict__ seq_lens, int n_kv_heads, int N,
                                                         int P, float alpha, float beta, float gamma, int init,
                                                         SrWs ws) {
@@ -245,7 +248,8 @@ __global__ __launch_bounds__(kSrNT) void sr_hist_kernel(const float* __restrict_
   const int L = clamp_len(seq_lens[b], N, P);
   const int np = (L + P - 1) / P;
   const size_t rb = (size_t)unit * N;
-  const SrRow row{scores + rb, level + rb, trend + rb, alpha, beta, gamma, arr, init};
+  const SrRow row{scores + rb, level ? level + rb : nullptr, trend ? trend + rb : nullptr, pred + rb, alpha, beta,
+                  gamma, arr, init};
   const int r = unit * 2 + arr;
 
   // loads up to N, so they do not wait for the sequence length
@@ -344,7 +348,8 @@ __global__ __launch_bounds__(kSrNT) void sr_select_kernel(
   const int L = clamp_len(seq_lens[b], N, P);
   const int np = (L + P - 1) / P;
   const size_t rb = (size_t)unit * N;
-  const SrRow row{scores + rb, level + rb, trend + rb, alpha, beta, gamma, arr, init};
+  const SrRow row{scores + rb, level ? level + rb : nullptr, trend ? trend + rb : nullptr, pred + rb, alpha, beta,
+                  gamma, arr, init};
   const int r = unit * 2 + arr;
   const int kk = arr ? k_spec : k;
   const int keff = min(kk, np);
@@ -361,7 +366,7 @@ __global__ __launch_bounds__(kSrNT) void sr_select_kernel(
       float nl, nt;
       const float v = row.value(j, nl, nt);
       key[e] = order_key(v);
-      if (arr) { level[rb + j] = nl; trend[rb + j] = nt; pred[rb + j] = v; }
+      if (arr && level) { level[rb + j] = nl; trend[rb + j] = nt; pred[rb + j] = v; }
     }
   }
   // P^t entries (the first kSrReg) and their scores, loaded up front
@@ -658,8 +663,8 @@ static int launch_prr_split(const float* scores, float* level, float* trend, flo
   const int W = (N + kSrC - 1) / kSrC;
   const SrWs s = sr_ws(ws, (size_t)units * 2, N);
   const dim3 grid(W, units, 2);
-  hipLaunchKernelGGL(sr_hist_kernel, grid, dim3(kSrNT), 0, st, scores, level, trend, seq_lens, Hkv, N, P, alpha, beta,
-                     gamma, init, s);
+  hipLaunchKernelGGL(sr_hist_kernel, grid, dim3(kSrNT), 0, st, scores, level, trend, pred, seq_lens, Hkv, N, P, alpha,
+                     beta, gamma, init, s);
   int rc = launch_status();
   if (rc) return rc;
   const size_t dyn = m_ids ? (size_t)((N + 31) / 32) * sizeof(uint32_t) : 0;
@@ -682,9 +687,10 @@ extern "C" int dsa_prr_select(const float* scores, int32_t batch, int32_t n_kv_h
   if (batch < 0 || n_kv_heads < 1 || max_pages < 1 || page_size < 1 || k < 1 || k_spec < 1) return DSA_ERR_SHAPE;
   if (max_pages > 65536) return DSA_ERR_UNSUPPORTED;
   if (batch == 0) return DSA_OK;
-  if (!scores || !seq_lens || !a_ids || !a_counts || !level || !trend || !pred || !p_ids || !p_counts)
-    return DSA_ERR_NULL;
-  if (pred == level || pred == trend || level == trend) return DSA_ERR_SHAPE;
+  if (!scores || !seq_lens || !a_ids || !a_counts || !pred || !p_ids || !p_counts) return DSA_ERR_NULL;
+  if (!level != !trend) return DSA_ERR_NULL;   // both NULL: pred already holds the updated prediction
+  const bool ema = level != nullptr;
+  if (ema && (pred == level || pred == trend || level == trend)) return DSA_ERR_SHAPE;
   if (m_ids && (!m_counts || !p_cur_ids || !p_cur_counts)) return DSA_ERR_NULL;
   if (m_ids && (p_cur_ids == p_ids || p_cur_counts == p_counts)) return DSA_ERR_SHAPE;   // P^t is read while P^{t+1} is written
   hipStream_t st = (hipStream_t)stream;
@@ -699,9 +705,11 @@ extern "C" int dsa_prr_select(const float* scores, int32_t batch, int32_t n_kv_h
   }
   // the EMA update is elementwise and spread over the whole GPU; the two
   // selections then run in one grid
-  int rc = dsa_ema_predict_update(scores, level, trend, pred, (int64_t)batch * n_kv_heads * max_pages, alpha, beta,
-                                  gamma, init, stream);
-  if (rc) return rc;
+  if (ema) {
+    const int rc = dsa_ema_predict_update(scores, level, trend, pred, (int64_t)batch * n_kv_heads * max_pages, alpha,
+                                          beta, gamma, init, stream);
+    if (rc) return rc;
+  }
   const int N = max_pages;
 #define DSA_PRR(E, NW) return launch_prr_select_e<E, NW>(scores, pred, batch, n_kv_heads, max_pages, seq_lens, \
                                                           page_size, k, a_ids, a_counts, k_spec, p_ids, p_counts, \

@@ -38,8 +38,8 @@ from dataclasses import dataclass, field
 
 import torch
 
-from . import (OP_ATTN_REPAIR, PagedKV, attn_repair, ema_predict_update, page_score, page_select_topk,
-               prr_select, sparse_decode_attn, workspace_bytes)
+from . import (OP_ATTN_REPAIR, PagedKV, attn_repair, ema_predict_update, page_score, page_score_ema,
+               page_select_topk, prr_select, sparse_decode_attn, workspace_bytes)
 
 
 class PRRDecoder:
@@ -129,15 +129,16 @@ class PRRDecoder:
             p_counts.copy_(counts)
 
     def _select_and_predict(self, q, init: bool, buf: int, cur: int | None = None):
-        """IS^t, A^t, the EMA update and P^{t+1} (into buffer buf): one
-        score launch and one launch that runs both selections side by side
-        when |A| = |P| -- which also writes M^t = A^t \\ P^t when P^t is in
-        buffer cur -- else the separate calls."""
+        """IS^t, A^t, the EMA update and P^{t+1} (into buffer buf): when
+        |A| = |P|, one launch for the scores and the EMA update and one that
+        runs both selections side by side -- which also writes M^t =
+        A^t \\ P^t when P^t is in buffer cur -- else the separate calls."""
         if self.k == self.k_spec:
-            page_score(q, self.kv, self.meta, self.lp, scores=self.scores)
+            page_score_ema(q, self.kv, self.meta, self.level, self.trend, self.pred, self.alpha, self.beta,
+                           self.gamma, init=init, logical_page=self.lp, scores=self.scores)
             p_ids, p_counts = self._p[buf]
             with_m = cur is not None
-            prr_select(self.scores, self.kv.seq_lens, self.kv.page_size, self.k, self.level, self.trend,
+            prr_select(self.scores, self.kv.seq_lens, self.kv.page_size, self.k, None, None,
                        self.pred.view(-1), self.alpha, self.beta, self.gamma, init, self.k_spec, self.a_ids,
                        self.a_counts, p_ids, p_counts, p_cur=self._p[cur] if with_m else None,
                        m_out=(self.m_ids, self.m_counts) if with_m else None, split=False)

@@ -190,6 +190,23 @@ int dsa_page_score(const void *q, int32_t n_q_heads, const dsa_kv *kv, const voi
                    void *stream);
 
 /*
+ * dsa_page_score_ema -- dsa_page_score with PRR's EMA predictor update
+ * ([PRR] section 3.1) applied to the new scores in the same launch.
+ *
+ * Equivalent to dsa_page_score(...) followed by
+ * dsa_ema_predict_update(scores, level, trend, pred,
+ *                        batch * n_kv_heads * max_pages, alpha, beta, gamma, init)
+ * (bit for bit: the same float operations in the same order), without the
+ * second launch.  level, trend, pred: device float [batch][n_kv_heads][max_pages],
+ * distinct from each other and from scores (DSA_ERR_SHAPE), none NULL
+ * (DSA_ERR_NULL).  Other arguments and errors as dsa_page_score.
+ */
+int dsa_page_score_ema(const void *q, int32_t n_q_heads, const dsa_kv *kv, const void *meta,
+                       int32_t logical_page, const dsa_stream_cfg *stream_cfg, float *scores,
+                       float *level, float *trend, float *pred, float alpha, float beta,
+                       float gamma, int32_t init, void *stream);
+
+/*
  * dsa_page_select_topk -- fixed top-k page selection ([PSA] section 2.2;
  * [PRR] section 2, the selection stage of a DSA step).
  *
@@ -335,7 +352,10 @@ int dsa_ema_predict_update(const float *is_true, float *level, float *trend, flo
  * p_cur_ids/p_cur_counts must not be p_ids/p_counts; all four M pointers may
  * be NULL.
  * scores: IS^t, device float [batch][n_kv_heads][max_pages]; level, trend,
- * pred: device float arrays of the same shape, distinct; a_ids: int32
+ * pred: device float arrays of the same shape, distinct.  level and trend
+ * may both be NULL when pred already holds the updated prediction (after
+ * dsa_page_score_ema): the EMA step is then skipped; one of them NULL is
+ * DSA_ERR_NULL.  a_ids: int32
  * [batch][n_kv_heads][k]; p_ids: int32 [batch][n_kv_heads][k_spec]; ids
  * ascending, -1 padded.  No streaming heads.  max_pages <= 65536.
  * ws: device scratch of dsa_prr_select_workspace_bytes(batch, n_kv_heads,

@@ -136,6 +136,9 @@ def test_validation_errors(dsa):
             ok_ptr, ok_ptr]
     assert L.dsa_prr_select(*args, None, None, ok_ptr, ok_ptr, None, 0, None) == -1
     assert L.dsa_prr_select(*args, ok_ptr, P(20480), ok_ptr, ok_ptr, None, 0, None) == -2
+    # the prediction already updated: level and trend both NULL, not one of them
+    assert L.dsa_prr_select(ok_ptr, 1, 2, 64, ok_ptr, 16, 8, ok_ptr, ok_ptr, None, P(12288), P(16384), F(0.6), F(0.3),
+                            F(0.25), 0, 8, ok_ptr, ok_ptr, None, None, None, None, None, 0, None) == -1
     # split-row selection of long rows: workspace size, too small a workspace
     assert L.dsa_prr_select_workspace_bytes(1, 2, 4096) == 0
     need = L.dsa_prr_select_workspace_bytes(1, 2, 8192)
@@ -143,6 +146,11 @@ def test_validation_errors(dsa):
     long_args = list(args)
     long_args[3] = 8192
     assert L.dsa_prr_select(*long_args, None, None, None, None, ok_ptr, need - 1, None) == -5
+    # scores with the EMA update: missing state, state aliasing the scores
+    assert L.dsa_page_score_ema(ok_ptr, 4, ctypes.byref(kv), ok_ptr, 16, None, ok_ptr, None, P(8192), P(12288),
+                                F(0.6), F(0.3), F(0.25), 0, None) == -1
+    assert L.dsa_page_score_ema(ok_ptr, 4, ctypes.byref(kv), ok_ptr, 16, None, P(8192), P(8192), P(12288), P(16384),
+                                F(0.6), F(0.3), F(0.25), 0, None) == -2
     # repair: P ids without counts
     assert L.dsa_attn_repair(ok_ptr, 4, ctypes.byref(kv), ok_ptr, ok_ptr, ok_ptr, None, 8, F(0.088), ok_ptr, ok_ptr,
                              ok_ptr, ok_ptr, 1 << 30, None) == -1
