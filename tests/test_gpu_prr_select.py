@@ -164,3 +164,48 @@ def test_prr_select_split_rows(gpu_lib, kind):
                 n = int(spl["mc"][b, h])
                 assert n == len(ref) and np.array_equal(spl["m"][b, h, :n], ref)
                 assert np.all(spl["m"][b, h, n:] == -1)
+
+
+@pytest.mark.parametrize("N,lens,k", [(4097, [16 * 4097, 16 * 2049 + 1], 1),      # 3 chunks, the last of 1 page
+                                      (4097, [16 * 4097, 16 * 4096], 4097),        # budget = every valid page
+                                      (65536, [16 * 65536], 3000)])                # the largest row: 32 chunks
+def test_prr_select_split_edges(gpu_lib, N, lens, k):
+    """Chunk-count edges of the split-row selection: a last chunk of one
+    page, a budget covering every valid page, and the 65536-page maximum;
+    bit-equal to the one-workgroup path and to the oracle's top-k."""
+    dsa = gpu_lib
+    print(f"[case] prr_select split edges N={N} k={k}", flush=True)
+    P = 16
+    B, H = len(lens), 2
+    rng = np.random.default_rng(N + k)
+    s = rng.standard_normal((B, H, N)).astype(np.float32)
+    sc = torch.from_numpy(s).cuda()
+    lens_t = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    lvl = rng.standard_normal(B * H * N).astype(np.float32)
+    trd = rng.standard_normal(B * H * N).astype(np.float32)
+    lvl0, trd0 = torch.from_numpy(lvl).cuda(), torch.from_numpy(trd).cuda()
+    k_spec = k
+    pcur = np.full((B, H, k_spec), -1, np.int32)
+    pcnt = np.zeros((B, H), np.int32)
+    for b in range(B):
+        nv = oracle.n_pages(lens[b], P)
+        for h in range(H):
+            c = min(k_spec, nv) // 2
+            pcur[b, h, :c] = np.sort(rng.choice(nv, c, replace=False))
+            pcnt[b, h] = c
+    pcur_t, pcnt_t = torch.from_numpy(pcur).cuda(), torch.from_numpy(pcnt).cuda()
+    one = _prr_run(dsa, sc, lens_t, P, k, k_spec, lvl0, trd0, False, pcur_t, pcnt_t, split=False)
+    spl = _prr_run(dsa, sc, lens_t, P, k, k_spec, lvl0, trd0, False, pcur_t, pcnt_t, split=True)
+    for name in one:
+        assert np.array_equal(one[name], spl[name]), f"{name} differs"
+    lv_ref, tr_ref = oracle.ema_step_f32(s.reshape(-1), lvl, trd, 0.6, 0.3)
+    prn = oracle.ema_predict_f32(lv_ref, tr_ref, 0.25).astype(np.float64).reshape(B, H, N)
+    for b in range(B):
+        nv = oracle.n_pages(lens[b], P)
+        for h in range(H):
+            a = spl["a"][b, h, :spl["ac"][b, h]]
+            assert np.array_equal(a, oracle.topk_pages(s[b, h].astype(np.float64), nv, k))
+            assert np.array_equal(spl["p"][b, h, :spl["pc"][b, h]], oracle.topk_pages(prn[b, h], nv, k_spec))
+            ref = oracle.missing_pages(a, pcur[b, h, :pcnt[b, h]])
+            n = int(spl["mc"][b, h])
+            assert n == len(ref) and np.array_equal(spl["m"][b, h, :n], ref)
