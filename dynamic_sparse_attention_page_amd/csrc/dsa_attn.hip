@@ -543,7 +543,9 @@ __device__ __forceinline__ float log_add(float a, float b) {
   return mx + log1pf(expf(mn - mx));
 }
 
-template <typename T, int D, int G>
+// E scores per thread: rows up to E * NT pages (the launch takes the
+// smallest E that holds max_pages, so short rows carry no padding).
+template <typename T, int D, int G, int E>
 __global__ __launch_bounds__((psa_waves<T, G>() * 64)) void psa_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const int32_t* __restrict__ page_table, const int32_t* __restrict__ seq_lens, const float* __restrict__ scores,
@@ -554,11 +556,11 @@ __global__ __launch_bounds__((psa_waves<T, G>() * 64)) void psa_kernel(
   constexpr int CPL = A::CPL, DW = A::DW;
   constexpr int NWV = psa_waves<T, G>();
   constexpr int NT = NWV * 64;
-  constexpr int E = kPsaMaxPages / NT;
+  static_assert(E * NT <= kPsaMaxPages, "row capacity");
   static_assert(G * D <= NT, "one output element per thread");
   __shared__ SelectSmem<E, NWV> sm;
   __shared__ unsigned long long s_key[kPsaRound];  // picks of the round: score key << 32 | ~index
-  __shared__ uint32_t s_keys[kPsaMaxPages];            // score keys, element order
+  __shared__ uint32_t s_keys[E * NT];                  // score keys, element order
   __shared__ int s_page[kPsaRound], s_slot[kPsaRound];  // in rank order
   __shared__ __align__(16) float lds_rows[NWV][A::LDS_FLOATS];
   __shared__ __align__(16) float ch_o[NWV][G][D];
@@ -629,6 +631,7 @@ __global__ __launch_bounds__((psa_waves<T, G>() * 64)) void psa_kernel(
       const int page = (int)(0xFFFFFFFFu - (uint32_t)(mine & 0xFFFFFFFFull));
       const int slot = ptrow[page];   // in flight during the ranking loop
       int r = 0;
+#pragma unroll 8
       for (int x = 0; x < n_pick; ++x) r += s_key[x] > mine ? 1 : 0;   // keys are distinct
       s_page[r] = page;
       s_slot[r] = slot;
@@ -910,10 +913,17 @@ static int launch_psa_g(const void* q, const dsa_kv* kv, const float* scores, fl
   const int always_stop = thr <= 0.0f;
   const float ln_odds = (never_stop || always_stop) ? 0.0f : (float)log((double)thr / (1.0 - (double)thr));
   const float c = scale * kLog2e;
-  hipLaunchKernelGGL((psa_kernel<T, D, G>), dim3(kv->n_kv_heads, kv->batch), dim3(psa_waves<T, G>() * 64), 0, st, (const T*)q,
-                     (const T*)kv->k, (const T*)kv->v, kv->page_table, kv->seq_lens, scores, kv->n_kv_heads,
-                     kv->page_size, kv->max_pages, kv->num_slots, stop_mode, never_stop, always_stop, ln_odds,
-                     scale, c, ids, counts, O, l, m);
+  constexpr int NT = psa_waves<T, G>() * 64;
+  constexpr int EMAX = kPsaMaxPages / NT;
+#define DSA_PSA(E_)                                                                                                \
+  hipLaunchKernelGGL((psa_kernel<T, D, G, E_>), dim3(kv->n_kv_heads, kv->batch), dim3(NT), 0, st, (const T*)q,     \
+                     (const T*)kv->k, (const T*)kv->v, kv->page_table, kv->seq_lens, scores, kv->n_kv_heads,       \
+                     kv->page_size, kv->max_pages, kv->num_slots, stop_mode, never_stop, always_stop, ln_odds,     \
+                     scale, c, ids, counts, O, l, m)
+  if (kv->max_pages <= NT * (EMAX / 4)) DSA_PSA(EMAX / 4);
+  else if (kv->max_pages <= NT * (EMAX / 2)) DSA_PSA(EMAX / 2);
+  else DSA_PSA(EMAX);
+#undef DSA_PSA
   return launch_status();
 }
 
