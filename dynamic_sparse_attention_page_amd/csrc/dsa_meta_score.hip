@@ -133,20 +133,29 @@ template <typename T, int D, int G, int GL>
 __global__ __launch_bounds__(256) void score_kernel(
     const T* __restrict__ q, const T* __restrict__ meta, const int32_t* __restrict__ page_table,
     const int32_t* __restrict__ seq_lens, int n_kv_heads, int P, int Pl, int max_pages, int num_slots,
-    unsigned long long streaming, int pages_per_wave, float* __restrict__ scores, EmaArgs ema) {
+    unsigned long long streaming, int pages_per_wave, int wgs_per_row, float* __restrict__ scores, EmaArgs ema) {
   using L_ = Lay<T, D>;
   constexpr int CPL = L_::CPL, DW = L_::DW;
   constexpr int U = DSA_SCORE_LOADS / 2;     // load pairs in flight per lane
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int b = blockIdx.z, h = blockIdx.y;
-  const int j0 = (blockIdx.x * 4 + wave) * pages_per_wave;
-  if (j0 >= max_pages) return;
-  const int j1 = min(max_pages, j0 + pages_per_wave);
-  float* srow = scores + ((size_t)b * n_kv_heads + h) * max_pages;
-  const int L = clamp_len(seq_lens[b], max_pages, P);
-  const int np = (L + P - 1) / P;
-
+  const int b = blockIdx.z;
+  // with streaming heads the grid is compact: wgs_per_row workgroups for each
+  // dense head (in head order), then one workgroup per streaming head
+  int h = blockIdx.y, xb = blockIdx.x;
+  if (streaming) {
+    const int n_dense_wg = wgs_per_row * (n_kv_heads - __popcll(streaming));
+    const bool dense = (int)blockIdx.x < n_dense_wg;
+    int want = dense ? (int)blockIdx.x / wgs_per_row : (int)blockIdx.x - n_dense_wg;
+    xb = dense ? (int)blockIdx.x % wgs_per_row : 0;
+    for (h = 0; h < n_kv_heads; ++h) {   // the want-th head of its kind
+      if ((((streaming >> h) & 1ull) == 0) == dense) {
+        if (want == 0) break;
+        --want;
+      }
+    }
+  }
   const size_t rowbase = ((size_t)b * n_kv_heads + h) * max_pages;
+  float* srow = scores + rowbase;
   auto put = [&](int j, float sc) {
     srow[j] = sc;
     if (ema.level) {
@@ -158,10 +167,16 @@ __global__ __launch_bounds__(256) void score_kernel(
       ema.pred[x] = pr;
     }
   };
-  if ((streaming >> h) & 1ull) {
-    for (int j = j0 + lane; j < j1; j += 64) put(j, kNegInf);
+  if ((streaming >> h) & 1ull) {   // the whole row by one workgroup
+    for (int j = threadIdx.x; j < max_pages; j += 256) put(j, kNegInf);
     return;
   }
+  const int j0 = (xb * 4 + wave) * pages_per_wave;
+  if (j0 >= max_pages) return;
+  const int j1 = min(max_pages, j0 + pages_per_wave);
+  const int L = clamp_len(seq_lens[b], max_pages, P);
+  const int np = (L + P - 1) / P;
+
   const int r = lane >> 4, cg = lane & 15;
   // slots of this wave's pages (pages_per_wave <= 64)
   const int my_slot = (j0 + lane < min(j1, np)) ? page_table[(size_t)b * max_pages + j0 + lane] : -1;
@@ -301,10 +316,13 @@ static int launch_score_g(const void* q, const dsa_kv* kv, const void* meta, int
   ppw = ppw < 4 ? 4 : (ppw > 64 ? 64 : ppw);
   ppw = (ppw + 3) / 4 * 4;
   const int waves = ceil_div(kv->max_pages, ppw);
-  dim3 grid(ceil_div(waves, 4), kv->n_kv_heads, kv->batch);
+  const int wgs = ceil_div(waves, 4);
+  const int n_stream = __builtin_popcountll(smask);
+  const dim3 grid = smask ? dim3(wgs * (kv->n_kv_heads - n_stream) + n_stream, 1, kv->batch)
+                          : dim3(wgs, kv->n_kv_heads, kv->batch);
   hipLaunchKernelGGL((score_kernel<T, D, G, GL>), grid, dim3(256), 0, st, (const T*)q, (const T*)meta,
                      kv->page_table, kv->seq_lens, kv->n_kv_heads, kv->page_size, Pl, kv->max_pages,
-                     kv->num_slots, (unsigned long long)smask, (int)ppw, scores, ema);
+                     kv->num_slots, (unsigned long long)smask, (int)ppw, wgs, scores, ema);
   return launch_status();
 }
 
