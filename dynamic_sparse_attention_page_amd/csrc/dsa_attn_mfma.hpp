@@ -145,12 +145,18 @@ struct MfmaWave {
       keep23 = (ok[2] ? 0x0000FFFFu : 0u) | (ok[3] ? 0xFFFF0000u : 0u);
     }
     wave_sync();
-    const uint16_t* vr = vs + (4 * g) * VS + h;
+    // A = V^T by transposed LDS reads: lane 16k + m addresses the 4 values
+    // V[4k + m/4][16n + 4(m%4) .. +3] of the row-major tile, and the read
+    // hands lane 16k + 4a + b the b-th value of the blocks of lanes 16k + a +
+    // 4t (t < 4): V[4k + t][16n + 4a + b], i.e. channel 16n + h of keys 4g + t
+    const int lane16 = lane & 15;
+    const uint16_t* vt = vs + (4 * g + (lane16 >> 2)) * VS + 4 * (lane16 & 3);
 #pragma unroll
     for (int n = 0; n < NB; ++n) {
-      const uint32_t a01 = (uint32_t)vr[16 * n] | ((uint32_t)vr[VS + 16 * n] << 16);
-      const uint32_t a23 = (uint32_t)vr[2 * VS + 16 * n] | ((uint32_t)vr[3 * VS + 16 * n] << 16);
-      const s16x4_t a = __builtin_bit_cast(s16x4_t, make_uint2(a01 & keep01, a23 & keep23));
+      const s16x4_t raw = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4_t*)(vt + 16 * n));
+      const uint2 w = __builtin_bit_cast(uint2, raw);
+      const s16x4_t a = __builtin_bit_cast(s16x4_t, make_uint2(w.x & keep01, w.y & keep23));
       acc[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, bhi, acc[n], 0, 0, 0);
       acc[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, blo, acc[n], 0, 0, 0);
     }
