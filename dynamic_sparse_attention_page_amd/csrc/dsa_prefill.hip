@@ -12,8 +12,8 @@
 // last query for a dense head (causal), the sink tiles and the tiles of the
 // local window for a streaming head; a skipped tile holds no attended
 // (query, key) pair.  Inside a visited tile the token mask
-// is exact.  Per tile the workgroup stages K (row-major) and V (transposed)
-// in LDS, and every wave runs the online-softmax recurrence on the matrix
+// is exact.  Per tile the workgroup stages K and V row-major in LDS (V is
+// read back transposed by the gfx950 transposed LDS reads), and every wave runs the online-softmax recurrence on the matrix
 // cores with the layouts of the decode tile (dsa_attn_mfma.hpp), queries in
 // place of heads:
 //   S^T = K Q^T      v_mfma_f32_16x16x32_bf16, D/32 steps per 16 keys;
@@ -22,7 +22,7 @@
 //                    lo parts; the k index 8g + j stands for key 4g + j of
 //                    the chunk's first 16 keys (j < 4) and 16 + 4g + j - 4 of
 //                    its second, so B is the lane's own logits and A two
-//                    8-byte reads of the transposed V tile
+//                    transposed 8-byte reads of the row-major V tile
 // Tiles below the diagonal of a dense head (and sink tiles below it) need
 // no token mask.
 // Heaviest query tiles (most key tiles) are launched first.
@@ -42,16 +42,10 @@ constexpr int kPfTile = 64;   // T_K
 
 template <int D>
 struct PrefillSmem {
-  static constexpr int KS = D + 8;          // K row stride (bf16): rows of a read spread over banks
-  static constexpr int VS = kPfTile + 8;    // V^T row stride (bf16), 8-byte aligned rows
+  static constexpr int KS = D + 8;          // K and V row stride (bf16): rows of a read spread over banks
   __align__(16) uint16_t k[kPfTile * KS];
-  __align__(16) uint16_t vt[D * VS];
+  __align__(16) uint16_t v[kPfTile * KS];   // row-major; read transposed
 };
-
-__device__ __forceinline__ uint32_t bf16_at(const uint4& x, int i) {
-  const uint32_t w = i < 2 ? x.x : i < 4 ? x.y : i < 6 ? x.z : x.w;
-  return (i & 1) ? (w >> 16) : (w & 0xFFFFu);
-}
 
 template <int D, int NWQ, int QS>
 __global__ __launch_bounds__(NWQ * 64) void prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -61,9 +55,7 @@ __global__ __launch_bounds__(NWQ * 64) void prefill_kernel(const uint16_t* __res
                                                       float* __restrict__ mout) {
   constexpr int NK = D / 32, NB = D / 16;
   constexpr int NT = NWQ * 64, QT = 16 * QS * NWQ;   // threads; queries per tile
-  constexpr int KCH = D / (8 * NWQ);           // K chunks per thread
-  constexpr int VCH = D / (16 * NWQ) > 0 ? D / (16 * NWQ) : 1;   // V chunks per half-wave
-  constexpr int VHW = D / (8 * VCH);           // half-waves that stage V
+  constexpr int KCH = D / (8 * NWQ);           // K (and V) chunks per thread
   static_assert(KCH * NT * 8 == kPfTile * D, "K staging");
   using S = PrefillSmem<D>;
   __shared__ S sm;
@@ -106,29 +98,21 @@ __global__ __launch_bounds__(NWQ * 64) void prefill_kernel(const uint16_t* __res
   const int n_iter = n_first + max(0, kb_max + 1 - lo2);
 
   // Global -> register staging of a key tile; the next tile's loads are in
-  // flight while the current one is computed.  K: 16-byte chunk tid + 256x
-  // of the row-major tile.  V: a half-wave takes keys (2p, 2p+1), p =
-  // lane % 32, and D/64 channel chunks (written transposed, one 32-bit word
-  // per channel row).
-  const int hw = tid >> 5, pp = tid & 31;
-  uint4 kr[KCH], va[VCH], vb[VCH];
+  // flight while the current one is computed.  K and V: 16-byte chunk
+  // tid + NT x of the row-major tile.
+  uint4 kr[KCH], vr4[KCH];
   auto fetch = [&](int key0) {
 #pragma unroll
     for (int x = 0; x < KCH; ++x) {
       const int chunk = tid + NT * x;
       const int row = chunk / (D / 8), col = (chunk % (D / 8)) * 8;
       kr[x] = make_uint4(0u, 0u, 0u, 0u);
-      if (key0 + row < L) kr[x] = *reinterpret_cast<const uint4*>(k + (size_t)(key0 + row) * kv_row + (size_t)hk * D + col);
-    }
-#pragma unroll
-    for (int x = 0; x < VCH; ++x) {
-      const int col = (hw * VCH + x) * 8;
-      const int t0 = key0 + 2 * pp;
-      va[x] = make_uint4(0u, 0u, 0u, 0u);
-      vb[x] = va[x];
-      if (hw >= VHW) continue;
-      if (t0 < L) va[x] = *reinterpret_cast<const uint4*>(v + (size_t)t0 * kv_row + (size_t)hk * D + col);
-      if (t0 + 1 < L) vb[x] = *reinterpret_cast<const uint4*>(v + (size_t)(t0 + 1) * kv_row + (size_t)hk * D + col);
+      vr4[x] = kr[x];
+      if (key0 + row < L) {
+        const size_t off = (size_t)(key0 + row) * kv_row + (size_t)hk * D + col;
+        kr[x] = *reinterpret_cast<const uint4*>(k + off);
+        vr4[x] = *reinterpret_cast<const uint4*>(v + off);
+      }
     }
   };
   auto tile_of = [&](int it) { return it < n_first ? it : lo2 + (it - n_first); };
@@ -143,14 +127,7 @@ __global__ __launch_bounds__(NWQ * 64) void prefill_kernel(const uint16_t* __res
       const int chunk = tid + NT * x;
       const int row = chunk / (D / 8), col = (chunk % (D / 8)) * 8;
       *reinterpret_cast<uint4*>(sm.k + row * S::KS + col) = kr[x];
-    }
-#pragma unroll
-    for (int x = 0; x < VCH; ++x) {
-      const int col = (hw * VCH + x) * 8;
-      if (hw >= VHW) continue;
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        *reinterpret_cast<uint32_t*>(sm.vt + (col + i) * S::VS + 2 * pp) = bf16_at(va[x], i) | (bf16_at(vb[x], i) << 16);
+      *reinterpret_cast<uint4*>(sm.v + row * S::KS + col) = vr4[x];
     }
     __syncthreads();
     if (it + 1 < n_iter) fetch(tile_of(it + 1) * kPfTile);
@@ -213,10 +190,18 @@ __global__ __launch_bounds__(NWQ * 64) void prefill_kernel(const uint16_t* __res
         bhi[u] = __builtin_bit_cast(bf16x8_t, make_uint4(hw[0], hw[1], hw[2], hw[3]));
         blo[u] = __builtin_bit_cast(bf16x8_t, make_uint4(lw[0], lw[1], lw[2], lw[3]));
       }
+      // A = V^T by transposed LDS reads (see the decode tile): lane 16k + m
+      // addresses V[key0 + 4k + m/4][16n + 4(m%4) .. +3] of the chunk's
+      // first 16 keys, then of its second; each read hands the lane the
+      // 4 keys 4g + t of channel 16n + h
+      const uint16_t* vt = sm.v + (32 * ch + 4 * g + ((lane & 15) >> 2)) * S::KS + 4 * (lane & 3);
 #pragma unroll
       for (int n = 0; n < NB; ++n) {
-        const uint16_t* vr = sm.vt + (16 * n + h) * S::VS + 32 * ch + 4 * g;
-        const uint2 a0 = *reinterpret_cast<const uint2*>(vr), a1 = *reinterpret_cast<const uint2*>(vr + 16);
+        const s16x4_t r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4_t*)(vt + 16 * n));
+        const s16x4_t r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4_t*)(vt + 16 * S::KS + 16 * n));
+        const uint2 a0 = __builtin_bit_cast(uint2, r0), a1 = __builtin_bit_cast(uint2, r1);
         const bf16x8_t a = __builtin_bit_cast(bf16x8_t, make_uint4(a0.x, a0.y, a1.x, a1.y));
 #pragma unroll
         for (int u = 0; u < QS; ++u) {
