@@ -124,8 +124,9 @@ struct MfmaWave {
     const float mn = fmaxf(m, tm);
     const float alpha = (mn == kNegInf) ? 1.0f : fast_exp2((m - mn) * c);
     float p[4];
+    const float nmc = exp2_offset(mn, c);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) p[j] = exp2_diff(s[j], mn, c);
+    for (int j = 0; j < 4; ++j) p[j] = exp2_fma(s[j], c, nmc);
     lpart = fmaf(lpart, alpha, (p[0] + p[1]) + (p[2] + p[3]));
     m = mn;
     // P^T as bf16 hi + lo

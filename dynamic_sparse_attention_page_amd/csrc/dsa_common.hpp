@@ -181,6 +181,11 @@ __device__ __forceinline__ float exp2_diff(float a, float m, float c) {
   return (m == kNegInf) ? 0.0f : fast_exp2((a - m) * c);
 }
 
+// The same weight as one fused multiply-add: 2^(a c + nmc) with
+// nmc = exp2_offset(m, c) = -m c (0 when m = -inf, where every a is -inf).
+__device__ __forceinline__ float exp2_offset(float m, float c) { return (m == kNegInf) ? 0.0f : -m * c; }
+__device__ __forceinline__ float exp2_fma(float a, float c, float nmc) { return fast_exp2(fmaf(a, c, nmc)); }
+
 // ---------------------------------------------------------------- layout
 template <typename T, int D>
 struct Lay {

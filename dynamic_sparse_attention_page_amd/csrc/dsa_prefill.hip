@@ -148,7 +148,7 @@ __global__ __launch_bounds__(NWQ * 64) void prefill_kernel(const uint16_t* __res
     // every pair of a tile below the diagonal is attended (for a streaming
     // head only if the tile is all sink); others are masked per token
     const bool full = key0 + kPfTile <= q_first && (!smask || key0 + kPfTile <= sink);
-    float alpha[QS], mn[QS], psum[QS];
+    float alpha[QS], mn[QS], psum[QS], nmc[QS];
 #pragma unroll
     for (int u = 0; u < QS; ++u) {
       float tm = kNegInf;
@@ -166,6 +166,7 @@ __global__ __launch_bounds__(NWQ * 64) void prefill_kernel(const uint16_t* __res
       tm = fmaxf(tm, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(tm), 0x401F)));  // lanes ^ 16
       tm = fmaxf(tm, shfl_xor_f(tm, 32));
       mn[u] = fmaxf(m[u], tm);
+      nmc[u] = exp2_offset(mn[u], c);
       alpha[u] = (mn[u] == kNegInf) ? 1.0f : fast_exp2((m[u] - mn[u]) * c);
       if (__builtin_amdgcn_read_exec() & __ballot(alpha[u] != 1.0f)) {
 #pragma unroll
@@ -182,7 +183,7 @@ __global__ __launch_bounds__(NWQ * 64) void prefill_kernel(const uint16_t* __res
 #pragma unroll
         for (int x = 0; x < 4; ++x) {  // words: keys (4g, 4g+1), (4g+2, 4g+3) of each sub-tile
           const int sub = 2 * ch + (x >> 1), j = 2 * (x & 1);
-          const float p0 = exp2_diff(s[u][sub][j], mn[u], c), p1 = exp2_diff(s[u][sub][j + 1], mn[u], c);
+          const float p0 = exp2_fma(s[u][sub][j], c, nmc[u]), p1 = exp2_fma(s[u][sub][j + 1], c, nmc[u]);
           psum[u] += p0 + p1;
           hw[x] = pack_bf16(p0, p1);
           lw[x] = pack_bf16(p0 - bf_lo(hw[x]), p1 - bf_hi(hw[x]));
