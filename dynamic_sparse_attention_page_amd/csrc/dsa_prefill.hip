@@ -38,11 +38,16 @@ namespace dsa {
 #define DSA_PREFILL_QSETS 1   // sets of 16 queries per wave (each LDS read feeds all)
 #endif
 
+#ifndef DSA_PREFILL_KPAD
+#define DSA_PREFILL_KPAD 16   // row padding of the K and V tiles in LDS (bf16 values; rows stay 16-byte aligned)
+#endif
+
 constexpr int kPfTile = 64;   // T_K
 
 template <int D>
 struct PrefillSmem {
-  static constexpr int KS = D + 8;          // K and V row stride (bf16): rows of a read spread over banks
+  static constexpr int KS = D + DSA_PREFILL_KPAD;   // K and V row stride (bf16): rows of a read spread over banks
+  static_assert((KS * 2) % 16 == 0, "16-byte aligned rows");
   __align__(16) uint16_t k[kPfTile * KS];
   __align__(16) uint16_t v[kPfTile * KS];   // row-major; read transposed
 };
