@@ -12,15 +12,17 @@
 //                 A = K: lane holds K[token h][channels 32i + 8g, +8)
 //                 B = Q^T: lane holds Q[head h][same channels]
 //                 result: lane holds S[head h][tokens 4g + j], j < 4
-//   O^T += V^T P^T  v_mfma_f32_16x16x16_bf16, one per 16-channel block n.
-//                 A = V^T: lane holds V[tokens 4g + j][channel 16n + h]
-//                 B = P^T: lane holds P[head h][tokens 4g + j] -- exactly
-//                 the logit layout, so the softmax stays lane-local
+//   O^T += V^T P^T  v_mfma_f32_16x16x32_bf16, one per 16-channel block n,
+//                 the K dimension holding P's bf16 hi parts then its lo parts.
+//                 A = V^T: lane holds V[tokens 4g + j][channel 16n + h], twice
+//                 B = P^T: lane holds P[head h][tokens 4g + j] (hi, then lo)
+//                 -- exactly the logit layout, so the softmax stays lane-local
 //                 result: lane holds O[head h][channels 16n + 4g + j]
 // Softmax statistics of head h live in lanes h, h+16, h+32, h+48; the tile
-// max needs two lane swaps.  V^T comes from an LDS copy of the tile read
-// transposed.  P enters the product as bf16 hi + lo parts (two MFMAs), so
-// the weights keep ~16 mantissa bits.
+// max needs two lane swaps.  V^T comes from the row-major LDS copy of the
+// tile through transposed LDS reads.  P enters the product as bf16 hi + lo
+// parts, so the weights keep ~16 mantissa bits; one 32-deep product takes
+// both.
 #pragma once
 
 #include "dsa_common.hpp"
@@ -133,8 +135,10 @@ struct MfmaWave {
     const uint32_t h01 = pack_bf16(p[0], p[1]), h23 = pack_bf16(p[2], p[3]);
     const uint32_t l01 = pack_bf16(p[0] - bf_lo(h01), p[1] - bf_hi(h01));
     const uint32_t l23 = pack_bf16(p[2] - bf_lo(h23), p[3] - bf_hi(h23));
-    const s16x4_t bhi = __builtin_bit_cast(s16x4_t, make_uint2(h01, h23));
-    const s16x4_t blo = __builtin_bit_cast(s16x4_t, make_uint2(l01, l23));
+    // B of one 16x16x32 product per channel block: k = 8g + j holds the hi
+    // part of key 4g + j (j < 4), then its lo part (j >= 4); A repeats the
+    // lane's 4 V values, so the product adds V (P_hi + P_lo)
+    const bf16x8_t bhl = __builtin_bit_cast(bf16x8_t, make_uint4(h01, h23, l01, l23));
     if (__builtin_amdgcn_read_exec() & __ballot(alpha != 1.0f)) {   // skip once the maxima settle
 #pragma unroll
       for (int n = 0; n < NB; ++n) acc[n] *= alpha;
@@ -157,9 +161,9 @@ struct MfmaWave {
       const s16x4_t raw = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (__attribute__((address_space(3))) s16x4_t*)(vt + 16 * n));
       const uint2 w = __builtin_bit_cast(uint2, raw);
-      const s16x4_t a = __builtin_bit_cast(s16x4_t, make_uint2(w.x & keep01, w.y & keep23));
-      acc[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, bhi, acc[n], 0, 0, 0);
-      acc[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, blo, acc[n], 0, 0, 0);
+      const uint32_t a01 = w.x & keep01, a23 = w.y & keep23;
+      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, make_uint4(a01, a23, a01, a23));
+      acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bhl, acc[n], 0, 0, 0);
     }
     wave_sync();   // the next tile rewrites the LDS copy
   }
