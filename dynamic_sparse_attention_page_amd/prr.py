@@ -39,7 +39,7 @@ from dataclasses import dataclass, field
 import torch
 
 from . import (OP_ATTN_REPAIR, PagedKV, attn_repair, ema_predict_update, page_score, page_score_ema,
-               page_select_topk, prr_select, sparse_decode_attn, workspace_bytes)
+               page_select_topk, prr_select, prr_select_workspace_bytes, sparse_decode_attn, workspace_bytes)
 
 
 class PRRDecoder:
@@ -81,9 +81,17 @@ class PRRDecoder:
         self.m = torch.empty((B, n_q_heads), dtype=f32, device=dev)
         self.ws = torch.zeros(workspace_bytes(OP_ATTN_REPAIR, kv, n_q_heads, self.stride), dtype=torch.uint8,
                               device=dev)
+        self.sel_ws = None                 # a split-row selection workspace (see split_selection)
         self.side = torch.cuda.Stream(device=dev)      # default priority
         self._p_ready = None               # event: P^t written (side stream of the previous step)
         self.t = 0
+
+    def split_selection(self, on: bool = True):
+        """Give dsa_prr_select a workspace, so that long rows take the
+        split-row selection (many CUs) instead of one workgroup each."""
+        B, H, N = self.scores.shape
+        nb = prr_select_workspace_bytes(B, H, N) if on else 0
+        self.sel_ws = torch.empty(nb, dtype=torch.uint8, device=self.scores.device) if nb else None
 
     def join(self):
         """Make the current stream wait for the side stream's last work (the
@@ -141,7 +149,8 @@ class PRRDecoder:
             prr_select(self.scores, self.kv.seq_lens, self.kv.page_size, self.k, None, None,
                        self.pred.view(-1), self.alpha, self.beta, self.gamma, init, self.k_spec, self.a_ids,
                        self.a_counts, p_ids, p_counts, p_cur=self._p[cur] if with_m else None,
-                       m_out=(self.m_ids, self.m_counts) if with_m else None, split=False)
+                       m_out=(self.m_ids, self.m_counts) if with_m else None, ws=self.sel_ws,
+                       split=self.sel_ws is not None)
         else:
             self._select(q)
             self._predict_next(init=init, buf=buf)
