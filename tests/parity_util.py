@@ -71,3 +71,46 @@ def ids_lists(ids: np.ndarray, counts: np.ndarray):
     """[B][H][stride] + counts -> nested python lists of id arrays."""
     B, H = counts.shape
     return [[ids[b, h, :counts[b, h]].astype(np.int64) for h in range(H)] for b in range(B)]
+
+
+def upload_ids(ref_ids, stride: int):
+    """Nested id lists [b][h] -> int32 device tensors (ids [B][H][stride], -1
+    padded; counts [B][H])."""
+    import torch
+    B, H = len(ref_ids), len(ref_ids[0])
+    ids = np.full((B, H, stride), -1, np.int32)
+    counts = np.zeros((B, H), np.int32)
+    for b in range(B):
+        for h in range(H):
+            r = np.asarray(ref_ids[b][h], np.int64)[:stride]
+            ids[b, h, :len(r)] = r
+            counts[b, h] = len(r)
+    return torch.from_numpy(ids).cuda(), torch.from_numpy(counts).cuda()
+
+
+def check_selected_attention(dsa, batch, q, kv, st, ids, counts, out, ref_ids, units, what="", **attn_kw):
+    """Outputs of an attention over the kernel's own selection, against the
+    oracle's attention over the oracle's selection ``ref_ids`` ([b][h] lists;
+    the sets were compared by check_selection before).  A unit whose set
+    equals the oracle's is compared directly.  Where a unit's set differs by
+    an exempted boundary pair, the attention kernel runs again on the
+    oracle's ids and that output is compared for the unit, so no value the
+    kernels produced becomes an input of the oracle.  Returns the number of
+    such units."""
+    G = batch.group
+    On, ln, mn = (np_(x) for x in out)
+    differ = []
+    for b, h in units:
+        sl = slice(h * G, (h + 1) * G)
+        ref = oracle.attend_pages(batch, b, h, np.asarray(ref_ids[b][h], np.int64))
+        if np.array_equal(ids[b, h, :counts[b, h]], ref_ids[b][h]):
+            check_attention(batch.dtype, On[b, sl], ln[b, sl], mn[b, sl], *ref, f"{what} (b={b}, h={h})")
+        else:
+            differ.append((b, h, ref))
+    if differ:
+        it, ct = upload_ids(ref_ids, ids.shape[2])
+        O2, l2, m2 = (np_(x) for x in dsa.sparse_decode_attn(q, kv, it, ct, streaming=st, **attn_kw))
+        for b, h, ref in differ:
+            sl = slice(h * G, (h + 1) * G)
+            check_attention(batch.dtype, O2[b, sl], l2[b, sl], m2[b, sl], *ref, f"{what} on oracle ids (b={b}, h={h})")
+    return len(differ)

@@ -11,7 +11,7 @@ import torch
 
 import oracle
 import workloads as wl
-from parity_util import check_attention, ids_lists, np_, to_device
+from parity_util import check_selected_attention, check_selection, np_, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -33,8 +33,16 @@ def _run(dsa, bt, k, st=None):
     assert np.array_equal(np_(ids_f), np_(ids_s)), "ids differ from dsa_page_select_topk"
     # same pages, same kernels: the outputs of the two routes agree to rounding
     np.testing.assert_allclose(np_(O), np_(O2), rtol=0, atol=1e-6)
-    rO, rl, rm = oracle.sparse_decode(bt, ids_lists(np_(ids_f), np_(cnt_f)))
-    check_attention(bt.dtype, np_(O), np_(l), np_(m), rO, rl, rm, "fused")
+    # against the oracle: its scores and its selection (boundary rule), and
+    # the outputs against its attention over its own selection
+    ref = oracle.page_scores(bt)
+    idn, cn = np_(ids_f), np_(cnt_f)
+    units = [(b, h) for b in range(bt.batch) for h in range(bt.n_kv_heads)]
+    for b, h in units:
+        if bt.streaming is None or not bt.streaming[h]:
+            check_selection(idn[b, h], int(cn[b, h]), ref[b, h], oracle.n_pages(bt.seq_lens[b], bt.page_size), k,
+                            f"fused (b={b}, h={h})")
+    check_selected_attention(dsa, bt, q, kv, st, idn, cn, (O, l, m), oracle.select_topk(bt, ref, k), units, "fused")
 
 
 @pytest.mark.parametrize("dtype,D,P,G,max_pages,k", [

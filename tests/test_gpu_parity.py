@@ -10,7 +10,7 @@ import torch
 
 import oracle
 import workloads as wl
-from parity_util import TOL, check_attention, check_selection, ids_lists, np_, to_device
+from parity_util import TOL, check_attention, check_selected_attention, check_selection, ids_lists, np_, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -202,10 +202,14 @@ def test_attention_streaming_heads(gpu_lib, G):
     ids, counts = dsa.page_select_topk(sc, kv.seq_lens, 64, 8, streaming=st)
     O, l, m = dsa.sparse_decode_attn(q, kv, ids, counts, streaming=st)
     idn, cn = np_(ids), np_(counts)
-    rO, rl, rm = oracle.sparse_decode(bt, ids_lists(idn, cn))
-    check_attention("bf16", np_(O), np_(l), np_(m), rO, rl, rm, "streaming")
+    ref = oracle.page_scores(bt)
+    ref_ids = oracle.select_topk(bt, ref, 8)
+    units = [(b, h) for b in range(bt.batch) for h in range(bt.n_kv_heads)]
+    for b, h in units:
+        if not bt.streaming[h]:
+            check_selection(idn[b, h], int(cn[b, h]), ref[b, h], oracle.n_pages(bt.seq_lens[b], 64), 8, f"({b}, {h})")
+    check_selected_attention(dsa, bt, q, kv, st, idn, cn, (O, l, m), ref_ids, units, "streaming")
     # streaming heads really see only sink + local tokens
-    ref_ids = oracle.select_topk(bt, oracle.page_scores(bt), 8)
     for b in range(bt.batch):
         for h in (0, 3):
             assert np.array_equal(idn[b, h, :cn[b, h]], ref_ids[b][h])
@@ -232,11 +236,13 @@ def test_psa_random(gpu_lib, G, P, D, dtype):
 
 
 def _psa_check(dsa, bt, thr, mode):
+    """The progressive selection takes the oracle's scores (rounded to
+    float32) as its input; the oracle ranks and walks the same values."""
     q, kv, _ = to_device(dsa, bt)
-    meta = dsa.page_meta_build(kv)
-    sc = dsa.page_score(q, kv, meta)
+    s32 = oracle.page_scores(bt).astype(np.float32)
+    sc = torch.from_numpy(s32).cuda()
     ids, counts, O, l, m = dsa.page_select_progressive(q, kv, sc, thr, mode, float(bt.scale))
-    scn, idn, cn = np_(sc).astype(np.float64), np_(ids), np_(counts)
+    scn, idn, cn = s32.astype(np.float64), np_(ids), np_(counts)
     On, ln, mn = np_(O), np_(l), np_(m)
     G = bt.group
     for b in range(bt.batch):
@@ -325,7 +331,7 @@ def test_ema(gpu_lib, n):
         assert np.allclose(np_(pr), rp, rtol=1e-6, atol=1e-5)
     pr2 = torch.empty(n, device="cuda")
     dsa.ema_predict_update(None, lv, tr, pr2, a, b_, g)
-    assert np.allclose(np_(pr2), oracle.ema_predict(np_(lv), np_(tr), g), rtol=1e-6, atol=1e-5)
+    assert np.allclose(np_(pr2), oracle.ema_predict(rl, rt, g), rtol=1e-6, atol=1e-5)
 
 
 # ---------------------------------------------------------------- HIP graph replay

@@ -24,14 +24,17 @@ def test_prr_select_matches_separate_calls(gpu_lib, max_pages, k, k_spec):
     lens = [P * max_pages, P * (max_pages // 2) + 5, 7]
     bt = wl.random_batch(91, lens, n_q_heads=4, n_kv_heads=2, head_dim=64, page_size=P, max_pages=max_pages)
     q, kv, _ = to_device(dsa, bt)
-    meta = dsa.page_meta_build(kv)
     B, H, N = bt.batch, bt.n_kv_heads, max_pages
-    rng = torch.Generator(device="cuda").manual_seed(5)
-    lvl0 = torch.randn(B * H * N, device="cuda", generator=rng)
-    trd0 = torch.randn(B * H * N, device="cuda", generator=rng)
+    # inputs from the host: the oracle's scores (rounded to float32, -inf past
+    # each sequence) and seeded EMA state
+    s_h = oracle.page_scores(bt).astype(np.float32)
+    hr0 = np.random.default_rng(5)
+    lvl_h = hr0.standard_normal(B * H * N).astype(np.float32)
+    trd_h = hr0.standard_normal(B * H * N).astype(np.float32)
+    lvl0, trd0 = torch.from_numpy(lvl_h).cuda(), torch.from_numpy(trd_h).cuda()
     i32 = torch.int32
     for init in (True, False):
-        sc = dsa.page_score(q, kv, meta)
+        sc = torch.from_numpy(s_h).cuda()
         # fused
         lv1, tr1, pr1 = lvl0.clone(), trd0.clone(), torch.empty(B * H * N, device="cuda")
         a1, ac1 = torch.empty((B, H, k), dtype=i32, device="cuda"), torch.empty((B, H), dtype=i32, device="cuda")
@@ -47,11 +50,19 @@ def test_prr_select_matches_separate_calls(gpu_lib, max_pages, k, k_spec):
         assert np.array_equal(np_(pc1), np_(pc2)) and np.array_equal(np_(p1), np_(p2)), "P differs"
         for x, y, what in ((lv1, lv2, "level"), (tr1, tr2, "trend"), (pr1, pr2, "pred")):
             assert np.array_equal(np_(x), np_(y)), f"{what} differs from dsa_ema_predict_update"
-        scn, prn = np_(sc).astype(np.float64), np_(pr1).astype(np.float64).reshape(B, H, N)
+        # the prediction in the kernel's float32 arithmetic, then both selections
+        if init:
+            pr_ref = s_h.reshape(-1)
+        else:
+            pr_ref = oracle.ema_predict_f32(*oracle.ema_step_f32(s_h.reshape(-1), lvl_h, trd_h, 0.6, 0.3), 0.25)
+        assert np.array_equal(np_(pr1), pr_ref), "prediction differs from the oracle's float32 EMA"
+        scn, prn = s_h.astype(np.float64), pr_ref.astype(np.float64).reshape(B, H, N)
+        ref_a = {}
         for b in range(B):
             n_valid = oracle.n_pages(bt.seq_lens[b], P)
             for h in range(H):
-                assert np.array_equal(np_(a1)[b, h, :np_(ac1)[b, h]], oracle.topk_pages(scn[b, h], n_valid, k))
+                ref_a[b, h] = oracle.topk_pages(scn[b, h], n_valid, k)
+                assert np.array_equal(np_(a1)[b, h, :np_(ac1)[b, h]], ref_a[b, h])
                 assert np.array_equal(np_(p1)[b, h, :np_(pc1)[b, h]], oracle.topk_pages(prn[b, h], n_valid, k_spec))
         # with this step's speculative set: M = A \ P_cur, the rest unchanged
         hr = np.random.default_rng(11)
@@ -73,7 +84,7 @@ def test_prr_select_matches_separate_calls(gpu_lib, max_pages, k, k_spec):
         assert torch.equal(a3, a1) and torch.equal(ac3, ac1) and torch.equal(p3, p1) and torch.equal(pr3, pr1)
         for b in range(B):
             for h in range(H):
-                ref = oracle.missing_pages(np_(a1)[b, h, :np_(ac1)[b, h]], pcur[b, h, :pcnt[b, h]])
+                ref = oracle.missing_pages(ref_a[b, h], pcur[b, h, :pcnt[b, h]])
                 n = int(np_(mc3)[b, h])
                 assert n == len(ref) and np.array_equal(np_(m3)[b, h, :n], ref), f"M differs ({b}, {h})"
                 assert np.all(np_(m3)[b, h, n:] == -1)
@@ -155,12 +166,13 @@ def test_prr_select_split_rows(gpu_lib, kind):
             nv = oracle.n_pages(lens[b], P)
             for h in range(H):
                 a = spl["a"][b, h, :spl["ac"][b, h]]
-                assert np.array_equal(a, oracle.topk_pages(s[b, h].astype(np.float64), nv, k))
+                ra = oracle.topk_pages(s[b, h].astype(np.float64), nv, k)
+                assert np.array_equal(a, ra)
                 assert np.all(spl["a"][b, h, spl["ac"][b, h]:] == -1)
                 p = spl["p"][b, h, :spl["pc"][b, h]]
                 assert np.array_equal(p, oracle.topk_pages(prn[b, h], nv, k_spec))
                 assert np.all(spl["p"][b, h, spl["pc"][b, h]:] == -1)
-                ref = oracle.missing_pages(a, pcur[b, h, :pcnt[b, h]])
+                ref = oracle.missing_pages(ra, pcur[b, h, :pcnt[b, h]])
                 n = int(spl["mc"][b, h])
                 assert n == len(ref) and np.array_equal(spl["m"][b, h, :n], ref)
                 assert np.all(spl["m"][b, h, n:] == -1)
@@ -204,8 +216,9 @@ def test_prr_select_split_edges(gpu_lib, N, lens, k):
         nv = oracle.n_pages(lens[b], P)
         for h in range(H):
             a = spl["a"][b, h, :spl["ac"][b, h]]
-            assert np.array_equal(a, oracle.topk_pages(s[b, h].astype(np.float64), nv, k))
+            ra = oracle.topk_pages(s[b, h].astype(np.float64), nv, k)
+            assert np.array_equal(a, ra)
             assert np.array_equal(spl["p"][b, h, :spl["pc"][b, h]], oracle.topk_pages(prn[b, h], nv, k_spec))
-            ref = oracle.missing_pages(a, pcur[b, h, :pcnt[b, h]])
+            ref = oracle.missing_pages(ra, pcur[b, h, :pcnt[b, h]])
             n = int(spl["mc"][b, h])
             assert n == len(ref) and np.array_equal(spl["m"][b, h, :n], ref)

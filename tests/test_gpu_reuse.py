@@ -12,7 +12,7 @@ import torch
 import oracle
 import workloads as wl
 from dynamic_sparse_attention_page_amd.reuse import ChunkedReuseDecoder
-from parity_util import check_attention, check_selection, ids_lists, np_, to_device
+from parity_util import check_selected_attention, check_selection, np_, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -35,7 +35,8 @@ def test_chunked_reuse_matches_oracle(gpu_lib, dtype, P, Pl, streaming):
     for t in range(len(qs)):
         opens = dec.selects_now
         assert opens == (t % 4 == 0)
-        O, l, m = dec.step(dsa.upload_q(qs[t], dtype))
+        qd = dsa.upload_q(qs[t], dtype)
+        O, l, m = dec.step(qd)
         torch.cuda.synchronize()
         ids, cnt = np_(dec.ids), np_(dec.counts)
         s = oracle.chunk_start(t, 4)
@@ -50,10 +51,12 @@ def test_chunked_reuse_matches_oracle(gpu_lib, dtype, P, Pl, streaming):
                     else:
                         check_selection(ids[b, h], int(cnt[b, h]), ref_sc[b, h], n, k, f"t={t} b={b} h={h}")
             kept = (ids.copy(), cnt.copy())
+            ref_ids = oracle.select_topk(bt, ref_sc, k)   # the oracle's own chunk selection
         else:
             assert np.array_equal(ids, kept[0]) and np.array_equal(cnt, kept[1]), f"t={t}: kept pages changed"
-        rO, rl, rm = oracle.sparse_decode(bt, ids_lists(ids, cnt), qs[t])
-        check_attention(dtype, np_(O), np_(l), np_(m), rO, rl, rm, f"step {t}")
+        bq = wl.Batch(**{**bt.__dict__, "q": qs[t]})
+        units = [(b, h) for b in range(bt.batch) for h in range(bt.n_kv_heads)]
+        check_selected_attention(dsa, bq, qd, kv, st, ids, cnt, (O, l, m), ref_ids, units, f"step {t}")
 
 
 def test_chunk_one_is_the_per_step_pipeline(gpu_lib):
