@@ -23,6 +23,9 @@
 #ifndef DSA_SCORE_PIPE
 #define DSA_SCORE_PIPE 1  // 1: the next rows' loads overlap the current rows' scores
 #endif
+#ifndef DSA_SCORE_MIN_PPW
+#define DSA_SCORE_MIN_PPW 8  // fewest physical pages per wave while the grid keeps >= 1024 waves
+#endif
 #ifndef DSA_SCORE_WAVES
 #define DSA_SCORE_WAVES 8192  // target waves of the score grid
 #endif
@@ -313,7 +316,9 @@ static int launch_score_g(const void* q, const dsa_kv* kv, const void* meta, int
   // fewer, longer waves read less of it
   const long long target_waves = (long long)DSA_SCORE_WAVES * 4 / (G > 4 ? G : 4);
   long long ppw = (units * kv->max_pages + target_waves - 1) / target_waves;
-  ppw = ppw < 4 ? 4 : (ppw > 64 ? 64 : ppw);
+  // small grids take fewer, longer waves, unless that would leave under 1024
+  const long long min_ppw = units * kv->max_pages >= (long long)DSA_SCORE_MIN_PPW * 1024 ? DSA_SCORE_MIN_PPW : 4;
+  ppw = ppw < min_ppw ? min_ppw : (ppw > 64 ? 64 : ppw);
   ppw = (ppw + 3) / 4 * 4;
   const int waves = ceil_div(kv->max_pages, ppw);
   const int wgs = ceil_div(waves, 4);
