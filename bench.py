@@ -65,6 +65,8 @@ def parse():
     ap.add_argument("--replicas", type=int, default=0, help="0 = enough for > 1 GiB per rotation")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU oracle sample")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-workers", type=int, default=min(16, len(os.sched_getaffinity(0))),
+                    help="processes of the parallel oracle sample (1: single-threaded only)")
     ap.add_argument("--delta-profile", action="store_true",
                     help="prr_512k: also run PRR's offline speculation-budget profile (4K-64K contexts)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -144,6 +146,37 @@ def streaming_bytes(bt):
 # --------------------------------------------------------------------------
 # CPU baseline (the oracle as it stands)
 # --------------------------------------------------------------------------
+def _cpu_sample(bt):
+    """Units the oracle runs on: all of them, or a fixed sample of 16 for
+    larger batches (scaled by the fraction)."""
+    units = None
+    if bt.batch * bt.n_kv_heads > 16:
+        rng = np.random.default_rng(0)
+        all_units = [(b, h) for b in range(bt.batch) for h in range(bt.n_kv_heads)]
+        units = set(all_units[i] for i in rng.choice(len(all_units), 16, replace=False))
+    frac = 1.0 if units is None else len(units) / (bt.batch * bt.n_kv_heads)
+    return units, frac
+
+
+def _oracle_unit(bt, meta, has, b, h, scores=None):
+    """One (sequence, KV head) of a decode step through the oracle: scores,
+    selection, attention (PSA: the progressive walk)."""
+    import oracle
+    if scores is None:
+        scores = oracle.page_scores(bt, meta=meta, has=has, units={(b, h)})
+    if bt.topk is None:
+        oracle.psa_progressive(bt, b, h, scores[b, h], bt.threshold, 0)
+        return
+    n = oracle.n_pages(bt.seq_lens[b], bt.page_size)
+    if bt.streaming is not None and bt.streaming[h]:
+        ids = oracle.streaming_pages(bt.seq_lens[b], bt.page_size, bt.sink, bt.local)
+    else:
+        ids = oracle.topk_pages(scores[b, h], n, bt.topk)
+    oracle.attend_pages(bt, b, h, ids)
+    if bt.threshold is not None:
+        oracle.psa_progressive(bt, b, h, scores[b, h], bt.threshold, 0)
+
+
 def cpu_baseline(bt, budget_s):
     """The oracle, single-threaded, on whole decode steps of the workload
     (PRR: the plain selection + attention its repair reproduces), repeated
@@ -152,12 +185,7 @@ def cpu_baseline(bt, budget_s):
     16 units and scale by the fraction."""
     import oracle
     from threadpoolctl import threadpool_limits
-    units = None
-    if bt.batch * bt.n_kv_heads > 16:
-        rng = np.random.default_rng(0)
-        all_units = [(b, h) for b in range(bt.batch) for h in range(bt.n_kv_heads)]
-        units = set(all_units[i] for i in rng.choice(len(all_units), 16, replace=False))
-    frac = 1.0 if units is None else len(units) / (bt.batch * bt.n_kv_heads)
+    units, frac = _cpu_sample(bt)
     meta, has = oracle.page_meta(bt, units)          # prefill-time work, not timed
     steps, t_used = 0, 0.0
     with threadpool_limits(1):
@@ -168,17 +196,7 @@ def cpu_baseline(bt, budget_s):
                 for h in range(bt.n_kv_heads):
                     if units is not None and (b, h) not in units:
                         continue
-                    if bt.topk is None:
-                        oracle.psa_progressive(bt, b, h, scores[b, h], bt.threshold, 0)
-                        continue
-                    n = oracle.n_pages(bt.seq_lens[b], bt.page_size)
-                    if bt.streaming is not None and bt.streaming[h]:
-                        ids = oracle.streaming_pages(bt.seq_lens[b], bt.page_size, bt.sink, bt.local)
-                    else:
-                        ids = oracle.topk_pages(scores[b, h], n, bt.topk)
-                    oracle.attend_pages(bt, b, h, ids)
-                    if bt.threshold is not None:
-                        oracle.psa_progressive(bt, b, h, scores[b, h], bt.threshold, 0)
+                    _oracle_unit(bt, meta, has, b, h, scores)
             t_used += time.perf_counter() - t0
             steps += 1
     sample = (f"{steps} whole decode steps" if units is None else
@@ -186,6 +204,45 @@ def cpu_baseline(bt, budget_s):
               f"{1 / frac:.0f},")
     return {"value": bt.batch * steps * frac / t_used, "unit": "queries/s", "cores": 1, "kind": "oracle",
             "sample": f"{sample} of the workload; {t_used:.1f} s single-threaded fp64 numpy"}
+
+
+_PAR = None   # (batch, meta, has) inherited by the forked oracle workers
+
+
+def _par_unit(u):
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(1):
+        _oracle_unit(*_PAR, *u)
+
+
+def cpu_baseline_parallel(bt, budget_s, workers):
+    """The same oracle steps with the (sequence, KV head) units spread over a
+    pool of `workers` single-threaded processes (fork: call it before the GPU
+    is touched); wall time per step."""
+    import multiprocessing as mp
+
+    import oracle
+    global _PAR
+    units, frac = _cpu_sample(bt)
+    ulist = sorted(units) if units is not None else [(b, h) for b in range(bt.batch) for h in range(bt.n_kv_heads)]
+    workers = min(workers, len(ulist))
+    if workers < 2:
+        return None
+    meta, has = oracle.page_meta(bt, units)
+    _PAR = (bt, meta, has)
+    steps, t_used = 0, 0.0
+    with mp.get_context("fork").Pool(workers) as pool:
+        pool.map(_par_unit, ulist[:workers], chunksize=1)          # start-up, untimed
+        while t_used < budget_s:
+            t0 = time.perf_counter()
+            pool.map(_par_unit, ulist, chunksize=1)
+            t_used += time.perf_counter() - t0
+            steps += 1
+    _PAR = None
+    return {"value": bt.batch * steps * frac / t_used, "unit": "queries/s", "cores": workers, "kind": "oracle",
+            "sample": f"{steps} decode steps of {len(ulist)} (sequence, KV head) units"
+                      f"{'' if units is None else f' (sampled, scaled by {1 / frac:.0f})'} over {workers} "
+                      f"single-threaded processes; {t_used:.1f} s wall"}
 
 
 # --------------------------------------------------------------------------
@@ -347,12 +404,16 @@ def main():
     import workloads as wl
     import dynamic_sparse_attention_page_amd as dsa
 
-    torch.cuda.set_device(0)
-    dev = torch.device("cuda", 0)
     if a.workload == PREFILL:
+        torch.cuda.set_device(0)
         run_prefill(a, dsa, torch, wl)
         return
     bt = wl.make(a.workload)
+    cpu_par = None
+    if not a.no_cpu and a.cpu_workers > 1:   # forks: before the GPU is initialised
+        cpu_par = cpu_baseline_parallel(bt, a.cpu_seconds, a.cpu_workers)
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
     B, Hq, Hkv, D, N = bt.batch, bt.n_q_heads, bt.n_kv_heads, bt.head_dim, bt.max_pages
     scale = float(bt.scale)
     st = None if bt.streaming is None else dsa.Streaming(bt.streaming, bt.sink, bt.local)
@@ -629,6 +690,8 @@ def main():
     res.update(extra)
     if not a.no_cpu:
         res["cpu_baseline"] = cpu_baseline(bt, a.cpu_seconds)
+        if cpu_par is not None:
+            res["cpu_baseline_parallel"] = cpu_par
     print(json.dumps(res), flush=True)
 
 
