@@ -708,3 +708,27 @@ def test_quest_bias_pages_have_cosine_0_4_and_rank_high():
             assert np.allclose(cos, 0.4, atol=0.01)        # bf16 rounding of the keys
         ranks = np.argsort(np.argsort(-S[0, h, :256]))
         assert np.median(ranks[pages]) < 64
+
+
+def test_golden_calibration_grid():
+    """tests/golden/prr_calibration_grid.txt holds the search space the PRR
+    page prints (section 3.2); the oracle's grid is its full product with
+    alpha slowest and gamma fastest, and has the printed count."""
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", "prr_calibration_grid.txt")
+    spec, count = {}, None
+    for line in open(path):
+        f = line.split("#")[0].split()
+        if not f:
+            continue
+        if f[0] == "count":
+            count = int(f[1])
+        else:
+            first, last, step = (float(x) for x in f[1:4])
+            n = int(round((last - first) / step)) + 1
+            spec[f[0]] = [first + i * step for i in range(n)]
+    want = [(a, b, g) for a in spec["alpha"] for b in spec["beta"] for g in spec["gamma"]]
+    grid = oracle.calibration_grid()
+    assert len(want) == count == len(grid)
+    for x, y in zip(grid, want):
+        assert x == pytest.approx(y, abs=1e-12)
