@@ -5,19 +5,27 @@
 A step is the whole hot path for one batch of decode queries on inputs
 already resident in HBM; page metadata is built beforehand (prefill work).
 
-  quest_gqa_32k (default)  page_score -> sparse_decode_attn_topk (top-k selection + sparse
+With no --workload (or --workload all) every workload below runs, each in a
+child process of its own and one after the other, and one JSON line is
+printed: the headline fields are those of psa_mha_64k, the largest workload
+(8 sequences, an 8 GiB bf16 pool, about 0.56 GB of algorithmic bytes per
+step), and "workloads" holds the full result of each of the others, timed in
+the same run the same way.
+
+  psa_mha_64k (headline)   page_score -> page_select_progressive (threshold 0.95)
+      batch 8, 32 heads MHA, d=128, 65536 tokens in 16-token pages, bf16
+  quest_gqa_32k            page_score -> sparse_decode_attn_topk (top-k selection + sparse
       attention in one call; the separate page_select_topk and sparse_decode_attn are
       timed beside it)
       batch 1, 32 q / 8 KV heads, d=128, 32768 tokens in 16-token pages, top-256, bf16
   lserve_hier_128k         the same calls with 64/16 hierarchical paging and
       4 of 8 KV heads streaming (sink 128 + local 256); batch 4, 131072 tokens, top-64
-  psa_mha_64k              page_score -> page_select_progressive (threshold 0.95)
-      batch 8, 32 heads MHA, 65536 tokens
   prr_512k                 PRR: score and one launch selecting A and (after the EMA
-      update) the next speculative set, on a side stream overlapped with the
-      speculative attention; then the repair;
+      update) the next speculative set, overlapped with the speculative attention;
+      then the repair;
       batch 1, 32 q / 2 KV heads, 524288 tokens, top-2048, 64-step query trace
   tiny_f32                 score, top-8, attention and PSA on one fp32 head
+  lserve_prefill_16k       LServe block-sparse prefill of one 16K-token prompt
 
 Each timed step reads a different replica of the KV pool and metadata (R
 copies at distinct addresses, R * per-step bytes > 1 GiB) so the 256 MB
@@ -54,6 +62,8 @@ MFMA_BF16_TFLOPS = 2500.0        # dense bf16 matrix-core peak
 T_CAL = 32   # steps of the score trace the PRR calibration searches over
 REUSE_CHUNK = 4   # LServe's default selector-reuse interval
 WORKLOADS = ["quest_gqa_32k", "lserve_hier_128k", "psa_mha_64k", "prr_512k", "tiny_f32"]
+HEADLINE = "psa_mha_64k"   # the largest workload: its fields head the line
+SUB_WORKLOADS = ["quest_gqa_32k", "lserve_hier_128k", "prr_512k", "tiny_f32", PREFILL]
 
 
 def parse():
@@ -61,9 +71,11 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="quest_gqa_32k", choices=list(WORKLOADS) + [PREFILL])
+    ap.add_argument("--workload", default="all", choices=["all"] + list(WORKLOADS) + [PREFILL])
     ap.add_argument("--replicas", type=int, default=0, help="0 = enough for > 1 GiB per rotation")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU oracle sample")
+    ap.add_argument("--sub-cpu-seconds", type=float, default=5.0,
+                    help="budget of each CPU oracle sample of the workloads after the headline (--workload all)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-workers", type=int, default=min(16, len(os.sched_getaffinity(0))),
                     help="processes of the parallel oracle sample (1: single-threaded only)")
@@ -391,6 +403,37 @@ def run_prefill(a, dsa, torch, wl):
     print(json.dumps(res), flush=True)
 
 
+def run_all(a):
+    """Every workload in a child process of its own, one after the other
+    (each forks its CPU oracle pool before touching the GPU; this process
+    never touches it); prints the headline workload's line with the other
+    results under "workloads"."""
+    import subprocess
+    results = {}
+    for w in [HEADLINE] + SUB_WORKLOADS:
+        cmd = [sys.executable, os.path.abspath(__file__), "--workload", w, "--steps", str(a.steps), "--warmup",
+               str(a.warmup), "--cpu-workers", str(a.cpu_workers),
+               "--cpu-seconds", str(a.cpu_seconds if w == HEADLINE else a.sub_cpu_seconds)]
+        if a.no_cpu:
+            cmd.append("--no-cpu")
+        if a.replicas:
+            cmd += ["--replicas", str(a.replicas)]
+        print(f"bench: {w} ...", file=sys.stderr, flush=True)
+        t0 = time.perf_counter()
+        r = subprocess.run(cmd, stdout=subprocess.PIPE, text=True)
+        lines = [x for x in r.stdout.splitlines() if x.startswith("{")]
+        if r.returncode != 0 or not lines:
+            sys.stderr.write(r.stdout)
+            print(f"bench: {w} failed (exit {r.returncode})", file=sys.stderr, flush=True)
+            sys.exit(r.returncode or 1)
+        results[w] = json.loads(lines[-1])
+        print(f"bench: {w} done in {time.perf_counter() - t0:.1f} s: {results[w]['value']:.1f} "
+              f"{results[w]['unit']}", file=sys.stderr, flush=True)
+    head = dict(results[HEADLINE])
+    head["workloads"] = {w: results[w] for w in SUB_WORKLOADS}
+    print(json.dumps(head), flush=True)
+
+
 def main():
     a = parse()
     if a.copy_calibration:
@@ -400,6 +443,9 @@ def main():
         print(json.dumps({"error": "this build runs on exactly one GPU; multi-GPU sharding is described "
                                    "in the design notes but not built", "n_gpus": a.gpus}))
         sys.exit(2)
+    if a.workload == "all":
+        run_all(a)
+        return
     import torch
     import workloads as wl
     import dynamic_sparse_attention_page_amd as dsa

@@ -198,10 +198,20 @@ _ws_cache: dict = {}
 
 
 def _workspace(nbytes: int, device) -> torch.Tensor:
-    key = (str(device),)
+    """Scratch for calls given no `ws`: one buffer per (device, stream), so
+    calls on different streams never share one.  Calls enqueued on one
+    stream run in order, so they may share it.  A buffer that grows is
+    replaced; the old one is marked as used by its stream, so the caching
+    allocator does not hand its memory out before the work queued there has
+    finished.  Kernels never need the content initialised."""
+    dev = torch.device(device)
+    stream = torch.cuda.current_stream(dev)
+    key = (str(dev), stream.cuda_stream)
     t = _ws_cache.get(key)
     if t is None or t.numel() < nbytes:
-        t = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)   # tickets start at zero
+        if t is not None:
+            t.record_stream(stream)
+        t = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
         _ws_cache[key] = t
     return t
 

@@ -36,6 +36,7 @@ import bisect
 import math
 from dataclasses import dataclass, field
 
+import numpy as np
 import torch
 
 from . import (OP_ATTN_REPAIR, PagedKV, attn_repair, ema_predict_update, page_score, page_score_ema,
@@ -217,17 +218,43 @@ def choose_delta(t_select_us: float, t_spec_us: dict) -> float:
 
 @dataclass
 class DeltaTable:
-    """(context tokens, delta) pairs, ascending in context."""
+    """(context tokens, delta) pairs, ascending in context, and optionally
+    the profiled timings behind them: {context: (select_us, {delta:
+    spec_us})}.  Inside the profiled range the pairs are looked up; past the
+    longest profiled context the timings are extrapolated (section 3.4 of
+    the page profiles 4K-64K and extends the table to longer contexts by
+    polynomial regression)."""
     entries: list = field(default_factory=list)
+    timings: dict = field(default_factory=dict)
 
     def lookup(self, context_tokens: int) -> float:
         """delta of the longest profiled context not above context_tokens
-        (of the shortest one for shorter contexts)."""
+        (of the shortest one for shorter contexts); beyond the longest
+        profiled context, the delta chosen on extrapolated timings when the
+        table holds them."""
         if not self.entries:
             raise ValueError("empty delta table")
         ctx = [c for c, _ in self.entries]
+        if int(context_tokens) > ctx[-1] and len(self.timings) >= 2:
+            return self.extrapolate(int(context_tokens))
         i = bisect.bisect_right(ctx, int(context_tokens)) - 1
         return self.entries[max(i, 0)][1]
+
+    def extrapolate(self, context_tokens: int, degree: int = 2) -> float:
+        """Least-squares polynomials in the context length (degree 2, or
+        lower when fewer contexts were profiled) through the selection
+        window and through each delta's speculative-attention time, taken at
+        context_tokens, then the same choice as inside the table."""
+        ctx = sorted(self.timings)
+        deg = min(degree, len(ctx) - 1)
+        x = np.asarray(ctx, dtype=np.float64)
+
+        def at(values):
+            return float(np.polyval(np.polyfit(x, np.asarray(values, dtype=np.float64), deg), context_tokens))
+        t_sel = at([self.timings[c][0] for c in ctx])
+        deltas = sorted(self.timings[ctx[0]][1])
+        t_spec = {d: at([self.timings[c][1][d] for c in ctx]) for d in deltas}
+        return choose_delta(t_sel, t_spec)
 
 
 def _time_us(fn, reps: int, trials: int = 7) -> float:
@@ -263,7 +290,7 @@ def profile_delta_table(n_q_heads: int = 32, n_kv_heads: int = 2, head_dim: int 
     dev = torch.device("cuda", torch.cuda.current_device())
     gen = torch.Generator(device=dev)
     gen.manual_seed(seed)
-    entries, report = [], {}
+    entries, report, timings = [], {}, {}
     for L in sorted(contexts):
         N = -(-L // page_size)
         k = max(1, N // sparsity)
@@ -287,6 +314,7 @@ def profile_delta_table(n_q_heads: int = 32, n_kv_heads: int = 2, head_dim: int 
             t_spec[d] = _time_us(lambda: sparse_decode_attn(q, kv, ids, cnt, out=out, ws=ws), reps)
         delta = choose_delta(t_sel, t_spec)
         entries.append((L, delta))
+        timings[L] = (t_sel, dict(t_spec))
         report[L] = {"pages": N, "k": k, "select_us": round(t_sel, 3),
                      "spec_us": {str(d): round(v, 3) for d, v in t_spec.items()}, "delta": delta}
-    return DeltaTable(entries), report
+    return DeltaTable(entries, timings), report
