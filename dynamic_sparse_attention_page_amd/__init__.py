@@ -19,9 +19,9 @@ import torch
 __all__ = [
     "DsaError", "PagedKV", "Streaming", "lib", "LIB_PATH",
     "page_meta_build", "kv_append", "page_score", "page_score_ema", "page_select_topk", "page_select_progressive",
-    "sparse_decode_attn", "sparse_decode_attn_topk", "attn_repair", "ema_predict_update", "prr_select", "prr_calibrate", "signal_host", "block_sparse_prefill",
+    "sparse_decode_attn", "sparse_decode_attn_noalloc", "sparse_decode_attn_topk", "attn_repair", "ema_predict_update", "prr_select", "prr_calibrate", "signal_host", "block_sparse_prefill",
     "workspace_bytes",
-    "OP_SPARSE_DECODE_ATTN", "OP_ATTN_REPAIR", "EXPORTED", "prr_select_workspace_bytes",
+    "OP_SPARSE_DECODE_ATTN", "OP_ATTN_REPAIR", "EXPORTED", "prr_select_workspace_bytes", "NOALLOC_SCRATCH_BYTES",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsa.so")
@@ -31,7 +31,8 @@ OP_SPARSE_DECODE_ATTN, OP_ATTN_REPAIR = 1, 2
 EXPORTED = (
     "dsa_status_str", "dsa_version", "dsa_page_meta_build", "dsa_kv_append", "dsa_page_score", "dsa_page_score_ema",
     "dsa_page_select_topk",
-    "dsa_page_select_progressive", "dsa_sparse_decode_attn", "dsa_sparse_decode_attn_topk", "dsa_attn_repair",
+    "dsa_page_select_progressive", "dsa_sparse_decode_attn", "dsa_sparse_decode_attn_noalloc",
+    "dsa_sparse_decode_attn_topk", "dsa_attn_repair",
     "dsa_ema_predict_update", "dsa_prr_select", "dsa_prr_select_workspace_bytes", "dsa_prr_calibrate",
     "dsa_prr_calibrate_workspace_bytes",
     "dsa_signal_host", "dsa_block_sparse_prefill",
@@ -75,6 +76,7 @@ def _load(path: str = LIB_PATH):
         "dsa_page_select_topk": (ctypes.c_int, [P, I32, I32, I32, P, I32, I32, ST, P, P, P]),
         "dsa_page_select_progressive": (ctypes.c_int, [P, I32, KV, P, F32, I32, F32, P, P, P, P, P, P]),
         "dsa_sparse_decode_attn": (ctypes.c_int, [P, I32, KV, P, P, I32, ST, F32, P, P, P, P, SZ, P]),
+        "dsa_sparse_decode_attn_noalloc": (ctypes.c_int, [P, I32, KV, P, P, I32, ST, F32, P, P, P, P]),
         "dsa_sparse_decode_attn_topk": (ctypes.c_int, [P, I32, KV, P, I32, ST, F32, P, P, P, P, P, P, SZ, P]),
         "dsa_attn_repair": (ctypes.c_int, [P, I32, KV, P, P, P, P, I32, F32, P, P, P, P, SZ, P]),
         "dsa_ema_predict_update": (ctypes.c_int, [P, P, P, P, I64, F32, F32, F32, I32, P]),
@@ -335,6 +337,22 @@ def sparse_decode_attn(q: torch.Tensor, kv: PagedKV, ids: torch.Tensor, counts: 
     _check("dsa_sparse_decode_attn", lib.dsa_sparse_decode_attn(
         _ptr(q), Hq, ctypes.byref(kv.c()), _ptr(ids), _ptr(counts), stride, _stream_arg(streaming), sc,
         _ptr(O), _ptr(l), _ptr(m), _ptr(ws), ws.numel() * ws.element_size(), _stream()))
+    return O, l, m
+
+
+NOALLOC_SCRATCH_BYTES = 8 << 20   # DSA_NOALLOC_SCRATCH_BYTES of include/dsa.h
+
+
+def sparse_decode_attn_noalloc(q: torch.Tensor, kv: PagedKV, ids: torch.Tensor, counts: torch.Tensor,
+                               O: torch.Tensor, l: torch.Tensor, m: torch.Tensor, streaming: Streaming | None = None,
+                               scale: float | None = None):
+    """sparse_decode_attn into caller-given outputs with no workspace: the
+    library's fixed per-GPU scratch holds the partials (calls on one GPU must
+    not overlap in time)."""
+    sc = _default_scale(kv.head_dim) if scale is None else scale
+    _check("dsa_sparse_decode_attn_noalloc", lib.dsa_sparse_decode_attn_noalloc(
+        _ptr(q), q.shape[1], ctypes.byref(kv.c()), _ptr(ids), _ptr(counts), ids.shape[-1], _stream_arg(streaming),
+        sc, _ptr(O), _ptr(l), _ptr(m), _stream()))
     return O, l, m
 
 

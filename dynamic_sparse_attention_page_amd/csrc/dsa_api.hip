@@ -11,6 +11,7 @@ extern "C" const char* dsa_status_str(int status) {
     case DSA_ERR_WORKSPACE: return "workspace missing or too small";
     case DSA_ERR_ALIGN: return "pointer not 16-byte aligned";
     case DSA_ERR_LAUNCH: return "kernel launch failed";
+    case DSA_ERR_SCRATCH: return "needs more than the fixed no-allocation scratch";
   }
   return "unknown status";
 }

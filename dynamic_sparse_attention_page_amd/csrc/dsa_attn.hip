@@ -23,6 +23,8 @@
 #include "dsa_host.hpp"
 #include "dsa_select.hpp"
 
+#include <mutex>
+
 #ifndef DSA_SPLIT_TARGET
 #define DSA_SPLIT_TARGET 384  // target workgroups of the split-KV grid
 #endif
@@ -953,21 +955,88 @@ extern "C" size_t dsa_workspace_bytes(int32_t op, const dsa_kv* kv, int32_t n_q_
   return 0;
 }
 
+// Validation shared by dsa_sparse_decode_attn and its no-allocation variant;
+// on success *need holds the scratch bytes of the call (0 when nothing runs).
+static int check_sparse_decode_attn(const void* q, int32_t n_q_heads, const dsa_kv* kv, const int32_t* ids,
+                                    const int32_t* counts, int32_t ids_stride, const dsa_stream_cfg* stream_cfg,
+                                    float scale, const float* O, const float* l, const float* m, int* G,
+                                    uint64_t* smask, size_t* need) {
+  *need = 0;
+  int rc = check_attn_common(q, n_q_heads, kv, scale, G);
+  if (rc) return rc;
+  if (ids_stride < 1) return DSA_ERR_SHAPE;
+  if ((rc = streaming_mask(stream_cfg, kv->n_kv_heads, smask))) return rc;
+  if (kv->batch == 0) return DSA_OK;
+  if (!ids || !counts || !O || !l || !m) return DSA_ERR_NULL;
+  *need = dsa_workspace_bytes(DSA_OP_SPARSE_DECODE_ATTN, kv, n_q_heads, ids_stride);
+  return DSA_OK;
+}
+
 extern "C" int dsa_sparse_decode_attn(const void* q, int32_t n_q_heads, const dsa_kv* kv, const int32_t* ids,
                                       const int32_t* counts, int32_t ids_stride, const dsa_stream_cfg* stream_cfg,
                                       float scale, float* O, float* l, float* m, void* ws, size_t ws_bytes,
                                       void* stream) {
   int G = 0;
-  int rc = check_attn_common(q, n_q_heads, kv, scale, &G);
-  if (rc) return rc;
-  if (ids_stride < 1) return DSA_ERR_SHAPE;
-  uint64_t smask;
-  if ((rc = streaming_mask(stream_cfg, kv->n_kv_heads, &smask))) return rc;
-  if (kv->batch == 0) return DSA_OK;
-  if (!ids || !counts || !O || !l || !m) return DSA_ERR_NULL;
-  const size_t need = dsa_workspace_bytes(DSA_OP_SPARSE_DECODE_ATTN, kv, n_q_heads, ids_stride);
+  uint64_t smask = 0;
+  size_t need = 0;
+  int rc = check_sparse_decode_attn(q, n_q_heads, kv, ids, counts, ids_stride, stream_cfg, scale, O, l, m, &G,
+                                    &smask, &need);
+  if (rc || kv->batch == 0) return rc;
   if (!ws || ws_bytes < need) return DSA_ERR_WORKSPACE;
   if (!aligned16(ws)) return DSA_ERR_ALIGN;
+  const int sink = stream_cfg ? stream_cfg->sink : 0, local = stream_cfg ? stream_cfg->local : 0;
+  return launch_attn(q, G, kv, ids, counts, ids_stride, smask, sink, local, scale, O, l, m, ws, 0, nullptr,
+                     nullptr, SelectArgs{}, (hipStream_t)stream);
+}
+
+// ------------------------------------------------------------ no-allocation variant
+// The split partials of dsa_sparse_decode_attn_noalloc live in this
+// file-scope device array instead of a caller workspace.  Each GPU the
+// library runs on holds its own copy, at its own address, until the process
+// ends.  In host code `scratch` names a host-side stand-in, never the device
+// memory: kernels get the address that hipGetSymbolAddress returns for the
+// device, looked up once per device and kept in scratch_dev.
+static __device__ __align__(256) unsigned char scratch[DSA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+static std::mutex scratch_mu;
+static void* scratch_dev[kMaxDevices];
+
+// Device address of `scratch` on the device that owns `stream`, looked up
+// with that device current the first time (the caller's current device is
+// restored afterwards).
+static int scratch_address(hipStream_t stream, void** out) {
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return DSA_ERR_LAUNCH;
+  hipDevice_t dev = cur;
+  if (stream && hipStreamGetDevice(stream, &dev) != hipSuccess) return DSA_ERR_LAUNCH;
+  if (dev < 0 || dev >= kMaxDevices) return DSA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_dev[dev]) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return DSA_ERR_LAUNCH;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur && hipSetDevice(cur) != hipSuccess) return DSA_ERR_LAUNCH;
+    if (e != hipSuccess || !p) return DSA_ERR_LAUNCH;
+    scratch_dev[dev] = p;
+  }
+  *out = scratch_dev[dev];
+  return DSA_OK;
+}
+
+extern "C" int dsa_sparse_decode_attn_noalloc(const void* q, int32_t n_q_heads, const dsa_kv* kv,
+                                              const int32_t* ids, const int32_t* counts, int32_t ids_stride,
+                                              const dsa_stream_cfg* stream_cfg, float scale, float* O, float* l,
+                                              float* m, void* stream) {
+  int G = 0;
+  uint64_t smask = 0;
+  size_t need = 0;
+  int rc = check_sparse_decode_attn(q, n_q_heads, kv, ids, counts, ids_stride, stream_cfg, scale, O, l, m, &G,
+                                    &smask, &need);
+  if (rc || kv->batch == 0) return rc;
+  if (need > (size_t)DSA_NOALLOC_SCRATCH_BYTES) return DSA_ERR_SCRATCH;
+  void* ws = nullptr;
+  if ((rc = scratch_address((hipStream_t)stream, &ws))) return rc;
   const int sink = stream_cfg ? stream_cfg->sink : 0, local = stream_cfg ? stream_cfg->local : 0;
   return launch_attn(q, G, kv, ids, counts, ids_stride, smask, sink, local, scale, O, l, m, ws, 0, nullptr,
                      nullptr, SelectArgs{}, (hipStream_t)stream);

@@ -84,7 +84,9 @@ enum {
   DSA_ERR_UNSUPPORTED = -4, /* valid but not built (head_dim, group, ...)     */
   DSA_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than required        */
   DSA_ERR_ALIGN = -6,       /* pointer not 16-byte aligned                    */
-  DSA_ERR_LAUNCH = -7       /* the HIP runtime rejected a launch              */
+  DSA_ERR_LAUNCH = -7,      /* the HIP runtime rejected a launch              */
+  DSA_ERR_SCRATCH = -8      /* the call needs more than the fixed scratch of
+                               dsa_sparse_decode_attn_noalloc                 */
 };
 
 enum { DSA_F32 = 0, DSA_BF16 = 1 };
@@ -271,6 +273,32 @@ int dsa_sparse_decode_attn(const void *q, int32_t n_q_heads, const dsa_kv *kv,
                            const int32_t *ids, const int32_t *counts, int32_t ids_stride,
                            const dsa_stream_cfg *stream_cfg, float scale, float *O, float *l,
                            float *m, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * dsa_sparse_decode_attn_noalloc -- dsa_sparse_decode_attn for callers that
+ * cannot allocate: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments, semantics and results
+ * as dsa_sparse_decode_attn (the same kernels run), minus the workspace:
+ * the split partials go to a fixed device array inside the library, of
+ * DSA_NOALLOC_SCRATCH_BYTES bytes, that each GPU the library runs on holds
+ * until the process ends.  The call allocates nothing, ever.
+ *
+ * Limit: a call that needs more scratch than that, i.e.
+ * dsa_workspace_bytes(DSA_OP_SPARSE_DECODE_ATTN, kv, n_q_heads, ids_stride)
+ * > DSA_NOALLOC_SCRATCH_BYTES, returns DSA_ERR_SCRATCH and enqueues nothing.
+ * Every call on one GPU shares that GPU's array (its content carries over
+ * from the last call and is never read before it is written), so calls
+ * that overlap in time on one GPU -- on different streams, or from several
+ * host threads -- race and must be avoided; calls on one stream are
+ * ordered and safe.  The first call on a device looks up the array's
+ * address on that device (the stream's device, or the current device for
+ * the NULL stream).
+ */
+#define DSA_NOALLOC_SCRATCH_BYTES (8u << 20)
+int dsa_sparse_decode_attn_noalloc(const void *q, int32_t n_q_heads, const dsa_kv *kv,
+                                   const int32_t *ids, const int32_t *counts, int32_t ids_stride,
+                                   const dsa_stream_cfg *stream_cfg, float scale, float *O, float *l,
+                                   float *m, void *stream);
 
 /*
  * dsa_sparse_decode_attn_topk -- dsa_page_select_topk followed by

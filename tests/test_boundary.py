@@ -176,3 +176,26 @@ def test_empty_inputs_are_noops(dsa):
     assert L.dsa_ema_predict_update(None, None, None, None, 0, 0.6, 0.3, 0.25, 0, None) == 0
     assert L.dsa_sparse_decode_attn(None, 4, ctypes.byref(kv), None, None, 8, None, 0.1, None, None, None, None,
                                     0, None) == 0
+
+
+def test_noalloc_validation(dsa):
+    """The no-allocation variant validates like the workspace call and
+    refuses, before any HIP call, a shape whose partials exceed its fixed
+    scratch; batch 0 is a no-op."""
+    L = dsa.lib
+    P, F = ctypes.c_void_p, ctypes.c_float
+    ok_ptr = P(4096)
+    kv = _kv(dsa)
+    assert L.dsa_sparse_decode_attn_noalloc(None, 4, ctypes.byref(kv), ok_ptr, ok_ptr, 8, None, F(0.088), ok_ptr,
+                                            ok_ptr, ok_ptr, None) == -1
+    assert L.dsa_sparse_decode_attn_noalloc(ok_ptr, 4, ctypes.byref(kv), ok_ptr, ok_ptr, 0, None, F(0.088), ok_ptr,
+                                            ok_ptr, ok_ptr, None) == -2
+    big = _kv(dsa, max_pages=8192)
+    need = L.dsa_workspace_bytes(1, ctypes.byref(big), 32, 8192)
+    assert need > dsa.NOALLOC_SCRATCH_BYTES
+    assert L.dsa_sparse_decode_attn_noalloc(ok_ptr, 32, ctypes.byref(big), ok_ptr, ok_ptr, 8192, None, F(0.088),
+                                            ok_ptr, ok_ptr, ok_ptr, None) == -8
+    assert b"no-allocation scratch" in L.dsa_status_str(-8)
+    empty = _kv(dsa, batch=0, page_table=0, seq_lens=0)
+    assert L.dsa_sparse_decode_attn_noalloc(None, 4, ctypes.byref(empty), None, None, 8, None, F(0.1), None, None,
+                                            None, None) == 0
