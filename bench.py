@@ -524,8 +524,13 @@ def main():
                                                                bt.topk, ids=decs[r].a_ids, counts=decs[r].a_counts),
             "sparse_decode_attn": lambda r: dsa.sparse_decode_attn(q, kvs[r], decs[r].p_ids, decs[r].p_counts,
                                                                    scale=scale, out=(O, l, m), ws=decs[r].ws),
-            "attn_repair": lambda r: dsa.attn_repair(q, kvs[r], decs[r].a_ids, decs[r].a_counts, decs[r].p_ids,
-                                                     decs[r].p_counts, O, l, m, scale=scale, ws=decs[r].ws),
+            # the repair as the decoder runs it: over the missing set M = A \ P the selection wrote
+            "attn_repair": lambda r: dsa.attn_repair(q, kvs[r], decs[r].m_ids, decs[r].m_counts, None, None, O, l,
+                                                     m, scale=scale, ws=decs[r].ws),
+            # the same repair given A and P (M formed inside, through an LDS bitmap of P)
+            "attn_repair_filter": lambda r: dsa.attn_repair(q, kvs[r], decs[r].a_ids, decs[r].a_counts,
+                                                            decs[r].p_ids, decs[r].p_counts, O, l, m, scale=scale,
+                                                            ws=decs[r].ws),
             "ema_predict_update": lambda r: dsa.ema_predict_update(decs[r].scores, decs[r].level, decs[r].trend,
                                                                    decs[r].pred, a_, b_, g_),
             "prr_select": lambda r: dsa.prr_select(decs[r].scores, kvs[r].seq_lens, bt.page_size, bt.topk,
@@ -538,7 +543,8 @@ def main():
                                                          False, decs[r].k_spec, decs[r].a_ids, decs[r].a_counts,
                                                          decs[r].p_ids, decs[r].p_counts, ws=sel_ws),
         }
-        op_bytes = {"page_score": mb, "sparse_decode_attn": kvb, "ema_predict_update": B * Hkv * N * 24}
+        op_bytes = {"page_score": mb, "sparse_decode_attn": kvb, "ema_predict_update": B * Hkv * N * 24,
+                    "attn_repair": int(miss_rate * kvb)}
         # online calibration of (alpha, beta, gamma) over the 80-candidate grid
         # on a score trace of T_CAL steps (runs beside prefill, not in the step)
         cal_trace = torch.from_numpy(wl.score_trace(77, T_CAL, B * Hkv, N)).to(dev)

@@ -25,22 +25,18 @@
 
 #include <mutex>
 
-#ifndef DSA_SPLIT_TARGET
-#define DSA_SPLIT_TARGET 384  // target workgroups of the split-KV grid
+#ifndef DSA_TILES_PER_WAVE
+#define DSA_TILES_PER_WAVE 2  // 16-token K/V tiles per wave of the VALU partial kernel (all in flight at once)
 #endif
-#ifndef DSA_MFMA_SPLIT_DIV
-#define DSA_MFMA_SPLIT_DIV 2  // the matrix-core grid targets DSA_SPLIT_TARGET / this
-#endif
-#ifndef DSA_MFMA_DEPTH
-#define DSA_MFMA_DEPTH 2  // K/V tiles in flight per wave (matrix-core kernel)
-#endif
-#ifndef DSA_COMBINE_NB
-#define DSA_COMBINE_NB 8  // splits per batch and wave in the combine
+#ifndef DSA_TILES_PER_WAVE_MFMA
+#define DSA_TILES_PER_WAVE_MFMA 4  // the same for the matrix-core partial kernel
 #endif
 
 namespace dsa {
 
 constexpr int kWgWaves = 4;
+constexpr int kTilesPerWave = DSA_TILES_PER_WAVE;
+constexpr int kTilesPerWaveMfma = DSA_TILES_PER_WAVE_MFMA;
 
 // Fused selection (dsa_sparse_decode_attn_topk): each split workgroup ranks
 // its row of scores itself and takes the entries of its range; split 0
@@ -181,34 +177,31 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
   const size_t slot_stride = (size_t)n_kv_heads * P * D;
   const size_t head_off = (size_t)h * P * D;
 
-  // Software pipeline: tile t+4 (this wave's next) is loaded while t is computed.
-  uint32_t ka[4][DW], va[4][DW], kb[4][DW], vb[4][DW];
-  int nva = 0, tka = 0, nvb = 0, tkb = 0;
-  auto fetch = [&](int t, uint32_t (&kd)[4][DW], uint32_t (&vd)[4][DW], int& nvalid, int& tok0) {
-    nvalid = 0;
-    tok0 = 0;
-    if (t >= t_end) return;
-    const int e = t / TPP - first_entry, tin = t % TPP;
-    const int page = __builtin_amdgcn_readlane(my_page, e);   // e is wave-uniform
+  // The TW tiles of this wave (t_begin + wave + 4i) are loaded together and
+  // then computed in order: every load is issued before the first wait, and
+  // unconditionally (a tile past the split's end, or of a page without a
+  // slot, re-reads tile 0 of slot 0 of this head and is skipped), so no
+  // wait covers a load that is not needed yet.
+  constexpr int TW = kTilesPerWave;
+  uint32_t kd[TW][4][DW], vd[TW][4][DW];
+  int nv[TW], tk[TW];
+#pragma unroll
+  for (int i = 0; i < TW; ++i) {
+    const int t = t_begin + wave + kWgWaves * i;
+    const int e = t / TPP - first_entry, tin = t % TPP;   // e < 64: a split holds at most 64 entries
+    const int page = __builtin_amdgcn_readlane(my_page, e);
     const int slot = __builtin_amdgcn_readlane(my_slot, e);
-    if (slot < 0) return;
-    tok0 = page * P + tin * 16;
-    nvalid = min(16, L - tok0);
-    const size_t off = (size_t)slot * slot_stride + head_off + (size_t)tin * 16 * D;
-    A::load_tile(k + off, lane, kd);
-    A::load_tile(v + off, lane, vd);
-  };
-  int t = t_begin + wave;
-  fetch(t, ka, va, nva, tka);
-  while (t < t_end) {
-    fetch(t + kWgWaves, kb, vb, nvb, tkb);
-    if (nva > 0) st.tile(ka, va, nva, smask, tka, L, sink, local, c);
-    t += kWgWaves;
-    if (t >= t_end) break;
-    fetch(t + kWgWaves, ka, va, nva, tka);
-    if (nvb > 0) st.tile(kb, vb, nvb, smask, tkb, L, sink, local, c);
-    t += kWgWaves;
+    const bool ok = t < t_end && slot >= 0;
+    tk[i] = page * P + tin * 16;
+    nv[i] = ok ? min(16, L - tk[i]) : 0;
+    const size_t off = ok ? (size_t)slot * slot_stride + head_off + (size_t)tin * 16 * D : head_off;
+    A::load_tile(k + off, lane, kd[i]);
+    A::load_tile(v + off, lane, vd[i]);
+    __builtin_amdgcn_sched_barrier(0);   // keep the issue order tile by tile (K, V, next tile)
   }
+#pragma unroll
+  for (int i = 0; i < TW; ++i)
+    if (nv[i] > 0) st.tile(kd[i], vd[i], nv[i], smask, tk[i], L, sink, local, c);
 
   const size_t pbase = ((size_t)unit * n_splits + split) * G;
   if constexpr (G <= 4) {
@@ -347,38 +340,28 @@ __global__ __launch_bounds__(256) void attn_partial_mfma_kernel(
   const size_t slot_stride = (size_t)n_kv_heads * P * D;
   const size_t head_off = (size_t)h * P * D;
 
-  auto fetch = [&](int t, uint4 (&kd)[NK], uint4 (&vd)[NK], int& nvalid, int& tok0) {
-    nvalid = 0;
-    tok0 = 0;
-    if (t >= t_end) return;
-    const int e = t / TPP - first_entry, tin = t % TPP;
+  // The TW tiles of this wave, loaded together and computed in order (see
+  // attn_partial_kernel).
+  constexpr int TW = kTilesPerWaveMfma;
+  uint4 kr[TW][NK], vr[TW][NK];
+  int nv[TW], tk[TW];
+#pragma unroll
+  for (int i = 0; i < TW; ++i) {
+    const int t = t_begin + wave + kWgWaves * i;
+    const int e = t / TPP - first_entry, tin = t % TPP;   // e < 64: a split holds at most 64 entries
     const int page = __builtin_amdgcn_readlane(my_page, e);
     const int slot = __builtin_amdgcn_readlane(my_slot, e);
-    if (slot < 0) return;
-    tok0 = page * P + tin * 16;
-    nvalid = min(16, L - tok0);
-    const size_t off = (size_t)slot * slot_stride + head_off + (size_t)tin * 16 * D;
-    M::load_k(k + off, lane, kd);
-    M::load_v(v + off, lane, vd);
-  };
-  // a ring of DEPTH tiles per wave: slot d is refilled right after its tile
-  // is computed, so DEPTH - 1 loads stay in flight behind the computation
-  constexpr int DEPTH = DSA_MFMA_DEPTH;
-  uint4 kr[DEPTH][NK], vr[DEPTH][NK];
-  int nv[DEPTH], tk[DEPTH];
-  const int t0 = t_begin + wave;
-#pragma unroll
-  for (int d = 0; d < DEPTH; ++d) fetch(t0 + d * kWgWaves, kr[d], vr[d], nv[d], tk[d]);
-  for (int t = t0; t < t_end; t += DEPTH * kWgWaves) {
-#pragma unroll
-    for (int d = 0; d < DEPTH; ++d) {
-      const int td = t + d * kWgWaves;
-      if (td < t_end) {
-        if (nv[d] > 0) st.tile(kr[d], vr[d], nv[d], smask, tk[d], L, sink, local, c);
-        fetch(td + DEPTH * kWgWaves, kr[d], vr[d], nv[d], tk[d]);
-      }
-    }
+    const bool ok = t < t_end && slot >= 0;
+    tk[i] = page * P + tin * 16;
+    nv[i] = ok ? min(16, L - tk[i]) : 0;
+    const size_t off = ok ? (size_t)slot * slot_stride + head_off + (size_t)tin * 16 * D : head_off;
+    M::load_k(k + off, lane, kr[i]);
+    M::load_v(v + off, lane, vr[i]);
+    __builtin_amdgcn_sched_barrier(0);   // keep the issue order tile by tile (K, V, next tile)
   }
+#pragma unroll
+  for (int i = 0; i < TW; ++i)
+    if (nv[i] > 0) st.tile(kr[i], vr[i], nv[i], smask, tk[i], L, sink, local, c);
 
   // wave states meet in LDS: lane holds O[head h][16n + 4g + j]
   const float lsum = st.total_l();
@@ -412,111 +395,102 @@ __global__ __launch_bounds__(256) void attn_partial_mfma_kernel(
 }
 
 // ============================================================ combine
-// One workgroup (4 waves) per (sequence, q head).  Wave w folds splits w,
-// w+4, ... with the online-softmax merge, lanes over channels; the partials
-// of all n_splits splits are loaded without waiting for the count (entries
-// of inactive splits are never written and are selected away, not
-// multiplied), so the count, the (m, l) pairs and the outputs arrive in one
-// round trip.  The 4 wave states meet in LDS.  For repair the caller's
-// (O, l, m) is one more term.  Writes normalised O.
+// One workgroup per (sequence, q head).  The active splits are merged with
+// the online-softmax rule in chunks of 64: every thread first issues the
+// loads of all the O values it needs from the chunk (thread (sub, c) takes
+// channel c of splits sub, sub + SPT, ...), wave 0 loads the chunk's
+// (m, l) pairs, one per lane, and turns them into merge weights against the
+// running maximum (wave reductions, no barrier), and after one barrier every
+// thread folds its values.  So a chunk costs one memory round trip, and
+// rows of up to 64 splits (every top-k and repair call here) exactly one.
+// For repair the caller's (O, l, m) is one more term.  Writes normalised O.
 template <int D>
 __global__ __launch_bounds__(256) void attn_combine_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_ml, const int32_t* __restrict__ counts,
     int ids_stride, int n_kv_heads, int G, int TPP, int tiles_per_split, int n_splits, int fold,
     float* __restrict__ O, float* __restrict__ l, float* __restrict__ m) {
-  constexpr int CPT = D / 64;
-  __shared__ float s_acc[4][D];
-  __shared__ float s_ml[4][2];
+  constexpr int SPT = 256 / D;   // split lanes per channel
+  constexpr int CH = 64;         // splits per chunk
+  constexpr int PER = CH / SPT;  // O values per thread and chunk
+  __shared__ float s_w[CH];
+  __shared__ float s_acc[SPT][D];
+  __shared__ float s_alpha, s_M, s_L;
   const int hq = blockIdx.x, b = blockIdx.y;
   const int Hq = n_kv_heads * G;
   const int h = hq / G, g = hq % G;
   const int unit = b * n_kv_heads + h;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int cnt = counts[unit];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c = tid % D, sub = tid / D;   // sub is uniform within a wave
   const size_t row = (size_t)b * Hq + hq;
-  float m_in = kNegInf, l_in = 0.0f, o_in[CPT];
-  if (fold && wave == 0) {
-    m_in = m[row];
-    l_in = l[row];
-#pragma unroll
-    for (int x = 0; x < CPT; ++x) o_in[x] = O[row * D + lane + 64 * x];
-  }
+  int cnt = counts[unit];
   cnt = cnt < 0 ? 0 : (cnt > ids_stride ? ids_stride : cnt);
   const int active = min(n_splits, (cnt * TPP + tiles_per_split - 1) / tiles_per_split);
+  const size_t base = (size_t)unit * n_splits * G + g;   // split s: partial row base + s * G
+  // the caller's (O, l, m) for repair, read before any of it is rewritten
+  // (the writes follow the last barrier)
+  float o_in = 0.0f, m_in = kNegInf, l_in = 0.0f;
+  if (fold && tid < D) {
+    o_in = O[row * D + c];
+    m_in = m[row];
+    l_in = l[row];
+  }
 
-  float mw = kNegInf, lw = 0.0f, acc[CPT];
+  float acc = 0.0f;
+  float M = kNegInf, Lw = 0.0f;   // running max and denominator (wave 0)
+  for (int s0 = 0; s0 < active; s0 += CH) {
+    const int n = min(CH, active - s0);
+    float ov[PER];
 #pragma unroll
-  for (int x = 0; x < CPT; ++x) acc[x] = 0.0f;
-  constexpr int NB = DSA_COMBINE_NB;   // splits per batch and wave: all loads of a batch are in flight together
-  // one batch covers up to 4 * NB splits without waiting for the count;
-  // beyond that only the active splits are visited
-  const int lim = n_splits <= 4 * NB ? n_splits : active;
-  for (int s0 = wave; s0 < lim; s0 += 4 * NB) {
-    float ms[NB], lsp[NB], os[NB][CPT];
-#pragma unroll
-    for (int u = 0; u < NB; ++u) {
-      const int sp = min(s0 + 4 * u, max(lim, 1) - 1);   // in bounds; duplicates are masked below
-      const size_t pi = ((size_t)unit * n_splits + sp) * G + g;
-      ms[u] = part_ml[pi * 2];
-      lsp[u] = part_ml[pi * 2 + 1];
-#pragma unroll
-      for (int x = 0; x < CPT; ++x) os[u][x] = part_o[pi * D + lane + 64 * x];
+    for (int j = 0; j < PER; ++j) {
+      const int sp = s0 + min(sub + SPT * j, n - 1);   // in bounds; the surplus is weighted out
+      ov[j] = part_o[(base + (size_t)sp * G) * D + c];
     }
-    float mb = kNegInf;
-    bool ok[NB];
+    if (wave == 0) {
+      const int sp = s0 + min(lane, n - 1);
+      float ms = part_ml[(base + (size_t)sp * G) * 2];
+      const float ls = part_ml[(base + (size_t)sp * G) * 2 + 1];
+      if (lane >= n || !(ls > 0.0f)) ms = kNegInf;    // surplus lanes and empty splits drop out
+      float mb = ms;
 #pragma unroll
-    for (int u = 0; u < NB; ++u) {
-      ok[u] = s0 + 4 * u < active && ms[u] != kNegInf && lsp[u] > 0.0f;   // inactive or empty splits drop out
-      if (ok[u]) mb = fmaxf(mb, ms[u]);
+      for (int d = 1; d < 64; d <<= 1) mb = fmaxf(mb, __shfl_xor(mb, d, 64));
+      const float Mn = fmaxf(M, mb);
+      const float w = (ms == kNegInf) ? 0.0f : expf(ms - Mn);
+      const float alpha = (M == kNegInf) ? 0.0f : expf(M - Mn);
+      float lw = w * (ms == kNegInf ? 0.0f : ls);
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) lw += __shfl_xor(lw, d, 64);
+      Lw = fmaf(Lw, alpha, lw);
+      M = Mn;
+      s_w[lane] = w;
+      if (lane == 0) s_alpha = alpha;
     }
-    if (mb == kNegInf) continue;                      // uniform across the wave
-    const float mn = fmaxf(mw, mb);
-    const float a = (mw == kNegInf) ? 0.0f : expf(mw - mn);
-    lw *= a;
+    __syncthreads();
+    const float alpha = s_alpha;
+    acc *= alpha;
 #pragma unroll
-    for (int x = 0; x < CPT; ++x) acc[x] *= a;
-#pragma unroll
-    for (int u = 0; u < NB; ++u) {
-      const float wt = ok[u] ? expf(ms[u] - mn) : 0.0f;
-      lw = fmaf(ok[u] ? lsp[u] : 0.0f, wt, lw);
-#pragma unroll
-      for (int x = 0; x < CPT; ++x) acc[x] = fmaf(ok[u] ? os[u][x] : 0.0f, wt, acc[x]);
-    }
-    mw = mn;
+    for (int j = 0; j < PER; ++j) acc = fmaf(ov[j], s_w[sub + SPT * j], acc);   // s_w is 0 past n
+    __syncthreads();   // s_w and s_alpha are rewritten by the next chunk
   }
-  if (wave == 0 && fold && l_in > 0.0f && m_in != kNegInf) {   // the caller's (O, l, m): O is normalised
-    const float mn = fmaxf(mw, m_in);
-    const float a = (mw == kNegInf) ? 0.0f : expf(mw - mn);
-    const float wt = expf(m_in - mn) * l_in;
-    lw = fmaf(lw, a, wt);
-#pragma unroll
-    for (int x = 0; x < CPT; ++x) acc[x] = fmaf(acc[x], a, o_in[x] * wt);
-    mw = mn;
-  }
-#pragma unroll
-  for (int x = 0; x < CPT; ++x) s_acc[wave][lane + 64 * x] = acc[x];
-  if (lane == 0) { s_ml[wave][0] = mw; s_ml[wave][1] = lw; }
+  if (wave == 0 && lane == 0) { s_M = M; s_L = Lw; }
+  s_acc[sub][c] = acc;
   __syncthreads();
-  if (wave == 0) {
-    const float M = fmaxf(fmaxf(s_ml[0][0], s_ml[1][0]), fmaxf(s_ml[2][0], s_ml[3][0]));
-    float wts[4], L = 0.0f;
+  if (tid < D) {
+    float Mf = s_M, Lf = s_L, o = 0.0f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      wts[w] = (s_ml[w][0] == kNegInf) ? 0.0f : expf(s_ml[w][0] - M);
-      L = fmaf(s_ml[w][1], wts[w], L);
+    for (int x = 0; x < SPT; ++x) o += s_acc[x][c];
+    if (fold && l_in > 0.0f && m_in != kNegInf) {   // the caller's term: its O is normalised
+      const float Mn = fmaxf(Mf, m_in);
+      const float a = (Mf == kNegInf) ? 0.0f : expf(Mf - Mn);
+      const float wt = expf(m_in - Mn) * l_in;
+      o = fmaf(o, a, o_in * wt);
+      Lf = fmaf(Lf, a, wt);
+      Mf = Mn;
     }
-    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-#pragma unroll
-    for (int x = 0; x < CPT; ++x) {
-      const int c = lane + 64 * x;
-      float o = 0.0f;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) o = fmaf(s_acc[w][c], wts[w], o);
-      O[row * D + c] = o * inv;
-    }
-    if (lane == 0) {
-      l[row] = L;
-      m[row] = L > 0.0f ? M : kNegInf;
+    O[row * D + c] = Lf > 0.0f ? o / Lf : 0.0f;
+    if (c == 0) {
+      l[row] = Lf;
+      m[row] = Lf > 0.0f ? Mf : kNegInf;
     }
   }
 }
@@ -776,36 +750,29 @@ struct SplitPlan {
   int tiles_per_split, n_splits, TPP;
 };
 
-// Tiles per workgroup so that about DSA_SPLIT_TARGET workgroups cover the
-// largest possible selection (counts live on the device, so the grid is
-// sized for ids_stride).  The matrix-core tile (8+ heads) is cheap enough
-// for twice the tiles per workgroup; the smaller grid also leaves CUs to a
-// kernel running beside it (PRR's selection runs beside its speculative
-// attention).
-inline SplitPlan plan_splits(const dsa_kv* kv, int ids_stride, int n_streaming_heads, int G) {
+// A split is one workgroup: 4 waves of TW tiles each, all in flight at once
+// (TW = kTilesPerWaveMfma for the matrix-core kernel, 8+ heads per KV head
+// with bf16 KV), so the grid grows with the selection: counts live on the
+// device, so it is sized for ids_stride entries, and splits past a row's
+// count exit at once.
+inline SplitPlan plan_splits(const dsa_kv* kv, int ids_stride, bool mfma) {
   SplitPlan p;
-  const long long target = G >= 8 ? DSA_SPLIT_TARGET / DSA_MFMA_SPLIT_DIV : DSA_SPLIT_TARGET;
   p.TPP = kv->page_size / 16;
   const long long tiles_max = (long long)ids_stride * p.TPP;
-  const int dense_heads = kv->n_kv_heads - n_streaming_heads;
-  const long long total = tiles_max * kv->batch * (dense_heads > 0 ? dense_heads : 1);
-  // a split's pages must fit the 64 lanes that resolve them
-  const long long cap = 64LL * p.TPP < 128 ? 64LL * p.TPP : 128;
-  long long tps = 2 * kWgWaves;
-  while (tps < cap && total / tps > target) tps <<= 1;
-  p.tiles_per_split = (int)tps;
-  p.n_splits = (int)((tiles_max + tps - 1) / tps);
+  p.tiles_per_split = kWgWaves * (mfma ? kTilesPerWaveMfma : kTilesPerWave);
+  p.n_splits = (int)((tiles_max + p.tiles_per_split - 1) / p.tiles_per_split);
   if (p.n_splits < 1) p.n_splits = 1;
   return p;
 }
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Workspace for any plan of this shape: the smallest split size gives the
-// most splits.
+// Workspace for any plan of this shape: the smallest split gives the most
+// splits.
 inline size_t max_splits_of(const dsa_kv* kv, int ids_stride) {
+  constexpr int kMinTiles = kWgWaves * (kTilesPerWave < kTilesPerWaveMfma ? kTilesPerWave : kTilesPerWaveMfma);
   const size_t tiles_max = (size_t)ids_stride * (kv->page_size / 16);
-  return (tiles_max + 2 * kWgWaves - 1) / (2 * kWgWaves);
+  return (tiles_max + kMinTiles - 1) / kMinTiles;
 }
 
 inline size_t partial_bytes(const dsa_kv* kv, int G, int ids_stride) {
@@ -819,11 +786,7 @@ static int launch_attn_g(const void* q, const dsa_kv* kv, const int32_t* ids, co
                          int ids_stride, uint64_t smask, int sink, int local, float scale, float* O, float* l,
                          float* m, void* ws, int fold, const int32_t* skip_ids, const int32_t* skip_counts,
                          const SelectArgs& sel, hipStream_t st) {
-  SplitPlan p = plan_splits(kv, ids_stride, __builtin_popcountll(smask), G);
-  if (sel.fine) {   // the smallest split: a short id list still spreads over many workgroups
-    p.tiles_per_split = 2 * kWgWaves;
-    p.n_splits = (int)max_splits_of(kv, ids_stride);
-  }
+  const SplitPlan p = plan_splits(kv, ids_stride, sizeof(T) == 2 && G >= 8);
   const size_t units = (size_t)kv->batch * kv->n_kv_heads;
   float* part_o = (float*)ws;
   float* part_ml = (float*)((char*)ws + align256(units * max_splits_of(kv, ids_stride) * G * D * sizeof(float)));
@@ -1099,11 +1062,9 @@ extern "C" int dsa_attn_repair(const void* q, int32_t n_q_heads, const dsa_kv* k
     if ((int)lds + 52 * 1024 > max_lds_per_block()) return DSA_ERR_UNSUPPORTED;
   }
   // without P the a_ids are M already (usually a short prefix of the row):
-  // the plain split-KV path at the finest split, folded
-  SelectArgs sel{};
-  sel.fine = p_ids ? 0 : 1;
-  return launch_attn(q, G, kv, a_ids, a_counts, ids_stride, 0, 0, 0, scale, O, l, m, ws, 1, p_ids, p_counts, sel,
-                     (hipStream_t)stream);
+  // the plain split-KV path, folded; splits past the count exit at once
+  return launch_attn(q, G, kv, a_ids, a_counts, ids_stride, 0, 0, 0, scale, O, l, m, ws, 1, p_ids, p_counts,
+                     SelectArgs{}, (hipStream_t)stream);
 }
 
 extern "C" int dsa_page_select_progressive(const void* q, int32_t n_q_heads, const dsa_kv* kv, const float* scores,

@@ -83,3 +83,59 @@ def test_fused_exact_ties(gpu_lib):
     bt = wl.random_batch(83, [16 * 900 + 5, 16 * 400], n_q_heads=8, n_kv_heads=2, head_dim=128, max_pages=1000,
                          dup_pages=40)
     _run(dsa, bt, 30)
+
+
+def _host_scores(rng, B, H, N, kind):
+    """Adversarial float32 score rows for the selection inside the fused
+    call: exact ties (with -0 and +0), wide magnitude ranges with -inf,
+    +inf entries, a constant row and a two-valued row."""
+    if kind == "ties":
+        s = rng.integers(-3, 4, size=(B, H, N)).astype(np.float32)
+        s[s == 0] = np.where(rng.random((s == 0).sum()) < 0.5, -0.0, 0.0)
+    elif kind == "mixed":
+        s = (rng.standard_normal((B, H, N)) * 10.0 ** rng.integers(-3, 4, size=(B, H, N))).astype(np.float32)
+        s[rng.random((B, H, N)) < 0.02] = -np.inf
+        s[rng.random((B, H, N)) < 0.005] = np.inf
+    elif kind == "constant":
+        s = np.full((B, H, N), 7.25, np.float32)
+    else:  # two values, far apart
+        s = np.where(rng.random((B, H, N)) < 0.3, np.float32(1e30), np.float32(-1e-30)).astype(np.float32)
+    return s
+
+
+@pytest.mark.parametrize("N", [5, 64, 65, 700, 2048, 4096])
+@pytest.mark.parametrize("kind", ["ties", "mixed", "constant", "two"])
+def test_fused_selection_exact(gpu_lib, N, kind):
+    """Host-made scores fed to the fused call: its ids and counts equal the
+    oracle's top-k (ties to the lower index) bit for bit, for k in
+    {1, 63, 64, 65, N/16, N-1, N, N+5}, with ragged lengths; the attention is
+    checked against the oracle over those pages."""
+    dsa = gpu_lib
+    rng = np.random.default_rng(N * 13 + len(kind))
+    P = 16
+    lens = [N * P, max(0, N * P - 37), 3]
+    bt = wl.random_batch(91, lens, n_q_heads=8, n_kv_heads=2, head_dim=128, page_size=P, dtype="bf16",
+                         max_pages=N)
+    q, kv, _ = to_device(dsa, bt)
+    B, H = bt.batch, bt.n_kv_heads
+    s = _host_scores(rng, B, H, N, kind)
+    sc = torch.from_numpy(s).cuda()
+    for k in sorted({1, 63, 64, 65, max(1, N // 16), max(1, N - 1), N, N + 5}):
+        _banner(f"fused selection N={N} kind={kind} k={k}")
+        ids, cnt, O, l, m = dsa.sparse_decode_attn_topk(q, kv, sc, k)
+        torch.cuda.synchronize()
+        ids, cnt = np_(ids), np_(cnt)
+        ref_sel = {}
+        for b in range(B):
+            nv = oracle.n_pages(bt.seq_lens[b], P)
+            for h in range(H):
+                ref = oracle.topk_pages(s[b, h].astype(np.float64), nv, k)
+                assert cnt[b, h] == len(ref), (b, h, k)
+                assert np.array_equal(ids[b, h, :len(ref)], ref), (b, h, k)
+                assert np.all(ids[b, h, len(ref):] == -1)
+                ref_sel[(b, h)] = ref
+        if k in (64, N + 5):
+            units = [(b, h) for b in range(B) for h in range(H)]
+            ref_ids = [[ref_sel[(b, h)] for h in range(H)] for b in range(B)]
+            check_selected_attention(dsa, bt, q, kv, None, ids, cnt, (O, l, m), ref_ids, units,
+                                     f"fused selection N={N} {kind} k={k}")
