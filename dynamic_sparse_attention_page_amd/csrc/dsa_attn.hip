@@ -497,17 +497,34 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(
 
 // ============================================================ PSA progressive
 // One workgroup of NWV waves per (sequence, KV head).  Pages are taken in
-// rounds: the block radix select picks the next 64 (then 256) pages by score
-// among those not yet taken, a counting sort puts them in rank order (score
-// descending, lower index first on ties), and the walk attends to them NWV
-// at a time -- wave w computes the (o, l, m) of the page at rank cs + w.
-// The stop test of each group runs as prefix scans over NWV lanes of wave
-// 0: running log-sum of the block masses and running minimum, then the first
-// rank whose test passes ends the walk.  The visited blocks are folded into
-// the output with the online-softmax merge, in rank order.
-constexpr int kPsaMaxPages = 8192;
-constexpr int kPsaFirst = 64;    // pages of the first round
-constexpr int kPsaRound = 256;   // pages of each later round
+// rounds: the first round picks the 64 highest-ranked pages, each later
+// round the next 256 (rank: score descending, lower index first on equal
+// scores).  Rank order is the order of the 64-bit value
+// (score key << 32 | ~index), so the pages still in play are exactly those
+// whose value lies below that of the last page taken: a round keeps no
+// per-page state and re-reads the score row.
+//
+// A round's pick: when at most kPsaCand pages are in play they all become
+// candidates; otherwise radix passes over the pages in play (min / max,
+// a 2048-bucket LDS histogram, and a bucket search that every wave does for
+// itself from the histogram) narrow the range around the n_pick-th value
+// until the pages above the cut bucket plus those in it number at most
+// kPsaCand.  The candidates are ranked by counting, and the first n_pick
+// ranks are the round's pages in rank order.  The first pass maps the
+// score values linearly onto the buckets, later ones shift the key; once
+// the keys in play are all equal the passes run on the index.
+//
+// The walk attends to NWV pages at a time -- wave w to the page at rank
+// cs + w -- and every wave then evaluates the stop test of the group on the
+// same values (prefix scans over NWV lanes: running log-sum of the block
+// masses and running minimum), so the group needs one barrier.  The visited
+// blocks are folded into the output with the online-softmax merge, in rank
+// order.
+constexpr int kPsaMaxPages = 65536;
+constexpr int kPsaFirst = 64;     // pages of the first round
+constexpr int kPsaRound = 256;    // pages of each later round
+constexpr int kPsaCand = 512;     // most candidates ranked directly
+constexpr int kPsaRegKeys = 16;   // score keys a thread holds at once
 
 // 16 waves where a wave's tile state fits 128 registers, else 8
 template <typename T, int G>
@@ -519,8 +536,291 @@ __device__ __forceinline__ float log_add(float a, float b) {
   return mx + log1pf(expf(mn - mx));
 }
 
-// E scores per thread: rows up to E * NT pages (the launch takes the
-// smallest E that holds max_pages, so short rows carry no padding).
+__device__ __forceinline__ float readlane_f(float x, int src) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), src));
+}
+
+__device__ __forceinline__ unsigned long long page_order(uint32_t key, int idx) {
+  return ((unsigned long long)key << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)idx);
+}
+
+// Histogram buckets are stored with one pad word after every 32, so the 64
+// lanes of a wave reading 32 consecutive buckets each hit distinct banks.
+constexpr int kHistWords = kBuckets + kBuckets / 32;
+__device__ __forceinline__ int hist_at(uint32_t b) { return (int)(b + (b >> 5)); }
+
+template <int NW>
+struct PsaSmem {
+  unsigned hist[2][kHistWords];      // alternate passes use alternate buffers
+  uint32_t mm[2][2 * NW];
+  __align__(16) unsigned long long cand[kPsaCand];
+  int cand_slot[kPsaCand];
+  int n_cand[2];                     // candidate counters of alternate rounds
+  unsigned long long kbound;         // order value of the round's last page
+  int page[kPsaRound], slot[kPsaRound];   // the round's pages in rank order
+};
+
+// This thread's pages are idx = e * NT + tid, e < E.  Rows of at most
+// 8 * NT pages hold their keys and page-table entries in registers for a
+// whole round; longer rows stream the keys from the score row in chunks of
+// kPsaRegKeys per pass.
+template <int E, int NT>
+struct PsaKeys {
+  static constexpr bool kResident = E <= 8;
+  static constexpr int R = kResident ? E : kPsaRegKeys;
+  uint32_t key[R];
+  int slot[kResident ? R : 1];
+  const float* srow;
+  const int32_t* ptrow;
+  int max_pages, np, tid;
+
+  // every load is issued before the first use (addresses clamped into the row)
+  __device__ __forceinline__ void load(int e0) {
+    float v[R];
+    int t = tid;
+    // streamed keys are re-read by every pass: the empty asm hides that the
+    // addresses repeat, so the compiler does not keep them all live instead
+    if constexpr (!kResident) asm volatile("" : "+v"(t));
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int c = min((e0 + r) * NT + t, max_pages - 1);
+      v[r] = srow[c];
+      if constexpr (kResident) slot[r] = ptrow[c];
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) key[r] = order_key(v[r]);
+  }
+  __device__ __forceinline__ void round_start() {
+    if constexpr (kResident) load(0);
+  }
+  // f(e0) once per chunk of R element slots e0 .. e0 + R - 1 of this
+  // thread, with their keys (and, when resident, page-table entries) in
+  // key[] / slot[]; e0 is the same across the workgroup
+  template <class F>
+  __device__ __forceinline__ void each_chunk(F&& f) {
+    if constexpr (kResident) {
+      f(0);
+    } else {
+      for (int e0 = 0; e0 < E && e0 * NT < np; e0 += R) {
+        load(e0);
+        f(e0);
+      }
+    }
+  }
+  // f(key, idx, slot, valid) for every element slot of this thread, in
+  // step across the wave (valid: idx < np; slot only when resident)
+  template <class F>
+  __device__ __forceinline__ void each(F&& f) {
+    if constexpr (kResident) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int idx = r * NT + tid;
+        f(key[r], idx, slot[r], idx < np);
+      }
+    } else {
+      for (int e0 = 0; e0 < E && e0 * NT < np; e0 += R) {
+        load(e0);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const int idx = (e0 + r) * NT + tid;
+          f(key[r], idx, 0, idx < np);
+        }
+      }
+    }
+  }
+};
+
+// The n_pick highest-ranked of the n_act pages in play in round `round`
+// (all valid pages in round 0, FIRST; later, those whose order value is below kb),
+// in rank order into sm.page / sm.slot; kb becomes the order value of the
+// last one.  Candidates are ranked by counting.  Rounds
+// alternate candidate counters: a round clears the one of the round after
+// it, which every thread read before the ranking barrier of the round before.
+template <int E, int NW, bool FIRST>
+__device__ __forceinline__ void psa_pick(PsaKeys<E, NW * 64>& ks, int round, unsigned long long& kb, int n_act,
+                                         int n_pick, PsaSmem<NW>& sm) {
+  constexpr int NT = NW * 64;
+  const int tid = threadIdx.x, lane = tid & 63;
+  int* n_cand_p = &sm.n_cand[round & 1];
+  if (tid == 0) sm.n_cand[(round + 1) & 1] = 0;
+  const unsigned long long below = (1ull << lane) - 1ull;
+  const unsigned long long kb_in = kb;
+  auto live = [&](uint32_t key, int idx, bool valid) {
+    if constexpr (FIRST) return valid;
+    else return valid & (page_order(key, idx) < kb_in);
+  };
+  // range in play: level 0, keys in [lo, hi] (and, after a linear pass until
+  // the next min / max, in bucket pb of map pm); level 1, key t and ~index in
+  // [lo, hi].  The tests below are written without branches: both levels'
+  // terms are computed and the uniform level selects.
+  bool lvl1 = false;
+  uint32_t lo = 0u, hi = 0xFFFFFFFFu, t = 0u, pb = 0u;
+  bool pend = false;
+  BucketMap pm{}, map{};
+  uint32_t bstar = 0u;
+  bool cut = false;
+  int need = n_pick;
+  auto field = [&](uint32_t key, int idx) { return lvl1 ? 0xFFFFFFFFu - (uint32_t)idx : key; };
+  auto in_range = [&](uint32_t key, int idx) {
+    const uint32_t f = field(key, idx);
+    return (f >= lo) & (f <= hi) & (!lvl1 | (key == t)) & (!pend | (pm.linear(key) == pb));
+  };
+  auto above = [&](uint32_t key, int idx) {
+    const uint32_t f = field(key, idx);
+    return lvl1 ? ((key > t) | ((key == t) & (f > hi))) : (key > hi);
+  };
+  auto bucket = [&](uint32_t key, int idx) {
+    const uint32_t a = map.linear(key), b = map.shifted(field(key, idx));
+    return map.lin ? a : b;
+  };
+
+  if (n_pick < n_act && n_act > kPsaCand) {
+    bool first_hist = true;
+    // at most: a linear pass, three shift passes on the key, a min / max
+    // that finds the key equal, one shift pass on the index (< 2^16 apart)
+    for (int pass = 0; pass < 8; ++pass) {
+      unsigned* hist = sm.hist[pass & 1];
+      for (int x = tid; x < kHistWords; x += NT) hist[x] = 0u;   // last read two barriers ago
+      uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+      ks.each([&](uint32_t key, int idx, int, bool valid) {
+        if (live(key, idx, valid) && in_range(key, idx)) {
+          const uint32_t f = field(key, idx);
+          mn = min(mn, f);
+          mx = max(mx, f);
+        }
+      });
+      block_minmax_1b<NW>(mn, mx, sm.mm[pass & 1]);   // also orders the zeroing before the atomics
+      lo = mn;
+      hi = mx;
+      pend = false;
+      if (lo == hi) {
+        if (lvl1) break;   // one page left in range: the cut takes the whole range
+        lvl1 = true;
+        t = lo;
+        lo = 0u;
+        hi = 0xFFFFFFFFu;
+        continue;
+      }
+      const uint32_t span = hi - lo;
+      map.lo = lo;
+      map.shift = span < (uint32_t)kBuckets ? 0 : (32 - __clz((int)span) - 11);
+      map.lin = false;
+      map.f0 = 0.0f;
+      map.inv = 0.0f;
+      if (!lvl1 && first_hist && span >= (uint32_t)kBuckets) {
+        const float f0 = key_value(lo), f1 = key_value(hi);
+        const float inv = (float)(kBuckets - 1) / (f1 - f0);
+        if (__builtin_isfinite(f0) && __builtin_isfinite(f1) && __builtin_isfinite(f1 - f0) && f1 > f0 &&
+            __builtin_isfinite(inv) && inv > 0.0f) {
+          map.lin = true;
+          map.f0 = f0;
+          map.inv = inv;
+        }
+      }
+      first_hist = false;
+      ks.each([&](uint32_t key, int idx, int, bool valid) {
+        if (live(key, idx, valid) && in_range(key, idx)) atomicAdd(&hist[hist_at(bucket(key, idx))], 1u);
+      });
+      __syncthreads();
+      // bucket search, in every wave: lane x sums buckets [kBuckets - 32(x+1), kBuckets - 32x);
+      // the lane whose buckets hold the need-th page is found by a scan,
+      // then its 32 buckets are scanned across lanes 0..31 from the top down
+      static_assert(kBuckets == 64 * 32, "32 buckets per lane");
+      int mine = 0;
+      {
+        const unsigned* h0 = hist + hist_at(kBuckets - 32 * (lane + 1));
+#pragma unroll
+        for (int x = 0; x < 32; ++x) mine += (int)h0[x];
+      }
+      const int incl = wave_incl_scan(mine);
+      const unsigned long long hm = __ballot(incl - mine < need && need <= incl);
+      const int src = __ffsll((long long)hm) - 1;
+      const int acc0 = __builtin_amdgcn_readlane(incl - mine, src);   // pages in higher lanes' buckets
+      const int sb0 = kBuckets - 32 * (src + 1);
+      const int hb = lane < 32 ? (int)hist[hist_at(sb0 + 31 - lane)] : 0;
+      const int pre = wave_incl_scan(hb);
+      const unsigned long long fm = __ballot(lane < 32 && acc0 + pre >= need);
+      const int fl = __ffsll((long long)fm) - 1;
+      bstar = (uint32_t)(sb0 + 31 - fl);
+      const int above_b = acc0 + __builtin_amdgcn_readlane(pre - hb, fl);
+      const int nb = __builtin_amdgcn_readlane(hb, fl);
+      if ((n_pick - need) + above_b + nb <= kPsaCand) {
+        cut = true;
+        break;
+      }
+      need -= above_b;
+      if (map.lin) {
+        pend = true;
+        pm = map;
+        pb = bstar;
+      } else {
+        const uint32_t l2 = lo + (bstar << map.shift);
+        const unsigned long long h2 = (unsigned long long)l2 + (1ull << map.shift) - 1ull;
+        lo = l2;
+        hi = (uint32_t)min((unsigned long long)hi, h2);
+      }
+    }
+  }
+  // candidates: every page in play above the range, and those of the range
+  // at or above the cut; a wave reserves room for a chunk's hits with one atomic
+  ks.each_chunk([&](int e0) {
+    constexpr int R = PsaKeys<E, NT>::R;
+    bool hit[R];
+    unsigned long long bm[R];
+    int cnt = 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int idx = (e0 + r) * NT + tid;
+      const uint32_t key = ks.key[r];
+      hit[r] = live(key, idx, idx < ks.np) &&
+               (above(key, idx) || (in_range(key, idx) && (!cut || bucket(key, idx) >= bstar)));
+      bm[r] = __ballot(hit[r]);
+      cnt += __popcll(bm[r]);
+    }
+    if (cnt) {
+      int base = 0;
+      if (lane == 0) base = atomicAdd(n_cand_p, cnt);
+      base = __builtin_amdgcn_readlane(base, 0);
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int p = base + __popcll(bm[r] & below);
+        if (hit[r] && p < kPsaCand) {
+          sm.cand[p] = page_order(ks.key[r], (e0 + r) * NT + tid);
+          sm.cand_slot[p] = PsaKeys<E, NT>::kResident ? ks.slot[PsaKeys<E, NT>::kResident ? r : 0] : 0;
+        }
+        base += __popcll(bm[r]);
+      }
+    }
+  });
+  __syncthreads();
+  // ranks by counting: lpc lanes per candidate (a power of two, up to 16)
+  // each count a share of the candidates above it and sum across the group
+  const int n_cand = min(*n_cand_p, kPsaCand);
+  int lpc = 16;
+  while (lpc > 1 && n_cand * lpc > NT) lpc >>= 1;
+  const int ci = tid / lpc, part = tid & (lpc - 1);
+  if (ci < n_cand) {
+    const unsigned long long mine_o = sm.cand[ci];
+    const int idx = (int)(0xFFFFFFFFu - (uint32_t)(mine_o & 0xFFFFFFFFull));
+    int slot = 0;
+    if (part == 0) slot = PsaKeys<E, NT>::kResident ? sm.cand_slot[ci] : ks.ptrow[idx];   // in flight during the count
+    int r = 0;
+    for (int x = part; x < n_cand; x += lpc) r += sm.cand[x] > mine_o ? 1 : 0;   // order values are distinct
+    for (int msk = 1; msk < lpc; msk <<= 1) r += __shfl_xor(r, msk, 64);
+    if (part == 0) {
+      if (r < n_pick) {
+        sm.page[r] = idx;
+        sm.slot[r] = slot;
+      }
+      if (r == n_pick - 1) sm.kbound = mine_o;
+    }
+  }
+  __syncthreads();
+  kb = sm.kbound;
+}
+
+// E pages per thread at most: rows up to E * NT pages (the launch takes the
+// smallest E that holds max_pages).
 template <typename T, int D, int G, int E>
 __global__ __launch_bounds__((psa_waves<T, G>() * 64)) void psa_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
@@ -533,94 +833,59 @@ __global__ __launch_bounds__((psa_waves<T, G>() * 64)) void psa_kernel(
   constexpr int NWV = psa_waves<T, G>();
   constexpr int NT = NWV * 64;
   static_assert(E * NT <= kPsaMaxPages, "row capacity");
-  static_assert(G * D <= NT, "one output element per thread");
-  __shared__ SelectSmem<E, NWV> sm;
-  __shared__ unsigned long long s_key[kPsaRound];  // picks of the round: score key << 32 | ~index
-  __shared__ uint32_t s_keys[E * NT];                  // score keys, element order
-  __shared__ int s_page[kPsaRound], s_slot[kPsaRound];  // in rank order
+  static_assert(G * D <= NT && D >= 64, "one output element per thread, one head per wave");
+  __shared__ PsaSmem<NWV> sm;
   __shared__ __align__(16) float lds_rows[NWV][A::LDS_FLOATS];
-  __shared__ __align__(16) float ch_o[NWV][G][D];
-  __shared__ float ch_ml[NWV][G][2];
-  __shared__ int s_take, s_stop, s_left;
-  __shared__ float s_lnacc, s_lnmin;
-  __shared__ float s_wt[NWV][G], s_alpha[G], s_accm[G];  // merge weights; running max per head
+  __shared__ __align__(16) float ch_o[2][NWV][G][D];   // alternate groups use alternate buffers
+  __shared__ float ch_ml[2][NWV][G][2];
 
   const int h = blockIdx.x, b = blockIdx.y;
   const int unit = b * n_kv_heads + h;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int L = clamp_len(seq_lens[b], max_pages, P);
   const int np = (L + P - 1) / P;
-  const float* srow = scores + (size_t)unit * max_pages;
   int32_t* irow = ids + (size_t)unit * max_pages;
-  const int32_t* ptrow = page_table + (size_t)b * max_pages;
 
-  // scores are loaded up to max_pages, so the loads do not wait for seq_lens
-  float sv[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) sv[e] = (e * NT + tid < max_pages) ? srow[e * NT + tid] : 0.0f;
-  uint32_t key[E];
-  unsigned long long remm = 0ull;  // bit e: page e * NT + tid not taken yet
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int idx = e * NT + tid;
-    key[e] = order_key(sv[e]);
-    if (idx < np) remm |= 1ull << e;
-  }
+  PsaKeys<E, NT> ks;
+  ks.srow = scores + (size_t)unit * max_pages;
+  ks.ptrow = page_table + (size_t)b * max_pages;
+  ks.max_pages = max_pages;
+  ks.np = np;
+  ks.tid = tid;
+  ks.round_start();
 
   A st;
   st.init(q + ((size_t)b * n_kv_heads * G + (size_t)h * G) * D, lds_rows[wave]);
+  if (tid == 0) { sm.n_cand[0] = 0; sm.n_cand[1] = 0; }
+  __syncthreads();
   const size_t slot_stride = (size_t)n_kv_heads * P * D;
   const size_t head_off = (size_t)h * P * D;
   const int TPP = P / 16;
   float acc_o = 0.0f, acc_l = 0.0f;  // thread tid < G*D owns element tid
-  const int my_h = tid / D, my_c = tid % D;
-  if (tid == 0) { s_lnacc = kNegInf; s_lnmin = __builtin_huge_valf(); s_left = np; s_stop = 0; }
-  if (tid < G) s_accm[tid] = kNegInf;
-  int visited = 0, n_rem = np;
+  const int my_h = tid / D, my_c = tid % D;   // my_h is uniform over a wave
+  // stop-test state, the same in every wave
+  float lnacc_run = kNegInf, lnmin_run = __builtin_huge_valf();
+  int left_run = np;
+  float accm[G];   // running max per head of the merged blocks
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) accm[hh] = kNegInf;
+  int visited = 0, n_rem = np, grp = 0;
+  unsigned long long kb = 0ull;
   bool stop = false;
   for (int round = 0; !stop && n_rem > 0; ++round) {
-    // 1. the next pages by score, in rank order (the keys wait in LDS
-    //    while a round is walked)
-    if (round > 0) {
-#pragma unroll
-      for (int e = 0; e < E; ++e) key[e] = s_keys[e * NT + tid];
-    }
     const int n_pick = min(round == 0 ? kPsaFirst : kPsaRound, n_rem);
-    const unsigned long long pick = block_select_top<E, NWV>(key, remm, n_rem, n_pick, sm);
-    remm &= ~pick;
+    if (round == 0) psa_pick<E, NWV, true>(ks, round, kb, n_rem, n_pick, sm);
+    else psa_pick<E, NWV, false>(ks, round, kb, n_rem, n_pick, sm);
     n_rem -= n_pick;
-    {
-      if (round == 0) {
-#pragma unroll
-        for (int e = 0; e < E; ++e) s_keys[e * NT + tid] = key[e];
-      }
-      int rk[E];
-      ordered_ranks<E, NWV>(pick, rk, sm.rank, sm.scan);
-#pragma unroll
-      for (int e = 0; e < E; ++e)
-        if ((pick >> e) & 1ull)
-          s_key[rk[e]] = ((unsigned long long)key[e] << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)(e * NT + tid));
-    }
-    __syncthreads();
-    if (tid < n_pick) {
-      const unsigned long long mine = s_key[tid];
-      const int page = (int)(0xFFFFFFFFu - (uint32_t)(mine & 0xFFFFFFFFull));
-      const int slot = ptrow[page];   // in flight during the ranking loop
-      int r = 0;
-#pragma unroll 8
-      for (int x = 0; x < n_pick; ++x) r += s_key[x] > mine ? 1 : 0;   // keys are distinct
-      s_page[r] = page;
-      s_slot[r] = slot;
-    }
-    __syncthreads();
 
-    // 2. walk the round NWV pages at a time
     for (int cs = 0; cs < n_pick; cs += NWV) {
+      const int buf = grp & 1;
+      ++grp;
       const int pos = cs + wave;
       st.reset();
       float pm[G], pl[G];
       if (pos < n_pick) {
-        const int page = s_page[pos], slot = s_slot[pos];
+        const int page = sm.page[pos], slot = sm.slot[pos];
         if (slot >= 0 && slot < num_slots) {
           for (int tin = 0; tin < TPP; ++tin) {
             const int tok0 = page * P + tin * 16;
@@ -639,108 +904,109 @@ __global__ __launch_bounds__((psa_waves<T, G>() * 64)) void psa_kernel(
 #pragma unroll
         for (int hh = 0; hh < G; ++hh)
 #pragma unroll
-          for (int cc = 0; cc < CPL; ++cc) ch_o[wave][hh][lane * CPL + cc] = st.o[hh][cc];
+          for (int cc = 0; cc < CPL; ++cc) ch_o[buf][wave][hh][lane * CPL + cc] = st.o[hh][cc];
       }
       if (lane == 0) {
 #pragma unroll
         for (int hh = 0; hh < G; ++hh) {
-          ch_ml[wave][hh][0] = (pm[hh] == kNegInf) ? kNegInf : pm[hh] * scale;
-          ch_ml[wave][hh][1] = pl[hh];
+          ch_ml[buf][wave][hh][0] = (pm[hh] == kNegInf) ? kNegInf : pm[hh] * scale;
+          ch_ml[buf][wave][hh][1] = pl[hh];
         }
       }
       __syncthreads();
-      // stop test in rank order: lane w of row 0 of wave 0 stands for rank
-      // cs + w.  Block masses are summed over the group's heads, kept as
-      // logs; prefix sums run in the linear domain relative to the largest.
-      if (wave == 0) {
-        const int n_here = min(NWV, n_pick - cs);
-        const bool here = lane < n_here;
-        float mh[G];
-        float ln_as = kNegInf;
-        {
-          float mx = kNegInf;
-#pragma unroll
-          for (int hh = 0; hh < G; ++hh) {
-            mh[hh] = here ? ch_ml[lane & (NWV - 1)][hh][0] : kNegInf;
-            mx = fmaxf(mx, mh[hh]);
-          }
-          if (mx != kNegInf) {
-            float sum = 0.0f;
-#pragma unroll
-            for (int hh = 0; hh < G; ++hh)
-              if (mh[hh] != kNegInf) sum = fmaf(ch_ml[lane & (NWV - 1)][hh][1], __expf(mh[hh] - mx), sum);
-            ln_as = sum > 0.0f ? mx + __logf(sum) : kNegInf;
-          }
-        }
-        const float acc0 = s_lnacc;
-        const float big = fmaxf(acc0, row_max(ln_as));
-        float lnacc = kNegInf;
-        {
-          const float x = (ln_as == kNegInf) ? 0.0f : __expf(ln_as - big);
-          const float pre = row_scan_sum(x) + ((acc0 == kNegInf) ? 0.0f : __expf(acc0 - big));
-          if (big != kNegInf && pre > 0.0f) lnacc = big + __logf(pre);
-        }
-        const float lnmin = fminf(s_lnmin, row_scan_min(here ? ln_as : __builtin_huge_valf()));
-        const int left = s_left - (lane + 1);
-        bool pass;
-        if (never_stop) pass = false;
-        else if (always_stop) pass = true;
-        else if (stop_mode == 0) pass = lnacc - lnmin >= ln_odds;
-        else pass = (left == 0) || (lnacc - (lnmin + __logf((float)left)) >= ln_odds);
-        const unsigned long long hit = __ballot(here && pass);
-        const int take = hit ? (__ffsll((long long)hit)) : n_here;   // 1-based rank of the first pass
-        // merge weights of the taken blocks, per head: exp(m_w - M), M the new running max
+      // stop test in rank order, in every wave: lane w of row 0 stands for
+      // rank cs + w.  Block masses are summed over the group's heads, kept
+      // as logs; prefix sums run in the linear domain relative to the largest.
+      const int n_here = min(NWV, n_pick - cs);
+      const bool here = lane < n_here;
+      const int wl = lane & (NWV - 1);
+      float mh[G];
+      float ln_as = kNegInf;
+      {
+        float mx = kNegInf;
 #pragma unroll
         for (int hh = 0; hh < G; ++hh) {
-          const float mo = s_accm[hh];
-          const float mt = lane < take ? mh[hh] : kNegInf;
-          const float M = fmaxf(mo, row_max(mt));
-          if (lane < NWV) s_wt[lane][hh] = (mt == kNegInf) ? 0.0f : __expf(mt - M);
-          if (lane == 0) {
-            s_alpha[hh] = (mo == kNegInf) ? (M == kNegInf ? 1.0f : 0.0f) : __expf(mo - M);
-            s_accm[hh] = M;
-          }
+          mh[hh] = here ? ch_ml[buf][wl][hh][0] : kNegInf;
+          mx = fmaxf(mx, mh[hh]);
         }
-        if (lane == take - 1) {
-          s_lnacc = lnacc;
-          s_lnmin = lnmin;
-          s_left = left;
-          s_take = take;
-          s_stop = hit ? 1 : 0;
+        if (mx != kNegInf) {
+          float sum = 0.0f;
+#pragma unroll
+          for (int hh = 0; hh < G; ++hh)
+            if (mh[hh] != kNegInf) sum = fmaf(ch_ml[buf][wl][hh][1], __expf(mh[hh] - mx), sum);
+          ln_as = sum > 0.0f ? mx + __logf(sum) : kNegInf;
         }
       }
-      __syncthreads();
-      const int take = s_take;
+      const float big = fmaxf(lnacc_run, row_max(ln_as));
+      float lnacc = kNegInf;
+      {
+        const float x = (ln_as == kNegInf) ? 0.0f : __expf(ln_as - big);
+        const float pre = row_scan_sum(x) + ((lnacc_run == kNegInf) ? 0.0f : __expf(lnacc_run - big));
+        if (big != kNegInf && pre > 0.0f) lnacc = big + __logf(pre);
+      }
+      const float lnmin = fminf(lnmin_run, row_scan_min(here ? ln_as : __builtin_huge_valf()));
+      const int left = left_run - (lane + 1);
+      bool pass;
+      if (never_stop) pass = false;
+      else if (always_stop) pass = true;
+      else if (stop_mode == 0) pass = lnacc - lnmin >= ln_odds;
+      else pass = (left == 0) || (lnacc - (lnmin + __logf((float)left)) >= ln_odds);
+      const unsigned long long hit = __ballot(here && pass);
+      const int take = hit ? __ffsll((long long)hit) : n_here;   // 1-based rank of the first pass
+      lnacc_run = readlane_f(lnacc, take - 1);
+      lnmin_run = readlane_f(lnmin, take - 1);
+      left_run = __builtin_amdgcn_readlane(left, take - 1);
+      // merge weights of the taken blocks: lane w holds exp(m_w - M) for
+      // every head, M the new running max (the same in every lane)
+      float wt[G], alpha[G];
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        const float mo = accm[hh];
+        const float mt = lane < take ? mh[hh] : kNegInf;
+        const float M = fmaxf(mo, readlane_f(row_max(mt), 0));
+        wt[hh] = (mt == kNegInf) ? 0.0f : __expf(mt - M);
+        alpha[hh] = (mo == kNegInf) ? (M == kNegInf ? 1.0f : 0.0f) : __expf(mo - M);
+        accm[hh] = M;
+      }
       if (tid < G * D) {
-        const float a = s_alpha[my_h];
-        acc_o *= a;
-        acc_l *= a;
+        float w_h = wt[0], a_h = alpha[0];
+#pragma unroll
+        for (int hh = 1; hh < G; ++hh)
+          if (my_h == hh) { w_h = wt[hh]; a_h = alpha[hh]; }
+        acc_o *= a_h;
+        acc_l *= a_h;
 #pragma unroll
         for (int w = 0; w < NWV; ++w) {
           if (w < take) {
-            const float wt = s_wt[w][my_h];
-            acc_o = fmaf(ch_o[w][my_h][my_c], wt, acc_o);
-            acc_l = fmaf(ch_ml[w][my_h][1], wt, acc_l);
+            const float ww = readlane_f(w_h, w);
+            acc_o = fmaf(ch_o[buf][w][my_h][my_c], ww, acc_o);
+            acc_l = fmaf(ch_ml[buf][w][my_h][1], ww, acc_l);
           }
         }
       }
-      if (tid < take) irow[visited + tid] = s_page[cs + tid];
+      if (tid < take) irow[visited + tid] = sm.page[cs + tid];
       visited += take;
-      stop = s_stop != 0;
-      __syncthreads();   // ch_o / ch_ml / s_* are rewritten next
-      if (stop) break;
+      if (hit) {
+        stop = true;
+        break;
+      }
     }
+    if (!stop && n_rem > 0) ks.round_start();   // the next round's keys (not held during the walk)
   }
 
-  // 3. outputs
+  // outputs
   for (int x = visited + tid; x < max_pages; x += NT) irow[x] = -1;
   if (tid == 0) counts[unit] = visited;
   if (tid < G * D) {
+    float m_h = accm[0];
+#pragma unroll
+    for (int hh = 1; hh < G; ++hh)
+      if (my_h == hh) m_h = accm[hh];
     const size_t row = (size_t)b * n_kv_heads * G + (size_t)h * G + my_h;
     O[row * D + my_c] = acc_l > 0.0f ? acc_o / acc_l : 0.0f;
     if (my_c == 0) {
       l[row] = acc_l;
-      m[row] = acc_l > 0.0f ? s_accm[my_h] : kNegInf;
+      m[row] = acc_l > 0.0f ? m_h : kNegInf;
     }
   }
 }
@@ -880,13 +1146,14 @@ static int launch_psa_g(const void* q, const dsa_kv* kv, const float* scores, fl
   const float c = scale * kLog2e;
   constexpr int NT = psa_waves<T, G>() * 64;
   constexpr int EMAX = kPsaMaxPages / NT;
+  constexpr int ESHORT = 4096 / NT;   // rows of up to 4096 pages
 #define DSA_PSA(E_)                                                                                                \
   hipLaunchKernelGGL((psa_kernel<T, D, G, E_>), dim3(kv->n_kv_heads, kv->batch), dim3(NT), 0, st, (const T*)q,     \
                      (const T*)kv->k, (const T*)kv->v, kv->page_table, kv->seq_lens, scores, kv->n_kv_heads,       \
                      kv->page_size, kv->max_pages, kv->num_slots, stop_mode, never_stop, always_stop, ln_odds,     \
                      scale, c, ids, counts, O, l, m)
-  if (kv->max_pages <= NT * (EMAX / 4)) DSA_PSA(EMAX / 4);
-  else if (kv->max_pages <= NT * (EMAX / 2)) DSA_PSA(EMAX / 2);
+  if (kv->max_pages <= NT * ESHORT) DSA_PSA(ESHORT);
+  else if (kv->max_pages <= NT * kPsaRegKeys) DSA_PSA(kPsaRegKeys);
   else DSA_PSA(EMAX);
 #undef DSA_PSA
   return launch_status();

@@ -248,7 +248,8 @@ int dsa_page_select_topk(const float *scores, int32_t batch, int32_t n_kv_heads,
  * over the visited pages.
  * scores as from dsa_page_score; ids: device int32 [batch][n_kv_heads][max_pages];
  * O: device float [batch][n_q_heads][head_dim]; l, m: device float [batch][n_q_heads].
- * Requires max_pages <= 8192.  Streaming heads are not supported here.
+ * Requires max_pages <= 65536 (else DSA_ERR_UNSUPPORTED).  Streaming heads are
+ * not supported here.
  */
 int dsa_page_select_progressive(const void *q, int32_t n_q_heads, const dsa_kv *kv,
                                 const float *scores, float threshold, int32_t stop_mode,

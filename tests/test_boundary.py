@@ -99,7 +99,7 @@ def test_validation_errors(dsa):
     # progressive: bad stop mode, too many pages, G=8 unsupported
     assert L.dsa_page_select_progressive(ok_ptr, 4, ctypes.byref(kv), ok_ptr, ctypes.c_float(0.9), 2,
                                          ctypes.c_float(0.088), ok_ptr, ok_ptr, ok_ptr, ok_ptr, ok_ptr, None) == -2
-    assert L.dsa_page_select_progressive(ok_ptr, 4, ctypes.byref(_kv(dsa, max_pages=9000)), ok_ptr,
+    assert L.dsa_page_select_progressive(ok_ptr, 4, ctypes.byref(_kv(dsa, max_pages=65537)), ok_ptr,
                                          ctypes.c_float(0.9), 0, ctypes.c_float(0.088), ok_ptr, ok_ptr, ok_ptr,
                                          ok_ptr, ok_ptr, None) == -4
     # append: null new rows / lengths, misaligned rows or metadata, bad logical page

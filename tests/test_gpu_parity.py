@@ -10,7 +10,8 @@ import torch
 
 import oracle
 import workloads as wl
-from parity_util import TOL, check_attention, check_selected_attention, check_selection, ids_lists, np_, to_device
+from parity_util import (TOL, check_attention, check_psa, check_selected_attention, check_selection, ids_lists,
+                         np_, to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -239,28 +240,7 @@ def _psa_check(dsa, bt, thr, mode):
     """The progressive selection takes the oracle's scores (rounded to
     float32) as its input; the oracle ranks and walks the same values."""
     q, kv, _ = to_device(dsa, bt)
-    s32 = oracle.page_scores(bt).astype(np.float32)
-    sc = torch.from_numpy(s32).cuda()
-    ids, counts, O, l, m = dsa.page_select_progressive(q, kv, sc, thr, mode, float(bt.scale))
-    scn, idn, cn = s32.astype(np.float64), np_(ids), np_(counts)
-    On, ln, mn = np_(O), np_(l), np_(m)
-    G = bt.group
-    for b in range(bt.batch):
-        for h in range(bt.n_kv_heads):
-            nv = oracle.n_pages(bt.seq_lens[b], bt.page_size)
-            rid, rn, rO, rl, rm = oracle.psa_progressive(bt, b, h, scn[b, h], thr, mode)
-            n = int(cn[b, h])
-            if n != rn:   # rule (ii): allowed only where a ratio sits on the threshold
-                ratios = oracle.psa_ratios(bt, b, h, scn[b, h], mode)
-                lo, hi = min(n, rn), max(n, rn)
-                near = np.abs(ratios[lo - 1:hi] - thr) <= 1e-5 * thr
-                assert near.any(), f"stop {n} != oracle {rn} at (b={b}, h={h})"
-            ranked = oracle.rank_pages(scn[b, h], nv)
-            assert np.array_equal(idn[b, h, :n], ranked[:n])
-            assert np.all(idn[b, h, n:] == -1)
-            ref = oracle.attend_pages(bt, b, h, idn[b, h, :n])
-            sl = slice(h * G, (h + 1) * G)
-            check_attention(bt.dtype, On[b, sl], ln[b, sl], mn[b, sl], *ref, f"psa b={b} h={h}")
+    check_psa(dsa, bt, q, kv, oracle.page_scores(bt).astype(np.float32), thr, mode, f"psa thr={thr} mode={mode}")
 
 
 # ---------------------------------------------------------------- repair
