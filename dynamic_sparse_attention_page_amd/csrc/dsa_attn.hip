@@ -544,11 +544,6 @@ __device__ __forceinline__ unsigned long long page_order(uint32_t key, int idx) 
   return ((unsigned long long)key << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)idx);
 }
 
-// Histogram buckets are stored with one pad word after every 32, so the 64
-// lanes of a wave reading 32 consecutive buckets each hit distinct banks.
-constexpr int kHistWords = kBuckets + kBuckets / 32;
-__device__ __forceinline__ int hist_at(uint32_t b) { return (int)(b + (b >> 5)); }
-
 template <int NW>
 struct PsaSmem {
   unsigned hist[2][kHistWords];      // alternate passes use alternate buffers
@@ -722,28 +717,10 @@ __device__ __forceinline__ void psa_pick(PsaKeys<E, NW * 64>& ks, int round, uns
         if (live(key, idx, valid) && in_range(key, idx)) atomicAdd(&hist[hist_at(bucket(key, idx))], 1u);
       });
       __syncthreads();
-      // bucket search, in every wave: lane x sums buckets [kBuckets - 32(x+1), kBuckets - 32x);
-      // the lane whose buckets hold the need-th page is found by a scan,
-      // then its 32 buckets are scanned across lanes 0..31 from the top down
-      static_assert(kBuckets == 64 * 32, "32 buckets per lane");
-      int mine = 0;
-      {
-        const unsigned* h0 = hist + hist_at(kBuckets - 32 * (lane + 1));
-#pragma unroll
-        for (int x = 0; x < 32; ++x) mine += (int)h0[x];
-      }
-      const int incl = wave_incl_scan(mine);
-      const unsigned long long hm = __ballot(incl - mine < need && need <= incl);
-      const int src = __ffsll((long long)hm) - 1;
-      const int acc0 = __builtin_amdgcn_readlane(incl - mine, src);   // pages in higher lanes' buckets
-      const int sb0 = kBuckets - 32 * (src + 1);
-      const int hb = lane < 32 ? (int)hist[hist_at(sb0 + 31 - lane)] : 0;
-      const int pre = wave_incl_scan(hb);
-      const unsigned long long fm = __ballot(lane < 32 && acc0 + pre >= need);
-      const int fl = __ffsll((long long)fm) - 1;
-      bstar = (uint32_t)(sb0 + 31 - fl);
-      const int above_b = acc0 + __builtin_amdgcn_readlane(pre - hb, fl);
-      const int nb = __builtin_amdgcn_readlane(hb, fl);
+      // every wave finds the cut bucket from the histogram itself
+      const BucketCut bc = bucket_search(hist, need);
+      bstar = bc.b;
+      const int above_b = bc.above, nb = bc.n;
       if ((n_pick - need) + above_b + nb <= kPsaCand) {
         cut = true;
         break;

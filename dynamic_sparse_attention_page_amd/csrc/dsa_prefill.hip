@@ -60,8 +60,8 @@ __global__ __launch_bounds__(NWQ * 64) void prefill_kernel(const uint16_t* __res
                                                       float* __restrict__ mout) {
   constexpr int NK = D / 32, NB = D / 16;
   constexpr int NT = NWQ * 64, QT = 16 * QS * NWQ;   // threads; queries per tile
-  constexpr int KCH = D / (8 * NWQ);           // K (and V) chunks per thread
-  static_assert(KCH * NT * 8 == kPfTile * D, "K staging");
+  constexpr int NCH = kPfTile * D / 8;         // 16-byte chunks of a K (or V) tile
+  constexpr int KCH = (NCH + NT - 1) / NT;     // K (and V) chunks per thread
   using S = PrefillSmem<D>;
   __shared__ S sm;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -113,7 +113,7 @@ __global__ __launch_bounds__(NWQ * 64) void prefill_kernel(const uint16_t* __res
       const int row = chunk / (D / 8), col = (chunk % (D / 8)) * 8;
       kr[x] = make_uint4(0u, 0u, 0u, 0u);
       vr4[x] = kr[x];
-      if (key0 + row < L) {
+      if (chunk < NCH && key0 + row < L) {
         const size_t off = (size_t)(key0 + row) * kv_row + (size_t)hk * D + col;
         kr[x] = *reinterpret_cast<const uint4*>(k + off);
         vr4[x] = *reinterpret_cast<const uint4*>(v + off);
@@ -131,8 +131,10 @@ __global__ __launch_bounds__(NWQ * 64) void prefill_kernel(const uint16_t* __res
     for (int x = 0; x < KCH; ++x) {
       const int chunk = tid + NT * x;
       const int row = chunk / (D / 8), col = (chunk % (D / 8)) * 8;
-      *reinterpret_cast<uint4*>(sm.k + row * S::KS + col) = kr[x];
-      *reinterpret_cast<uint4*>(sm.v + row * S::KS + col) = vr4[x];
+      if (chunk < NCH) {
+        *reinterpret_cast<uint4*>(sm.k + row * S::KS + col) = kr[x];
+        *reinterpret_cast<uint4*>(sm.v + row * S::KS + col) = vr4[x];
+      }
     }
     __syncthreads();
     if (it + 1 < n_iter) fetch(tile_of(it + 1) * kPfTile);

@@ -1,22 +1,23 @@
 // Block-wide radix selection of the largest keys, shared by the fixed top-k
-// (PSA, section 2.2; PRR, section 2) and the rounds of PSA's progressive
-// selection (section 3.2).
+// (PSA, section 2.2; PRR, section 2), the fused top-k attention and the
+// PRR calibration.
 //
 // A workgroup of NT = NW * 64 threads holds E keys per thread; thread t owns
 // element indices t, t + NT, t + 2NT, ... (bit e of a 64-bit mask stands for
 // element e * NT + t).  Keys are 32-bit with the order of the float scores
 // (-0 and +0 equal).  Radix select over the elements still in play, whose
 // keys span [lo, hi]: each pass maps them to at most 2048 buckets with a
-// map that is monotone in the key (equal keys share a bucket), builds an LDS
-// histogram, and a block suffix scan finds the bucket holding the wanted
-// rank; elements in higher buckets are chosen, lower ones dropped, and the
-// pass repeats on that bucket.  The first pass maps the score values
-// linearly onto the buckets (when they are finite), later passes take
-// (key - lo) >> s, which removes 11 bits of span per pass.  Once at most 64
-// elements are left they are ranked directly by (key, lower index first);
-// if more are left with equal keys, they are taken in index order -- the
-// lower-index tie rule either way.  Index-order ranks come from
-// per-(element slot, wave) ballot counts and one block scan over them.
+// map that is monotone in the key (equal keys share a bucket) and builds an
+// LDS histogram; every wave then finds the bucket holding the wanted rank
+// from the histogram by itself (no block scan).  Elements in higher buckets
+// are chosen, lower ones dropped; if the bucket is taken whole the
+// selection ends, else the pass repeats on that bucket.  The first pass maps
+// the score values linearly onto the buckets (when they are finite), later
+// passes take (key - lo) >> s, which removes 11 bits of span per pass.  Once
+// at most 64 elements are left they are ranked directly by (key, lower
+// index first); if more are left with equal keys, they are taken in index
+// order -- the lower-index tie rule either way.  Index-order ranks come from
+// per-(element slot, wave) ballot counts that every wave scans itself.
 #pragma once
 
 #include "dsa_common.hpp"
@@ -26,12 +27,51 @@ namespace dsa {
 constexpr int kBuckets = 2048;
 constexpr int kSmall = 64;  // elements left that are ranked directly
 
+// Histogram buckets are stored with one pad word after every 32, so the 64
+// lanes of a wave reading 32 consecutive buckets each hit distinct banks.
+constexpr int kHistWords = kBuckets + kBuckets / 32;
+__device__ __forceinline__ int hist_at(uint32_t b) { return (int)(b + (b >> 5)); }
+
+// The bucket holding the need-th largest element (1 <= need <= total count),
+// found by one wave from a complete histogram: lane x sums buckets
+// [kBuckets - 32(x+1), kBuckets - 32x), a wave scan finds the lane whose
+// buckets hold the need-th, then lanes 0..31 scan that lane's buckets from
+// the top down.  Returns the bucket, the elements in higher buckets and the
+// elements in it (the same values in every lane).
+struct BucketCut {
+  uint32_t b;
+  int above, n;
+};
+__device__ __forceinline__ BucketCut bucket_search(const unsigned* hist, int need) {
+  static_assert(kBuckets == 64 * 32, "32 buckets per lane");
+  const int lane = threadIdx.x & 63;
+  int mine = 0;
+  {
+    const unsigned* h0 = hist + hist_at(kBuckets - 32 * (lane + 1));
+#pragma unroll
+    for (int x = 0; x < 32; ++x) mine += (int)h0[x];
+  }
+  const int incl = wave_incl_scan(mine);
+  const unsigned long long hm = __ballot(incl - mine < need && need <= incl);
+  const int src = __ffsll((long long)hm) - 1;
+  const int acc0 = __builtin_amdgcn_readlane(incl - mine, src);   // elements in higher lanes' buckets
+  const int sb0 = kBuckets - 32 * (src + 1);
+  const int hb = lane < 32 ? (int)hist[hist_at(sb0 + 31 - lane)] : 0;
+  const int pre = wave_incl_scan(hb);
+  const unsigned long long fm = __ballot(lane < 32 && acc0 + pre >= need);
+  const int fl = __ffsll((long long)fm) - 1;
+  BucketCut c;
+  c.b = (uint32_t)(sb0 + 31 - fl);
+  c.above = acc0 + __builtin_amdgcn_readlane(pre - hb, fl);
+  c.n = __builtin_amdgcn_readlane(hb, fl);
+  return c;
+}
+
 template <int E, int NW>
 struct SelectSmem {
-  unsigned hist[2][kBuckets];        // alternate passes use alternate buffers
+  unsigned hist[2][kHistWords];      // alternate passes use alternate buffers
   unsigned long long small[kSmall];
   int scan[NW];                      // ordered_ranks
-  int pscan[2][NW];                  // pass scans, alternating
   int rank[E * NW];
   uint32_t mm[2][2 * NW];            // pass min/max, alternating
   int bstar, above, n_small;
@@ -70,8 +110,10 @@ __device__ __forceinline__ int block_excl_scan(int x, int* smem /* NW ints */, i
 }
 
 // Index-order rank of every set bit of `mask` among all set bits of the
-// workgroup, and their total.  Slots (e, wave) are counted with ballots, one
-// block scan orders them, lanes add their rank in the ballot.
+// workgroup, and their total.  Slots (e, wave) are counted with ballots;
+// with at most 64 slots every wave scans the counts itself (one barrier),
+// else one block scan orders them.  Consecutive calls on the same buffers
+// must be separated by a workgroup barrier.
 template <int E, int NW>
 __device__ __forceinline__ int ordered_ranks(unsigned long long mask, int (&rank)[E], int* cnt /* E*NW */,
                                              int* scan_smem /* NW */) {
@@ -85,16 +127,23 @@ __device__ __forceinline__ int ordered_ranks(unsigned long long mask, int (&rank
     if (lane == 0) cnt[e * NW + wave] = __popcll(b);
   }
   group_sync<NW>();
-  const int tid = threadIdx.x;
-  const int v = tid < E * NW ? cnt[tid] : 0;
-  int total;
-  const int before = block_excl_scan<NW>(v, scan_smem, total);
-  if (tid < E * NW) cnt[tid] = before;
-  group_sync<NW>();
+  if constexpr (E * NW <= 64) {
+    const int v = lane < E * NW ? cnt[lane] : 0;
+    const int incl = wave_incl_scan(v);
 #pragma unroll
-  for (int e = 0; e < E; ++e) rank[e] += cnt[e * NW + wave];
-  group_sync<NW>();   // cnt is reused by the next call
-  return total;
+    for (int e = 0; e < E; ++e) rank[e] += __builtin_amdgcn_readlane(incl - v, e * NW + wave);
+    return __builtin_amdgcn_readlane(incl, 63);
+  } else {
+    const int tid = threadIdx.x;
+    const int v = tid < E * NW ? cnt[tid] : 0;
+    int total;
+    const int before = block_excl_scan<NW>(v, scan_smem, total);
+    if (tid < E * NW) cnt[tid] = before;
+    group_sync<NW>();
+#pragma unroll
+    for (int e = 0; e < E; ++e) rank[e] += cnt[e * NW + wave];
+    return total;
+  }
 }
 
 // float -> uint32 with the same order; -0.0 maps like +0.0.
@@ -165,19 +214,22 @@ template <int E, int NW>
 __device__ __forceinline__ unsigned long long block_select_top(const uint32_t (&key)[E], unsigned long long actm,
                                                                int n_act, int need, SelectSmem<E, NW>& sm) {
   constexpr int NT = NW * 64;
-  constexpr int BPT = kBuckets / NT;  // buckets per thread in the suffix scan
-  static_assert(kBuckets % NT == 0, "bucket split");
   if (need <= 0) return 0ull;
   if (need >= n_act) return actm;
   const int tid = threadIdx.x;
   unsigned long long selm = 0ull;
+  // at most: a linear pass and three shift passes narrow the keys to one
+  // value, whose min / max then ends the loop
   for (int pass = 0; pass < 5; ++pass) {
     if (n_act == need) return selm | actm;
     if (n_act <= kSmall) {
       // rank the few left by (key, lower index first); the need-th largest
-      // composite value is the cut
-      if (tid == 0) sm.n_small = 0;
-      group_sync<NW>();
+      // composite value is the cut.  n_small was cleared before the last
+      // pass's barriers (on pass 0 here).
+      if (pass == 0) {
+        if (tid == 0) sm.n_small = 0;
+        group_sync<NW>();
+      }
 #pragma unroll
       for (int e = 0; e < E; ++e)
         if ((actm >> e) & 1ull) {
@@ -201,7 +253,8 @@ __device__ __forceinline__ unsigned long long block_select_top(const uint32_t (&
       return selm;   // the next writer of small / kappa / n_small passes a barrier first
     }
     unsigned* hist = sm.hist[pass & 1];
-    for (int x = tid; x < kBuckets; x += NT) hist[x] = 0u;   // last read two passes ago
+    for (int x = tid; x < kHistWords; x += NT) hist[x] = 0u;   // last read two barriers ago
+    if (tid == 0) sm.n_small = 0;
     uint32_t lo = 0xFFFFFFFFu, hi = 0u;
 #pragma unroll
     for (int e = 0; e < E; ++e)
@@ -228,46 +281,31 @@ __device__ __forceinline__ unsigned long long block_select_top(const uint32_t (&
     if (map.lin) {
 #pragma unroll
       for (int e = 0; e < E; ++e)
-        if ((actm >> e) & 1ull) atomicAdd(&hist[map.linear(key[e])], 1u);
+        if ((actm >> e) & 1ull) atomicAdd(&hist[hist_at(map.linear(key[e]))], 1u);
     } else {
 #pragma unroll
       for (int e = 0; e < E; ++e)
-        if ((actm >> e) & 1ull) atomicAdd(&hist[map.shifted(key[e])], 1u);
+        if ((actm >> e) & 1ull) atomicAdd(&hist[hist_at(map.shifted(key[e]))], 1u);
     }
     group_sync<NW>();
-    // suffix scan: thread t owns buckets [(NT-1-t)*BPT, +BPT), so lower t = higher buckets
-    const int b0 = (NT - 1 - tid) * BPT;
-    int mine = 0;
-#pragma unroll
-    for (int x = 0; x < BPT; ++x) mine += (int)hist[b0 + x];
-    int acc = block_excl_scan_1b<NW>(mine, sm.pscan[pass & 1]);
-    if (acc < need && need <= acc + mine) {
-      for (int x = BPT - 1; x >= 0; --x) {
-        const int hb = (int)hist[b0 + x];
-        if (acc + hb >= need) { sm.bstar = b0 + x; sm.above = acc; break; }
-        acc += hb;
-      }
-    }
-    group_sync<NW>();
-    const uint32_t bstar = (uint32_t)sm.bstar;
-    const int above = sm.above;
+    const BucketCut cut = bucket_search(hist, need);
     auto classify = [&](auto bucket) {
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         const unsigned long long bit = 1ull << e;
         if (actm & bit) {
           const uint32_t bk = bucket(key[e]);
-          if (bk > bstar) { selm |= bit; actm &= ~bit; }
-          else if (bk < bstar) actm &= ~bit;
+          if (bk > cut.b) { selm |= bit; actm &= ~bit; }
+          else if (bk < cut.b) actm &= ~bit;
         }
       }
     };
     if (map.lin) classify([&](uint32_t k) { return map.linear(k); });
     else classify([&](uint32_t k) { return map.shifted(k); });
-    need -= above;
-    n_act = (int)hist[bstar];
-    // no barrier: bstar / above are next written after two more barriers,
-    // and this hist buffer is next zeroed two passes later
+    need -= cut.above;
+    n_act = cut.n;
+    // no barrier: this hist buffer is next zeroed two passes later, after
+    // two more barriers
   }
   // the keys still in play are equal: take them in index order
   int rk[E];

@@ -620,6 +620,7 @@ __global__ __launch_bounds__(kSrNT) void sr_select_kernel(
   for (int x = keff + w * kSrNT + tid; x < kk; x += W * kSrNT) out[x] = -1;
   if (w == 0 && tid == 0) (arr ? p_counts : a_counts)[unit] = keff;
   if (with_m) {
+    __syncthreads();   // the first ranking's counts are read
     ordered_ranks<kSrE, kSrNW>(mselm, rk, sm.sel.rank, sm.sel.scan);
     int32_t* mo = m_ids + (size_t)unit * k;
 #pragma unroll
