@@ -12,7 +12,9 @@ printed: the headline fields are those of psa_mha_64k, the largest workload
 step), and "workloads" holds the full result of each of the others, timed in
 the same run the same way.
 
-  psa_mha_64k (headline)   page_score -> page_select_progressive (threshold 0.95)
+  psa_mha_64k (headline)   psa_decode = page_score -> page_select_progressive (threshold
+      0.95) in one call: one launch, each (sequence, head) workgroup scoring its own row;
+      the two separate calls are timed beside it
       batch 8, 32 heads MHA, d=128, 65536 tokens in 16-token pages, bf16
   quest_gqa_32k            page_score -> sparse_decode_attn_topk (top-k selection + sparse
       attention in one call; the separate page_select_topk and sparse_decode_attn are
@@ -570,6 +572,11 @@ def main():
             "page_select_progressive": lambda r: dsa.page_select_progressive(
                 q, kvs[r], scores, bt.threshold, 0, scale, out=(ids_p, cnt_p, *Op)),
         }
+        if bt.topk is None:
+            # the step: both calls in one (one launch when the rows cover the CUs);
+            # the two calls are timed beside it
+            ops["psa_decode"] = lambda r: dsa.psa_decode(q, kvs[r], meta, bt.threshold, 0, scale,
+                                                         out=(scores, ids_p, cnt_p, *Op))
         if bt.topk is not None:
             ids = torch.empty((B, Hkv, bt.topk), dtype=i32, device=dev)
             cnt = torch.empty((B, Hkv), dtype=i32, device=dev)
@@ -581,8 +588,11 @@ def main():
                                                                          out=(O, l, m), ws=ws)
 
         def step(i):
-            for fn in ops.values():
-                fn(i % R)
+            if "psa_decode" in ops:
+                ops["psa_decode"](i % R)
+            else:
+                for fn in ops.values():
+                    fn(i % R)
         step(0)
         torch.cuda.synchronize()
         visited = float(cnt_p.float().mean().item())
@@ -590,6 +600,8 @@ def main():
         extra["psa_host_signal"] = host_signal_latency(dsa, torch, ops, cnt_p)
         step_bytes = mb + page_kv_bytes(bt, visited, B * Hkv)
         op_bytes = {"page_score": mb, "page_select_progressive": page_kv_bytes(bt, visited, B * Hkv)}
+        if bt.topk is None:
+            op_bytes["psa_decode"] = mb + page_kv_bytes(bt, visited, B * Hkv)
         if bt.topk is not None:
             step_bytes += page_kv_bytes(bt, bt.topk, B * Hkv)
             op_bytes["sparse_decode_attn"] = page_kv_bytes(bt, bt.topk, B * Hkv)

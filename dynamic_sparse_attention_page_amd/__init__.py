@@ -19,7 +19,7 @@ import torch
 __all__ = [
     "DsaError", "PagedKV", "Streaming", "lib", "LIB_PATH",
     "page_meta_build", "kv_append", "page_score", "page_score_ema", "page_select_topk", "page_select_progressive",
-    "sparse_decode_attn", "sparse_decode_attn_noalloc", "sparse_decode_attn_topk", "attn_repair", "ema_predict_update", "prr_select", "prr_calibrate", "signal_host", "block_sparse_prefill",
+    "psa_decode", "sparse_decode_attn", "sparse_decode_attn_noalloc", "sparse_decode_attn_topk", "attn_repair", "ema_predict_update", "prr_select", "prr_calibrate", "signal_host", "block_sparse_prefill",
     "workspace_bytes",
     "OP_SPARSE_DECODE_ATTN", "OP_ATTN_REPAIR", "EXPORTED", "prr_select_workspace_bytes", "NOALLOC_SCRATCH_BYTES",
 ]
@@ -31,7 +31,7 @@ OP_SPARSE_DECODE_ATTN, OP_ATTN_REPAIR = 1, 2
 EXPORTED = (
     "dsa_status_str", "dsa_version", "dsa_page_meta_build", "dsa_kv_append", "dsa_page_score", "dsa_page_score_ema",
     "dsa_page_select_topk",
-    "dsa_page_select_progressive", "dsa_sparse_decode_attn", "dsa_sparse_decode_attn_noalloc",
+    "dsa_page_select_progressive", "dsa_psa_decode", "dsa_sparse_decode_attn", "dsa_sparse_decode_attn_noalloc",
     "dsa_sparse_decode_attn_topk", "dsa_attn_repair",
     "dsa_ema_predict_update", "dsa_prr_select", "dsa_prr_select_workspace_bytes", "dsa_prr_calibrate",
     "dsa_prr_calibrate_workspace_bytes",
@@ -75,6 +75,7 @@ def _load(path: str = LIB_PATH):
         "dsa_page_score_ema": (ctypes.c_int, [P, I32, KV, P, I32, ST, P, P, P, P, F32, F32, F32, I32, P]),
         "dsa_page_select_topk": (ctypes.c_int, [P, I32, I32, I32, P, I32, I32, ST, P, P, P]),
         "dsa_page_select_progressive": (ctypes.c_int, [P, I32, KV, P, F32, I32, F32, P, P, P, P, P, P]),
+        "dsa_psa_decode": (ctypes.c_int, [P, I32, KV, P, F32, I32, F32, P, P, P, P, P, P, P]),
         "dsa_sparse_decode_attn": (ctypes.c_int, [P, I32, KV, P, P, I32, ST, F32, P, P, P, P, SZ, P]),
         "dsa_sparse_decode_attn_noalloc": (ctypes.c_int, [P, I32, KV, P, P, I32, ST, F32, P, P, P, P]),
         "dsa_sparse_decode_attn_topk": (ctypes.c_int, [P, I32, KV, P, I32, ST, F32, P, P, P, P, P, P, SZ, P]),
@@ -316,6 +317,27 @@ def page_select_progressive(q: torch.Tensor, kv: PagedKV, scores: torch.Tensor, 
         _ptr(q), Hq, ctypes.byref(kv.c()), _ptr(scores), float(threshold), stop_mode, sc, _ptr(ids), _ptr(counts),
         _ptr(O), _ptr(l), _ptr(m), _stream()))
     return ids, counts, O, l, m
+
+
+def psa_decode(q: torch.Tensor, kv: PagedKV, meta: torch.Tensor, threshold: float, stop_mode: int = 0,
+               scale: float | None = None, out=None):
+    """page_score + page_select_progressive in one call (one launch when the
+    rows cover the GPU's CUs): (scores, ids, counts, O, l, m)."""
+    B, Hq = q.shape[0], q.shape[1]
+    dev = kv.k.device
+    if out is None:
+        out = (torch.empty((kv.batch, kv.n_kv_heads, kv.max_pages), dtype=torch.float32, device=dev),
+               torch.empty((kv.batch, kv.n_kv_heads, kv.max_pages), dtype=torch.int32, device=dev),
+               torch.empty((kv.batch, kv.n_kv_heads), dtype=torch.int32, device=dev),
+               torch.empty((B, Hq, kv.head_dim), dtype=torch.float32, device=dev),
+               torch.empty((B, Hq), dtype=torch.float32, device=dev),
+               torch.empty((B, Hq), dtype=torch.float32, device=dev))
+    scores, ids, counts, O, l, m = out
+    sc = _default_scale(kv.head_dim) if scale is None else scale
+    _check("dsa_psa_decode", lib.dsa_psa_decode(
+        _ptr(q), Hq, ctypes.byref(kv.c()), _ptr(meta), float(threshold), stop_mode, sc, _ptr(scores), _ptr(ids),
+        _ptr(counts), _ptr(O), _ptr(l), _ptr(m), _stream()))
+    return scores, ids, counts, O, l, m
 
 
 def sparse_decode_attn(q: torch.Tensor, kv: PagedKV, ids: torch.Tensor, counts: torch.Tensor,

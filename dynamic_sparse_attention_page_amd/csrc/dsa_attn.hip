@@ -796,15 +796,16 @@ __device__ __forceinline__ void psa_pick(PsaKeys<E, NW * 64>& ks, int round, uns
   kb = sm.kbound;
 }
 
-// E pages per thread at most: rows up to E * NT pages (the launch takes the
-// smallest E that holds max_pages).
+// The progressive selection and walk of one (b, KV head): srow is the
+// row's scores and ptrow its page-table row (global memory, or the LDS copy
+// of the fused kernel).  E pages per thread at most: rows up to E * NT pages
+// (the launch takes the smallest E that holds max_pages).
 template <typename T, int D, int G, int E>
-__global__ __launch_bounds__((psa_waves<T, G>() * 64)) void psa_kernel(
-    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-    const int32_t* __restrict__ page_table, const int32_t* __restrict__ seq_lens, const float* __restrict__ scores,
-    int n_kv_heads, int P, int max_pages, int num_slots, int stop_mode, int never_stop, int always_stop,
-    float ln_odds, float scale, float c, int32_t* __restrict__ ids, int32_t* __restrict__ counts,
-    float* __restrict__ O, float* __restrict__ l, float* __restrict__ m) {
+__device__ __forceinline__ void psa_body(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const float* srow,
+    const int32_t* ptrow, int L, int h, int b, int n_kv_heads, int P, int max_pages, int num_slots, int stop_mode,
+    int never_stop, int always_stop, float ln_odds, float scale, float c, int32_t* __restrict__ ids,
+    int32_t* __restrict__ counts, float* __restrict__ O, float* __restrict__ l, float* __restrict__ m) {
   using A = AttnWave<T, D, G>;
   constexpr int CPL = A::CPL, DW = A::DW;
   constexpr int NWV = psa_waves<T, G>();
@@ -816,16 +817,14 @@ __global__ __launch_bounds__((psa_waves<T, G>() * 64)) void psa_kernel(
   __shared__ __align__(16) float ch_o[2][NWV][G][D];   // alternate groups use alternate buffers
   __shared__ float ch_ml[2][NWV][G][2];
 
-  const int h = blockIdx.x, b = blockIdx.y;
   const int unit = b * n_kv_heads + h;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int L = clamp_len(seq_lens[b], max_pages, P);
   const int np = (L + P - 1) / P;
   int32_t* irow = ids + (size_t)unit * max_pages;
 
   PsaKeys<E, NT> ks;
-  ks.srow = scores + (size_t)unit * max_pages;
-  ks.ptrow = page_table + (size_t)b * max_pages;
+  ks.srow = srow;
+  ks.ptrow = ptrow;
   ks.max_pages = max_pages;
   ks.np = np;
   ks.tid = tid;
@@ -988,6 +987,119 @@ __global__ __launch_bounds__((psa_waves<T, G>() * 64)) void psa_kernel(
   }
 }
 
+template <typename T, int D, int G, int E>
+__global__ __launch_bounds__((psa_waves<T, G>() * 64)) void psa_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const int32_t* __restrict__ page_table, const int32_t* __restrict__ seq_lens, const float* __restrict__ scores,
+    int n_kv_heads, int P, int max_pages, int num_slots, int stop_mode, int never_stop, int always_stop,
+    float ln_odds, float scale, float c, int32_t* __restrict__ ids, int32_t* __restrict__ counts,
+    float* __restrict__ O, float* __restrict__ l, float* __restrict__ m) {
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int L = clamp_len(seq_lens[b], max_pages, P);
+  psa_body<T, D, G, E>(q, k, v, scores + ((size_t)b * n_kv_heads + h) * max_pages, page_table + (size_t)b * max_pages,
+                       L, h, b, n_kv_heads, P, max_pages, num_slots, stop_mode, never_stop, always_stop, ln_odds, scale,
+                       c, ids, counts, O, l, m);
+}
+
+// ============================================================ PSA with its own scores
+// dsa_psa_decode: one workgroup per (b, KV head) scores its own row into LDS
+// and goes straight on to the progressive selection and walk -- no second
+// launch and no global round trip of the scores.  Worth it when there are
+// at least as many rows as CUs (each workgroup streams its row's metadata
+// on one CU).  The scores are the page_score kernel's, operation for
+// operation (group-mean query split by sign, kmax / kmin terms in channel
+// order, DPP row sum), so both paths select the same pages; they are also
+// written to global memory.  Page-table row and scores live in dynamic LDS.
+constexpr int kPsaFusedMaxPages = 8192;
+#ifndef DSA_PSA_FUSED_LOADS
+#define DSA_PSA_FUSED_LOADS 8
+#endif
+constexpr int kPsaFusedLoads = DSA_PSA_FUSED_LOADS;   // load pairs in flight per lane
+
+template <typename T, int D, int G, int E>
+__global__ __launch_bounds__((psa_waves<T, G>() * 64)) void psa_fused_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ meta,
+    const int32_t* __restrict__ page_table, const int32_t* __restrict__ seq_lens, int n_kv_heads, int P,
+    int max_pages, int num_slots, int stop_mode, int never_stop, int always_stop, float ln_odds, float scale,
+    float c, float* __restrict__ scores, int32_t* __restrict__ ids, int32_t* __restrict__ counts,
+    float* __restrict__ O, float* __restrict__ l, float* __restrict__ m) {
+  using L_ = Lay<T, D>;
+  constexpr int CPL = L_::CPL, DW = L_::DW;
+  constexpr int NWV = psa_waves<T, G>();
+  constexpr int NT = NWV * 64;
+  constexpr int U = kPsaFusedLoads;
+  extern __shared__ __align__(16) unsigned char psa_dyn[];
+  float* s_score = reinterpret_cast<float*>(psa_dyn);                                  // [max_pages]
+  int32_t* s_slot = reinterpret_cast<int32_t*>(psa_dyn + (((size_t)max_pages * 4 + 15) & ~(size_t)15));
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int unit = b * n_kv_heads + h;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int r = lane >> 4, cg = lane & 15;
+  const int L = clamp_len(seq_lens[b], max_pages, P);
+  const int np = (L + P - 1) / P;
+  const int32_t* ptg = page_table + (size_t)b * max_pages;
+  for (int x = tid; x < max_pages; x += NT) s_slot[x] = ptg[x];
+  // group-mean query, this lane's channels, split by sign
+  float qpos[CPL], qneg[CPL];
+  {
+    float acc[CPL];
+#pragma unroll
+    for (int cc = 0; cc < CPL; ++cc) acc[cc] = 0.0f;
+#pragma unroll
+    for (int gg = 0; gg < G; ++gg) {
+      uint32_t w[DW];
+      load_dw<DW>(q + ((size_t)b * n_kv_heads * G + (size_t)h * G + gg) * D + cg * CPL, w);
+#pragma unroll
+      for (int cc = 0; cc < CPL; ++cc) acc[cc] += chan<T>(w, cc);
+    }
+#pragma unroll
+    for (int cc = 0; cc < CPL; ++cc) {
+      const float qb = acc[cc] * (1.0f / G);
+      qpos[cc] = fmaxf(qb, 0.0f);
+      qneg[cc] = fminf(qb, 0.0f);
+    }
+  }
+  __syncthreads();
+  // row r of wave w scores page 4 (it * NWV + w) + r; U iterations' loads
+  // are issued together (invalid pages read a valid address and score -inf)
+  float* sg = scores + (size_t)unit * max_pages;
+  const size_t head_stride = (size_t)2 * D;
+  const int n_it = (max_pages + 4 * NWV - 1) / (4 * NWV);
+  for (int it0 = 0; it0 < n_it; it0 += U) {
+    uint32_t wmin[U][DW], wmax[U][DW];
+    bool ok[U];
+    int jj[U];
+#pragma unroll
+    for (int uu = 0; uu < U; ++uu) {
+      const int j = 4 * ((it0 + uu) * NWV + wave) + r;
+      jj[uu] = j;
+      const int slot = j < max_pages ? s_slot[j] : -1;
+      ok[uu] = j < np && slot >= 0 && slot < num_slots;
+      const T* src = ok[uu] ? meta + ((size_t)slot * n_kv_heads + h) * head_stride + cg * CPL : meta + cg * CPL;
+      load_dw_stream<DW>(src, wmin[uu]);
+      load_dw_stream<DW>(src + D, wmax[uu]);
+    }
+#pragma unroll
+    for (int uu = 0; uu < U; ++uu) {
+      float part = 0.0f;
+#pragma unroll
+      for (int cc = 0; cc < CPL; ++cc) {
+        part = fmaf(qpos[cc], chan<T>(wmax[uu], cc), part);
+        part = fmaf(qneg[cc], chan<T>(wmin[uu], cc), part);
+      }
+      float sc = row_sum(part);
+      if (!ok[uu]) sc = kNegInf;
+      if (cg == 0 && jj[uu] < max_pages) {
+        s_score[jj[uu]] = sc;
+        sg[jj[uu]] = sc;
+      }
+    }
+  }
+  __syncthreads();
+  psa_body<T, D, G, E>(q, k, v, s_score, s_slot, L, h, b, n_kv_heads, P, max_pages, num_slots, stop_mode,
+                       never_stop, always_stop, ln_odds, scale, c, ids, counts, O, l, m);
+}
+
 // ============================================================ host planning
 struct SplitPlan {
   int tiles_per_split, n_splits, TPP;
@@ -1143,6 +1255,63 @@ static int launch_psa_d(const void* q, int G, const dsa_kv* kv, const float* sco
     case 1: return launch_psa_g<T, D, 1>(q, kv, scores, thr, stop_mode, scale, ids, counts, O, l, m, st);
     case 2: return launch_psa_g<T, D, 2>(q, kv, scores, thr, stop_mode, scale, ids, counts, O, l, m, st);
     case 4: return launch_psa_g<T, D, 4>(q, kv, scores, thr, stop_mode, scale, ids, counts, O, l, m, st);
+  }
+  return DSA_ERR_UNSUPPORTED;
+}
+
+static int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cached[dev]) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    cached[dev] = v;
+  }
+  return cached[dev];
+}
+
+inline size_t psa_fused_lds(int max_pages) {
+  return (((size_t)max_pages * 4 + 15) & ~(size_t)15) + (size_t)max_pages * 4;
+}
+
+// The fused kernel for this shape, or DSA_ERR_UNSUPPORTED when its LDS
+// (static + page-table row + scores) does not fit a workgroup.
+template <typename T, int D, int G>
+static int launch_psa_fused_g(const void* q, const dsa_kv* kv, const void* meta, float thr, int stop_mode,
+                              float scale, float* scores, int32_t* ids, int32_t* counts, float* O, float* l, float* m,
+                              hipStream_t st) {
+  const int never_stop = thr >= 1.0f;
+  const int always_stop = thr <= 0.0f;
+  const float ln_odds = (never_stop || always_stop) ? 0.0f : (float)log((double)thr / (1.0 - (double)thr));
+  const float c = scale * kLog2e;
+  constexpr int NT = psa_waves<T, G>() * 64;
+  const size_t dyn = psa_fused_lds(kv->max_pages);
+  auto go = [&](auto kernel) -> int {
+    hipFuncAttributes fa{};
+    if (hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(kernel)) != hipSuccess) return DSA_ERR_LAUNCH;
+    if (fa.sharedSizeBytes + dyn > (size_t)max_lds_per_block()) return DSA_ERR_UNSUPPORTED;
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)dyn) != hipSuccess)
+      return DSA_ERR_LAUNCH;
+    hipLaunchKernelGGL(kernel, dim3(kv->n_kv_heads, kv->batch), dim3(NT), dyn, st, (const T*)q, (const T*)kv->k,
+                       (const T*)kv->v, (const T*)meta, kv->page_table, kv->seq_lens, kv->n_kv_heads, kv->page_size,
+                       kv->max_pages, kv->num_slots, stop_mode, never_stop, always_stop, ln_odds, scale, c, scores,
+                       ids, counts, O, l, m);
+    return launch_status();
+  };
+  if (kv->max_pages <= 4096) return go(psa_fused_kernel<T, D, G, 4096 / NT>);
+  return go(psa_fused_kernel<T, D, G, kPsaFusedMaxPages / NT>);
+}
+
+template <typename T, int D>
+static int launch_psa_fused_d(const void* q, int G, const dsa_kv* kv, const void* meta, float thr, int stop_mode,
+                              float scale, float* scores, int32_t* ids, int32_t* counts, float* O, float* l, float* m,
+                              hipStream_t st) {
+  switch (G) {
+    case 1: return launch_psa_fused_g<T, D, 1>(q, kv, meta, thr, stop_mode, scale, scores, ids, counts, O, l, m, st);
+    case 2: return launch_psa_fused_g<T, D, 2>(q, kv, meta, thr, stop_mode, scale, scores, ids, counts, O, l, m, st);
+    case 4: return launch_psa_fused_g<T, D, 4>(q, kv, meta, thr, stop_mode, scale, scores, ids, counts, O, l, m, st);
   }
   return DSA_ERR_UNSUPPORTED;
 }
@@ -1329,4 +1498,34 @@ extern "C" int dsa_page_select_progressive(const void* q, int32_t n_q_heads, con
               : launch_psa_d<float, 128>(q, G, kv, scores, threshold, stop_mode, scale, ids, counts, O, l, m, st);
   return bf ? launch_psa_d<uint16_t, 64>(q, G, kv, scores, threshold, stop_mode, scale, ids, counts, O, l, m, st)
             : launch_psa_d<float, 64>(q, G, kv, scores, threshold, stop_mode, scale, ids, counts, O, l, m, st);
+}
+
+extern "C" int dsa_psa_decode(const void* q, int32_t n_q_heads, const dsa_kv* kv, const void* meta, float threshold,
+                              int32_t stop_mode, float scale, float* scores, int32_t* ids, int32_t* counts, float* O,
+                              float* l, float* m, void* stream) {
+  int G = 0;
+  int rc = check_attn_common(q, n_q_heads, kv, scale, &G);
+  if (rc) return rc;
+  if (stop_mode != 0 && stop_mode != 1) return DSA_ERR_SHAPE;
+  if (threshold != threshold) return DSA_ERR_SHAPE;
+  if (kv->max_pages > kPsaMaxPages) return DSA_ERR_UNSUPPORTED;
+  if (G > 4) return DSA_ERR_UNSUPPORTED;
+  if (kv->batch == 0) return DSA_OK;
+  if (!meta || !scores || !ids || !counts || !O || !l || !m) return DSA_ERR_NULL;
+  if (!aligned16(meta)) return DSA_ERR_ALIGN;
+  hipStream_t st = (hipStream_t)stream;
+  const bool bf = kv->dtype == DSA_BF16;
+  if (kv->max_pages <= kPsaFusedMaxPages && (long long)kv->batch * kv->n_kv_heads >= cu_count()) {
+    if (kv->head_dim == 128)
+      rc = bf ? launch_psa_fused_d<uint16_t, 128>(q, G, kv, meta, threshold, stop_mode, scale, scores, ids, counts, O, l, m, st)
+              : launch_psa_fused_d<float, 128>(q, G, kv, meta, threshold, stop_mode, scale, scores, ids, counts, O, l, m, st);
+    else
+      rc = bf ? launch_psa_fused_d<uint16_t, 64>(q, G, kv, meta, threshold, stop_mode, scale, scores, ids, counts, O, l, m, st)
+              : launch_psa_fused_d<float, 64>(q, G, kv, meta, threshold, stop_mode, scale, scores, ids, counts, O, l, m, st);
+    if (rc != DSA_ERR_UNSUPPORTED) return rc;
+  }
+  // fewer rows than CUs, long rows, or an LDS budget that does not fit: the two calls
+  if ((rc = dsa_page_score(q, n_q_heads, kv, meta, kv->page_size, nullptr, scores, stream))) return rc;
+  return dsa_page_select_progressive(q, n_q_heads, kv, scores, threshold, stop_mode, scale, ids, counts, O, l, m,
+                                     stream);
 }

@@ -257,6 +257,22 @@ int dsa_page_select_progressive(const void *q, int32_t n_q_heads, const dsa_kv *
                                 float *m, void *stream);
 
 /*
+ * dsa_psa_decode -- dsa_page_score followed by dsa_page_select_progressive
+ * ([LServe] section 4.2 criticality, [PSA] section 3.2 progressive
+ * selection) in one call, for meta built with logical_page = page_size and no
+ * streaming heads.  When there are at least as many (b, KV head) rows as the
+ * GPU has CUs and max_pages <= 8192, one workgroup per row computes its
+ * row's scores into LDS and goes straight on to the selection and walk (one
+ * launch); otherwise the two calls run in sequence.  Either way the results
+ * are those of the two calls: scores (device float [batch][n_kv_heads]
+ * [max_pages], written), ids, counts, O, l, m as dsa_page_select_progressive.
+ * Requires max_pages <= 65536 and 1, 2 or 4 q heads per KV head.
+ */
+int dsa_psa_decode(const void *q, int32_t n_q_heads, const dsa_kv *kv, const void *meta,
+                   float threshold, int32_t stop_mode, float scale, float *scores, int32_t *ids,
+                   int32_t *counts, float *O, float *l, float *m, void *stream);
+
+/*
  * dsa_sparse_decode_attn -- attention over the selected pages only ([LServe]
  * section 3.3: the decode kernel loops only over the needed pages through a
  * two-level index, step -> page -> cache slot; [PRR] section 3.3: the

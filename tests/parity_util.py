@@ -118,29 +118,36 @@ def check_selected_attention(dsa, batch, q, kv, st, ids, counts, out, ref_ids, u
 
 def check_psa(dsa, bt, q, kv, s32: np.ndarray, thr: float, mode: int, what=""):
     """PSA's progressive selection on the score rows `s32` ([B][H][max_pages]
-    float32) against the oracle's walk over the same values, unit by unit:
-    the stop count (a different count only where a stop-test ratio sits on
-    the threshold), the visited pages in rank order, -1 after them, and the
-    attention over the visited pages.  Returns the counts."""
+    float32) against the oracle's walk over the same values, unit by unit
+    (see check_psa_result).  Returns the counts."""
     import torch
     sc = torch.from_numpy(np.ascontiguousarray(s32, np.float32)).cuda()
-    ids, counts, O, l, m = (np_(x) for x in dsa.page_select_progressive(q, kv, sc, thr, mode, float(bt.scale)))
+    res = [np_(x) for x in dsa.page_select_progressive(q, kv, sc, thr, mode, float(bt.scale))]
+    check_psa_result(bt, s32, *res, thr, mode, what)
+    return res[1]
+
+
+def check_psa_result(bt, s32, ids, counts, O, l, m, thr: float, mode: int, what="", units=None):
+    """One progressive-selection result against the oracle's walk over the
+    same float32 scores: the stop count (a different count only where a
+    stop-test ratio sits on the threshold), the visited pages in rank order,
+    -1 after them, and the attention over the visited pages."""
     G = bt.group
-    for b in range(bt.batch):
+    if units is None:
+        units = [(b, h) for b in range(bt.batch) for h in range(bt.n_kv_heads)]
+    for b, h in units:
         nv = oracle.n_pages(bt.seq_lens[b], bt.page_size)
-        for h in range(bt.n_kv_heads):
-            row = s32[b, h].astype(np.float64)
-            rid, rn, *_ = oracle.psa_progressive(bt, b, h, row, thr, mode)
-            n = int(counts[b, h])
-            if n != rn:
-                ratios = oracle.psa_ratios(bt, b, h, row, mode)
-                lo, hi = min(n, rn), max(n, rn)
-                near = np.abs(ratios[lo - 1:hi] - thr) <= 1e-5 * thr
-                assert near.any(), f"{what}: stop {n} != oracle {rn} at (b={b}, h={h})"
-            ranked = oracle.rank_pages(row, nv)
-            assert np.array_equal(ids[b, h, :n], ranked[:n]), f"{what}: visit order differs at (b={b}, h={h})"
-            assert np.all(ids[b, h, n:] == -1), f"{what}: padding not -1 at (b={b}, h={h})"
-            ref = oracle.attend_pages(bt, b, h, ids[b, h, :n])
-            sl = slice(h * G, (h + 1) * G)
-            check_attention(bt.dtype, O[b, sl], l[b, sl], m[b, sl], *ref, f"{what} (b={b}, h={h})")
-    return counts
+        row = s32[b, h].astype(np.float64)
+        rid, rn, *_ = oracle.psa_progressive(bt, b, h, row, thr, mode)
+        n = int(counts[b, h])
+        if n != rn:
+            ratios = oracle.psa_ratios(bt, b, h, row, mode)
+            lo, hi = min(n, rn), max(n, rn)
+            near = np.abs(ratios[lo - 1:hi] - thr) <= 1e-5 * thr
+            assert near.any(), f"{what}: stop {n} != oracle {rn} at (b={b}, h={h})"
+        ranked = oracle.rank_pages(row, nv)
+        assert np.array_equal(ids[b, h, :n], ranked[:n]), f"{what}: visit order differs at (b={b}, h={h})"
+        assert np.all(ids[b, h, n:] == -1), f"{what}: padding not -1 at (b={b}, h={h})"
+        ref = oracle.attend_pages(bt, b, h, ids[b, h, :n])
+        sl = slice(h * G, (h + 1) * G)
+        check_attention(bt.dtype, O[b, sl], l[b, sl], m[b, sl], *ref, f"{what} (b={b}, h={h})")

@@ -102,6 +102,15 @@ def test_validation_errors(dsa):
     assert L.dsa_page_select_progressive(ok_ptr, 4, ctypes.byref(_kv(dsa, max_pages=65537)), ok_ptr,
                                          ctypes.c_float(0.9), 0, ctypes.c_float(0.088), ok_ptr, ok_ptr, ok_ptr,
                                          ok_ptr, ok_ptr, None) == -4
+    # psa_decode: bad stop mode, G=8 unsupported, missing metadata, too many pages
+    assert L.dsa_psa_decode(ok_ptr, 4, ctypes.byref(kv), ok_ptr, ctypes.c_float(0.9), 2, ctypes.c_float(0.088),
+                            ok_ptr, ok_ptr, ok_ptr, ok_ptr, ok_ptr, ok_ptr, None) == -2
+    assert L.dsa_psa_decode(ok_ptr, 16, ctypes.byref(kv), ok_ptr, ctypes.c_float(0.9), 0, ctypes.c_float(0.088),
+                            ok_ptr, ok_ptr, ok_ptr, ok_ptr, ok_ptr, ok_ptr, None) == -4
+    assert L.dsa_psa_decode(ok_ptr, 4, ctypes.byref(kv), None, ctypes.c_float(0.9), 0, ctypes.c_float(0.088),
+                            ok_ptr, ok_ptr, ok_ptr, ok_ptr, ok_ptr, ok_ptr, None) == -1
+    assert L.dsa_psa_decode(ok_ptr, 4, ctypes.byref(_kv(dsa, max_pages=65537)), ok_ptr, ctypes.c_float(0.9), 0,
+                            ctypes.c_float(0.088), ok_ptr, ok_ptr, ok_ptr, ok_ptr, ok_ptr, ok_ptr, None) == -4
     # append: null new rows / lengths, misaligned rows or metadata, bad logical page
     assert L.dsa_kv_append(ctypes.byref(kv), 16, None, ok_ptr, ok_ptr, ok_ptr, None, None) == -1
     assert L.dsa_kv_append(ctypes.byref(kv), 16, ok_ptr, ok_ptr, ok_ptr, None, None, None) == -1
