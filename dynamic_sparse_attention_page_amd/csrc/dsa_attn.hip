@@ -28,6 +28,9 @@
 #ifndef DSA_TILES_PER_WAVE
 #define DSA_TILES_PER_WAVE 2  // 16-token K/V tiles per wave of the VALU partial kernel (all in flight at once)
 #endif
+#ifndef DSA_TILES_PER_WAVE_WIDE
+#define DSA_TILES_PER_WAVE_WIDE 3  // the same when the grid would hold more splits than the GPU has CUs
+#endif
 #ifndef DSA_TILES_PER_WAVE_MFMA
 #define DSA_TILES_PER_WAVE_MFMA 4  // the same for the matrix-core partial kernel
 #endif
@@ -36,6 +39,8 @@ namespace dsa {
 
 constexpr int kWgWaves = 4;
 constexpr int kTilesPerWave = DSA_TILES_PER_WAVE;
+constexpr int kTilesPerWaveWide = DSA_TILES_PER_WAVE_WIDE;
+static_assert(kTilesPerWaveWide >= kTilesPerWave, "the narrow split is the smallest");
 constexpr int kTilesPerWaveMfma = DSA_TILES_PER_WAVE_MFMA;
 
 // Fused selection (dsa_sparse_decode_attn_topk): each split workgroup ranks
@@ -51,7 +56,7 @@ struct SelectArgs {
 };
 
 // ============================================================ split-KV partial
-template <typename T, int D, int G, bool FILTER, int SEL_E>
+template <typename T, int D, int G, bool FILTER, int SEL_E, int TW>
 __global__ __launch_bounds__(256) void attn_partial_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const int32_t* __restrict__ page_table, const int32_t* __restrict__ seq_lens,
@@ -182,7 +187,6 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
   // unconditionally (a tile past the split's end, or of a page without a
   // slot, re-reads tile 0 of slot 0 of this head and is skipped), so no
   // wait covers a load that is not needed yet.
-  constexpr int TW = kTilesPerWave;
   uint32_t kd[TW][4][DW], vd[TW][4][DW];
   int nv[TW], tk[TW];
 #pragma unroll
@@ -1101,20 +1105,34 @@ __global__ __launch_bounds__((psa_waves<T, G>() * 64)) void psa_fused_kernel(
 }
 
 // ============================================================ host planning
+static int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cached[dev]) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    cached[dev] = v;
+  }
+  return cached[dev];
+}
+
 struct SplitPlan {
   int tiles_per_split, n_splits, TPP;
 };
 
 // A split is one workgroup: 4 waves of TW tiles each, all in flight at once
 // (TW = kTilesPerWaveMfma for the matrix-core kernel, 8+ heads per KV head
-// with bf16 KV), so the grid grows with the selection: counts live on the
-// device, so it is sized for ids_stride entries, and splits past a row's
-// count exit at once.
-inline SplitPlan plan_splits(const dsa_kv* kv, int ids_stride, bool mfma) {
+// with bf16 KV; for the VALU kernel kTilesPerWave, or kTilesPerWaveWide when
+// that would give more splits than the GPU has CUs: fewer, longer splits
+// then repeat the fused selection less often), so the grid grows with the
+// selection: counts live on the device, so it is sized for ids_stride
+// entries, and splits past a row's count exit at once.
+inline SplitPlan plan_splits(const dsa_kv* kv, int ids_stride, int tw) {
   SplitPlan p;
   p.TPP = kv->page_size / 16;
   const long long tiles_max = (long long)ids_stride * p.TPP;
-  p.tiles_per_split = kWgWaves * (mfma ? kTilesPerWaveMfma : kTilesPerWave);
+  p.tiles_per_split = kWgWaves * tw;
   p.n_splits = (int)((tiles_max + p.tiles_per_split - 1) / p.tiles_per_split);
   if (p.n_splits < 1) p.n_splits = 1;
   return p;
@@ -1141,8 +1159,14 @@ static int launch_attn_g(const void* q, const dsa_kv* kv, const int32_t* ids, co
                          int ids_stride, uint64_t smask, int sink, int local, float scale, float* O, float* l,
                          float* m, void* ws, int fold, const int32_t* skip_ids, const int32_t* skip_counts,
                          const SelectArgs& sel, hipStream_t st) {
-  const SplitPlan p = plan_splits(kv, ids_stride, sizeof(T) == 2 && G >= 8);
+  constexpr bool kMfma = sizeof(T) == 2 && G >= 8;
   const size_t units = (size_t)kv->batch * kv->n_kv_heads;
+  int tw = kMfma ? kTilesPerWaveMfma : kTilesPerWave;
+  if (!kMfma) {
+    const long long tiles = (long long)units * ids_stride * (kv->page_size / 16);
+    if ((tiles + kWgWaves * tw - 1) / (kWgWaves * tw) > cu_count()) tw = kTilesPerWaveWide;
+  }
+  const SplitPlan p = plan_splits(kv, ids_stride, tw);
   float* part_o = (float*)ws;
   float* part_ml = (float*)((char*)ws + align256(units * max_splits_of(kv, ids_stride) * G * D * sizeof(float)));
   const float c = scale * kLog2e;
@@ -1158,11 +1182,23 @@ static int launch_attn_g(const void* q, const dsa_kv* kv, const int32_t* ids, co
     if (skip_ids) DSA_PARTIAL(attn_partial_mfma_kernel, uint16_t, D, G, true);
     else DSA_PARTIAL(attn_partial_mfma_kernel, uint16_t, D, G, false);
   } else {
-    if (sel.e == 8) DSA_PARTIAL(attn_partial_kernel, T, T, D, G, false, 8);
-    else if (sel.e == 16) DSA_PARTIAL(attn_partial_kernel, T, T, D, G, false, 16);
-    else if (sel.e) return DSA_ERR_UNSUPPORTED;
-    else if (skip_ids) DSA_PARTIAL(attn_partial_kernel, T, T, D, G, true, 0);
-    else DSA_PARTIAL(attn_partial_kernel, T, T, D, G, false, 0);
+    constexpr int W1 = kTilesPerWave, W2 = kTilesPerWaveWide;
+    const bool wide = tw == W2 && W2 != W1;
+    if (sel.e == 8) {
+      if (wide) DSA_PARTIAL(attn_partial_kernel, T, T, D, G, false, 8, W2);
+      else DSA_PARTIAL(attn_partial_kernel, T, T, D, G, false, 8, W1);
+    } else if (sel.e == 16) {
+      if (wide) DSA_PARTIAL(attn_partial_kernel, T, T, D, G, false, 16, W2);
+      else DSA_PARTIAL(attn_partial_kernel, T, T, D, G, false, 16, W1);
+    } else if (sel.e) {
+      return DSA_ERR_UNSUPPORTED;
+    } else if (skip_ids) {
+      if (wide) DSA_PARTIAL(attn_partial_kernel, T, T, D, G, true, 0, W2);
+      else DSA_PARTIAL(attn_partial_kernel, T, T, D, G, true, 0, W1);
+    } else {
+      if (wide) DSA_PARTIAL(attn_partial_kernel, T, T, D, G, false, 0, W2);
+      else DSA_PARTIAL(attn_partial_kernel, T, T, D, G, false, 0, W1);
+    }
   }
 #undef DSA_PARTIAL
   int rc = launch_status();
@@ -1259,17 +1295,6 @@ static int launch_psa_d(const void* q, int G, const dsa_kv* kv, const float* sco
   return DSA_ERR_UNSUPPORTED;
 }
 
-static int cu_count() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (!cached[dev]) {
-    int v = 0;
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
-    cached[dev] = v;
-  }
-  return cached[dev];
-}
 
 inline size_t psa_fused_lds(int max_pages) {
   return (((size_t)max_pages * 4 + 15) & ~(size_t)15) + (size_t)max_pages * 4;
