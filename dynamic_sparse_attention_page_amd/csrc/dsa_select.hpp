@@ -69,7 +69,7 @@ __device__ __forceinline__ BucketCut bucket_search(const unsigned* hist, int nee
 
 template <int E, int NW>
 struct SelectSmem {
-  unsigned hist[2][kHistWords];      // alternate passes use alternate buffers
+  __align__(16) unsigned hist[2][kHistWords];   // alternate passes use alternate buffers
   unsigned long long small[kSmall];
   int scan[NW];                      // ordered_ranks
   int rank[E * NW];
@@ -253,7 +253,9 @@ __device__ __forceinline__ unsigned long long block_select_top(const uint32_t (&
       return selm;   // the next writer of small / kappa / n_small passes a barrier first
     }
     unsigned* hist = sm.hist[pass & 1];
-    for (int x = tid; x < kHistWords; x += NT) hist[x] = 0u;   // last read two barriers ago
+    static_assert(kHistWords % 4 == 0, "16-byte clears");
+    for (int x = tid; x < kHistWords / 4; x += NT)   // last read two barriers ago
+      reinterpret_cast<uint4*>(hist)[x] = make_uint4(0u, 0u, 0u, 0u);
     if (tid == 0) sm.n_small = 0;
     uint32_t lo = 0xFFFFFFFFu, hi = 0u;
 #pragma unroll
@@ -278,30 +280,28 @@ __device__ __forceinline__ unsigned long long block_select_top(const uint32_t (&
         map.inv = inv;
       }
     }
+    // each element's bucket, kept for the classification after the search
+    uint32_t bk[E];
     if (map.lin) {
 #pragma unroll
-      for (int e = 0; e < E; ++e)
-        if ((actm >> e) & 1ull) atomicAdd(&hist[hist_at(map.linear(key[e]))], 1u);
+      for (int e = 0; e < E; ++e) bk[e] = map.linear(key[e]);
     } else {
 #pragma unroll
-      for (int e = 0; e < E; ++e)
-        if ((actm >> e) & 1ull) atomicAdd(&hist[hist_at(map.shifted(key[e]))], 1u);
+      for (int e = 0; e < E; ++e) bk[e] = map.shifted(key[e]);
     }
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if ((actm >> e) & 1ull) atomicAdd(&hist[hist_at(bk[e])], 1u);
     group_sync<NW>();
     const BucketCut cut = bucket_search(hist, need);
-    auto classify = [&](auto bucket) {
+    unsigned long long above = 0ull, at = 0ull;
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const unsigned long long bit = 1ull << e;
-        if (actm & bit) {
-          const uint32_t bk = bucket(key[e]);
-          if (bk > cut.b) { selm |= bit; actm &= ~bit; }
-          else if (bk < cut.b) actm &= ~bit;
-        }
-      }
-    };
-    if (map.lin) classify([&](uint32_t k) { return map.linear(k); });
-    else classify([&](uint32_t k) { return map.shifted(k); });
+    for (int e = 0; e < E; ++e) {
+      above |= (unsigned long long)(bk[e] > cut.b) << e;
+      at |= (unsigned long long)(bk[e] == cut.b) << e;
+    }
+    selm |= actm & above;
+    actm &= at;
     need -= cut.above;
     n_act = cut.n;
     // no barrier: this hist buffer is next zeroed two passes later, after
