@@ -20,6 +20,8 @@
 // per-(element slot, wave) ballot counts that every wave scans itself.
 #pragma once
 
+#include <type_traits>
+
 #include "dsa_common.hpp"
 
 namespace dsa {
@@ -66,6 +68,13 @@ __device__ __forceinline__ BucketCut bucket_search(const unsigned* hist, int nee
   c.n = __builtin_amdgcn_readlane(hb, fl);
   return c;
 }
+
+// Per-thread element masks: 32 bits when a thread holds at most 32 elements
+// (half the mask arithmetic), else 64.
+template <int E>
+struct MaskOf {
+  using type = typename std::conditional<(E <= 32), uint32_t, unsigned long long>::type;
+};
 
 template <int E, int NW>
 struct SelectSmem {
@@ -115,14 +124,16 @@ __device__ __forceinline__ int block_excl_scan(int x, int* smem /* NW ints */, i
 // else one block scan orders them.  Consecutive calls on the same buffers
 // must be separated by a workgroup barrier.
 template <int E, int NW>
-__device__ __forceinline__ int ordered_ranks(unsigned long long mask, int (&rank)[E], int* cnt /* E*NW */,
+__device__ __forceinline__ int ordered_ranks(unsigned long long mask64, int (&rank)[E], int* cnt /* E*NW */,
                                              int* scan_smem /* NW */) {
   static_assert(E * NW <= NW * 64, "one (element, wave) slot per thread");
+  using M = typename MaskOf<E>::type;
+  const M mask = (M)mask64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const unsigned long long below = (1ull << lane) - 1ull;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    const unsigned long long b = __ballot((mask >> e) & 1ull);
+    const unsigned long long b = __ballot((mask >> e) & 1u);
     rank[e] = __popcll(b & below);
     if (lane == 0) cnt[e * NW + wave] = __popcll(b);
   }
@@ -211,13 +222,15 @@ __device__ __forceinline__ int block_excl_scan_1b(int x, int* smem /* NW */) {
 }
 
 template <int E, int NW>
-__device__ __forceinline__ unsigned long long block_select_top(const uint32_t (&key)[E], unsigned long long actm,
+__device__ __forceinline__ unsigned long long block_select_top(const uint32_t (&key)[E], unsigned long long actm64,
                                                                int n_act, int need, SelectSmem<E, NW>& sm) {
+  using M = typename MaskOf<E>::type;
+  M actm = (M)actm64;
   constexpr int NT = NW * 64;
   if (need <= 0) return 0ull;
   if (need >= n_act) return actm;
   const int tid = threadIdx.x;
-  unsigned long long selm = 0ull;
+  M selm = 0;
   // at most: a linear pass and three shift passes narrow the keys to one
   // value, whose min / max then ends the loop
   for (int pass = 0; pass < 5; ++pass) {
@@ -232,7 +245,7 @@ __device__ __forceinline__ unsigned long long block_select_top(const uint32_t (&
       }
 #pragma unroll
       for (int e = 0; e < E; ++e)
-        if ((actm >> e) & 1ull) {
+        if ((actm >> e) & 1u) {
           const int p = atomicAdd(&sm.n_small, 1);
           sm.small[p] = ((unsigned long long)key[e] << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)(e * NT + tid));
         }
@@ -248,8 +261,8 @@ __device__ __forceinline__ unsigned long long block_select_top(const uint32_t (&
       const int cut_idx = (int)(0xFFFFFFFFu - (uint32_t)(sm.kappa & 0xFFFFFFFFull));
 #pragma unroll
       for (int e = 0; e < E; ++e)
-        if (((actm >> e) & 1ull) && (key[e] > cut_key || (key[e] == cut_key && e * NT + tid <= cut_idx)))
-          selm |= 1ull << e;
+        if (((actm >> e) & 1u) && (key[e] > cut_key || (key[e] == cut_key && e * NT + tid <= cut_idx)))
+          selm |= (M)1 << e;
       return selm;   // the next writer of small / kappa / n_small passes a barrier first
     }
     unsigned* hist = sm.hist[pass & 1];
@@ -260,7 +273,7 @@ __device__ __forceinline__ unsigned long long block_select_top(const uint32_t (&
     uint32_t lo = 0xFFFFFFFFu, hi = 0u;
 #pragma unroll
     for (int e = 0; e < E; ++e)
-      if ((actm >> e) & 1ull) { lo = min(lo, key[e]); hi = max(hi, key[e]); }
+      if ((actm >> e) & 1u) { lo = min(lo, key[e]); hi = max(hi, key[e]); }
     block_minmax_1b<NW>(lo, hi, sm.mm[pass & 1]);   // also orders the zeroing before the atomics
     if (lo == hi) break;
     BucketMap map;
@@ -291,14 +304,14 @@ __device__ __forceinline__ unsigned long long block_select_top(const uint32_t (&
     }
 #pragma unroll
     for (int e = 0; e < E; ++e)
-      if ((actm >> e) & 1ull) atomicAdd(&hist[hist_at(bk[e])], 1u);
+      if ((actm >> e) & 1u) atomicAdd(&hist[hist_at(bk[e])], 1u);
     group_sync<NW>();
     const BucketCut cut = bucket_search(hist, need);
-    unsigned long long above = 0ull, at = 0ull;
+    M above = 0, at = 0;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      above |= (unsigned long long)(bk[e] > cut.b) << e;
-      at |= (unsigned long long)(bk[e] == cut.b) << e;
+      above |= (M)(bk[e] > cut.b) << e;
+      at |= (M)(bk[e] == cut.b) << e;
     }
     selm |= actm & above;
     actm &= at;
@@ -312,7 +325,7 @@ __device__ __forceinline__ unsigned long long block_select_top(const uint32_t (&
   ordered_ranks<E, NW>(actm, rk, sm.rank, sm.scan);
 #pragma unroll
   for (int e = 0; e < E; ++e)
-    if (((actm >> e) & 1ull) && rk[e] < need) selm |= 1ull << e;
+    if (((actm >> e) & 1u) && rk[e] < need) selm |= (M)1 << e;
   return selm;
 }
 
