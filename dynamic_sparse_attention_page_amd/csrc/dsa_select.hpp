@@ -326,6 +326,7 @@ __device__ __forceinline__ unsigned long long block_select_top(const uint32_t (&
 #pragma unroll
   for (int e = 0; e < E; ++e)
     if (((actm >> e) & 1u) && rk[e] < need) selm |= (M)1 << e;
+  group_sync<NW>();   // every wave has read the counts: the caller may rank with sm.rank next
   return selm;
 }
 
