@@ -42,6 +42,10 @@ constexpr int kTilesPerWave = DSA_TILES_PER_WAVE;
 constexpr int kTilesPerWaveWide = DSA_TILES_PER_WAVE_WIDE;
 static_assert(kTilesPerWaveWide >= kTilesPerWave, "the narrow split is the smallest");
 constexpr int kTilesPerWaveMfma = DSA_TILES_PER_WAVE_MFMA;
+#ifndef DSA_TILES_PER_WAVE_REPAIR
+#define DSA_TILES_PER_WAVE_REPAIR 1  // the same for the repair over a compacted M (both kernels): M is short
+#endif
+constexpr int kTilesPerWaveRepair = DSA_TILES_PER_WAVE_REPAIR;
 
 // Fused selection (dsa_sparse_decode_attn_topk): each split workgroup ranks
 // its row of scores itself and takes the entries of its range; split 0
@@ -279,7 +283,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
 // Same split and output as attn_partial_kernel, for bf16 KV with 8 or 16 q
 // heads per KV head: each wave runs the MFMA tile of dsa_attn_mfma.hpp over
 // its tiles, and the 4 wave states meet in LDS.
-template <int D, int G, bool FILTER>
+template <int D, int G, bool FILTER, int TW>
 __global__ __launch_bounds__(256) void attn_partial_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ page_table, const int32_t* __restrict__ seq_lens,
@@ -346,7 +350,6 @@ __global__ __launch_bounds__(256) void attn_partial_mfma_kernel(
 
   // The TW tiles of this wave, loaded together and computed in order (see
   // attn_partial_kernel).
-  constexpr int TW = kTilesPerWaveMfma;
   uint4 kr[TW][NK], vr[TW][NK];
   int nv[TW], tk[TW];
 #pragma unroll
@@ -1140,17 +1143,22 @@ inline SplitPlan plan_splits(const dsa_kv* kv, int ids_stride, int tw) {
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Workspace for any plan of this shape: the smallest split gives the most
-// splits.
-inline size_t max_splits_of(const dsa_kv* kv, int ids_stride) {
-  constexpr int kMinTiles = kWgWaves * (kTilesPerWave < kTilesPerWaveMfma ? kTilesPerWave : kTilesPerWaveMfma);
+// Workspace for any plan of this shape whose waves take at least min_tw
+// tiles: the smallest split gives the most splits.  The partial O values
+// come first, then the (m, l) pairs at an offset set by the plan's own
+// split count.
+inline size_t max_splits_of(const dsa_kv* kv, int ids_stride, int min_tw) {
+  const size_t min_tiles = (size_t)kWgWaves * min_tw;
   const size_t tiles_max = (size_t)ids_stride * (kv->page_size / 16);
-  return (tiles_max + kMinTiles - 1) / kMinTiles;
+  return (tiles_max + min_tiles - 1) / min_tiles;
 }
 
-inline size_t partial_bytes(const dsa_kv* kv, int G, int ids_stride) {
+constexpr int kMinTwAttn = kTilesPerWave < kTilesPerWaveMfma ? kTilesPerWave : kTilesPerWaveMfma;
+constexpr int kMinTwRepair = kMinTwAttn < kTilesPerWaveRepair ? kMinTwAttn : kTilesPerWaveRepair;
+
+inline size_t partial_bytes(const dsa_kv* kv, int G, int ids_stride, int min_tw) {
   const size_t units = (size_t)kv->batch * kv->n_kv_heads;
-  const size_t ms = max_splits_of(kv, ids_stride);
+  const size_t ms = max_splits_of(kv, ids_stride, min_tw);
   return align256(units * ms * G * kv->head_dim * sizeof(float)) + align256(units * ms * G * 2 * sizeof(float));
 }
 
@@ -1161,14 +1169,19 @@ static int launch_attn_g(const void* q, const dsa_kv* kv, const int32_t* ids, co
                          const SelectArgs& sel, hipStream_t st) {
   constexpr bool kMfma = sizeof(T) == 2 && G >= 8;
   const size_t units = (size_t)kv->batch * kv->n_kv_heads;
-  int tw = kMfma ? kTilesPerWaveMfma : kTilesPerWave;
-  if (!kMfma) {
+  // the repair over a compacted M (fold, no P to filter) reads a short
+  // prefix of a long id row: many short splits, each one latency chain,
+  // finish it sooner than a few long ones.  With P to filter every split
+  // builds P's bitmap first, so that path keeps the usual splits.
+  const bool repair = fold != 0 && skip_ids == nullptr;
+  int tw = repair ? kTilesPerWaveRepair : (kMfma ? kTilesPerWaveMfma : kTilesPerWave);
+  if (!kMfma && !repair) {
     const long long tiles = (long long)units * ids_stride * (kv->page_size / 16);
     if ((tiles + kWgWaves * tw - 1) / (kWgWaves * tw) > cu_count()) tw = kTilesPerWaveWide;
   }
   const SplitPlan p = plan_splits(kv, ids_stride, tw);
   float* part_o = (float*)ws;
-  float* part_ml = (float*)((char*)ws + align256(units * max_splits_of(kv, ids_stride) * G * D * sizeof(float)));
+  float* part_ml = (float*)((char*)ws + align256(units * (size_t)p.n_splits * G * D * sizeof(float)));
   const float c = scale * kLog2e;
   dim3 grid(p.n_splits, kv->n_kv_heads, kv->batch);
   const size_t dyn = skip_ids ? (size_t)((kv->max_pages + 31) / 32) * sizeof(uint32_t) : 0;
@@ -1178,13 +1191,18 @@ static int launch_attn_g(const void* q, const dsa_kv* kv, const int32_t* ids, co
                      kv->page_size, kv->max_pages, kv->num_slots, (unsigned long long)smask, sink, local, scale, \
                      c, p.tiles_per_split, p.n_splits, skip_ids, skip_counts, sel, part_o, part_ml)
   if constexpr (sizeof(T) == 2 && G >= 8) {
+    constexpr int WM = kTilesPerWaveMfma, WR = kTilesPerWaveRepair;
     if (sel.e) return DSA_ERR_UNSUPPORTED;
-    if (skip_ids) DSA_PARTIAL(attn_partial_mfma_kernel, uint16_t, D, G, true);
-    else DSA_PARTIAL(attn_partial_mfma_kernel, uint16_t, D, G, false);
+    if (repair) DSA_PARTIAL(attn_partial_mfma_kernel, uint16_t, D, G, false, WR);
+    else if (skip_ids) DSA_PARTIAL(attn_partial_mfma_kernel, uint16_t, D, G, true, WM);
+    else DSA_PARTIAL(attn_partial_mfma_kernel, uint16_t, D, G, false, WM);
   } else {
-    constexpr int W1 = kTilesPerWave, W2 = kTilesPerWaveWide;
+    constexpr int W1 = kTilesPerWave, W2 = kTilesPerWaveWide, WR = kTilesPerWaveRepair;
     const bool wide = tw == W2 && W2 != W1;
-    if (sel.e == 8) {
+    if (repair) {
+      if (sel.e) return DSA_ERR_UNSUPPORTED;
+      DSA_PARTIAL(attn_partial_kernel, T, T, D, G, false, 0, WR);
+    } else if (sel.e == 8) {
       if (wide) DSA_PARTIAL(attn_partial_kernel, T, T, D, G, false, 8, W2);
       else DSA_PARTIAL(attn_partial_kernel, T, T, D, G, false, 8, W1);
     } else if (sel.e == 16) {
@@ -1350,9 +1368,8 @@ extern "C" size_t dsa_workspace_bytes(int32_t op, const dsa_kv* kv, int32_t n_q_
   if (check_kv(kv, false) != DSA_OK || n_q_heads < 1 || n_q_heads % kv->n_kv_heads || ids_stride < 1) return 0;
   const int G = n_q_heads / kv->n_kv_heads;
   if (!pow2_group(G)) return 0;
-  const size_t part = partial_bytes(kv, G, ids_stride);
-  if (op == DSA_OP_SPARSE_DECODE_ATTN) return part;
-  if (op == DSA_OP_ATTN_REPAIR) return part;
+  if (op == DSA_OP_SPARSE_DECODE_ATTN) return partial_bytes(kv, G, ids_stride, kMinTwAttn);
+  if (op == DSA_OP_ATTN_REPAIR) return partial_bytes(kv, G, ids_stride, kMinTwRepair);
   return 0;
 }
 
