@@ -288,6 +288,42 @@ def test_repair(gpu_lib, G, P):
     check_attention("bf16", np_(O), np_(l), np_(m), rO, rl, rm, "repair")
 
 
+
+@pytest.mark.parametrize("G,P", [(4, 16), (16, 16), (8, 64)])
+def test_repair_compacted(gpu_lib, G, P):
+    """Repair given M = A \\ P already compacted (no P argument; the PRR
+    step's form, run with short splits): spec over P + repair over M ==
+    attention over P u A.  M counts span empty, one page, ragged lengths
+    and the whole id row."""
+    dsa = gpu_lib
+    _banner(f"repair compacted G={G} P={P}")
+    lens = [P * 150 + 3, P * 64, P * 10]
+    bt = wl.random_batch(73, lens, n_q_heads=2 * G, n_kv_heads=2, head_dim=128, page_size=P)
+    q, kv, _ = to_device(dsa, bt)
+    rng = np.random.default_rng(11)
+    stride = 48
+    M = np.full((3, 2, stride), -1, np.int32)
+    Pp = np.full((3, 2, stride), -1, np.int32)
+    mc = np.zeros((3, 2), np.int32)
+    pc = np.zeros((3, 2), np.int32)
+    m_sizes = [0, 1, 5, 17, 33, stride]
+    for b in range(3):
+        n = oracle.n_pages(lens[b], P)
+        for h in range(2):
+            want = min(m_sizes[(2 * b + h) % len(m_sizes)], n)
+            perm = rng.permutation(n)
+            m_ = np.sort(perm[:want])
+            p_ = np.sort(perm[want:want + min(stride, n - want, 20)])
+            M[b, h, :len(m_)], mc[b, h] = m_, len(m_)
+            Pp[b, h, :len(p_)], pc[b, h] = p_, len(p_)
+    t = lambda x: torch.from_numpy(x).cuda()
+    O, l, m = dsa.sparse_decode_attn(q, kv, t(Pp), t(pc))
+    dsa.attn_repair(q, kv, t(M), t(mc), None, None, O, l, m)
+    union = [[np.array(sorted(set(M[b, h, :mc[b, h]]) | set(Pp[b, h, :pc[b, h]])), np.int64) for h in range(2)]
+             for b in range(3)]
+    rO, rl, rm = oracle.sparse_decode(bt, union)
+    check_attention("bf16", np_(O), np_(l), np_(m), rO, rl, rm, "repair compacted")
+
 # ---------------------------------------------------------------- EMA
 @pytest.mark.parametrize("n", [1, 3, 1000, 65539])
 def test_ema(gpu_lib, n):
