@@ -19,20 +19,20 @@ import torch
 __all__ = [
     "DsaError", "PagedKV", "Streaming", "lib", "LIB_PATH",
     "page_meta_build", "kv_append", "page_score", "page_score_ema", "page_select_topk", "page_select_progressive",
-    "psa_decode", "sparse_decode_attn", "sparse_decode_attn_noalloc", "sparse_decode_attn_topk", "attn_repair", "ema_predict_update", "prr_select", "prr_calibrate", "signal_host", "block_sparse_prefill",
+    "psa_decode", "sparse_decode_attn", "sparse_decode_attn_noalloc", "sparse_decode_attn_topk", "attn_repair", "prr_decode_step", "ema_predict_update", "prr_select", "prr_calibrate", "signal_host", "block_sparse_prefill",
     "workspace_bytes",
-    "OP_SPARSE_DECODE_ATTN", "OP_ATTN_REPAIR", "EXPORTED", "prr_select_workspace_bytes", "NOALLOC_SCRATCH_BYTES",
+    "OP_SPARSE_DECODE_ATTN", "OP_ATTN_REPAIR", "OP_PRR_DECODE_STEP", "EXPORTED", "prr_select_workspace_bytes", "NOALLOC_SCRATCH_BYTES",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsa.so")
 
 DSA_F32, DSA_BF16 = 0, 1
-OP_SPARSE_DECODE_ATTN, OP_ATTN_REPAIR = 1, 2
+OP_SPARSE_DECODE_ATTN, OP_ATTN_REPAIR, OP_PRR_DECODE_STEP = 1, 2, 3
 EXPORTED = (
     "dsa_status_str", "dsa_version", "dsa_page_meta_build", "dsa_kv_append", "dsa_page_score", "dsa_page_score_ema",
     "dsa_page_select_topk",
     "dsa_page_select_progressive", "dsa_psa_decode", "dsa_sparse_decode_attn", "dsa_sparse_decode_attn_noalloc",
-    "dsa_sparse_decode_attn_topk", "dsa_attn_repair",
+    "dsa_sparse_decode_attn_topk", "dsa_attn_repair", "dsa_prr_decode_step",
     "dsa_ema_predict_update", "dsa_prr_select", "dsa_prr_select_workspace_bytes", "dsa_prr_calibrate",
     "dsa_prr_calibrate_workspace_bytes",
     "dsa_signal_host", "dsa_block_sparse_prefill",
@@ -80,6 +80,8 @@ def _load(path: str = LIB_PATH):
         "dsa_sparse_decode_attn_noalloc": (ctypes.c_int, [P, I32, KV, P, P, I32, ST, F32, P, P, P, P]),
         "dsa_sparse_decode_attn_topk": (ctypes.c_int, [P, I32, KV, P, I32, ST, F32, P, P, P, P, P, P, SZ, P]),
         "dsa_attn_repair": (ctypes.c_int, [P, I32, KV, P, P, P, P, I32, F32, P, P, P, P, SZ, P]),
+        "dsa_prr_decode_step": (ctypes.c_int, [P, I32, KV, P, I32, P, P, P, P, F32, F32, F32, I32, P, P, P, P, P, P,
+                                               P, P, F32, P, P, P, P, SZ, P]),
         "dsa_ema_predict_update": (ctypes.c_int, [P, P, P, P, I64, F32, F32, F32, I32, P]),
         "dsa_prr_select": (ctypes.c_int, [P, I32, I32, I32, P, I32, I32, P, P, P, P, P, F32, F32, F32, I32, I32, P, P,
                                           P, P, P, P, P, SZ, P]),
@@ -421,6 +423,28 @@ def attn_repair(q: torch.Tensor, kv: PagedKV, a_ids, a_counts, p_ids, p_counts, 
     _check("dsa_attn_repair", lib.dsa_attn_repair(
         _ptr(q), Hq, ctypes.byref(kv.c()), _ptr(a_ids), _ptr(a_counts), _ptr(p_ids), _ptr(p_counts), stride, sc,
         _ptr(O), _ptr(l), _ptr(m), _ptr(ws), ws.numel() * ws.element_size(), _stream()))
+    return O, l, m
+
+
+def prr_decode_step(q: torch.Tensor, kv: PagedKV, meta: torch.Tensor, scores: torch.Tensor, level: torch.Tensor,
+                    trend: torch.Tensor, pred: torch.Tensor, alpha: float, beta: float, gamma: float, k: int,
+                    p_cur: tuple, a_out: tuple, m_out: tuple, p_out: tuple, O, l, m,
+                    logical_page: int | None = None, scale: float | None = None, ws: torch.Tensor | None = None):
+    """One speculative PRR step in one call on the current stream (see
+    dsa_prr_decode_step): scores + EMA, attention over P^t = p_cur, A^t into
+    a_out, M^t into m_out, P^{t+1} into p_out, (O, l, m) over P^t u A^t.
+    Every id tuple is (ids [batch][n_kv_heads][k], counts [batch][n_kv_heads])."""
+    lp = logical_page or kv.page_size
+    Hq = q.shape[1]
+    need = workspace_bytes(OP_PRR_DECODE_STEP, kv, Hq, k)
+    if ws is None:
+        ws = _workspace(need, kv.k.device)
+    sc = _default_scale(kv.head_dim) if scale is None else scale
+    _check("dsa_prr_decode_step", lib.dsa_prr_decode_step(
+        _ptr(q), Hq, ctypes.byref(kv.c()), _ptr(meta), lp, _ptr(scores), _ptr(level), _ptr(trend), _ptr(pred),
+        float(alpha), float(beta), float(gamma), k, _ptr(p_cur[0]), _ptr(p_cur[1]), _ptr(a_out[0]), _ptr(a_out[1]),
+        _ptr(m_out[0]), _ptr(m_out[1]), _ptr(p_out[0]), _ptr(p_out[1]), sc, _ptr(O), _ptr(l), _ptr(m), _ptr(ws),
+        ws.numel() * ws.element_size(), _stream()))
     return O, l, m
 
 

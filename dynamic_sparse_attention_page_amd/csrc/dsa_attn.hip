@@ -21,6 +21,7 @@
 #include "dsa_attn_core.hpp"
 #include "dsa_attn_mfma.hpp"
 #include "dsa_host.hpp"
+#include "dsa_score.hpp"
 #include "dsa_select.hpp"
 
 #include <mutex>
@@ -283,15 +284,17 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
 // Same split and output as attn_partial_kernel, for bf16 KV with 8 or 16 q
 // heads per KV head: each wave runs the MFMA tile of dsa_attn_mfma.hpp over
 // its tiles, and the 4 wave states meet in LDS.
+// The workgroup (split, h, b) as a device function, so that other kernels
+// can run these splits beside their own workgroups.
 template <int D, int G, bool FILTER, int TW>
-__global__ __launch_bounds__(256) void attn_partial_mfma_kernel(
+__device__ __forceinline__ void attn_partial_mfma_body(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ page_table, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ ids, const int32_t* __restrict__ counts, int ids_stride, int n_kv_heads, int P,
     int max_pages, int num_slots, unsigned long long streaming, int sink, int local, float scale, float c,
     int tiles_per_split, int n_splits, const int32_t* __restrict__ skip_ids,
-    const int32_t* __restrict__ skip_counts, SelectArgs, float* __restrict__ part_o,
-    float* __restrict__ part_ml) {
+    const int32_t* __restrict__ skip_counts, float* __restrict__ part_o, float* __restrict__ part_ml, int split,
+    int h, int b) {
   using M = MfmaWave<D, G>;
   constexpr int NK = M::NK, NB = M::NB;
   constexpr int OS = D + 4;   // LDS row stride of the merge buffer (floats)
@@ -299,7 +302,6 @@ __global__ __launch_bounds__(256) void attn_partial_mfma_kernel(
   __shared__ __align__(16) float lds_o[kWgWaves][G][OS];
   __shared__ float lds_ml[kWgWaves][G][2];
 
-  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   // the wave index is uniform: loop bounds and branches derived from it stay scalar
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int unit = b * n_kv_heads + h;
@@ -401,6 +403,21 @@ __global__ __launch_bounds__(256) void attn_partial_mfma_kernel(
   }
 }
 
+template <int D, int G, bool FILTER, int TW>
+__global__ __launch_bounds__(256) void attn_partial_mfma_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const int32_t* __restrict__ page_table, const int32_t* __restrict__ seq_lens,
+    const int32_t* __restrict__ ids, const int32_t* __restrict__ counts, int ids_stride, int n_kv_heads, int P,
+    int max_pages, int num_slots, unsigned long long streaming, int sink, int local, float scale, float c,
+    int tiles_per_split, int n_splits, const int32_t* __restrict__ skip_ids,
+    const int32_t* __restrict__ skip_counts, SelectArgs, float* __restrict__ part_o,
+    float* __restrict__ part_ml) {
+  attn_partial_mfma_body<D, G, FILTER, TW>(q, k, v, page_table, seq_lens, ids, counts, ids_stride, n_kv_heads, P,
+                                           max_pages, num_slots, streaming, sink, local, scale, c, tiles_per_split,
+                                           n_splits, skip_ids, skip_counts, part_o, part_ml, (int)blockIdx.x,
+                                           (int)blockIdx.y, (int)blockIdx.z);
+}
+
 // ============================================================ combine
 // One workgroup per (sequence, q head).  The active splits are merged with
 // the online-softmax rule in chunks of 64: every thread first issues the
@@ -412,17 +429,16 @@ __global__ __launch_bounds__(256) void attn_partial_mfma_kernel(
 // rows of up to 64 splits (every top-k and repair call here) exactly one.
 // For repair the caller's (O, l, m) is one more term.  Writes normalised O.
 template <int D>
-__global__ __launch_bounds__(256) void attn_combine_kernel(
+__device__ __forceinline__ void attn_combine_body(
     const float* __restrict__ part_o, const float* __restrict__ part_ml, const int32_t* __restrict__ counts,
     int ids_stride, int n_kv_heads, int G, int TPP, int tiles_per_split, int n_splits, int fold,
-    float* __restrict__ O, float* __restrict__ l, float* __restrict__ m) {
+    float* __restrict__ O, float* __restrict__ l, float* __restrict__ m, int hq, int b) {
   constexpr int SPT = 256 / D;   // split lanes per channel
   constexpr int CH = 64;         // splits per chunk
   constexpr int PER = CH / SPT;  // O values per thread and chunk
   __shared__ float s_w[CH];
   __shared__ float s_acc[SPT][D];
   __shared__ float s_alpha, s_M, s_L;
-  const int hq = blockIdx.x, b = blockIdx.y;
   const int Hq = n_kv_heads * G;
   const int h = hq / G, g = hq % G;
   const int unit = b * n_kv_heads + h;
@@ -500,6 +516,15 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(
       m[row] = Lf > 0.0f ? Mf : kNegInf;
     }
   }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void attn_combine_kernel(
+    const float* __restrict__ part_o, const float* __restrict__ part_ml, const int32_t* __restrict__ counts,
+    int ids_stride, int n_kv_heads, int G, int TPP, int tiles_per_split, int n_splits, int fold,
+    float* __restrict__ O, float* __restrict__ l, float* __restrict__ m) {
+  attn_combine_body<D>(part_o, part_ml, counts, ids_stride, n_kv_heads, G, TPP, tiles_per_split, n_splits, fold, O,
+                       l, m, (int)blockIdx.x, (int)blockIdx.y);
 }
 
 // ============================================================ PSA progressive
@@ -1107,6 +1132,70 @@ __global__ __launch_bounds__((psa_waves<T, G>() * 64)) void psa_fused_kernel(
                        never_stop, always_stop, ln_odds, scale, c, ids, counts, O, l, m);
 }
 
+// ============================================================ PRR step on one stream
+// A speculative PRR step ("Predict, Reuse, and Repair", sections 2-3) has
+// two pairs of independent parts: the page scores (with the EMA update) and
+// the speculative attention over P^t; later the speculative combine and the
+// repair's partials over M^t = A^t \ P^t.  Run on two streams, each
+// dependency between the HIP graph's hardware queues costs several µs here,
+// so each pair instead shares one launch: the first workgroups of the grid
+// run one part, the rest the other (both parts use 256-thread workgroups).
+struct PrrStepArgs {
+  const uint16_t *q, *kp, *vp, *meta;   // query, K and V pools, page metadata
+  const int32_t *page_table, *seq_lens;
+  int n_kv_heads, P, Pl, max_pages, num_slots, batch;
+  float scale, c;
+  // scores and EMA
+  float* scores;
+  EmaArgs ema;
+  int score_ppw, score_wgs;
+  // speculative attention over P^t (row stride k), its partials
+  const int32_t *p_ids, *p_counts;
+  int k, spec_tps, spec_splits;   // k: entries per id row
+  float *spec_o, *spec_ml;
+  // repair over M^t (row stride k), its partials
+  const int32_t *m_ids, *m_counts;
+  int rep_tps, rep_splits;
+  float *rep_o, *rep_ml;
+  float *O, *l, *m;
+};
+
+template <int D, int G, int GL>
+__global__ __launch_bounds__(256) void prr_score_spec_kernel(PrrStepArgs a) {
+  const int n_spec = a.spec_splits * a.n_kv_heads * a.batch;   // speculative splits first: the longer chains
+  const int x = blockIdx.x;
+  if (x < n_spec) {
+    const int split = x % a.spec_splits, h = (x / a.spec_splits) % a.n_kv_heads, b = x / (a.spec_splits * a.n_kv_heads);
+    attn_partial_mfma_body<D, G, false, kTilesPerWaveMfma>(
+        a.q, a.kp, a.vp, a.page_table, a.seq_lens, a.p_ids, a.p_counts, a.k, a.n_kv_heads, a.P,
+        a.max_pages, a.num_slots, 0ull, 0, 0, a.scale, a.c, a.spec_tps, a.spec_splits, nullptr, nullptr, a.spec_o,
+        a.spec_ml, split, h, b);
+  } else {
+    const int i = x - n_spec;
+    score_body<uint16_t, D, G, GL>(a.q, a.meta, a.page_table, a.seq_lens, a.n_kv_heads, a.P, a.Pl, a.max_pages,
+                                   a.num_slots, 0ull, a.score_ppw, a.score_wgs, a.scores, a.ema, i % a.score_wgs,
+                                   (i / a.score_wgs) % a.n_kv_heads, i / (a.score_wgs * a.n_kv_heads));
+  }
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(256) void prr_combine_repair_kernel(PrrStepArgs a) {
+  const int Hq = a.n_kv_heads * G;
+  const int n_comb = Hq * a.batch;
+  const int x = blockIdx.x;
+  if (x < n_comb) {   // the speculative result over P^t into (O, l, m)
+    attn_combine_body<D>(a.spec_o, a.spec_ml, a.p_counts, a.k, a.n_kv_heads, G, a.P / 16, a.spec_tps, a.spec_splits,
+                         0, a.O, a.l, a.m, x % Hq, x / Hq);
+  } else {            // the repair's partials over M^t
+    const int i = x - n_comb;
+    const int split = i % a.rep_splits, h = (i / a.rep_splits) % a.n_kv_heads, b = i / (a.rep_splits * a.n_kv_heads);
+    attn_partial_mfma_body<D, G, false, kTilesPerWaveRepair>(
+        a.q, a.kp, a.vp, a.page_table, a.seq_lens, a.m_ids, a.m_counts, a.k, a.n_kv_heads, a.P, a.max_pages,
+        a.num_slots, 0ull, 0, 0, a.scale, a.c, a.rep_tps, a.rep_splits, nullptr, nullptr, a.rep_o, a.rep_ml, split,
+        h, b);
+  }
+}
+
 // ============================================================ host planning
 static int cu_count() {
   static int cached[64] = {0};
@@ -1370,6 +1459,8 @@ extern "C" size_t dsa_workspace_bytes(int32_t op, const dsa_kv* kv, int32_t n_q_
   if (!pow2_group(G)) return 0;
   if (op == DSA_OP_SPARSE_DECODE_ATTN) return partial_bytes(kv, G, ids_stride, kMinTwAttn);
   if (op == DSA_OP_ATTN_REPAIR) return partial_bytes(kv, G, ids_stride, kMinTwRepair);
+  if (op == DSA_OP_PRR_DECODE_STEP)   // speculative partials, then the repair's
+    return partial_bytes(kv, G, ids_stride, kTilesPerWaveMfma) + partial_bytes(kv, G, ids_stride, kTilesPerWaveRepair);
   return 0;
 }
 
@@ -1520,6 +1611,119 @@ extern "C" int dsa_attn_repair(const void* q, int32_t n_q_heads, const dsa_kv* k
   // the plain split-KV path, folded; splits past the count exit at once
   return launch_attn(q, G, kv, a_ids, a_counts, ids_stride, 0, 0, 0, scale, O, l, m, ws, 1, p_ids, p_counts,
                      SelectArgs{}, (hipStream_t)stream);
+}
+
+// One PRR speculative step on one stream: scores + EMA beside the
+// speculative partials, the selection, the speculative combine beside the
+// repair's partials, the repair's fold.
+template <int D, int G, int GL>
+static int launch_prr_step(PrrStepArgs a, const dsa_kv* kv, float alpha, float beta, float gamma, int32_t* a_ids,
+                           int32_t* a_counts, int32_t* m_ids, int32_t* m_counts, int32_t* p_ids, int32_t* p_counts,
+                           void* ws, hipStream_t st) {
+  const size_t units = (size_t)kv->batch * kv->n_kv_heads;
+  const SplitPlan ps = plan_splits(kv, a.k, kTilesPerWaveMfma);
+  const SplitPlan pr = plan_splits(kv, a.k, kTilesPerWaveRepair);
+  const ScorePlan sp = score_plan<G>(kv, 0);
+  char* w = (char*)ws;
+  a.spec_o = (float*)w;
+  a.spec_ml = (float*)(w + align256(units * ps.n_splits * G * D * sizeof(float)));
+  w += partial_bytes(kv, G, a.k, kTilesPerWaveMfma);
+  a.rep_o = (float*)w;
+  a.rep_ml = (float*)(w + align256(units * pr.n_splits * G * D * sizeof(float)));
+  a.spec_tps = ps.tiles_per_split;
+  a.spec_splits = ps.n_splits;
+  a.rep_tps = pr.tiles_per_split;
+  a.rep_splits = pr.n_splits;
+  a.score_ppw = sp.ppw;
+  a.score_wgs = sp.wgs;
+  const long long n_spec = (long long)ps.n_splits * units, n_score = (long long)sp.wgs * units;
+  const long long n_comb = (long long)kv->n_kv_heads * G * kv->batch, n_rep = (long long)pr.n_splits * units;
+  if (n_spec + n_score > 0x7FFFFFFFLL || n_comb + n_rep > 0x7FFFFFFFLL) return DSA_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL((prr_score_spec_kernel<D, G, GL>), dim3((unsigned)(n_spec + n_score)), dim3(256), 0, st, a);
+  int rc = launch_status();
+  if (rc) return rc;
+  rc = dsa_prr_select(a.scores, kv->batch, kv->n_kv_heads, kv->max_pages, kv->seq_lens, kv->page_size, a.k, a_ids,
+                      a_counts, nullptr, nullptr, a.ema.pred, alpha, beta, gamma, 0, a.k, p_ids, p_counts, a.p_ids,
+                      a.p_counts, m_ids, m_counts, nullptr, 0, st);
+  if (rc) return rc;
+  a.m_ids = m_ids;
+  a.m_counts = m_counts;
+  hipLaunchKernelGGL((prr_combine_repair_kernel<D, G>), dim3((unsigned)(n_comb + n_rep)), dim3(256), 0, st, a);
+  if ((rc = launch_status())) return rc;
+  hipLaunchKernelGGL((attn_combine_kernel<D>), dim3(kv->n_kv_heads * G, kv->batch), dim3(256), 0, st, a.rep_o,
+                     a.rep_ml, m_counts, a.k, kv->n_kv_heads, G, kv->page_size / 16, pr.tiles_per_split, pr.n_splits,
+                     1, a.O, a.l, a.m);
+  return launch_status();
+}
+
+template <int D, int G>
+static int launch_prr_step_gl(const PrrStepArgs& a, const dsa_kv* kv, float alpha, float beta, float gamma,
+                              int32_t* a_ids, int32_t* a_counts, int32_t* m_ids, int32_t* m_counts, int32_t* p_ids,
+                              int32_t* p_counts, void* ws, hipStream_t st) {
+  switch (kv->page_size / a.Pl) {
+    case 1: return launch_prr_step<D, G, 1>(a, kv, alpha, beta, gamma, a_ids, a_counts, m_ids, m_counts, p_ids, p_counts, ws, st);
+    case 2: return launch_prr_step<D, G, 2>(a, kv, alpha, beta, gamma, a_ids, a_counts, m_ids, m_counts, p_ids, p_counts, ws, st);
+    case 4: return launch_prr_step<D, G, 4>(a, kv, alpha, beta, gamma, a_ids, a_counts, m_ids, m_counts, p_ids, p_counts, ws, st);
+  }
+  return DSA_ERR_UNSUPPORTED;
+}
+
+extern "C" int dsa_prr_decode_step(const void* q, int32_t n_q_heads, const dsa_kv* kv, const void* meta,
+                                   int32_t logical_page, float* scores, float* level, float* trend, float* pred,
+                                   float alpha, float beta, float gamma, int32_t k, const int32_t* p_cur_ids,
+                                   const int32_t* p_cur_counts, int32_t* a_ids, int32_t* a_counts, int32_t* m_ids,
+                                   int32_t* m_counts, int32_t* p_ids, int32_t* p_counts, float scale, float* O,
+                                   float* l, float* m, void* ws, size_t ws_bytes, void* stream) {
+  int G = 0;
+  int rc = check_attn_common(q, n_q_heads, kv, scale, &G);
+  if (rc) return rc;
+  if ((rc = check_logical(kv, logical_page))) return rc;
+  if (k < 1) return DSA_ERR_SHAPE;
+  if (kv->dtype != DSA_BF16 || (G != 8 && G != 16) || kv->max_pages > kPsaMaxPages) return DSA_ERR_UNSUPPORTED;
+  if (kv->batch == 0) return DSA_OK;
+  if (!meta || !scores || !level || !trend || !pred || !p_cur_ids || !p_cur_counts || !a_ids || !a_counts ||
+      !m_ids || !m_counts || !p_ids || !p_counts || !O || !l || !m)
+    return DSA_ERR_NULL;
+  if (pred == level || pred == trend || level == trend || scores == pred || scores == level || scores == trend)
+    return DSA_ERR_SHAPE;
+  if (p_cur_ids == p_ids || p_cur_counts == p_counts) return DSA_ERR_SHAPE;   // P^t is read while P^{t+1} is written
+  if (!aligned16(meta)) return DSA_ERR_ALIGN;
+  const size_t need = dsa_workspace_bytes(DSA_OP_PRR_DECODE_STEP, kv, n_q_heads, k);
+  if (!ws || ws_bytes < need) return DSA_ERR_WORKSPACE;
+  if (!aligned16(ws)) return DSA_ERR_ALIGN;
+  PrrStepArgs a{};
+  a.q = (const uint16_t*)q;
+  a.kp = (const uint16_t*)kv->k;
+  a.vp = (const uint16_t*)kv->v;
+  a.meta = (const uint16_t*)meta;
+  a.page_table = kv->page_table;
+  a.seq_lens = kv->seq_lens;
+  a.n_kv_heads = kv->n_kv_heads;
+  a.P = kv->page_size;
+  a.Pl = logical_page;
+  a.max_pages = kv->max_pages;
+  a.num_slots = kv->num_slots;
+  a.batch = kv->batch;
+  a.scale = scale;
+  a.c = scale * kLog2e;
+  a.scores = scores;
+  a.ema = EmaArgs{level, trend, pred, alpha, beta, gamma, 0};
+  a.p_ids = p_cur_ids;
+  a.p_counts = p_cur_counts;
+  a.k = k;
+  a.O = O;
+  a.l = l;
+  a.m = m;
+  hipStream_t st = (hipStream_t)stream;
+#define DSA_STEP(D_, G_) \
+  return launch_prr_step_gl<D_, G_>(a, kv, alpha, beta, gamma, a_ids, a_counts, m_ids, m_counts, p_ids, p_counts, ws, st)
+  if (kv->head_dim == 128) {
+    if (G == 16) DSA_STEP(128, 16);
+    DSA_STEP(128, 8);
+  }
+  if (G == 16) DSA_STEP(64, 16);
+  DSA_STEP(64, 8);
+#undef DSA_STEP
 }
 
 extern "C" int dsa_page_select_progressive(const void* q, int32_t n_q_heads, const dsa_kv* kv, const float* scores,

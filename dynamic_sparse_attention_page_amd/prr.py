@@ -1,6 +1,5 @@
 """PRR decode step orchestration: the exact selection and the predictor run
-on a side stream while the speculative attention runs on the caller's
-stream; the repair joins them.
+beside the speculative attention; the repair joins them.
 
 "Predict, Reuse, and Repair", sections 1-3: in a plain dynamic-sparse step
 the page selection must finish before attention starts.  PRR predicts the
@@ -26,9 +25,17 @@ profile indexed by context length (section 3.4): the largest delta whose
 speculative attention still fits in the selection window
 (profile_delta_table, DeltaTable).
 
-This module only sequences calls of the C ABI (through the binding) on two
-streams joined by events; every step of the arithmetic runs in the HIP
-library.  Stream priorities stay at the default.
+Where the library has it (bf16 KV, 8 or 16 q heads per KV head, |A| = |P|)
+a speculative step is one call, dsa_prr_decode_step, on the caller's stream:
+the independent parts share launches (scores beside the speculative
+partials, the speculative combine beside the repair's partials) instead of
+streams, because each dependency between the hardware queues of a HIP
+graph costs several microseconds on this GPU.  Otherwise the selection runs
+on a side stream joined by events.
+
+This module only sequences calls of the C ABI (through the binding); every
+step of the arithmetic runs in the HIP library.  Stream priorities stay at
+the default.
 """
 from __future__ import annotations
 
@@ -39,21 +46,26 @@ from dataclasses import dataclass, field
 import numpy as np
 import torch
 
-from . import (OP_ATTN_REPAIR, PagedKV, attn_repair, ema_predict_update, page_score, page_score_ema,
-               page_select_topk, prr_select, prr_select_workspace_bytes, sparse_decode_attn, workspace_bytes)
+from . import (OP_ATTN_REPAIR, OP_PRR_DECODE_STEP, PagedKV, attn_repair, ema_predict_update, page_score,
+               page_score_ema, page_select_topk, prr_decode_step, prr_select, prr_select_workspace_bytes,
+               sparse_decode_attn, workspace_bytes)
 
 
 class PRRDecoder:
     """Per-layer PRR state for one batch of sequences: EMA level/trend per
     (sequence, KV head, page), the speculative sets, and the buffers of one
-    step.  `step(q)` enqueues one decode step on the current stream (plus a
-    side stream for the selection and the predictor) and returns (O, l, m);
-    nothing is synchronised with the host.  After a step, `a_ids` holds A^t
-    and `p_ids` the prediction P^{t+1} for the next step."""
+    step.  `step(q)` enqueues one decode step on the current stream (in one
+    call where the library supports the shape, else with a side stream for
+    the selection and the predictor) and returns (O, l, m); nothing is
+    synchronised with the host.  After a step, `a_ids` holds A^t and
+    `p_ids` the prediction P^{t+1} for the next step.  one_stream=False
+    forces the two-stream form (one_stream=None: the one-call step where
+    supported)."""
 
     def __init__(self, kv: PagedKV, meta: torch.Tensor, n_q_heads: int, k: int, alpha: float, beta: float,
                  gamma: float, delta: float = 1.0, logical_page: int | None = None, scale: float | None = None,
-                 delta_table: "DeltaTable | None" = None, context_tokens: int | None = None):
+                 delta_table: "DeltaTable | None" = None, context_tokens: int | None = None,
+                 one_stream: bool | None = None):
         if delta_table is not None:   # section 3.4: delta by context length
             delta = delta_table.lookup(context_tokens or kv.max_pages * kv.page_size)
         self.kv, self.meta, self.k = kv, meta, k
@@ -83,6 +95,13 @@ class PRRDecoder:
         self.ws = torch.zeros(workspace_bytes(OP_ATTN_REPAIR, kv, n_q_heads, self.stride), dtype=torch.uint8,
                               device=dev)
         self.sel_ws = None                 # a split-row selection workspace (see split_selection)
+        G = n_q_heads // kv.n_kv_heads
+        can = self.k == self.k_spec and kv.k.dtype == torch.bfloat16 and G in (8, 16) and N <= 65536
+        if one_stream and not can:
+            raise ValueError("the one-call PRR step needs bf16 KV, 8 or 16 q heads per KV head and |A| = |P|")
+        self.one_stream = can if one_stream is None else bool(one_stream)
+        self.step_ws = (torch.zeros(workspace_bytes(OP_PRR_DECODE_STEP, kv, n_q_heads, self.k), dtype=torch.uint8,
+                                    device=dev) if self.one_stream else None)
         self.side = torch.cuda.Stream(device=dev)      # default priority
         self._p_ready = None               # event: P^t written (side stream of the previous step)
         self.t = 0
@@ -93,6 +112,8 @@ class PRRDecoder:
         B, H, N = self.scores.shape
         nb = prr_select_workspace_bytes(B, H, N) if on else 0
         self.sel_ws = torch.empty(nb, dtype=torch.uint8, device=self.scores.device) if nb else None
+        if self.sel_ws is not None:
+            self.one_stream = False        # the one-call step takes no selection workspace
 
     def join(self):
         """Make the current stream wait for the side stream's last work (the
@@ -160,7 +181,14 @@ class PRRDecoder:
         out = (self.O, self.l, self.m)
         main = torch.cuda.current_stream()
         cur, nxt = self._cur, 1 - self._cur
-        if self.t == 0:
+        if self.t > 0 and self.one_stream:
+            # the whole speculative step in one call on this stream
+            self.join()
+            prr_decode_step(q, self.kv, self.meta, self.scores, self.level, self.trend, self.pred, self.alpha,
+                            self.beta, self.gamma, self.k, self._p[cur], (self.a_ids, self.a_counts),
+                            (self.m_ids, self.m_counts), self._p[nxt], *out, logical_page=self.lp, scale=self.scale,
+                            ws=self.step_ws)
+        elif self.t == 0:
             # no prediction yet: a plain selection-then-attention step
             self._select_and_predict(q, init=True, buf=nxt)
             sparse_decode_attn(q, self.kv, self.a_ids, self.a_counts, scale=self.scale, out=out, ws=self.ws)

@@ -114,7 +114,7 @@ typedef struct dsa_stream_cfg {
 } dsa_stream_cfg;
 
 /* Operation ids for dsa_workspace_bytes(). */
-enum { DSA_OP_SPARSE_DECODE_ATTN = 1, DSA_OP_ATTN_REPAIR = 2 };
+enum { DSA_OP_SPARSE_DECODE_ATTN = 1, DSA_OP_ATTN_REPAIR = 2, DSA_OP_PRR_DECODE_STEP = 3 };
 
 /* Human-readable name of a status code (static storage). */
 const char *dsa_status_str(int status);
@@ -363,6 +363,45 @@ int dsa_attn_repair(const void *q, int32_t n_q_heads, const dsa_kv *kv, const in
                     size_t ws_bytes, void *stream);
 
 /*
+ * dsa_prr_decode_step -- one speculative PRR decode step on one stream
+ * ([PRR] sections 2-3: the speculative attention over the predicted set
+ * runs while the page scores are computed and the exact set selected; the
+ * repair then folds in the pages the prediction missed; section 3.1: the
+ * EMA update and the next prediction).
+ *
+ * Results are those of, in order:
+ *   dsa_page_score_ema(q, n_q_heads, kv, meta, logical_page, NULL, scores,
+ *                      level, trend, pred, alpha, beta, gamma, 0)
+ *   dsa_sparse_decode_attn(q, n_q_heads, kv, p_cur_ids, p_cur_counts, k, NULL,
+ *                          scale, O, l, m)
+ *   dsa_prr_select(scores, ..., k, a_ids, a_counts, NULL, NULL, pred, alpha,
+ *                  beta, gamma, 0, k, p_ids, p_counts, p_cur_ids, p_cur_counts,
+ *                  m_ids, m_counts, NULL, 0)
+ *   dsa_attn_repair(q, n_q_heads, kv, m_ids, m_counts, NULL, NULL, k, scale,
+ *                   O, l, m)
+ * i.e. IS^t into scores, level/trend/pred updated with it, O/l/m = attention
+ * over P^t union A^t, a_ids = A^t, m_ids = M^t = A^t \ P^t and p_ids =
+ * P^{t+1} (|A| = |P| = k; every id row has stride k, ascending, -1 padded).
+ * Independent parts share launches instead of streams (the scores with the
+ * speculative partials, the speculative combine with the repair's
+ * partials): 4 launches on the given stream, nothing for a caller to join.
+ * P^t = p_cur_ids/p_cur_counts must not be p_ids/p_counts; level, trend,
+ * pred and scores distinct (DSA_ERR_SHAPE); every pointer non-NULL
+ * (DSA_ERR_NULL); meta 16-byte aligned.  Requires bf16 KV with 8 or 16 q
+ * heads per KV head (the matrix-core attention), no streaming heads and
+ * max_pages <= 65536, else DSA_ERR_UNSUPPORTED (use the separate calls).
+ * ws: device scratch of dsa_workspace_bytes(DSA_OP_PRR_DECODE_STEP, kv,
+ * n_q_heads, k) bytes, 16-byte aligned.
+ */
+int dsa_prr_decode_step(const void *q, int32_t n_q_heads, const dsa_kv *kv, const void *meta,
+                        int32_t logical_page, float *scores, float *level, float *trend,
+                        float *pred, float alpha, float beta, float gamma, int32_t k,
+                        const int32_t *p_cur_ids, const int32_t *p_cur_counts, int32_t *a_ids,
+                        int32_t *a_counts, int32_t *m_ids, int32_t *m_counts, int32_t *p_ids,
+                        int32_t *p_counts, float scale, float *O, float *l, float *m, void *ws,
+                        size_t ws_bytes, void *stream);
+
+/*
  * dsa_ema_predict_update -- PRR EMA predictor ([PRR] section 3.1).
  *
  * Elementwise over n blocks (float, device):
@@ -502,8 +541,9 @@ size_t dsa_prr_calibrate_workspace_bytes(int32_t steps, int32_t units, int32_t n
 
 /*
  * dsa_workspace_bytes -- scratch needed by dsa_sparse_decode_attn (op
- * DSA_OP_SPARSE_DECODE_ATTN) or dsa_attn_repair (DSA_OP_ATTN_REPAIR) for
- * this pool, n_q_heads and ids_stride.  Returns 0 for invalid arguments.
+ * DSA_OP_SPARSE_DECODE_ATTN), dsa_attn_repair (DSA_OP_ATTN_REPAIR) or
+ * dsa_prr_decode_step (DSA_OP_PRR_DECODE_STEP, ids_stride = k) for this
+ * pool, n_q_heads and ids_stride.  Returns 0 for invalid arguments.
  */
 size_t dsa_workspace_bytes(int32_t op, const dsa_kv *kv, int32_t n_q_heads, int32_t ids_stride);
 

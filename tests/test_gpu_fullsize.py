@@ -195,7 +195,8 @@ def test_psa_mha_64k_full(gpu_lib):
 
 
 def test_prr_512k_full(gpu_lib):
-    """The 64-step PRR trace through the two-stream decoder, against the
+    """The 64-step PRR trace through the decoder (its speculative steps in one
+    dsa_prr_decode_step call at this shape), against the
     oracle's own run of the same trace (its scores, its top-k A^t, an fp64
     EMA fed its scores, its speculative sets P^{t+1}): per step the scores,
     A^t and P^{t+1} under the boundary rule, the predictions, and (sampled

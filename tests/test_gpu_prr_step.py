@@ -1,0 +1,67 @@
+"""The one-call PRR speculative step (dsa_prr_decode_step: the independent
+parts of the step share launches on one stream) against the two-stream
+decoder that chains the separate calls ("Predict, Reuse, and Repair",
+sections 2-3): same scores, EMA state, A^t, M^t, P^{t+1} and (O, l, m), bit
+for bit, step after step on a drifting query.  The separate calls are
+themselves checked against the oracle (test_gpu_parity, test_gpu_prr_select,
+and the full PRR trace in test_gpu_fullsize, which runs this one-call step)."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from parity_util import np_, to_device
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # (G, page_size, logical_page, seq_lens, k)
+    (16, 16, 16, [16 * 3000 + 5, 16 * 1200], 256),
+    (8, 16, 16, [16 * 5000 + 11], 512),
+    (16, 64, 16, [64 * 700 + 40, 64 * 300], 64),
+    (8, 32, 16, [32 * 90 + 7, 32 * 2], 200),   # k above a row's pages
+]
+
+
+def _same(x: torch.Tensor, y: torch.Tensor) -> bool:
+    """Bit for bit (NaNs of pages past a sequence's end included)."""
+    if x.dtype == torch.float32:
+        return torch.equal(x.view(torch.int32), y.view(torch.int32))
+    return torch.equal(x, y)
+
+
+def _drift(q: torch.Tensor, t: int, seed: int) -> torch.Tensor:
+    g = torch.Generator(device="cpu").manual_seed(seed + t)
+    xi = torch.randn(q.shape, generator=g).to(q.device)
+    th = 0.05 + 0.05 * t
+    return (q.float() * np.cos(th) + xi * np.sin(th)).to(q.dtype)
+
+
+@pytest.mark.parametrize("G,P,Pl,lens,k", CASES)
+def test_one_call_step_equals_two_streams(gpu_lib, G, P, Pl, lens, k):
+    dsa = gpu_lib
+    from dynamic_sparse_attention_page_amd.prr import PRRDecoder
+    print(f"[case] prr one-call step G={G} P={P} Pl={Pl} lens={lens} k={k}", flush=True)
+    bt = wl.random_batch(401 + G + P, lens, n_q_heads=2 * G, n_kv_heads=2, head_dim=128, page_size=P,
+                         logical_page=Pl)
+    q0, kv, _ = to_device(dsa, bt)
+    meta = dsa.page_meta_build(kv, Pl)
+    decs = [PRRDecoder(kv, meta, 2 * G, k, 0.6, 0.3, 0.25, 1.0, logical_page=Pl, one_stream=one)
+            for one in (True, False)]
+    assert decs[0].one_stream and not decs[1].one_stream
+    q = q0
+    for t in range(6):
+        outs = [d.step(q) for d in decs]
+        for d in decs:
+            d.join()
+        torch.cuda.synchronize()
+        a, b = decs
+        for name in ("scores", "level", "trend", "pred", "a_ids", "a_counts", "m_ids", "m_counts"):
+            assert _same(getattr(a, name), getattr(b, name)), f"step {t}: {name}"
+        assert _same(a.p_ids, b.p_ids) and _same(a.p_counts, b.p_counts), f"step {t}: P^(t+1)"
+        for x, y, nm in zip(outs[0], outs[1], "Olm"):
+            assert _same(x, y), f"step {t}: {nm} differs by {np.nanmax(np.abs(np_(x) - np_(y)))}"
+        if t > 0:   # the speculative steps: M^t is A^t minus P^t
+            mc = np_(a.m_counts)
+            assert (mc <= np_(a.a_counts)).all()
+        q = _drift(q0, t, 7)
