@@ -22,9 +22,10 @@ the same run the same way.
       batch 1, 32 q / 8 KV heads, d=128, 32768 tokens in 16-token pages, top-256, bf16
   lserve_hier_128k         the same calls with 64/16 hierarchical paging and
       4 of 8 KV heads streaming (sink 128 + local 256); batch 4, 131072 tokens, top-64
-  prr_512k                 PRR: score and one launch selecting A and (after the EMA
-      update) the next speculative set, overlapped with the speculative attention;
-      then the repair;
+  prr_512k                 PRR speculative step in one call (dsa_prr_decode_step): the scores
+      (with the EMA update) beside the speculative attention over P in one launch, the
+      selection of A, M = A \\ P and the next P, then the speculative combine beside the
+      repair's partials, then the repair's fold;
       batch 1, 32 q / 2 KV heads, 524288 tokens, top-2048, 64-step query trace
   tiny_f32                 score, top-8, attention and PSA on one fp32 head
   lserve_prefill_16k       LServe block-sparse prefill of one 16K-token prompt
@@ -545,6 +546,12 @@ def main():
                                                          False, decs[r].k_spec, decs[r].a_ids, decs[r].a_counts,
                                                          decs[r].p_ids, decs[r].p_counts, ws=sel_ws),
         }
+        if decs[0].one_stream:
+            # the whole speculative step as the decoder runs it: one call, four launches
+            ops["prr_decode_step"] = lambda r: dsa.prr_decode_step(
+                q, kvs[r], meta, decs[r].scores, decs[r].level, decs[r].trend, decs[r].pred, a_, b_, g_, bt.topk,
+                decs[r]._p[0], (decs[r].a_ids, decs[r].a_counts), (decs[r].m_ids, decs[r].m_counts), decs[r]._p[1],
+                O, l, m, scale=scale, ws=decs[r].step_ws)
         op_bytes = {"page_score": mb, "sparse_decode_attn": kvb, "ema_predict_update": B * Hkv * N * 24,
                     "attn_repair": int(miss_rate * kvb)}
         # online calibration of (alpha, beta, gamma) over the 80-candidate grid
