@@ -298,9 +298,14 @@ __device__ __forceinline__ void attn_partial_mfma_body(
   using M = MfmaWave<D, G>;
   constexpr int NK = M::NK, NB = M::NB;
   constexpr int OS = D + 4;   // LDS row stride of the merge buffer (floats)
-  __shared__ __align__(16) uint16_t lds_v[kWgWaves][M::LDS_ELEMS];
-  __shared__ __align__(16) float lds_o[kWgWaves][G][OS];
+  // a wave's V staging (during its tiles) and its merge rows (after them)
+  // share one LDS region: the wave writes its rows only once its own tiles
+  // are done, and the merge reads them after the barrier
+  constexpr int kVFloats = (M::LDS_ELEMS + 1) / 2, kOFloats = G * OS;
+  constexpr int kWaveFloats = kVFloats > kOFloats ? kVFloats : kOFloats;
+  __shared__ __align__(16) float lds_wave[kWgWaves][kWaveFloats];
   __shared__ float lds_ml[kWgWaves][G][2];
+  auto lds_o = [&](int w, int hh) { return &lds_wave[w][hh * OS]; };
 
   // the wave index is uniform: loop bounds and branches derived from it stay scalar
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -339,7 +344,7 @@ __device__ __forceinline__ void attn_partial_mfma_body(
   }
 
   M st;
-  st.init(q + ((size_t)b * n_kv_heads * G + (size_t)h * G) * D, lds_v[wave]);
+  st.init(q + ((size_t)b * n_kv_heads * G + (size_t)h * G) * D, reinterpret_cast<uint16_t*>(lds_wave[wave]));
 
   const int n_entries = (t_end - 1) / TPP - first_entry + 1;
   int my_page = -1, my_slot = -1;
@@ -377,7 +382,7 @@ __device__ __forceinline__ void attn_partial_mfma_body(
   if (st.h < G) {
 #pragma unroll
     for (int n = 0; n < NB; ++n)
-      *reinterpret_cast<float4*>(&lds_o[wave][st.h][16 * n + 4 * st.g]) =
+      *reinterpret_cast<float4*>(lds_o(wave, st.h) + 16 * n + 4 * st.g) =
           make_float4(st.acc[n][0], st.acc[n][1], st.acc[n][2], st.acc[n][3]);
     if (st.g == 0) { lds_ml[wave][st.h][0] = st.m; lds_ml[wave][st.h][1] = lsum; }
   }
@@ -392,7 +397,7 @@ __device__ __forceinline__ void attn_partial_mfma_body(
 #pragma unroll
     for (int w = 0; w < kWgWaves; ++w) {
       const float wt = exp2_diff(lds_ml[w][hh][0], mm, c);
-      acc = fmaf(lds_o[w][hh][cc], wt, acc);
+      acc = fmaf(lds_o(w, hh)[cc], wt, acc);
       ls = fmaf(lds_ml[w][hh][1], wt, ls);
     }
     part_o[(pbase + hh) * D + cc] = acc;
