@@ -15,11 +15,12 @@ from parity_util import np_, to_device
 pytestmark = pytest.mark.gpu
 
 CASES = [
-    # (G, page_size, logical_page, seq_lens, k)
-    (16, 16, 16, [16 * 3000 + 5, 16 * 1200], 256),
-    (8, 16, 16, [16 * 5000 + 11], 512),
-    (16, 64, 16, [64 * 700 + 40, 64 * 300], 64),
-    (8, 32, 16, [32 * 90 + 7, 32 * 2], 200),   # k above a row's pages
+    # (G, page_size, logical_page, seq_lens, k, head_dim)
+    (16, 16, 16, [16 * 3000 + 5, 16 * 1200], 256, 128),
+    (8, 16, 16, [16 * 5000 + 11], 512, 128),
+    (16, 64, 16, [64 * 700 + 40, 64 * 300], 64, 128),
+    (8, 32, 16, [32 * 90 + 7, 32 * 2], 200, 128),   # k above a row's pages
+    (16, 16, 16, [16 * 900 + 1, 16 * 2500, 16 * 40 + 9], 128, 64),
 ]
 
 
@@ -37,12 +38,12 @@ def _drift(q: torch.Tensor, t: int, seed: int) -> torch.Tensor:
     return (q.float() * np.cos(th) + xi * np.sin(th)).to(q.dtype)
 
 
-@pytest.mark.parametrize("G,P,Pl,lens,k", CASES)
-def test_one_call_step_equals_two_streams(gpu_lib, G, P, Pl, lens, k):
+@pytest.mark.parametrize("G,P,Pl,lens,k,D", CASES)
+def test_one_call_step_equals_two_streams(gpu_lib, G, P, Pl, lens, k, D):
     dsa = gpu_lib
     from dynamic_sparse_attention_page_amd.prr import PRRDecoder
-    print(f"[case] prr one-call step G={G} P={P} Pl={Pl} lens={lens} k={k}", flush=True)
-    bt = wl.random_batch(401 + G + P, lens, n_q_heads=2 * G, n_kv_heads=2, head_dim=128, page_size=P,
+    print(f"[case] prr one-call step G={G} P={P} Pl={Pl} lens={lens} k={k} D={D}", flush=True)
+    bt = wl.random_batch(401 + G + P, lens, n_q_heads=2 * G, n_kv_heads=2, head_dim=D, page_size=P,
                          logical_page=Pl)
     q0, kv, _ = to_device(dsa, bt)
     meta = dsa.page_meta_build(kv, Pl)
