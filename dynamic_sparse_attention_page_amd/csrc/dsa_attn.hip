@@ -61,15 +61,17 @@ struct SelectArgs {
 };
 
 // ============================================================ split-KV partial
+// The workgroup (split, h, b) as a device function (kernels that run these
+// splits beside other work call it too).
 template <typename T, int D, int G, bool FILTER, int SEL_E, int TW>
-__global__ __launch_bounds__(256) void attn_partial_kernel(
+__device__ __forceinline__ void attn_partial_body(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const int32_t* __restrict__ page_table, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ ids, const int32_t* __restrict__ counts, int ids_stride, int n_kv_heads, int P,
     int max_pages, int num_slots, unsigned long long streaming, int sink, int local, float scale, float c,
     int tiles_per_split, int n_splits, const int32_t* __restrict__ skip_ids,
-    const int32_t* __restrict__ skip_counts, SelectArgs sel, float* __restrict__ part_o,
-    float* __restrict__ part_ml) {
+    const int32_t* __restrict__ skip_counts, const SelectArgs& sel, float* __restrict__ part_o,
+    float* __restrict__ part_ml, int split, int h, int b) {
   using A = AttnWave<T, D, G>;
   constexpr int CPL = A::CPL, DW = A::DW;
   __shared__ __align__(16) float lds_rows[kWgWaves][A::LDS_FLOATS];
@@ -81,7 +83,6 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
   __shared__ __align__(16) float lds_o[NWS][G][D];
   __shared__ float lds_ml[NWS][G][2];
 
-  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   // the wave index is uniform: loop bounds and branches derived from it stay scalar
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int unit = b * n_kv_heads + h;
@@ -278,6 +279,21 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
       }
     }
   }
+}
+
+template <typename T, int D, int G, bool FILTER, int SEL_E, int TW>
+__global__ __launch_bounds__(256) void attn_partial_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const int32_t* __restrict__ page_table, const int32_t* __restrict__ seq_lens,
+    const int32_t* __restrict__ ids, const int32_t* __restrict__ counts, int ids_stride, int n_kv_heads, int P,
+    int max_pages, int num_slots, unsigned long long streaming, int sink, int local, float scale, float c,
+    int tiles_per_split, int n_splits, const int32_t* __restrict__ skip_ids,
+    const int32_t* __restrict__ skip_counts, SelectArgs sel, float* __restrict__ part_o,
+    float* __restrict__ part_ml) {
+  attn_partial_body<T, D, G, FILTER, SEL_E, TW>(q, k, v, page_table, seq_lens, ids, counts, ids_stride, n_kv_heads,
+                                                P, max_pages, num_slots, streaming, sink, local, scale, c,
+                                                tiles_per_split, n_splits, skip_ids, skip_counts, sel, part_o,
+                                                part_ml, (int)blockIdx.x, (int)blockIdx.y, (int)blockIdx.z);
 }
 
 // ============================================================ split-KV partial, matrix cores
@@ -1146,7 +1162,7 @@ __global__ __launch_bounds__((psa_waves<T, G>() * 64)) void psa_fused_kernel(
 // so each pair instead shares one launch: the first workgroups of the grid
 // run one part, the rest the other (both parts use 256-thread workgroups).
 struct PrrStepArgs {
-  const uint16_t *q, *kp, *vp, *meta;   // query, K and V pools, page metadata
+  const void *q, *kp, *vp, *meta;   // query, K and V pools, page metadata (bf16 or fp32)
   const int32_t *page_table, *seq_lens;
   int n_kv_heads, P, Pl, max_pages, num_slots, batch;
   float scale, c;
@@ -1165,25 +1181,40 @@ struct PrrStepArgs {
   float *O, *l, *m;
 };
 
-template <int D, int G, int GL>
+// The partials of one split: the matrix-core body for bf16 with 8 or 16 q
+// heads per KV head, else the VALU body (TW tiles per wave either way).
+template <typename T, int D, int G, int TW>
+__device__ __forceinline__ void prr_partial(const PrrStepArgs& a, const int32_t* ids, const int32_t* counts, int tps,
+                                            int n_splits, float* po, float* pm, int split, int h, int b) {
+  if constexpr (sizeof(T) == 2 && G >= 8) {
+    attn_partial_mfma_body<D, G, false, TW>((const uint16_t*)a.q, (const uint16_t*)a.kp, (const uint16_t*)a.vp,
+                                            a.page_table, a.seq_lens, ids, counts, a.k, a.n_kv_heads, a.P,
+                                            a.max_pages, a.num_slots, 0ull, 0, 0, a.scale, a.c, tps, n_splits,
+                                            nullptr, nullptr, po, pm, split, h, b);
+  } else {
+    attn_partial_body<T, D, G, false, 0, TW>((const T*)a.q, (const T*)a.kp, (const T*)a.vp, a.page_table,
+                                             a.seq_lens, ids, counts, a.k, a.n_kv_heads, a.P, a.max_pages,
+                                             a.num_slots, 0ull, 0, 0, a.scale, a.c, tps, n_splits, nullptr, nullptr,
+                                             SelectArgs{}, po, pm, split, h, b);
+  }
+}
+
+template <typename T, int D, int G, int GL, int SPEC_TW>
 __global__ __launch_bounds__(256) void prr_score_spec_kernel(PrrStepArgs a) {
   const int n_spec = a.spec_splits * a.n_kv_heads * a.batch;   // speculative splits first: the longer chains
   const int x = blockIdx.x;
   if (x < n_spec) {
     const int split = x % a.spec_splits, h = (x / a.spec_splits) % a.n_kv_heads, b = x / (a.spec_splits * a.n_kv_heads);
-    attn_partial_mfma_body<D, G, false, kTilesPerWaveMfma>(
-        a.q, a.kp, a.vp, a.page_table, a.seq_lens, a.p_ids, a.p_counts, a.k, a.n_kv_heads, a.P,
-        a.max_pages, a.num_slots, 0ull, 0, 0, a.scale, a.c, a.spec_tps, a.spec_splits, nullptr, nullptr, a.spec_o,
-        a.spec_ml, split, h, b);
+    prr_partial<T, D, G, SPEC_TW>(a, a.p_ids, a.p_counts, a.spec_tps, a.spec_splits, a.spec_o, a.spec_ml, split, h, b);
   } else {
     const int i = x - n_spec;
-    score_body<uint16_t, D, G, GL>(a.q, a.meta, a.page_table, a.seq_lens, a.n_kv_heads, a.P, a.Pl, a.max_pages,
-                                   a.num_slots, 0ull, a.score_ppw, a.score_wgs, a.scores, a.ema, i % a.score_wgs,
-                                   (i / a.score_wgs) % a.n_kv_heads, i / (a.score_wgs * a.n_kv_heads));
+    score_body<T, D, G, GL>((const T*)a.q, (const T*)a.meta, a.page_table, a.seq_lens, a.n_kv_heads, a.P, a.Pl,
+                            a.max_pages, a.num_slots, 0ull, a.score_ppw, a.score_wgs, a.scores, a.ema, i % a.score_wgs,
+                            (i / a.score_wgs) % a.n_kv_heads, i / (a.score_wgs * a.n_kv_heads));
   }
 }
 
-template <int D, int G>
+template <typename T, int D, int G>
 __global__ __launch_bounds__(256) void prr_combine_repair_kernel(PrrStepArgs a) {
   const int Hq = a.n_kv_heads * G;
   const int n_comb = Hq * a.batch;
@@ -1194,10 +1225,8 @@ __global__ __launch_bounds__(256) void prr_combine_repair_kernel(PrrStepArgs a) 
   } else {            // the repair's partials over M^t
     const int i = x - n_comb;
     const int split = i % a.rep_splits, h = (i / a.rep_splits) % a.n_kv_heads, b = i / (a.rep_splits * a.n_kv_heads);
-    attn_partial_mfma_body<D, G, false, kTilesPerWaveRepair>(
-        a.q, a.kp, a.vp, a.page_table, a.seq_lens, a.m_ids, a.m_counts, a.k, a.n_kv_heads, a.P, a.max_pages,
-        a.num_slots, 0ull, 0, 0, a.scale, a.c, a.rep_tps, a.rep_splits, nullptr, nullptr, a.rep_o, a.rep_ml, split,
-        h, b);
+    prr_partial<T, D, G, kTilesPerWaveRepair>(a, a.m_ids, a.m_counts, a.rep_tps, a.rep_splits, a.rep_o, a.rep_ml,
+                                              split, h, b);
   }
 }
 
@@ -1465,7 +1494,7 @@ extern "C" size_t dsa_workspace_bytes(int32_t op, const dsa_kv* kv, int32_t n_q_
   if (op == DSA_OP_SPARSE_DECODE_ATTN) return partial_bytes(kv, G, ids_stride, kMinTwAttn);
   if (op == DSA_OP_ATTN_REPAIR) return partial_bytes(kv, G, ids_stride, kMinTwRepair);
   if (op == DSA_OP_PRR_DECODE_STEP)   // speculative partials, then the repair's
-    return partial_bytes(kv, G, ids_stride, kTilesPerWaveMfma) + partial_bytes(kv, G, ids_stride, kTilesPerWaveRepair);
+    return partial_bytes(kv, G, ids_stride, kMinTwAttn) + partial_bytes(kv, G, ids_stride, kTilesPerWaveRepair);
   return 0;
 }
 
@@ -1620,19 +1649,27 @@ extern "C" int dsa_attn_repair(const void* q, int32_t n_q_heads, const dsa_kv* k
 
 // One PRR speculative step on one stream: scores + EMA beside the
 // speculative partials, the selection, the speculative combine beside the
-// repair's partials, the repair's fold.
-template <int D, int G, int GL>
+// repair's partials, the repair's fold.  The speculative split is the one
+// dsa_sparse_decode_attn would take for these rows, so the results are
+// those of the separate calls bit for bit.
+template <typename T, int D, int G, int GL>
 static int launch_prr_step(PrrStepArgs a, const dsa_kv* kv, float alpha, float beta, float gamma, int32_t* a_ids,
                            int32_t* a_counts, int32_t* m_ids, int32_t* m_counts, int32_t* p_ids, int32_t* p_counts,
                            void* ws, hipStream_t st) {
+  constexpr bool kMfma = sizeof(T) == 2 && G >= 8;
   const size_t units = (size_t)kv->batch * kv->n_kv_heads;
-  const SplitPlan ps = plan_splits(kv, a.k, kTilesPerWaveMfma);
+  int tw = kMfma ? kTilesPerWaveMfma : kTilesPerWave;
+  if (!kMfma) {
+    const long long tiles = (long long)units * a.k * (kv->page_size / 16);
+    if ((tiles + kWgWaves * tw - 1) / (kWgWaves * tw) > cu_count()) tw = kTilesPerWaveWide;
+  }
+  const SplitPlan ps = plan_splits(kv, a.k, tw);
   const SplitPlan pr = plan_splits(kv, a.k, kTilesPerWaveRepair);
   const ScorePlan sp = score_plan<G>(kv, 0);
   char* w = (char*)ws;
   a.spec_o = (float*)w;
   a.spec_ml = (float*)(w + align256(units * ps.n_splits * G * D * sizeof(float)));
-  w += partial_bytes(kv, G, a.k, kTilesPerWaveMfma);
+  w += partial_bytes(kv, G, a.k, kMinTwAttn);
   a.rep_o = (float*)w;
   a.rep_ml = (float*)(w + align256(units * pr.n_splits * G * D * sizeof(float)));
   a.spec_tps = ps.tiles_per_split;
@@ -1644,7 +1681,14 @@ static int launch_prr_step(PrrStepArgs a, const dsa_kv* kv, float alpha, float b
   const long long n_spec = (long long)ps.n_splits * units, n_score = (long long)sp.wgs * units;
   const long long n_comb = (long long)kv->n_kv_heads * G * kv->batch, n_rep = (long long)pr.n_splits * units;
   if (n_spec + n_score > 0x7FFFFFFFLL || n_comb + n_rep > 0x7FFFFFFFLL) return DSA_ERR_UNSUPPORTED;
-  hipLaunchKernelGGL((prr_score_spec_kernel<D, G, GL>), dim3((unsigned)(n_spec + n_score)), dim3(256), 0, st, a);
+  const dim3 g1((unsigned)(n_spec + n_score));
+  if constexpr (kMfma) {
+    hipLaunchKernelGGL((prr_score_spec_kernel<T, D, G, GL, kTilesPerWaveMfma>), g1, dim3(256), 0, st, a);
+  } else if (tw == kTilesPerWaveWide && kTilesPerWaveWide != kTilesPerWave) {
+    hipLaunchKernelGGL((prr_score_spec_kernel<T, D, G, GL, kTilesPerWaveWide>), g1, dim3(256), 0, st, a);
+  } else {
+    hipLaunchKernelGGL((prr_score_spec_kernel<T, D, G, GL, kTilesPerWave>), g1, dim3(256), 0, st, a);
+  }
   int rc = launch_status();
   if (rc) return rc;
   rc = dsa_prr_select(a.scores, kv->batch, kv->n_kv_heads, kv->max_pages, kv->seq_lens, kv->page_size, a.k, a_ids,
@@ -1653,7 +1697,7 @@ static int launch_prr_step(PrrStepArgs a, const dsa_kv* kv, float alpha, float b
   if (rc) return rc;
   a.m_ids = m_ids;
   a.m_counts = m_counts;
-  hipLaunchKernelGGL((prr_combine_repair_kernel<D, G>), dim3((unsigned)(n_comb + n_rep)), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((prr_combine_repair_kernel<T, D, G>), dim3((unsigned)(n_comb + n_rep)), dim3(256), 0, st, a);
   if ((rc = launch_status())) return rc;
   hipLaunchKernelGGL((attn_combine_kernel<D>), dim3(kv->n_kv_heads * G, kv->batch), dim3(256), 0, st, a.rep_o,
                      a.rep_ml, m_counts, a.k, kv->n_kv_heads, G, kv->page_size / 16, pr.tiles_per_split, pr.n_splits,
@@ -1661,14 +1705,26 @@ static int launch_prr_step(PrrStepArgs a, const dsa_kv* kv, float alpha, float b
   return launch_status();
 }
 
-template <int D, int G>
+// (logical page = physical page only: PRR's pages carry one score each)
+template <typename T, int D, int G>
 static int launch_prr_step_gl(const PrrStepArgs& a, const dsa_kv* kv, float alpha, float beta, float gamma,
                               int32_t* a_ids, int32_t* a_counts, int32_t* m_ids, int32_t* m_counts, int32_t* p_ids,
                               int32_t* p_counts, void* ws, hipStream_t st) {
-  switch (kv->page_size / a.Pl) {
-    case 1: return launch_prr_step<D, G, 1>(a, kv, alpha, beta, gamma, a_ids, a_counts, m_ids, m_counts, p_ids, p_counts, ws, st);
-    case 2: return launch_prr_step<D, G, 2>(a, kv, alpha, beta, gamma, a_ids, a_counts, m_ids, m_counts, p_ids, p_counts, ws, st);
-    case 4: return launch_prr_step<D, G, 4>(a, kv, alpha, beta, gamma, a_ids, a_counts, m_ids, m_counts, p_ids, p_counts, ws, st);
+  if (kv->page_size != a.Pl) return DSA_ERR_UNSUPPORTED;
+  return launch_prr_step<T, D, G, 1>(a, kv, alpha, beta, gamma, a_ids, a_counts, m_ids, m_counts, p_ids, p_counts, ws,
+                                     st);
+}
+
+template <typename T, int D>
+static int launch_prr_step_d(int G, const PrrStepArgs& a, const dsa_kv* kv, float alpha, float beta, float gamma,
+                             int32_t* a_ids, int32_t* a_counts, int32_t* m_ids, int32_t* m_counts, int32_t* p_ids,
+                             int32_t* p_counts, void* ws, hipStream_t st) {
+  switch (G) {
+    case 1: return launch_prr_step_gl<T, D, 1>(a, kv, alpha, beta, gamma, a_ids, a_counts, m_ids, m_counts, p_ids, p_counts, ws, st);
+    case 2: return launch_prr_step_gl<T, D, 2>(a, kv, alpha, beta, gamma, a_ids, a_counts, m_ids, m_counts, p_ids, p_counts, ws, st);
+    case 4: return launch_prr_step_gl<T, D, 4>(a, kv, alpha, beta, gamma, a_ids, a_counts, m_ids, m_counts, p_ids, p_counts, ws, st);
+    case 8: return launch_prr_step_gl<T, D, 8>(a, kv, alpha, beta, gamma, a_ids, a_counts, m_ids, m_counts, p_ids, p_counts, ws, st);
+    case 16: return launch_prr_step_gl<T, D, 16>(a, kv, alpha, beta, gamma, a_ids, a_counts, m_ids, m_counts, p_ids, p_counts, ws, st);
   }
   return DSA_ERR_UNSUPPORTED;
 }
@@ -1684,7 +1740,8 @@ extern "C" int dsa_prr_decode_step(const void* q, int32_t n_q_heads, const dsa_k
   if (rc) return rc;
   if ((rc = check_logical(kv, logical_page))) return rc;
   if (k < 1) return DSA_ERR_SHAPE;
-  if (kv->dtype != DSA_BF16 || (G != 8 && G != 16) || kv->max_pages > kPsaMaxPages) return DSA_ERR_UNSUPPORTED;
+  // bf16 KV, logical page = physical page, rows within the selection's limit
+  if (kv->dtype != DSA_BF16 || logical_page != kv->page_size || kv->max_pages > 65536) return DSA_ERR_UNSUPPORTED;
   if (kv->batch == 0) return DSA_OK;
   if (!meta || !scores || !level || !trend || !pred || !p_cur_ids || !p_cur_counts || !a_ids || !a_counts ||
       !m_ids || !m_counts || !p_ids || !p_counts || !O || !l || !m)
@@ -1697,10 +1754,10 @@ extern "C" int dsa_prr_decode_step(const void* q, int32_t n_q_heads, const dsa_k
   if (!ws || ws_bytes < need) return DSA_ERR_WORKSPACE;
   if (!aligned16(ws)) return DSA_ERR_ALIGN;
   PrrStepArgs a{};
-  a.q = (const uint16_t*)q;
-  a.kp = (const uint16_t*)kv->k;
-  a.vp = (const uint16_t*)kv->v;
-  a.meta = (const uint16_t*)meta;
+  a.q = q;
+  a.kp = kv->k;
+  a.vp = kv->v;
+  a.meta = meta;
   a.page_table = kv->page_table;
   a.seq_lens = kv->seq_lens;
   a.n_kv_heads = kv->n_kv_heads;
@@ -1720,15 +1777,11 @@ extern "C" int dsa_prr_decode_step(const void* q, int32_t n_q_heads, const dsa_k
   a.l = l;
   a.m = m;
   hipStream_t st = (hipStream_t)stream;
-#define DSA_STEP(D_, G_) \
-  return launch_prr_step_gl<D_, G_>(a, kv, alpha, beta, gamma, a_ids, a_counts, m_ids, m_counts, p_ids, p_counts, ws, st)
-  if (kv->head_dim == 128) {
-    if (G == 16) DSA_STEP(128, 16);
-    DSA_STEP(128, 8);
-  }
-  if (G == 16) DSA_STEP(64, 16);
-  DSA_STEP(64, 8);
-#undef DSA_STEP
+  if (kv->head_dim == 128)
+    return launch_prr_step_d<uint16_t, 128>(G, a, kv, alpha, beta, gamma, a_ids, a_counts, m_ids, m_counts, p_ids,
+                                            p_counts, ws, st);
+  return launch_prr_step_d<uint16_t, 64>(G, a, kv, alpha, beta, gamma, a_ids, a_counts, m_ids, m_counts, p_ids,
+                                         p_counts, ws, st);
 }
 
 extern "C" int dsa_page_select_progressive(const void* q, int32_t n_q_heads, const dsa_kv* kv, const float* scores,

@@ -25,8 +25,8 @@ profile indexed by context length (section 3.4): the largest delta whose
 speculative attention still fits in the selection window
 (profile_delta_table, DeltaTable).
 
-Where the library has it (bf16 KV, 8 or 16 q heads per KV head, |A| = |P|)
-a speculative step is one call, dsa_prr_decode_step, on the caller's stream:
+Where the library has it (bf16 KV, one score per page, |A| = |P|) a
+speculative step is one call, dsa_prr_decode_step, on the caller's stream:
 the independent parts share launches (scores beside the speculative
 partials, the speculative combine beside the repair's partials) instead of
 streams, because each dependency between the hardware queues of a HIP
@@ -95,10 +95,10 @@ class PRRDecoder:
         self.ws = torch.zeros(workspace_bytes(OP_ATTN_REPAIR, kv, n_q_heads, self.stride), dtype=torch.uint8,
                               device=dev)
         self.sel_ws = None                 # a split-row selection workspace (see split_selection)
-        G = n_q_heads // kv.n_kv_heads
-        can = self.k == self.k_spec and kv.k.dtype == torch.bfloat16 and G in (8, 16) and N <= 65536
+        can = (self.k == self.k_spec and kv.k.dtype == torch.bfloat16 and self.lp == kv.page_size
+               and N <= 65536)
         if one_stream and not can:
-            raise ValueError("the one-call PRR step needs bf16 KV, 8 or 16 q heads per KV head and |A| = |P|")
+            raise ValueError("the one-call PRR step needs bf16 KV, logical page = page and |A| = |P|")
         self.one_stream = can if one_stream is None else bool(one_stream)
         self.step_ws = (torch.zeros(workspace_bytes(OP_PRR_DECODE_STEP, kv, n_q_heads, self.k), dtype=torch.uint8,
                                     device=dev) if self.one_stream else None)

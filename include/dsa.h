@@ -387,9 +387,11 @@ int dsa_attn_repair(const void *q, int32_t n_q_heads, const dsa_kv *kv, const in
  * partials): 4 launches on the given stream, nothing for a caller to join.
  * P^t = p_cur_ids/p_cur_counts must not be p_ids/p_counts; level, trend,
  * pred and scores distinct (DSA_ERR_SHAPE); every pointer non-NULL
- * (DSA_ERR_NULL); meta 16-byte aligned.  Requires bf16 KV with 8 or 16 q
- * heads per KV head (the matrix-core attention), no streaming heads and
- * max_pages <= 65536, else DSA_ERR_UNSUPPORTED (use the separate calls).
+ * (DSA_ERR_NULL); meta 16-byte aligned.  Requires bf16 KV, logical_page =
+ * page_size, no streaming heads and max_pages <= 65536, else
+ * DSA_ERR_UNSUPPORTED (use the separate calls); any group size the
+ * attention calls take (the matrix-core partials for 8 or 16 q heads per
+ * KV head, the VALU partials below).
  * ws: device scratch of dsa_workspace_bytes(DSA_OP_PRR_DECODE_STEP, kv,
  * n_q_heads, k) bytes, 16-byte aligned.
  */

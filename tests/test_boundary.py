@@ -163,17 +163,17 @@ def test_validation_errors(dsa):
     # repair: P ids without counts
     assert L.dsa_attn_repair(ok_ptr, 4, ctypes.byref(kv), ok_ptr, ok_ptr, ok_ptr, None, 8, F(0.088), ok_ptr, ok_ptr,
                              ok_ptr, ok_ptr, 1 << 30, None) == -1
-    # one-call PRR step (16 q heads over 2 KV heads): bad k, G outside {8, 16}, fp32 KV, a NULL output,
-    # aliased EMA state, P^t aliasing P^{t+1}, too small a workspace; batch 0 is a no-op
-    def step(n_q=32, kvd=kv, k=8, lvl=P(8192), p_cur=P(20480), p_nxt=P(24576), O=ok_ptr, wsb=None):
+    # one-call PRR step (16 q heads over 2 KV heads): bad k, logical pages smaller than the page, fp32 KV,
+    # a NULL output, aliased EMA state, P^t aliasing P^{t+1}, too small a workspace; batch 0 is a no-op
+    def step(n_q=32, kvd=kv, k=8, lvl=P(8192), p_cur=P(20480), p_nxt=P(24576), O=ok_ptr, wsb=None, lp=16):
         need = L.dsa_workspace_bytes(3, ctypes.byref(kvd), n_q, max(k, 1))
-        return L.dsa_prr_decode_step(ok_ptr, n_q, ctypes.byref(kvd), ok_ptr, 16, ok_ptr, lvl, P(12288), P(16384),
+        return L.dsa_prr_decode_step(ok_ptr, n_q, ctypes.byref(kvd), ok_ptr, lp, ok_ptr, lvl, P(12288), P(16384),
                                      F(0.6), F(0.3), F(0.25), k, p_cur, P(28672), ok_ptr, ok_ptr, ok_ptr, ok_ptr,
                                      p_nxt, P(32768), F(0.088), O, ok_ptr, ok_ptr, ok_ptr,
                                      need if wsb is None else wsb, None)
     assert L.dsa_workspace_bytes(3, ctypes.byref(kv), 32, 8) > L.dsa_workspace_bytes(2, ctypes.byref(kv), 32, 8)
     assert step(k=0) == -2
-    assert step(n_q=8) == -4
+    assert step(kvd=_kv(dsa, page_size=32), lp=16) == -4
     assert step(kvd=_kv(dsa, dtype=0)) == -4
     assert step(O=None) == -1
     assert step(lvl=P(12288)) == -2

@@ -18,9 +18,13 @@ CASES = [
     # (G, page_size, logical_page, seq_lens, k, head_dim)
     (16, 16, 16, [16 * 3000 + 5, 16 * 1200], 256, 128),
     (8, 16, 16, [16 * 5000 + 11], 512, 128),
-    (16, 64, 16, [64 * 700 + 40, 64 * 300], 64, 128),
-    (8, 32, 16, [32 * 90 + 7, 32 * 2], 200, 128),   # k above a row's pages
+    (16, 64, 64, [64 * 700 + 40, 64 * 300], 64, 128),
+    (8, 32, 32, [32 * 90 + 7, 32 * 2], 200, 128),   # k above a row's pages
     (16, 16, 16, [16 * 900 + 1, 16 * 2500, 16 * 40 + 9], 128, 64),
+    # VALU partials (4 and 2 q heads per KV head), one with more speculative splits than CUs
+    (4, 16, 16, [16 * 4000 + 3, 16 * 900], 512, 128),
+    (4, 16, 16, [16 * 8000] * 4, 1024, 128),
+    (2, 32, 32, [32 * 600 + 17, 32 * 5], 100, 64),
 ]
 
 
