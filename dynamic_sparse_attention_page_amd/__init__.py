@@ -74,12 +74,12 @@ def _load(path: str = LIB_PATH):
         "dsa_page_score": (ctypes.c_int, [P, I32, KV, P, I32, ST, P, P]),
         "dsa_page_score_ema": (ctypes.c_int, [P, I32, KV, P, I32, ST, P, P, P, P, F32, F32, F32, I32, P]),
         "dsa_page_select_topk": (ctypes.c_int, [P, I32, I32, I32, P, I32, I32, ST, P, P, P]),
-        "dsa_page_select_progressive": (ctypes.c_int, [P, I32, KV, P, F32, I32, F32, P, P, P, P, P, P]),
-        "dsa_psa_decode": (ctypes.c_int, [P, I32, KV, P, F32, I32, F32, P, P, P, P, P, P, P]),
+        "dsa_page_select_progressive": (ctypes.c_int, [P, I32, KV, P, F32, I32, ST, F32, P, P, P, P, P, P]),
+        "dsa_psa_decode": (ctypes.c_int, [P, I32, KV, P, F32, I32, ST, F32, P, P, P, P, P, P, P]),
         "dsa_sparse_decode_attn": (ctypes.c_int, [P, I32, KV, P, P, I32, ST, F32, P, P, P, P, SZ, P]),
         "dsa_sparse_decode_attn_noalloc": (ctypes.c_int, [P, I32, KV, P, P, I32, ST, F32, P, P, P, P]),
         "dsa_sparse_decode_attn_topk": (ctypes.c_int, [P, I32, KV, P, I32, ST, F32, P, P, P, P, P, P, SZ, P]),
-        "dsa_attn_repair": (ctypes.c_int, [P, I32, KV, P, P, P, P, I32, F32, P, P, P, P, SZ, P]),
+        "dsa_attn_repair": (ctypes.c_int, [P, I32, KV, P, P, P, P, I32, ST, F32, P, P, P, P, SZ, P]),
         "dsa_prr_decode_step": (ctypes.c_int, [P, I32, KV, P, I32, P, P, P, P, F32, F32, F32, I32, P, P, P, P, P, P,
                                                P, P, F32, P, P, P, P, SZ, P]),
         "dsa_ema_predict_update": (ctypes.c_int, [P, P, P, P, I64, F32, F32, F32, I32, P]),
@@ -303,8 +303,10 @@ def page_select_topk(scores: torch.Tensor, seq_lens: torch.Tensor, page_size: in
 
 
 def page_select_progressive(q: torch.Tensor, kv: PagedKV, scores: torch.Tensor, threshold: float,
-                            stop_mode: int = 0, scale: float | None = None, out=None):
-    """PSA progressive selection + attention: (ids, counts, O, l, m)."""
+                            stop_mode: int = 0, scale: float | None = None, out=None,
+                            streaming: Streaming | None = None):
+    """PSA progressive selection + attention: (ids, counts, O, l, m); a
+    streaming head visits its sink and local pages."""
     B, Hq = q.shape[0], q.shape[1]
     dev = kv.k.device
     if out is None:
@@ -316,13 +318,13 @@ def page_select_progressive(q: torch.Tensor, kv: PagedKV, scores: torch.Tensor, 
     ids, counts, O, l, m = out
     sc = _default_scale(kv.head_dim) if scale is None else scale
     _check("dsa_page_select_progressive", lib.dsa_page_select_progressive(
-        _ptr(q), Hq, ctypes.byref(kv.c()), _ptr(scores), float(threshold), stop_mode, sc, _ptr(ids), _ptr(counts),
-        _ptr(O), _ptr(l), _ptr(m), _stream()))
+        _ptr(q), Hq, ctypes.byref(kv.c()), _ptr(scores), float(threshold), stop_mode, _stream_arg(streaming), sc,
+        _ptr(ids), _ptr(counts), _ptr(O), _ptr(l), _ptr(m), _stream()))
     return ids, counts, O, l, m
 
 
 def psa_decode(q: torch.Tensor, kv: PagedKV, meta: torch.Tensor, threshold: float, stop_mode: int = 0,
-               scale: float | None = None, out=None):
+               scale: float | None = None, out=None, streaming: Streaming | None = None):
     """page_score + page_select_progressive in one call (one launch when the
     rows cover the GPU's CUs): (scores, ids, counts, O, l, m)."""
     B, Hq = q.shape[0], q.shape[1]
@@ -337,8 +339,8 @@ def psa_decode(q: torch.Tensor, kv: PagedKV, meta: torch.Tensor, threshold: floa
     scores, ids, counts, O, l, m = out
     sc = _default_scale(kv.head_dim) if scale is None else scale
     _check("dsa_psa_decode", lib.dsa_psa_decode(
-        _ptr(q), Hq, ctypes.byref(kv.c()), _ptr(meta), float(threshold), stop_mode, sc, _ptr(scores), _ptr(ids),
-        _ptr(counts), _ptr(O), _ptr(l), _ptr(m), _stream()))
+        _ptr(q), Hq, ctypes.byref(kv.c()), _ptr(meta), float(threshold), stop_mode, _stream_arg(streaming), sc,
+        _ptr(scores), _ptr(ids), _ptr(counts), _ptr(O), _ptr(l), _ptr(m), _stream()))
     return scores, ids, counts, O, l, m
 
 
@@ -407,7 +409,7 @@ def sparse_decode_attn_topk(q: torch.Tensor, kv: PagedKV, scores: torch.Tensor, 
 
 
 def attn_repair(q: torch.Tensor, kv: PagedKV, a_ids, a_counts, p_ids, p_counts, O, l, m,
-                scale: float | None = None, ws: torch.Tensor | None = None):
+                scale: float | None = None, ws: torch.Tensor | None = None, streaming: Streaming | None = None):
     """Fold attention over A \\ P into the speculative (O, l, m) in place;
     with p_ids = p_counts = None, a_ids is the missing set itself."""
     Hq = q.shape[1]
@@ -421,8 +423,8 @@ def attn_repair(q: torch.Tensor, kv: PagedKV, a_ids, a_counts, p_ids, p_counts, 
         ws = _workspace(need, kv.k.device)
     sc = _default_scale(kv.head_dim) if scale is None else scale
     _check("dsa_attn_repair", lib.dsa_attn_repair(
-        _ptr(q), Hq, ctypes.byref(kv.c()), _ptr(a_ids), _ptr(a_counts), _ptr(p_ids), _ptr(p_counts), stride, sc,
-        _ptr(O), _ptr(l), _ptr(m), _ptr(ws), ws.numel() * ws.element_size(), _stream()))
+        _ptr(q), Hq, ctypes.byref(kv.c()), _ptr(a_ids), _ptr(a_counts), _ptr(p_ids), _ptr(p_counts), stride,
+        _stream_arg(streaming), sc, _ptr(O), _ptr(l), _ptr(m), _ptr(ws), ws.numel() * ws.element_size(), _stream()))
     return O, l, m
 
 

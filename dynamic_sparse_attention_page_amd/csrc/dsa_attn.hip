@@ -858,7 +858,8 @@ __device__ __forceinline__ void psa_body(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const float* srow,
     const int32_t* ptrow, int L, int h, int b, int n_kv_heads, int P, int max_pages, int num_slots, int stop_mode,
     int never_stop, int always_stop, float ln_odds, float scale, float c, int32_t* __restrict__ ids,
-    int32_t* __restrict__ counts, float* __restrict__ O, float* __restrict__ l, float* __restrict__ m) {
+    int32_t* __restrict__ counts, float* __restrict__ O, float* __restrict__ l, float* __restrict__ m,
+    int streaming = 0, int sink = 0, int local = 0) {
   using A = AttnWave<T, D, G>;
   constexpr int CPL = A::CPL, DW = A::DW;
   constexpr int NWV = psa_waves<T, G>();
@@ -901,10 +902,32 @@ __device__ __forceinline__ void psa_body(
   int visited = 0, n_rem = np, grp = 0;
   unsigned long long kb = 0ull;
   bool stop = false;
+  // A streaming head (LServe section 4.1) attends to the pages holding a
+  // sink or a local token, in ascending order, with the token mask; it is
+  // not ranked and never stops early.  The list is [0, n_sink) then
+  // [l_first, np).
+  const int n_sink = min(np, (min(sink, L) + P - 1) / P);
+  const int l_first = max(n_sink, (local > 0 && L > 0) ? max(0, L - local) / P : np);
+  const int n_fixed = n_sink + (np - l_first);
+  if (streaming) n_rem = n_fixed;
+  const bool no_stop = never_stop || streaming;
   for (int round = 0; !stop && n_rem > 0; ++round) {
     const int n_pick = min(round == 0 ? kPsaFirst : kPsaRound, n_rem);
-    if (round == 0) psa_pick<E, NWV, true>(ks, round, kb, n_rem, n_pick, sm);
-    else psa_pick<E, NWV, false>(ks, round, kb, n_rem, n_pick, sm);
+    if (streaming) {
+      __syncthreads();   // the last round's reads of the page list are done
+      const int e0 = (streaming ? n_fixed : np) - n_rem;
+      for (int x = tid; x < n_pick; x += NT) {
+        const int e = e0 + x;
+        const int pg = e < n_sink ? e : l_first + (e - n_sink);
+        sm.page[x] = pg;
+        sm.slot[x] = ptrow[pg];
+      }
+      __syncthreads();
+    } else if (round == 0) {
+      psa_pick<E, NWV, true>(ks, round, kb, n_rem, n_pick, sm);
+    } else {
+      psa_pick<E, NWV, false>(ks, round, kb, n_rem, n_pick, sm);
+    }
     n_rem -= n_pick;
 
     for (int cs = 0; cs < n_pick; cs += NWV) {
@@ -924,7 +947,7 @@ __device__ __forceinline__ void psa_body(
             const size_t off = (size_t)slot * slot_stride + head_off + (size_t)tin * 16 * D;
             A::load_tile(k + off, lane, kd);
             A::load_tile(v + off, lane, vd);
-            st.tile(kd, vd, nvalid, false, tok0, L, 0, 0, c);
+            st.tile(kd, vd, nvalid, streaming != 0, tok0, L, sink, local, c);
           }
         }
       }
@@ -976,7 +999,7 @@ __device__ __forceinline__ void psa_body(
       const float lnmin = fminf(lnmin_run, row_scan_min(here ? ln_as : __builtin_huge_valf()));
       const int left = left_run - (lane + 1);
       bool pass;
-      if (never_stop) pass = false;
+      if (no_stop) pass = false;
       else if (always_stop) pass = true;
       else if (stop_mode == 0) pass = lnacc - lnmin >= ln_odds;
       else pass = (left == 0) || (lnacc - (lnmin + __logf((float)left)) >= ln_odds);
@@ -1020,7 +1043,7 @@ __device__ __forceinline__ void psa_body(
         break;
       }
     }
-    if (!stop && n_rem > 0) ks.round_start();   // the next round's keys (not held during the walk)
+    if (!stop && n_rem > 0 && !streaming) ks.round_start();   // the next round's keys (not held during the walk)
   }
 
   // outputs
@@ -1046,12 +1069,13 @@ __global__ __launch_bounds__((psa_waves<T, G>() * 64)) void psa_kernel(
     const int32_t* __restrict__ page_table, const int32_t* __restrict__ seq_lens, const float* __restrict__ scores,
     int n_kv_heads, int P, int max_pages, int num_slots, int stop_mode, int never_stop, int always_stop,
     float ln_odds, float scale, float c, int32_t* __restrict__ ids, int32_t* __restrict__ counts,
-    float* __restrict__ O, float* __restrict__ l, float* __restrict__ m) {
+    float* __restrict__ O, float* __restrict__ l, float* __restrict__ m, unsigned long long streaming, int sink,
+    int local) {
   const int h = blockIdx.x, b = blockIdx.y;
   const int L = clamp_len(seq_lens[b], max_pages, P);
   psa_body<T, D, G, E>(q, k, v, scores + ((size_t)b * n_kv_heads + h) * max_pages, page_table + (size_t)b * max_pages,
                        L, h, b, n_kv_heads, P, max_pages, num_slots, stop_mode, never_stop, always_stop, ln_odds, scale,
-                       c, ids, counts, O, l, m);
+                       c, ids, counts, O, l, m, (int)((streaming >> h) & 1ull), sink, local);
 }
 
 // ============================================================ PSA with its own scores
@@ -1075,7 +1099,8 @@ __global__ __launch_bounds__((psa_waves<T, G>() * 64)) void psa_fused_kernel(
     const int32_t* __restrict__ page_table, const int32_t* __restrict__ seq_lens, int n_kv_heads, int P,
     int max_pages, int num_slots, int stop_mode, int never_stop, int always_stop, float ln_odds, float scale,
     float c, float* __restrict__ scores, int32_t* __restrict__ ids, int32_t* __restrict__ counts,
-    float* __restrict__ O, float* __restrict__ l, float* __restrict__ m) {
+    float* __restrict__ O, float* __restrict__ l, float* __restrict__ m, unsigned long long streaming, int sink,
+    int local) {
   using L_ = Lay<T, D>;
   constexpr int CPL = L_::CPL, DW = L_::DW;
   constexpr int NWV = psa_waves<T, G>();
@@ -1092,6 +1117,13 @@ __global__ __launch_bounds__((psa_waves<T, G>() * 64)) void psa_fused_kernel(
   const int np = (L + P - 1) / P;
   const int32_t* ptg = page_table + (size_t)b * max_pages;
   for (int x = tid; x < max_pages; x += NT) s_slot[x] = ptg[x];
+  if ((streaming >> h) & 1ull) {   // a streaming head: no scores (-inf, as page_score writes), fixed pages
+    for (int x = tid; x < max_pages; x += NT) scores[(size_t)unit * max_pages + x] = kNegInf;
+    __syncthreads();
+    psa_body<T, D, G, E>(q, k, v, s_score, s_slot, L, h, b, n_kv_heads, P, max_pages, num_slots, stop_mode,
+                         never_stop, always_stop, ln_odds, scale, c, ids, counts, O, l, m, 1, sink, local);
+    return;
+  }
   // group-mean query, this lane's channels, split by sign
   float qpos[CPL], qneg[CPL];
   {
@@ -1403,9 +1435,16 @@ static int max_lds_per_block() {
   return cached[dev];
 }
 
+// Streaming heads of a PSA call: flags per KV head, sink and local tokens.
+struct PsaStream {
+  unsigned long long mask;
+  int sink, local;
+};
+
 template <typename T, int D, int G>
 static int launch_psa_g(const void* q, const dsa_kv* kv, const float* scores, float thr, int stop_mode, float scale,
-                        int32_t* ids, int32_t* counts, float* O, float* l, float* m, hipStream_t st) {
+                        int32_t* ids, int32_t* counts, float* O, float* l, float* m, const PsaStream& ps,
+                        hipStream_t st) {
   const int never_stop = thr >= 1.0f;
   const int always_stop = thr <= 0.0f;
   const float ln_odds = (never_stop || always_stop) ? 0.0f : (float)log((double)thr / (1.0 - (double)thr));
@@ -1417,7 +1456,7 @@ static int launch_psa_g(const void* q, const dsa_kv* kv, const float* scores, fl
   hipLaunchKernelGGL((psa_kernel<T, D, G, E_>), dim3(kv->n_kv_heads, kv->batch), dim3(NT), 0, st, (const T*)q,     \
                      (const T*)kv->k, (const T*)kv->v, kv->page_table, kv->seq_lens, scores, kv->n_kv_heads,       \
                      kv->page_size, kv->max_pages, kv->num_slots, stop_mode, never_stop, always_stop, ln_odds,     \
-                     scale, c, ids, counts, O, l, m)
+                     scale, c, ids, counts, O, l, m, ps.mask, ps.sink, ps.local)
   if (kv->max_pages <= NT * ESHORT) DSA_PSA(ESHORT);
   else if (kv->max_pages <= NT * kPsaRegKeys) DSA_PSA(kPsaRegKeys);
   else DSA_PSA(EMAX);
@@ -1427,11 +1466,12 @@ static int launch_psa_g(const void* q, const dsa_kv* kv, const float* scores, fl
 
 template <typename T, int D>
 static int launch_psa_d(const void* q, int G, const dsa_kv* kv, const float* scores, float thr, int stop_mode,
-                        float scale, int32_t* ids, int32_t* counts, float* O, float* l, float* m, hipStream_t st) {
+                        float scale, int32_t* ids, int32_t* counts, float* O, float* l, float* m, const PsaStream& ps,
+                        hipStream_t st) {
   switch (G) {
-    case 1: return launch_psa_g<T, D, 1>(q, kv, scores, thr, stop_mode, scale, ids, counts, O, l, m, st);
-    case 2: return launch_psa_g<T, D, 2>(q, kv, scores, thr, stop_mode, scale, ids, counts, O, l, m, st);
-    case 4: return launch_psa_g<T, D, 4>(q, kv, scores, thr, stop_mode, scale, ids, counts, O, l, m, st);
+    case 1: return launch_psa_g<T, D, 1>(q, kv, scores, thr, stop_mode, scale, ids, counts, O, l, m, ps, st);
+    case 2: return launch_psa_g<T, D, 2>(q, kv, scores, thr, stop_mode, scale, ids, counts, O, l, m, ps, st);
+    case 4: return launch_psa_g<T, D, 4>(q, kv, scores, thr, stop_mode, scale, ids, counts, O, l, m, ps, st);
   }
   return DSA_ERR_UNSUPPORTED;
 }
@@ -1446,7 +1486,7 @@ inline size_t psa_fused_lds(int max_pages) {
 template <typename T, int D, int G>
 static int launch_psa_fused_g(const void* q, const dsa_kv* kv, const void* meta, float thr, int stop_mode,
                               float scale, float* scores, int32_t* ids, int32_t* counts, float* O, float* l, float* m,
-                              hipStream_t st) {
+                              const PsaStream& ps, hipStream_t st) {
   const int never_stop = thr >= 1.0f;
   const int always_stop = thr <= 0.0f;
   const float ln_odds = (never_stop || always_stop) ? 0.0f : (float)log((double)thr / (1.0 - (double)thr));
@@ -1463,7 +1503,7 @@ static int launch_psa_fused_g(const void* q, const dsa_kv* kv, const void* meta,
     hipLaunchKernelGGL(kernel, dim3(kv->n_kv_heads, kv->batch), dim3(NT), dyn, st, (const T*)q, (const T*)kv->k,
                        (const T*)kv->v, (const T*)meta, kv->page_table, kv->seq_lens, kv->n_kv_heads, kv->page_size,
                        kv->max_pages, kv->num_slots, stop_mode, never_stop, always_stop, ln_odds, scale, c, scores,
-                       ids, counts, O, l, m);
+                       ids, counts, O, l, m, ps.mask, ps.sink, ps.local);
     return launch_status();
   };
   if (kv->max_pages <= 4096) return go(psa_fused_kernel<T, D, G, 4096 / NT>);
@@ -1473,11 +1513,11 @@ static int launch_psa_fused_g(const void* q, const dsa_kv* kv, const void* meta,
 template <typename T, int D>
 static int launch_psa_fused_d(const void* q, int G, const dsa_kv* kv, const void* meta, float thr, int stop_mode,
                               float scale, float* scores, int32_t* ids, int32_t* counts, float* O, float* l, float* m,
-                              hipStream_t st) {
+                              const PsaStream& ps, hipStream_t st) {
   switch (G) {
-    case 1: return launch_psa_fused_g<T, D, 1>(q, kv, meta, thr, stop_mode, scale, scores, ids, counts, O, l, m, st);
-    case 2: return launch_psa_fused_g<T, D, 2>(q, kv, meta, thr, stop_mode, scale, scores, ids, counts, O, l, m, st);
-    case 4: return launch_psa_fused_g<T, D, 4>(q, kv, meta, thr, stop_mode, scale, scores, ids, counts, O, l, m, st);
+    case 1: return launch_psa_fused_g<T, D, 1>(q, kv, meta, thr, stop_mode, scale, scores, ids, counts, O, l, m, ps, st);
+    case 2: return launch_psa_fused_g<T, D, 2>(q, kv, meta, thr, stop_mode, scale, scores, ids, counts, O, l, m, ps, st);
+    case 4: return launch_psa_fused_g<T, D, 4>(q, kv, meta, thr, stop_mode, scale, scores, ids, counts, O, l, m, ps, st);
   }
   return DSA_ERR_UNSUPPORTED;
 }
@@ -1625,12 +1665,14 @@ extern "C" int dsa_sparse_decode_attn_topk(const void* q, int32_t n_q_heads, con
 
 extern "C" int dsa_attn_repair(const void* q, int32_t n_q_heads, const dsa_kv* kv, const int32_t* a_ids,
                                const int32_t* a_counts, const int32_t* p_ids, const int32_t* p_counts,
-                               int32_t ids_stride, float scale, float* O, float* l, float* m, void* ws,
-                               size_t ws_bytes, void* stream) {
+                               int32_t ids_stride, const dsa_stream_cfg* stream_cfg, float scale, float* O, float* l,
+                               float* m, void* ws, size_t ws_bytes, void* stream) {
   int G = 0;
   int rc = check_attn_common(q, n_q_heads, kv, scale, &G);
   if (rc) return rc;
   if (ids_stride < 1) return DSA_ERR_SHAPE;
+  uint64_t smask;
+  if ((rc = streaming_mask(stream_cfg, kv->n_kv_heads, &smask))) return rc;
   if (kv->batch == 0) return DSA_OK;
   if (!a_ids || !a_counts || !O || !l || !m) return DSA_ERR_NULL;
   if (!p_ids != !p_counts) return DSA_ERR_NULL;
@@ -1643,7 +1685,8 @@ extern "C" int dsa_attn_repair(const void* q, int32_t n_q_heads, const dsa_kv* k
   }
   // without P the a_ids are M already (usually a short prefix of the row):
   // the plain split-KV path, folded; splits past the count exit at once
-  return launch_attn(q, G, kv, a_ids, a_counts, ids_stride, 0, 0, 0, scale, O, l, m, ws, 1, p_ids, p_counts,
+  const int sink = stream_cfg ? stream_cfg->sink : 0, local = stream_cfg ? stream_cfg->local : 0;
+  return launch_attn(q, G, kv, a_ids, a_counts, ids_stride, smask, sink, local, scale, O, l, m, ws, 1, p_ids, p_counts,
                      SelectArgs{}, (hipStream_t)stream);
 }
 
@@ -1785,51 +1828,58 @@ extern "C" int dsa_prr_decode_step(const void* q, int32_t n_q_heads, const dsa_k
 }
 
 extern "C" int dsa_page_select_progressive(const void* q, int32_t n_q_heads, const dsa_kv* kv, const float* scores,
-                                           float threshold, int32_t stop_mode, float scale, int32_t* ids,
-                                           int32_t* counts, float* O, float* l, float* m, void* stream) {
+                                           float threshold, int32_t stop_mode, const dsa_stream_cfg* stream_cfg,
+                                           float scale, int32_t* ids, int32_t* counts, float* O, float* l, float* m,
+                                           void* stream) {
   int G = 0;
   int rc = check_attn_common(q, n_q_heads, kv, scale, &G);
   if (rc) return rc;
   if (stop_mode != 0 && stop_mode != 1) return DSA_ERR_SHAPE;
   if (threshold != threshold) return DSA_ERR_SHAPE;
+  uint64_t smask;
+  if ((rc = streaming_mask(stream_cfg, kv->n_kv_heads, &smask))) return rc;
   if (kv->max_pages > kPsaMaxPages) return DSA_ERR_UNSUPPORTED;
   if (kv->batch == 0) return DSA_OK;
   if (!scores || !ids || !counts || !O || !l || !m) return DSA_ERR_NULL;
+  const PsaStream ps{(unsigned long long)smask, stream_cfg ? stream_cfg->sink : 0, stream_cfg ? stream_cfg->local : 0};
   hipStream_t st = (hipStream_t)stream;
   const bool bf = kv->dtype == DSA_BF16;
   if (kv->head_dim == 128)
-    return bf ? launch_psa_d<uint16_t, 128>(q, G, kv, scores, threshold, stop_mode, scale, ids, counts, O, l, m, st)
-              : launch_psa_d<float, 128>(q, G, kv, scores, threshold, stop_mode, scale, ids, counts, O, l, m, st);
-  return bf ? launch_psa_d<uint16_t, 64>(q, G, kv, scores, threshold, stop_mode, scale, ids, counts, O, l, m, st)
-            : launch_psa_d<float, 64>(q, G, kv, scores, threshold, stop_mode, scale, ids, counts, O, l, m, st);
+    return bf ? launch_psa_d<uint16_t, 128>(q, G, kv, scores, threshold, stop_mode, scale, ids, counts, O, l, m, ps, st)
+              : launch_psa_d<float, 128>(q, G, kv, scores, threshold, stop_mode, scale, ids, counts, O, l, m, ps, st);
+  return bf ? launch_psa_d<uint16_t, 64>(q, G, kv, scores, threshold, stop_mode, scale, ids, counts, O, l, m, ps, st)
+            : launch_psa_d<float, 64>(q, G, kv, scores, threshold, stop_mode, scale, ids, counts, O, l, m, ps, st);
 }
 
 extern "C" int dsa_psa_decode(const void* q, int32_t n_q_heads, const dsa_kv* kv, const void* meta, float threshold,
-                              int32_t stop_mode, float scale, float* scores, int32_t* ids, int32_t* counts, float* O,
-                              float* l, float* m, void* stream) {
+                              int32_t stop_mode, const dsa_stream_cfg* stream_cfg, float scale, float* scores,
+                              int32_t* ids, int32_t* counts, float* O, float* l, float* m, void* stream) {
   int G = 0;
   int rc = check_attn_common(q, n_q_heads, kv, scale, &G);
   if (rc) return rc;
   if (stop_mode != 0 && stop_mode != 1) return DSA_ERR_SHAPE;
   if (threshold != threshold) return DSA_ERR_SHAPE;
+  uint64_t smask;
+  if ((rc = streaming_mask(stream_cfg, kv->n_kv_heads, &smask))) return rc;
   if (kv->max_pages > kPsaMaxPages) return DSA_ERR_UNSUPPORTED;
   if (G > 4) return DSA_ERR_UNSUPPORTED;
   if (kv->batch == 0) return DSA_OK;
   if (!meta || !scores || !ids || !counts || !O || !l || !m) return DSA_ERR_NULL;
   if (!aligned16(meta)) return DSA_ERR_ALIGN;
+  const PsaStream ps{(unsigned long long)smask, stream_cfg ? stream_cfg->sink : 0, stream_cfg ? stream_cfg->local : 0};
   hipStream_t st = (hipStream_t)stream;
   const bool bf = kv->dtype == DSA_BF16;
   if (kv->max_pages <= kPsaFusedMaxPages && (long long)kv->batch * kv->n_kv_heads >= cu_count()) {
     if (kv->head_dim == 128)
-      rc = bf ? launch_psa_fused_d<uint16_t, 128>(q, G, kv, meta, threshold, stop_mode, scale, scores, ids, counts, O, l, m, st)
-              : launch_psa_fused_d<float, 128>(q, G, kv, meta, threshold, stop_mode, scale, scores, ids, counts, O, l, m, st);
+      rc = bf ? launch_psa_fused_d<uint16_t, 128>(q, G, kv, meta, threshold, stop_mode, scale, scores, ids, counts, O, l, m, ps, st)
+              : launch_psa_fused_d<float, 128>(q, G, kv, meta, threshold, stop_mode, scale, scores, ids, counts, O, l, m, ps, st);
     else
-      rc = bf ? launch_psa_fused_d<uint16_t, 64>(q, G, kv, meta, threshold, stop_mode, scale, scores, ids, counts, O, l, m, st)
-              : launch_psa_fused_d<float, 64>(q, G, kv, meta, threshold, stop_mode, scale, scores, ids, counts, O, l, m, st);
+      rc = bf ? launch_psa_fused_d<uint16_t, 64>(q, G, kv, meta, threshold, stop_mode, scale, scores, ids, counts, O, l, m, ps, st)
+              : launch_psa_fused_d<float, 64>(q, G, kv, meta, threshold, stop_mode, scale, scores, ids, counts, O, l, m, ps, st);
     if (rc != DSA_ERR_UNSUPPORTED) return rc;
   }
   // fewer rows than CUs, long rows, or an LDS budget that does not fit: the two calls
-  if ((rc = dsa_page_score(q, n_q_heads, kv, meta, kv->page_size, nullptr, scores, stream))) return rc;
-  return dsa_page_select_progressive(q, n_q_heads, kv, scores, threshold, stop_mode, scale, ids, counts, O, l, m,
-                                     stream);
+  if ((rc = dsa_page_score(q, n_q_heads, kv, meta, kv->page_size, stream_cfg, scores, stream))) return rc;
+  return dsa_page_select_progressive(q, n_q_heads, kv, scores, threshold, stop_mode, stream_cfg, scale, ids, counts,
+                                     O, l, m, stream);
 }

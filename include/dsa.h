@@ -248,19 +248,23 @@ int dsa_page_select_topk(const float *scores, int32_t batch, int32_t n_kv_heads,
  * over the visited pages.
  * scores as from dsa_page_score; ids: device int32 [batch][n_kv_heads][max_pages];
  * O: device float [batch][n_q_heads][head_dim]; l, m: device float [batch][n_q_heads].
- * Requires max_pages <= 65536 (else DSA_ERR_UNSUPPORTED).  Streaming heads are
- * not supported here.
+ * Requires max_pages <= 65536 (else DSA_ERR_UNSUPPORTED).
+ * stream_cfg (nullable): a streaming head ([LServe] section 4.1) is not
+ * ranked: it visits the pages holding a sink or a local token, ascending,
+ * attends only to those tokens, and never stops early (ids = that list,
+ * counts = its length).
  */
 int dsa_page_select_progressive(const void *q, int32_t n_q_heads, const dsa_kv *kv,
                                 const float *scores, float threshold, int32_t stop_mode,
-                                float scale, int32_t *ids, int32_t *counts, float *O, float *l,
-                                float *m, void *stream);
+                                const dsa_stream_cfg *stream_cfg, float scale, int32_t *ids,
+                                int32_t *counts, float *O, float *l, float *m, void *stream);
 
 /*
  * dsa_psa_decode -- dsa_page_score followed by dsa_page_select_progressive
  * ([LServe] section 4.2 criticality, [PSA] section 3.2 progressive
- * selection) in one call, for meta built with logical_page = page_size and no
- * streaming heads.  When there are at least as many (b, KV head) rows as the
+ * selection) in one call, for meta built with logical_page = page_size; a
+ * streaming head of stream_cfg (nullable) gets -inf scores and its sink and
+ * local pages, as in the two calls.  When there are at least as many (b, KV head) rows as the
  * GPU has CUs and max_pages <= 8192, one workgroup per row computes its
  * row's scores into LDS and goes straight on to the selection and walk (one
  * launch); otherwise the two calls run in sequence.  Either way the results
@@ -269,8 +273,9 @@ int dsa_page_select_progressive(const void *q, int32_t n_q_heads, const dsa_kv *
  * Requires max_pages <= 65536 and 1, 2 or 4 q heads per KV head.
  */
 int dsa_psa_decode(const void *q, int32_t n_q_heads, const dsa_kv *kv, const void *meta,
-                   float threshold, int32_t stop_mode, float scale, float *scores, int32_t *ids,
-                   int32_t *counts, float *O, float *l, float *m, void *stream);
+                   float threshold, int32_t stop_mode, const dsa_stream_cfg *stream_cfg, float scale,
+                   float *scores, int32_t *ids, int32_t *counts, float *O, float *l, float *m,
+                   void *stream);
 
 /*
  * dsa_sparse_decode_attn -- attention over the selected pages only ([LServe]
@@ -354,13 +359,14 @@ int dsa_sparse_decode_attn_topk(const void *q, int32_t n_q_heads, const dsa_kv *
  * p_ids and p_counts may both be NULL: then a_ids already lists M (as
  * dsa_prr_select writes it) and is attended as it is.
  * a_ids, p_ids: device int32 [batch][n_kv_heads][ids_stride] with page ids
- * < max_pages.  Streaming heads are not supported here.
+ * < max_pages.  stream_cfg (nullable): for a streaming head only the sink
+ * and local tokens of M's pages count, as in dsa_sparse_decode_attn.
  * ws: device scratch of dsa_workspace_bytes(DSA_OP_ATTN_REPAIR, ...).
  */
 int dsa_attn_repair(const void *q, int32_t n_q_heads, const dsa_kv *kv, const int32_t *a_ids,
                     const int32_t *a_counts, const int32_t *p_ids, const int32_t *p_counts,
-                    int32_t ids_stride, float scale, float *O, float *l, float *m, void *ws,
-                    size_t ws_bytes, void *stream);
+                    int32_t ids_stride, const dsa_stream_cfg *stream_cfg, float scale, float *O,
+                    float *l, float *m, void *ws, size_t ws_bytes, void *stream);
 
 /*
  * dsa_prr_decode_step -- one speculative PRR decode step on one stream
@@ -377,8 +383,8 @@ int dsa_attn_repair(const void *q, int32_t n_q_heads, const dsa_kv *kv, const in
  *   dsa_prr_select(scores, ..., k, a_ids, a_counts, NULL, NULL, pred, alpha,
  *                  beta, gamma, 0, k, p_ids, p_counts, p_cur_ids, p_cur_counts,
  *                  m_ids, m_counts, NULL, 0)
- *   dsa_attn_repair(q, n_q_heads, kv, m_ids, m_counts, NULL, NULL, k, scale,
- *                   O, l, m)
+ *   dsa_attn_repair(q, n_q_heads, kv, m_ids, m_counts, NULL, NULL, k, NULL,
+ *                   scale, O, l, m)
  * i.e. IS^t into scores, level/trend/pred updated with it, O/l/m = attention
  * over P^t union A^t, a_ids = A^t, m_ids = M^t = A^t \ P^t and p_ids =
  * P^{t+1} (|A| = |P| = k; every id row has stride k, ascending, -1 padded).

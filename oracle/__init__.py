@@ -366,6 +366,20 @@ def psa_progressive(batch, b: int, h: int, scores_row: np.ndarray, threshold: fl
     return np.array(visited, np.int64), len(visited), O_acc, l, m
 
 
+def psa_unit(batch, b: int, h: int, scores_row: np.ndarray, threshold: float, stop_mode: int = 0, q=None):
+    """PSA's result for one (sequence, KV head) of a batch that may hold
+    streaming heads: a dense head takes the progressive walk above; a
+    streaming head (LServe section 4.1: it attends only to its sink and
+    local tokens) is not ranked -- it visits the pages holding such tokens in
+    ascending order and attends to those tokens only, with no early stop.
+    Returns (ids visited, n_visited, O[G][D], l[G], m[G])."""
+    if batch.streaming is not None and batch.streaming[h]:
+        pages = streaming_pages(batch.seq_lens[b], batch.page_size, batch.sink, batch.local)
+        O, l, m = attend_pages(batch, b, h, pages, q)
+        return pages, len(pages), O, l, m
+    return psa_progressive(batch, b, h, scores_row, threshold, stop_mode, q)
+
+
 def psa_ratios(batch, b: int, h: int, scores_row: np.ndarray, stop_mode: int = 0, q=None) -> np.ndarray:
     """The stop-test ratio after each page in rank order (diagnostic used by
     the parity rule for stops that sit on the threshold)."""

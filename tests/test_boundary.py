@@ -97,19 +97,25 @@ def test_validation_errors(dsa):
     assert L.dsa_workspace_bytes(2, ctypes.byref(kv), 4, 8) >= need
     assert L.dsa_workspace_bytes(9, ctypes.byref(kv), 4, 8) == 0
     # progressive: bad stop mode, too many pages, G=8 unsupported
-    assert L.dsa_page_select_progressive(ok_ptr, 4, ctypes.byref(kv), ok_ptr, ctypes.c_float(0.9), 2,
+    assert L.dsa_page_select_progressive(ok_ptr, 4, ctypes.byref(kv), ok_ptr, ctypes.c_float(0.9), 2, None,
                                          ctypes.c_float(0.088), ok_ptr, ok_ptr, ok_ptr, ok_ptr, ok_ptr, None) == -2
     assert L.dsa_page_select_progressive(ok_ptr, 4, ctypes.byref(_kv(dsa, max_pages=65537)), ok_ptr,
-                                         ctypes.c_float(0.9), 0, ctypes.c_float(0.088), ok_ptr, ok_ptr, ok_ptr,
+                                         ctypes.c_float(0.9), 0, None, ctypes.c_float(0.088), ok_ptr, ok_ptr, ok_ptr,
                                          ok_ptr, ok_ptr, None) == -4
+    # progressive: a streaming configuration with a negative window
+    flags = ctypes.create_string_buffer(b"\x01\x00")
+    bad_st = dsa._Stream(ctypes.cast(flags, ctypes.c_void_p), -1, 4)
+    assert L.dsa_page_select_progressive(ok_ptr, 4, ctypes.byref(kv), ok_ptr, ctypes.c_float(0.9), 0,
+                                         ctypes.byref(bad_st), ctypes.c_float(0.088), ok_ptr, ok_ptr, ok_ptr, ok_ptr,
+                                         ok_ptr, None) == -2
     # psa_decode: bad stop mode, G=8 unsupported, missing metadata, too many pages
-    assert L.dsa_psa_decode(ok_ptr, 4, ctypes.byref(kv), ok_ptr, ctypes.c_float(0.9), 2, ctypes.c_float(0.088),
+    assert L.dsa_psa_decode(ok_ptr, 4, ctypes.byref(kv), ok_ptr, ctypes.c_float(0.9), 2, None, ctypes.c_float(0.088),
                             ok_ptr, ok_ptr, ok_ptr, ok_ptr, ok_ptr, ok_ptr, None) == -2
-    assert L.dsa_psa_decode(ok_ptr, 16, ctypes.byref(kv), ok_ptr, ctypes.c_float(0.9), 0, ctypes.c_float(0.088),
+    assert L.dsa_psa_decode(ok_ptr, 16, ctypes.byref(kv), ok_ptr, ctypes.c_float(0.9), 0, None, ctypes.c_float(0.088),
                             ok_ptr, ok_ptr, ok_ptr, ok_ptr, ok_ptr, ok_ptr, None) == -4
-    assert L.dsa_psa_decode(ok_ptr, 4, ctypes.byref(kv), None, ctypes.c_float(0.9), 0, ctypes.c_float(0.088),
+    assert L.dsa_psa_decode(ok_ptr, 4, ctypes.byref(kv), None, ctypes.c_float(0.9), 0, None, ctypes.c_float(0.088),
                             ok_ptr, ok_ptr, ok_ptr, ok_ptr, ok_ptr, ok_ptr, None) == -1
-    assert L.dsa_psa_decode(ok_ptr, 4, ctypes.byref(_kv(dsa, max_pages=65537)), ok_ptr, ctypes.c_float(0.9), 0,
+    assert L.dsa_psa_decode(ok_ptr, 4, ctypes.byref(_kv(dsa, max_pages=65537)), ok_ptr, ctypes.c_float(0.9), 0, None,
                             ctypes.c_float(0.088), ok_ptr, ok_ptr, ok_ptr, ok_ptr, ok_ptr, ok_ptr, None) == -4
     # append: null new rows / lengths, misaligned rows or metadata, bad logical page
     assert L.dsa_kv_append(ctypes.byref(kv), 16, None, ok_ptr, ok_ptr, ok_ptr, None, None) == -1
@@ -161,8 +167,8 @@ def test_validation_errors(dsa):
     assert L.dsa_page_score_ema(ok_ptr, 4, ctypes.byref(kv), ok_ptr, 16, None, P(8192), P(8192), P(12288), P(16384),
                                 F(0.6), F(0.3), F(0.25), 0, None) == -2
     # repair: P ids without counts
-    assert L.dsa_attn_repair(ok_ptr, 4, ctypes.byref(kv), ok_ptr, ok_ptr, ok_ptr, None, 8, F(0.088), ok_ptr, ok_ptr,
-                             ok_ptr, ok_ptr, 1 << 30, None) == -1
+    assert L.dsa_attn_repair(ok_ptr, 4, ctypes.byref(kv), ok_ptr, ok_ptr, ok_ptr, None, 8, None, F(0.088), ok_ptr,
+                             ok_ptr, ok_ptr, ok_ptr, 1 << 30, None) == -1
     # one-call PRR step (16 q heads over 2 KV heads): bad k, logical pages smaller than the page, fp32 KV,
     # a NULL output, aliased EMA state, P^t aliasing P^{t+1}, too small a workspace; batch 0 is a no-op
     def step(n_q=32, kvd=kv, k=8, lvl=P(8192), p_cur=P(20480), p_nxt=P(24576), O=ok_ptr, wsb=None, lp=16):

@@ -10,8 +10,8 @@ import torch
 
 import oracle
 import workloads as wl
-from parity_util import (TOL, check_attention, check_psa, check_selected_attention, check_selection, ids_lists,
-                         np_, to_device)
+from parity_util import (TOL, check_attention, check_psa, check_psa_result, check_selected_attention, check_selection,
+                         ids_lists, np_, to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -242,6 +242,78 @@ def _psa_check(dsa, bt, thr, mode):
     q, kv, _ = to_device(dsa, bt)
     check_psa(dsa, bt, q, kv, oracle.page_scores(bt).astype(np.float32), thr, mode, f"psa thr={thr} mode={mode}")
 
+
+
+@pytest.mark.parametrize("G,P,mode", [(1, 16, 0), (4, 16, 1), (2, 64, 0)])
+def test_psa_streaming_heads(gpu_lib, G, P, mode):
+    """Progressive selection with streaming heads (LServe section 4.1): dense
+    heads walk as usual, a streaming head visits its sink and local pages in
+    ascending order under the token mask, with no early stop (oracle.psa_unit)."""
+    dsa = gpu_lib
+    _banner(f"psa streaming G={G} P={P} mode={mode}")
+    lens = [P * 300 + 7, P * 40, P * 2 + 1, 0, 5]
+    bt = wl.random_batch(313 + G, lens, n_q_heads=4 * G, n_kv_heads=4, head_dim=128, page_size=P,
+                         streaming=[0, 1, 1, 0], sink=P + 3, local=3 * P + 2)
+    q, kv, st = to_device(dsa, bt)
+    s32 = oracle.page_scores(bt).astype(np.float32)
+    sc = torch.from_numpy(np.ascontiguousarray(s32)).cuda()
+    ids, counts, O, l, m = (np_(x) for x in dsa.page_select_progressive(q, kv, sc, 0.9, mode, float(bt.scale),
+                                                                         streaming=st))
+    dense = [(b, h) for b in range(bt.batch) for h in (0, 3)]
+    check_psa_result(bt, s32, ids, counts, O, l, m, 0.9, mode, f"psa streaming G={G}", dense)
+    for b in range(bt.batch):
+        for h in (1, 2):
+            rid, rn, rO, rl, rm = oracle.psa_unit(bt, b, h, s32[b, h].astype(np.float64), 0.9, mode)
+            n = int(counts[b, h])
+            assert n == rn and np.array_equal(ids[b, h, :n], rid), f"streaming pages (b={b}, h={h})"
+            assert np.all(ids[b, h, n:] == -1)
+            sl = slice(h * G, (h + 1) * G)
+            check_attention("bf16", O[b, sl], l[b, sl], m[b, sl], rO, rl, rm, f"streaming (b={b}, h={h})")
+
+
+@pytest.mark.parametrize("G,P", [(4, 16), (16, 16)])
+def test_repair_streaming_heads(gpu_lib, G, P):
+    """Repair with streaming heads: spec over P and repair over A \\ P, both
+    under the token mask of a streaming head, equal attention over P u A
+    with that mask (compacted M and P-filtered forms)."""
+    dsa = gpu_lib
+    _banner(f"repair streaming G={G} P={P}")
+    lens = [P * 150 + 3, P * 64, P * 10]
+    bt = wl.random_batch(75, lens, n_q_heads=2 * G, n_kv_heads=2, head_dim=128, page_size=P,
+                         streaming=[1, 0], sink=P + 5, local=5 * P)
+    q, kv, st = to_device(dsa, bt)
+    rng = np.random.default_rng(21)
+    stride = 48
+    A = np.full((3, 2, stride), -1, np.int32)
+    Pp = np.full((3, 2, stride), -1, np.int32)
+    ac = np.zeros((3, 2), np.int32)
+    pc = np.zeros((3, 2), np.int32)
+    for b in range(3):
+        n = oracle.n_pages(lens[b], P)
+        for h in range(2):
+            a = np.sort(rng.choice(n, size=min(n, 30), replace=False))
+            p = np.sort(np.concatenate([a[:12], rng.choice(np.setdiff1d(np.arange(n), a), size=min(6, n - len(a)),
+                                                           replace=False)]))
+            A[b, h, :len(a)], ac[b, h] = a, len(a)
+            Pp[b, h, :len(p)], pc[b, h] = p, len(p)
+    t = lambda x: torch.from_numpy(x).cuda()
+    union = [[np.array(sorted(set(A[b, h, :ac[b, h]]) | set(Pp[b, h, :pc[b, h]])), np.int64) for h in range(2)]
+             for b in range(3)]
+    rO, rl, rm = oracle.sparse_decode(bt, union)
+    # P filtered inside the call
+    O, l, m = dsa.sparse_decode_attn(q, kv, t(Pp), t(pc), streaming=st)
+    dsa.attn_repair(q, kv, t(A), t(ac), t(Pp), t(pc), O, l, m, streaming=st)
+    check_attention("bf16", np_(O), np_(l), np_(m), rO, rl, rm, "repair streaming (filtered)")
+    # M compacted by the caller
+    M = np.full((3, 2, stride), -1, np.int32)
+    mc = np.zeros((3, 2), np.int32)
+    for b in range(3):
+        for h in range(2):
+            mm = np.setdiff1d(A[b, h, :ac[b, h]], Pp[b, h, :pc[b, h]])
+            M[b, h, :len(mm)], mc[b, h] = mm, len(mm)
+    O, l, m = dsa.sparse_decode_attn(q, kv, t(Pp), t(pc), streaming=st)
+    dsa.attn_repair(q, kv, t(M), t(mc), None, None, O, l, m, streaming=st)
+    check_attention("bf16", np_(O), np_(l), np_(m), rO, rl, rm, "repair streaming (compacted)")
 
 # ---------------------------------------------------------------- repair
 @pytest.mark.parametrize("G,P", [(4, 16), (16, 16), (2, 64)])

@@ -20,11 +20,11 @@ def _banner(msg):
     print(f"[case] {msg}", flush=True)
 
 
-def _compare(dsa, bt, q, kv, meta, thr, mode, what):
+def _compare(dsa, bt, q, kv, meta, thr, mode, what, st=None):
     scale = float(bt.scale)
-    s_ref = dsa.page_score(q, kv, meta)
-    ref = dsa.page_select_progressive(q, kv, s_ref, thr, mode, scale)
-    got = dsa.psa_decode(q, kv, meta, thr, mode, scale)
+    s_ref = dsa.page_score(q, kv, meta, streaming=st)
+    ref = dsa.page_select_progressive(q, kv, s_ref, thr, mode, scale, streaming=st)
+    got = dsa.psa_decode(q, kv, meta, thr, mode, scale, streaming=st)
     torch.cuda.synchronize()
     assert torch.equal(got[0], s_ref), f"{what}: scores differ"
     for name, a, b in zip(("ids", "counts", "O", "l", "m"), got[1:], ref):
@@ -71,3 +71,41 @@ def test_psa_decode_few_rows_runs_the_two_calls(gpu_lib):
     meta = dsa.page_meta_build(kv)
     for thr, mode in ((0.95, 0), (0.7, 1)):
         _compare(dsa, bt, q, kv, meta, thr, mode, f"few rows thr={thr}")
+
+
+@pytest.mark.parametrize("G,P", [(1, 16), (4, 64)])
+def test_psa_decode_streaming_heads(gpu_lib, G, P):
+    """Streaming heads (LServe section 4.1) in the fused launch: their rows
+    score -inf and their workgroups attend to the sink and local pages; the
+    result equals the two calls' bit for bit and the oracle's unit by unit."""
+    import oracle
+    dsa = gpu_lib
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    Hkv = 32
+    B = max(8, -(-n_cu // Hkv))
+    _banner(f"psa_decode streaming G={G} P={P} rows={B * Hkv}")
+    rng = np.random.default_rng(17 + G)
+    lens = [0, 5, P * 3 + 1] + [int(x) for x in rng.integers(P * 40, P * 90, size=B - 3)]
+    flags = np.zeros(Hkv, np.uint8)
+    flags[::3] = 1
+    bt = wl.random_batch(820 + G, lens, n_q_heads=Hkv * G, n_kv_heads=Hkv, head_dim=128, page_size=P,
+                         streaming=flags, sink=3 * P // 2, local=4 * P + 5)
+    q, kv, st = to_device(dsa, bt)
+    meta = dsa.page_meta_build(kv)
+    for thr, mode in ((0.95, 0), (0.6, 1)):
+        _compare(dsa, bt, q, kv, meta, thr, mode, f"streaming G={G} thr={thr}", st)
+    s32, ids, counts, O, l, m = (np_(x) for x in dsa.psa_decode(q, kv, meta, 0.9, 0, float(bt.scale), streaming=st))
+    units = [(b, h) for b in (0, 1, 2, 3, B - 1) for h in (0, 1, 3, Hkv - 1)]
+    dense = [(b, h) for b, h in units if not flags[h]]
+    check_psa_result(bt, s32, ids, counts, O, l, m, 0.9, 0, f"psa_decode streaming oracle G={G}", dense)
+    from parity_util import check_attention
+    for b, h in units:
+        if not flags[h]:
+            continue
+        assert np.all(np.isneginf(s32[b, h])), f"streaming row scores (b={b}, h={h})"
+        rid, rn, rO, rl, rm = oracle.psa_unit(bt, b, h, s32[b, h].astype(np.float64), 0.9, 0)
+        n = int(counts[b, h])
+        assert n == rn and np.array_equal(ids[b, h, :n], rid), f"streaming pages (b={b}, h={h})"
+        assert np.all(ids[b, h, n:] == -1)
+        sl = slice(h * G, (h + 1) * G)
+        check_attention("bf16", O[b, sl], l[b, sl], m[b, sl], rO, rl, rm, f"streaming (b={b}, h={h})")

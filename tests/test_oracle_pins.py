@@ -304,6 +304,24 @@ def test_streaming_head_is_masked_dense_attention():
     assert np.allclose(O[0, 1], ref1, atol=1e-12)
 
 
+def test_psa_streaming_head_is_masked_dense_attention():
+    """PSA on a batch with a streaming head: the streaming head visits its
+    sink and local pages in ascending order, never stops, and its result is
+    softmax attention over the sink and local tokens only (textbook, scipy);
+    the dense head still takes the progressive walk."""
+    bt = wl.random_batch(9, [300], n_q_heads=2, n_kv_heads=2, head_dim=16, page_size=16, streaming=[1, 0],
+                         sink=20, local=70)
+    sc = oracle.page_scores(bt)
+    ids, n, O, l, m = oracle.psa_unit(bt, 0, 0, sc[0, 0], 0.5)
+    assert list(ids) == [0, 1, 14, 15, 16, 17, 18] and n == 7   # tokens [0, 20) and [230, 300)
+    t = np.arange(300)
+    ref, _ = textbook(bt, 0, 0, mask=(t < 20) | (t >= 230))
+    assert np.allclose(O[0], ref, atol=1e-12)
+    d = oracle.psa_unit(bt, 0, 1, sc[0, 1], 0.5)
+    p = oracle.psa_progressive(bt, 0, 1, sc[0, 1], 0.5)
+    assert np.array_equal(d[0], p[0]) and d[1] == p[1] and np.allclose(d[2], p[2])
+
+
 def test_empty_set_is_merge_identity():
     O, l, m = oracle.attention(np.ones(4), np.zeros((0, 4)), np.zeros((0, 4)), 0.5)
     assert l == 0.0 and m == -math.inf and np.all(O == 0)
