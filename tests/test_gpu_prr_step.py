@@ -73,3 +73,59 @@ def test_one_call_step_equals_two_streams(gpu_lib, G, P, Pl, lens, k, D):
             mc = np_(a.m_counts)
             assert (mc <= np_(a.a_counts)).all()
         q = _drift(q0, t, 7)
+
+
+def test_one_call_step_graph_replays(gpu_lib):
+    """The one-call step captured in a HIP graph gives the eager result on
+    every replay (its state restored before each, eager work and
+    synchronisations between replays): nothing in the step depends on a
+    memory clear that a replay would not repeat."""
+    dsa = gpu_lib
+    from dynamic_sparse_attention_page_amd.prr import PRRDecoder
+    print("[case] prr one-call step graph replay", flush=True)
+    bt = wl.random_batch(431, [16 * 2500 + 9, 16 * 800], n_q_heads=32, n_kv_heads=2, head_dim=128, page_size=16)
+    q0, kv, _ = to_device(dsa, bt)
+    meta = dsa.page_meta_build(kv)
+    dec = PRRDecoder(kv, meta, 32, 256, 0.6, 0.3, 0.25, 1.0, one_stream=True)
+    dec.step(q0)                       # the plain first step
+    q1 = _drift(q0, 0, 3)
+    state = ("level", "trend", "pred")
+    saved = {n: getattr(dec, n).clone() for n in state}
+    saved_p = [x.clone() for x in dec._p[dec._cur]]
+    cur = dec._cur
+
+    def restore():
+        for n in state:
+            getattr(dec, n).copy_(saved[n])
+        for dst, src in zip(dec._p[cur], saved_p):
+            dst.copy_(src)
+        dec._cur = cur
+        dec.t = 1
+
+    restore()
+    dec.step(q1)
+    torch.cuda.synchronize()
+    outs = ("scores", "level", "trend", "pred", "a_ids", "a_counts", "m_ids", "m_counts", "O", "l", "m")
+    ref = {n: getattr(dec, n).clone() for n in outs}
+    ref_p = [x.clone() for x in dec._p[1 - cur]]
+    restore()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            dec.step(q1)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        restore()
+        for n in ("scores", "O", "l", "m"):
+            getattr(dec, n).fill_(float("nan"))
+        for n in ("a_ids", "m_ids"):
+            getattr(dec, n).fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for n in outs:
+            assert _same(getattr(dec, n), ref[n]), f"replay {rep}: {n}"
+        assert all(_same(x, y) for x, y in zip(dec._p[1 - cur], ref_p)), f"replay {rep}: P^(t+1)"
+        _ = (torch.randn(1000, device="cuda") * 2).sum().item()   # eager work between replays
