@@ -447,7 +447,9 @@ __global__ __launch_bounds__(256) void attn_partial_mfma_kernel(
 // (m, l) pairs, one per lane, and turns them into merge weights against the
 // running maximum (wave reductions, no barrier), and after one barrier every
 // thread folds its values.  So a chunk costs one memory round trip, and
-// rows of up to 64 splits (every top-k and repair call here) exactly one.
+// rows of up to 64 splits exactly one.  (Chunks of 128 measured slower on
+// the whole: a round trip fewer for rows of 65-128 splits, but twice the
+// loads per thread for every row.)
 // For repair the caller's (O, l, m) is one more term.  Writes normalised O.
 template <int D>
 __device__ __forceinline__ void attn_combine_body(

@@ -25,6 +25,7 @@ CASES = [
     (4, 16, 16, [16 * 4000 + 3, 16 * 900], 512, 128),
     (4, 16, 16, [16 * 8000] * 4, 1024, 128),
     (2, 32, 32, [32 * 600 + 17, 32 * 5], 100, 64),
+    (1, 16, 16, [16 * 2000 + 7, 16 * 30], 128, 128),   # one q head per KV head
     # an empty sequence and one of a single partial page beside a long one
     (16, 16, 16, [0, 16 * 300 + 1, 5], 64, 128),
     (4, 16, 16, [5, 0, 16 * 700], 128, 128),
