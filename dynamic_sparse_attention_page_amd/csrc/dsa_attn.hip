@@ -1088,7 +1088,8 @@ __global__ __launch_bounds__((psa_waves<T, G>() * 64)) void psa_kernel(
 // on one CU).  The scores are the page_score kernel's, operation for
 // operation (group-mean query split by sign, kmax / kmin terms in channel
 // order, DPP row sum), so both paths select the same pages; they are also
-// written to global memory.  Page-table row and scores live in dynamic LDS.
+// written to global memory, after the walk.  Page-table row and scores live
+// in dynamic LDS.
 constexpr int kPsaFusedMaxPages = 8192;
 #ifndef DSA_PSA_FUSED_LOADS
 #define DSA_PSA_FUSED_LOADS 8
@@ -1176,15 +1177,15 @@ __global__ __launch_bounds__((psa_waves<T, G>() * 64)) void psa_fused_kernel(
       }
       float sc = row_sum(part);
       if (!ok[uu]) sc = kNegInf;
-      if (cg == 0 && jj[uu] < max_pages) {
-        s_score[jj[uu]] = sc;
-        sg[jj[uu]] = sc;
-      }
+      if (cg == 0 && jj[uu] < max_pages) s_score[jj[uu]] = sc;
     }
   }
   __syncthreads();
   psa_body<T, D, G, E>(q, k, v, s_score, s_slot, L, h, b, n_kv_heads, P, max_pages, num_slots, stop_mode,
                        never_stop, always_stop, ln_odds, scale, c, ids, counts, O, l, m);
+  // the row's scores leave LDS once, coalesced, after the walk: the scoring
+  // loads then share the memory system with no scattered 4-byte stores
+  for (int x = tid; x < max_pages; x += NT) sg[x] = s_score[x];
 }
 
 // ============================================================ PRR step on one stream
