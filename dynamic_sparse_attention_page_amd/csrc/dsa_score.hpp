@@ -1,5 +1,6 @@
 // Page criticality scores (LServe, section 4.2; PRR, section 5 for the
-// GQA query; PRR, section 3.1 for the EMA update in the writing lane):
+// GQA query; PRR, section 3.1 for the EMA update, done by the lane that
+// holds the page's state):
 // the score workgroup as a device function, its grid, and its tuning
 // constants, shared by the score kernel and kernels that run score
 // workgroups beside other work.
@@ -100,6 +101,15 @@ __device__ __forceinline__ void score_body(
   const int r = lane >> 4, cg = lane & 15;
   // slots of this wave's pages (pages_per_wave <= 64)
   const int my_slot = (j0 + lane < min(j1, np)) ? page_table[(size_t)b * max_pages + j0 + lane] : -1;
+  // lane i keeps page j0 + i's EMA state, loaded now and updated at the end
+  float my_level = 0.0f, my_trend = 0.0f;
+  if (ema.level && !ema.init && j0 + lane < j1) {
+    my_level = ema.level[rowbase + j0 + lane];
+    my_trend = ema.trend[rowbase + j0 + lane];
+  }
+  // the wave's scores, one per page, gathered here and written once at the
+  // end: one coalesced store per output row instead of a 4-byte store per page
+  __shared__ float s_wave_sc[4][64];
   // group-mean query, this lane's channels, split by sign
   float qpos[CPL], qneg[CPL];
   {
@@ -164,7 +174,7 @@ __device__ __forceinline__ void score_body(
         sc = fmaxf(sc, __shfl_xor(sc, 32, 64));                                                     // rows ^2
       }
       const bool writer = cg == 0 && (r % GL) == 0;
-      if (writer && j0 + pl < j1) put(j0 + pl, sc);
+      if (writer && j0 + pl < j1) s_wave_sc[wave][pl] = sc;
     }
   };
 #if DSA_SCORE_PIPE
@@ -187,6 +197,23 @@ __device__ __forceinline__ void score_body(
     consume(u0, wmin, wmax, ok);
   }
 #endif
+  // every page of [j0, j1) was scored by one writer lane of this wave
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  if (j0 + lane < j1) {
+    const int j = j0 + lane;
+    const float sc = s_wave_sc[wave][lane];
+    srow[j] = sc;
+    if (ema.level) {
+      const size_t x = rowbase + j;
+      float nl = sc, nt = 0.0f, pr = sc;
+      if (!ema.init) ema_step(sc, my_level, my_trend, ema.alpha, ema.beta, ema.gamma, nl, nt, pr);
+      ema.level[x] = nl;
+      ema.trend[x] = nt;
+      ema.pred[x] = pr;
+    }
+  }
 }
 
 
